@@ -1,0 +1,200 @@
+"""Benchmark of the KDA forward prefill on one MI355X.
+
+One step = one kda_prefill call over the whole packed batch (every kernel of
+the path: K1 + K2, or K1 + pre_scan + merge + segment-K2), inputs resident in
+HBM. Prints one JSON line: tokens/s, the roofline of the path's kernels
+measured with HIP events on the launch stream, and the CPU oracle timed on the
+host cores as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload varlen8_h32]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/sec (H=32, D=128, bf16) + % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+# Algorithmic work per token-head of the path (D = 128, chunk 16):
+#   bytes: q 256 + k 256 + v 256 (bf16) + g 512 (fp32) + beta 4 + o 256 (bf16)
+#   flops: K1 16384 (four 16x16x128 products per chunk) + K2 102400
+#          (three 16x128x128 products plus one 16x16x128 per chunk)
+BYTES_PER_TOKEN_HEAD = 1540
+FLOPS_PER_TOKEN_HEAD = 118784
+STATE_BYTES = 128 * 128 * 4
+
+WORKLOAD_TEXT = {
+    "varlen8_h32": "8 packed sequences, lengths uniform in [512, 4096] (seed 1002), H=32, D=128, "
+                   "bf16 q/k/v, fp32 g=-softplus(N(0,1)) and beta=sigmoid(N(0,1)), fp32 initial "
+                   "state N(0, 0.1), fp32 final state",
+    "long65536_h8": "one 65536-token sequence, H=8, D=128, initial state N(0, 0.1)",
+    "batch16x8192_h64": "16 sequences x 8192 tokens, H=64, D=128, g=-softplus(2 N(0,1)), zero "
+                        "initial state",
+}
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("kda_device.hpp", "kda_kernels.hip", "kda_launch.h"):
+        with open(os.path.join(ROOT, "kda_chunked_delta_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, digest):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    measurement was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_digest") != digest:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(d, max_seconds):
+    """The fp64 C oracle (plain per-token recurrence, OpenMP) on a bounded
+    sample: whole sequences, all heads, added in order until the estimated
+    time reaches max_seconds."""
+    from oracle import reference as ref
+    cu = d["cu_seqlens_host"]
+    H = d["H"]
+    threads = ref.c_max_threads()
+    # probe speed on the first 256 tokens of sequence 0 (all heads)
+    n_probe = min(256, cu[1] - cu[0])
+    sl = lambda x, a, b: x[a:b]
+    probe = [sl(d[k], 0, n_probe) for k in ("q", "k", "v", "g", "beta")]
+    t = time.time()
+    ref.recurrent_c(*probe, [0, n_probe], None)
+    rate = n_probe * H / max(time.time() - t, 1e-6)  # token-heads / s
+    budget = max_seconds * rate
+    nseq = 0
+    while nseq < len(cu) - 1 and (cu[nseq + 1] - cu[0]) * H <= budget:
+        nseq += 1
+    nseq = max(nseq, 1)
+    T = cu[nseq]
+    args = [sl(d[k], 0, T) for k in ("q", "k", "v", "g", "beta")]
+    s0 = d["initial_state"][:nseq] if d["initial_state"] is not None else None
+    t = time.time()
+    ref.recurrent_c(*args, cu[:nseq + 1], s0)
+    dt = time.time() - t
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d sequences (%d tokens), all %d heads; per-token fp64 recurrence "
+                      "in C, OpenMP over (sequence, head, 32-column block); %.1f s"
+                      % (nseq, len(cu) - 1, T, H, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="varlen8_h32", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--cp", default="auto", choices=["auto", "on", "off"])
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="target duration of the CPU-oracle baseline sample (0 disables it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+              "(the path shards by sequence or head with no communication, see DESIGN.md)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kda_chunked_delta_amd as kda
+    from kda_inputs import workload
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    d = workload(args.workload, device=dev)
+    H, cu = d["H"], d["cu_seqlens_host"]
+    Tt, N = cu[-1], len(cu) - 1
+    mode = {"auto": "auto", "on": True, "off": False}[args.cp]
+    plan = kda.plan(cu, H, mode, device=dev)
+    info = plan.info()
+    s0 = d["initial_state"]
+    s_out = torch.empty(N, H, 128, 128, dtype=torch.float32, device=dev)
+    o = torch.empty_like(d["q"])
+
+    def step():
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                    cu_seqlens_host=cu, initial_state=s0, final_state=s_out, out=o, plan=plan)
+
+    print("bench: workload %s Tt=%d H=%d plan=%s units=%d" % (args.workload, Tt, H,
+          "cp" if info["uses_cp"] else "serial", info["n_units"]), file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ctx = kda.context(dev)
+    ctx.set_timing(True)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    per_kernel = ctx.timing()
+    ctx.set_timing(False)
+    print("bench: %.3f ms/step; kernels %s" % (ms_step, {k: round(v[0] / v[1], 4) for k, v in per_kernel.items()}),
+          file=sys.stderr, flush=True)
+
+    token_heads = Tt * H
+    alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD + N * H * STATE_BYTES * (2 if s0 is not None else 1)
+    alg_flops = token_heads * FLOPS_PER_TOKEN_HEAD
+    kern_ms = {k: v[0] / v[1] for k, v in per_kernel.items()}
+    path_ms = sum(v[0] for v in per_kernel.values()) / args.steps  # all kernels of one step
+    dominant = max(kern_ms, key=lambda k: per_kernel[k][0])
+    names = "+".join(per_kernel.keys())
+    achieved = alg_bytes / (path_ms * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = traffic_from_profiles(names, digest)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": names, "dominant": dominant, "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+                "alg_bytes_per_step": alg_bytes, "source_digest": digest}
+    mfma_frac = alg_flops / (path_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+
+    line = {
+        "metric": METRIC,
+        "value": round(Tt / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %s" % (args.workload, WORKLOAD_TEXT[args.workload]), "tokens": Tt,
+                   "heads": H, "head_dim": 128, "sequences": N, "lengths": d["lengths"],
+                   "plan": "cp" if info["uses_cp"] else "serial", "cp_mode": args.cp},
+        "roofline": roofline,
+        "mfma_roofline": {"bound": "mfma", "achieved": round(alg_flops / (path_ms * 1e-3) / 1e12, 2),
+                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4)},
+    }
+    if args.cpu_seconds > 0:
+        print("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

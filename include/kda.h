@@ -1,0 +1,201 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA forward-prefill library.
+ *
+ * Operation. Kimi Delta Attention (KDA) forward prefill: for every packed
+ * sequence and head, the gated delta rule with per-key-channel decay
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
+ *   o_t = scale * S_t^T q_t,
+ * computed in chunked form as the two kernels named in the commit summary of
+ * "feat(kda/sm90): FlashKDA prefill port + intracard-CP prefill" (cuLA pull
+ * request #103): K1 prepares decayed q/k, beta and the WY inverse per 16-token
+ * chunk, K2 runs the inter-chunk recurrence (CHUNK = 16, D = 128, forward
+ * only). The same commit summary defines the intracard context-parallel mode
+ * (K1 once, then pre_scan, merge of segment carries, segment-K2; bit-identical
+ * to serial), and its description the FLA-compatible prefill API with varlen
+ * packing, initial/final state and a workspace arena reused across calls; its
+ * reviewer notes say the planner returns the plan the executor runs, a trivial
+ * plan meaning serial.
+ *
+ * Conventions shared by every entry point:
+ *  - Packed token-major layouts, contiguous, row-major:
+ *      q, k, out : bf16 [Tt, H, 128]      v : bf16 [Tt, H, 128]
+ *      g         : fp32 [Tt, H, 128]  raw per-token log-decay (g <= 0 expected;
+ *                  the in-chunk cumulative sum is taken by the library)
+ *      beta      : fp32 [Tt, H]
+ *      states    : fp32 [N, H, 128 (key channel), 128 (value channel)]
+ *      cu_seqlens: int32 [N + 1], 0 = cu[0] <= cu[1] <= ... <= cu[N] = Tt
+ *    Device pointers must be 16-byte aligned (states: 4-byte aligned).
+ *  - Ownership: the caller owns every tensor, stream and plan. The context
+ *    owns only its workspace arenas (one per stream), which it frees in
+ *    kda_destroy.
+ *  - Errors: every check runs on the host before any launch, so nothing is
+ *    written on error. Functions return a kda_status; kda_last_error() gives
+ *    a message for the calling thread's most recent failure.
+ *  - Asynchrony: kda_prefill only enqueues work on `stream` and never
+ *    synchronises, except when it must grow the stream's workspace arena (a
+ *    device synchronise, refused with KDA_ERR_CAPTURE while the stream is
+ *    being captured into a graph).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID = 1,     /* bad shape, size, pointer, alignment or argument */
+    KDA_ERR_UNSUPPORTED = 2, /* a head dimension other than 128 */
+    KDA_ERR_ALIAS = 3,       /* forbidden overlap between buffers */
+    KDA_ERR_CAPTURE = 4,     /* would allocate or synchronise during graph capture */
+    KDA_ERR_HIP = 5          /* a HIP runtime call failed */
+} kda_status;
+
+/* Intracard context parallelism (the use_intracard_cp switch of the cuLA pull
+ * request's description): off, forced on, or decided by the planner. */
+typedef enum { KDA_CP_OFF = 0, KDA_CP_ON = 1, KDA_CP_AUTO = 2 } kda_cp_mode;
+
+typedef struct kda_ctx kda_ctx;
+typedef struct kda_plan kda_plan;
+
+/* Summary of a plan, for inspection and tests. */
+typedef struct {
+    int32_t n_seqs, H, dk, dv;
+    int64_t total_tokens;
+    int32_t total_chunks;      /* sum over sequences of ceil(L_i / 16) */
+    int32_t uses_cp;           /* 0 = trivial plan (serial), 1 = segmented */
+    int32_t n_units;           /* K2 work units (sequences or segments) */
+    int32_t n_cp_seqs;         /* sequences split into more than one segment */
+    int32_t n_prescan;         /* segments that get a pre_scan summary */
+    int32_t n_carry_slots;     /* carries kept for segmented sequences */
+    int32_t max_unit_chunks;   /* longest serial chain of the plan, in chunks */
+    int32_t n_cus;             /* compute units the plan was made for */
+    size_t  workspace_bytes;   /* arena bytes kda_prefill needs for this plan */
+    double  est_serial_us;     /* planner's cost estimate of the serial path */
+    double  est_cp_us;         /* planner's cost estimate of the segmented path */
+} kda_plan_info;
+
+/* One K2 work unit of a plan (a whole sequence, or one segment of it). */
+typedef struct {
+    int32_t seq;          /* sequence index */
+    int32_t chunk0;       /* first chunk of the unit within its sequence */
+    int32_t n_chunks;     /* chunks in the unit (0 for an empty sequence) */
+    int32_t segment;      /* segment index within its sequence (0 if serial) */
+    int32_t n_segments;   /* segments of its sequence (1 if serial) */
+} kda_unit_info;
+
+/* Create a context on HIP device `device`: caches the device properties
+ * (compute-unit count) once. Returns KDA_ERR_HIP if the device is unusable. */
+kda_status kda_create(int device, kda_ctx **out);
+
+/* Wait for the device, free every workspace arena and the context. NULL is a
+ * no-op. */
+void kda_destroy(kda_ctx *ctx);
+
+/* Message of the calling thread's most recent failure ("" if none). */
+const char *kda_last_error(void);
+
+/* Library version string. */
+const char *kda_version(void);
+
+/* Build the plan for one packed batch: chunk table, K2 work units ordered
+ * longest chain first, and -- when `mode` asks for it, or AUTO predicts a win
+ * for the device's compute-unit count -- chunk-aligned segments for intracard
+ * CP. cu_seqlens_host: host int32 [n_seqs + 1]. dk and dv must be 128.
+ * The plan keeps its tables in device memory of ctx's device (uploaded here,
+ * synchronously; do not call while a stream of that device is being
+ * captured). The caller frees it with kda_plan_destroy. */
+kda_status kda_plan_prefill(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
+                            int32_t H, int32_t dk, int32_t dv, kda_cp_mode mode,
+                            kda_plan **out);
+
+/* The same planning for an explicit compute-unit count, host only (no device
+ * tables; such a plan can be inspected but not executed). Needs no GPU. */
+kda_status kda_plan_prefill_host(int32_t n_cus, const int32_t *cu_seqlens_host, int32_t n_seqs,
+                                 int32_t H, int32_t dk, int32_t dv, kda_cp_mode mode,
+                                 kda_plan **out);
+
+/* A segmented plan with an explicit segment length: every sequence longer
+ * than seg_chunks chunks is cut into chunk-aligned segments of seg_chunks
+ * chunks (the last may be shorter) and run through pre_scan, merge and
+ * segment-K2 -- the forced-CP mode of the cuLA pull request's tests. Device
+ * tables are uploaded as in kda_plan_prefill. */
+kda_status kda_plan_prefill_segments(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
+                                     int32_t H, int32_t dk, int32_t dv, int32_t seg_chunks,
+                                     kda_plan **out);
+
+void kda_plan_destroy(kda_plan *plan);
+
+/* Plan summary; returns KDA_ERR_INVALID for NULL arguments. */
+kda_status kda_plan_get_info(const kda_plan *plan, kda_plan_info *info);
+
+/* Copy up to `max_units` unit descriptors, in launch order. */
+kda_status kda_plan_get_units(const kda_plan *plan, kda_unit_info *units, int32_t max_units);
+
+/* Check a prefill call's arguments against the plan without launching
+ * anything (the same checks kda_prefill runs first). Pointers are compared as
+ * addresses only and never dereferenced. Needs no GPU. */
+kda_status kda_prefill_validate(const kda_plan *plan, const void *q, const void *k,
+                                const void *v, const float *g, const float *beta,
+                                const int32_t *cu_seqlens_dev, float scale,
+                                const float *initial_state, const float *final_state,
+                                const void *out);
+
+/* Run the forward prefill described by `plan` on `stream`.
+ *   q, k, v, out : bf16 [Tt, H, 128] (device)
+ *   g, beta      : fp32 [Tt, H, 128], [Tt, H] (device)
+ *   cu_seqlens_dev: int32 [N + 1] (device), the same values the plan was
+ *                  built from
+ *   scale        : multiplies every output (1.0 for the plain recurrence)
+ *   initial_state: fp32 [N, H, 128, 128] or NULL (zero state)
+ *   final_state  : fp32 [N, H, 128, 128] or NULL (not written); may equal
+ *                  initial_state (updated in place) but may not partly
+ *                  overlap it; may not overlap any input or out
+ *   out          : may not overlap any input or state
+ * Serial plans launch K1 (per chunk) then K2 (per unit); segmented plans
+ * launch K1, pre_scan, merge and segment-K2. Results of a segmented plan are
+ * bitwise equal to the serial plan's whenever the carried-in state is
+ * forgotten within a segment (strong decay); otherwise equal within fp32
+ * rounding. */
+kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const void *k,
+                       const void *v, const float *g, const float *beta,
+                       const int32_t *cu_seqlens_dev, float scale, const float *initial_state,
+                       float *final_state, void *out, hipStream_t stream);
+
+/* K1 alone, for inspection and tests: write every chunk record of the plan
+ * into `records` (device, total_chunks * H * KDA_RECORD_BYTES bytes, record
+ * of (chunk c, head h) at index h * total_chunks + c; layout in
+ * KDA_RECORD_* below). Arguments as in kda_prefill. */
+#define KDA_RECORD_BYTES 17408
+/* Record layout (lane l of a 64-wide wavefront: gg = l / 16, m = l % 16;
+ * dkperm(p, gg, j) = 32p + 16(j / 4) + 4gg + j % 4):
+ *   [0, 4096)      Qt = q * exp(G): bf16 [p 4][lane 64][j 8] = Qt[m][dkperm(p, gg, j)]
+ *   [4096, 8192)   W (WY keys):     same layout as Qt
+ *   [8192, 12288)  Kt = k * exp(G_C - G): bf16 [t 8][lane 64][j 4] = Kt[4gg + j][16t + m]
+ *   [12288, 16384) U~ (WY values):  bf16 [n 8][lane 64][j 4] = U~[4gg + j][16n + m]
+ *   [16384, 16896) A_qk (i <= r):   bf16 [lane 64][j 4] = A_qk[m][4gg + j]
+ *   [16896, 17408) exp(G_C):        fp32 [128]
+ */
+kda_status kda_debug_k1_records(kda_ctx *ctx, const kda_plan *plan, const void *q, const void *k,
+                                const void *v, const float *g, const float *beta,
+                                const int32_t *cu_seqlens_dev, void *records, hipStream_t stream);
+
+/* Per-kernel timing of kda_prefill calls on this context: while enabled,
+ * every call records HIP events around each of its launches on its stream.
+ * kda_get_timing waits for all recorded events, and returns, per kernel name
+ * (in order of first launch), the summed elapsed milliseconds and the number
+ * of launches since the previous kda_get_timing or kda_set_timing call; it
+ * then clears the log. Returns the number of names (<= max), or -1 on error. */
+kda_status kda_set_timing(kda_ctx *ctx, int enable);
+int32_t kda_get_timing(kda_ctx *ctx, const char **names, double *total_ms, int32_t *launches,
+                       int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

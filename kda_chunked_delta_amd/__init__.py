@@ -1,0 +1,353 @@
+"""KDA forward prefill on MI355X (gfx950): Python binding of libkda.so.
+
+Argument marshalling only: every step of the prefill runs in the library's HIP
+kernels, reached through the C ABI of include/kda.h. PyTorch provides device
+memory and the current HIP stream. There is no fallback: if the library is not
+built, every entry point raises.
+
+    import kda_chunked_delta_amd as kda
+    o, s = kda.prefill(q, k, v, g, beta, cu_seqlens=cu, initial_state=s0,
+                       output_final_state=True, use_intracard_cp="auto")
+
+The interface follows the FLA-compatible prefill of "feat(kda/sm90): FlashKDA
+prefill port + intracard-CP prefill" (cuLA pull request #103, description:
+varlen packing, initial/final state, use_intracard_cp = "auto" | True | False,
+default off) and the in-place state update exercised by "fix(cake_kda):
+support non-aligned recurrent prefill head counts" (FlashInfer pull request
+#4351, description).
+"""
+from __future__ import annotations
+
+import atexit
+import collections
+import ctypes
+import os
+import threading
+
+__all__ = ["prefill", "plan", "plan_host", "plan_segments", "Plan", "Context", "context",
+           "KDAError", "lib", "LIB_PATH", "CP_OFF", "CP_ON", "CP_AUTO"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+D = 128
+CP_OFF, CP_ON, CP_AUTO = 0, 1, 2
+
+
+class KDAError(RuntimeError):
+    """A libkda call returned an error status."""
+
+    def __init__(self, status, message):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("total_tokens", ctypes.c_int64),
+                ("total_chunks", ctypes.c_int32), ("uses_cp", ctypes.c_int32),
+                ("n_units", ctypes.c_int32), ("n_cp_seqs", ctypes.c_int32),
+                ("n_prescan", ctypes.c_int32), ("n_carry_slots", ctypes.c_int32),
+                ("max_unit_chunks", ctypes.c_int32), ("n_cus", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t), ("est_serial_us", ctypes.c_double),
+                ("est_cp_us", ctypes.c_double)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class UnitInfo(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("chunk0", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
+                ("segment", ctypes.c_int32), ("n_segments", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """The loaded libkda.so (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError("libkda.so is not built (%s); run `python -m kda_chunked_delta_amd.build`"
+                                  % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+            PP = ctypes.POINTER(ctypes.c_void_p)
+            sig = {
+                "kda_create": (ctypes.c_int, [ctypes.c_int, PP]),
+                "kda_destroy": (None, [P]),
+                "kda_last_error": (ctypes.c_char_p, []),
+                "kda_version": (ctypes.c_char_p, []),
+                "kda_plan_prefill": (ctypes.c_int, [P, P, I32, I32, I32, I32, ctypes.c_int, PP]),
+                "kda_plan_prefill_host": (ctypes.c_int, [I32, P, I32, I32, I32, I32, ctypes.c_int, PP]),
+                "kda_plan_prefill_segments": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, PP]),
+                "kda_plan_destroy": (None, [P]),
+                "kda_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(PlanInfo)]),
+                "kda_plan_get_units": (ctypes.c_int, [P, ctypes.POINTER(UnitInfo), I32]),
+                "kda_prefill_validate": (ctypes.c_int, [P, P, P, P, P, P, P, F32, P, P, P]),
+                "kda_prefill": (ctypes.c_int, [P, P, P, P, P, P, P, P, F32, P, P, P, P]),
+                "kda_debug_k1_records": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
+                "kda_set_timing": (ctypes.c_int, [P, ctypes.c_int]),
+                "kda_get_timing": (I32, [P, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(I32), I32]),
+            }
+            for name, (res, args) in sig.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+        return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        raise KDAError(status, "%s: %s" % (what, lib().kda_last_error().decode()))
+
+
+def _cp_mode(use_intracard_cp):
+    if use_intracard_cp is False or use_intracard_cp is None or use_intracard_cp == CP_OFF:
+        return CP_OFF
+    if use_intracard_cp is True or use_intracard_cp == CP_ON:
+        return CP_ON
+    if use_intracard_cp == "auto" or use_intracard_cp == CP_AUTO:
+        return CP_AUTO
+    raise ValueError("use_intracard_cp must be 'auto', True or False (got %r)" % (use_intracard_cp,))
+
+
+def _cu_array(cu):
+    cu = [int(x) for x in cu]
+    return (ctypes.c_int32 * len(cu))(*cu), len(cu) - 1
+
+
+class Context:
+    """A libkda context on one device (device properties cached once)."""
+
+    def __init__(self, device_index):
+        self.device = int(device_index)
+        h = ctypes.c_void_p()
+        _check(lib().kda_create(self.device, ctypes.byref(h)), "kda_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().kda_destroy(self.handle)
+            self.handle = None
+
+    def set_timing(self, enable=True):
+        _check(lib().kda_set_timing(self.handle, int(bool(enable))), "kda_set_timing")
+
+    def timing(self):
+        """{kernel name: (total ms, launches)} of the prefill calls since the
+        last read (waits for them; clears the log)."""
+        names = (ctypes.c_char_p * 16)()
+        ms = (ctypes.c_double * 16)()
+        cnt = (ctypes.c_int32 * 16)()
+        n = lib().kda_get_timing(self.handle, names, ms, cnt, 16)
+        if n < 0:
+            raise KDAError(5, "kda_get_timing: " + lib().kda_last_error().decode())
+        return {names[i].decode(): (ms[i], cnt[i]) for i in range(n)}
+
+
+_contexts = {}
+_ctx_lock = threading.Lock()
+
+
+def context(device=None):
+    """The shared Context of a torch device (default: the current device)."""
+    import torch
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    with _ctx_lock:
+        ctx = _contexts.get(idx)
+        if ctx is None:
+            ctx = _contexts[idx] = Context(idx)
+        return ctx
+
+
+_shutting_down = False
+
+
+@atexit.register
+def _close_contexts():
+    global _shutting_down
+    _plan_cache.clear()
+    _shutting_down = True
+    for ctx in list(_contexts.values()):
+        try:
+            ctx.close()
+        except Exception:
+            pass
+    _contexts.clear()
+
+
+class Plan:
+    """A libkda plan (chunk table, work units, CP segments)."""
+
+    def __init__(self, handle, cu_host, device=None):
+        self.handle = handle
+        self.cu_host = list(cu_host)
+        self.device = device
+        self._cu_dev = None
+
+    def __del__(self):
+        try:
+            if self.handle and _lib is not None and not _shutting_down:
+                _lib.kda_plan_destroy(self.handle)
+        except Exception:
+            pass
+        self.handle = None
+
+    def info(self):
+        pi = PlanInfo()
+        _check(lib().kda_plan_get_info(self.handle, ctypes.byref(pi)), "kda_plan_get_info")
+        return pi.as_dict()
+
+    def units(self):
+        n = self.info()["n_units"]
+        arr = (UnitInfo * max(n, 1))()
+        _check(lib().kda_plan_get_units(self.handle, arr, n), "kda_plan_get_units")
+        return [dict(seq=u.seq, chunk0=u.chunk0, n_chunks=u.n_chunks, segment=u.segment,
+                     n_segments=u.n_segments) for u in arr[:n]]
+
+    def cu_device(self):
+        import torch
+        if self._cu_dev is None:
+            self._cu_dev = torch.tensor(self.cu_host, dtype=torch.int32, device="cuda:%d" % self.device)
+        return self._cu_dev
+
+
+def plan_host(cu_seqlens, H, n_cus, use_intracard_cp=False):
+    """Host-only plan for an explicit CU count (inspection; no GPU needed)."""
+    arr, n = _cu_array(cu_seqlens)
+    h = ctypes.c_void_p()
+    _check(lib().kda_plan_prefill_host(int(n_cus), arr, n, int(H), D, D, _cp_mode(use_intracard_cp),
+                                       ctypes.byref(h)), "kda_plan_prefill_host")
+    return Plan(h, cu_seqlens)
+
+
+def plan(cu_seqlens, H, use_intracard_cp=False, device=None):
+    """Executable plan on a device (tables uploaded to it)."""
+    ctx = context(device)
+    arr, n = _cu_array(cu_seqlens)
+    h = ctypes.c_void_p()
+    _check(lib().kda_plan_prefill(ctx.handle, arr, n, int(H), D, D, _cp_mode(use_intracard_cp),
+                                  ctypes.byref(h)), "kda_plan_prefill")
+    return Plan(h, cu_seqlens, ctx.device)
+
+
+def plan_segments(cu_seqlens, H, seg_chunks, device=None):
+    """Executable CP plan with a forced segment length (in 16-token chunks)."""
+    ctx = context(device)
+    arr, n = _cu_array(cu_seqlens)
+    h = ctypes.c_void_p()
+    _check(lib().kda_plan_prefill_segments(ctx.handle, arr, n, int(H), D, D, int(seg_chunks),
+                                           ctypes.byref(h)), "kda_plan_prefill_segments")
+    return Plan(h, cu_seqlens, ctx.device)
+
+
+_plan_cache = collections.OrderedDict()
+_PLAN_CACHE_MAX = 64
+
+
+def _cached_plan(cu_host, H, mode, device):
+    key = (device, tuple(cu_host), H, mode)
+    p = _plan_cache.get(key)
+    if p is None:
+        p = plan(cu_host, H, mode, device="cuda:%d" % device)
+        _plan_cache[key] = p
+        if len(_plan_cache) > _PLAN_CACHE_MAX:
+            _plan_cache.popitem(last=False)
+    else:
+        _plan_cache.move_to_end(key)
+    return p
+
+
+def k1_records(q, k, v, g, beta, plan):
+    """Run K1 alone and return its chunk records as a uint8 tensor
+    [H, total_chunks, RECORD_BYTES] (layout documented in include/kda.h)."""
+    import torch
+    info = plan.info()
+    rec = torch.empty(info["H"], info["total_chunks"], RECORD_BYTES, dtype=torch.uint8, device=q.device)
+    ctx = context(q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().kda_debug_k1_records(ctx.handle, plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(plan.cu_device()), _ptr(rec), ctypes.c_void_p(stream)),
+           "kda_debug_k1_records")
+    return rec
+
+
+RECORD_BYTES = 17408
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=False,
+            use_intracard_cp=False, scale=1.0, final_state=None, out=None, plan=None,
+            cu_seqlens_host=None):
+    """KDA forward prefill.
+
+    q, k, v: bf16 [Tt, H, 128] packed, or [B, T, H, 128] (B equal-length
+    sequences when cu_seqlens is None); g: fp32 log-decay, same shape;
+    beta: fp32 [Tt, H] (or [B, T, H]). cu_seqlens: int32 [N + 1] (device
+    tensor, host list, or None). initial_state: fp32 [N, H, 128, 128] or None.
+    final_state: a tensor to write the final state into (may be
+    initial_state: in-place update); with output_final_state=True and no
+    final_state, a new one is allocated. Returns (o, final_state or None).
+    """
+    import torch
+    if q.dim() == 4:
+        B, T = q.shape[0], q.shape[1]
+        if cu_seqlens is None and cu_seqlens_host is None:
+            cu_seqlens_host = [i * T for i in range(B + 1)]
+        elif B != 1:
+            raise ValueError("4-D inputs with cu_seqlens must have batch size 1")
+        flat = lambda x: x.reshape(B * T, *x.shape[2:])
+        o, s = prefill(flat(q), flat(k), flat(v), flat(g), flat(beta), cu_seqlens, initial_state,
+                       output_final_state, use_intracard_cp, scale, final_state,
+                       None if out is None else flat(out), plan, cu_seqlens_host)
+        return o.view(q.shape), s
+    if q.dim() != 3 or q.shape[-1] != D:
+        raise ValueError("q must be [Tt, H, 128] or [B, T, H, 128], got %s" % (tuple(q.shape),))
+    Tt, H = q.shape[0], q.shape[1]
+    for name, t, dt, shape in (("q", q, torch.bfloat16, (Tt, H, D)), ("k", k, torch.bfloat16, (Tt, H, D)),
+                               ("v", v, torch.bfloat16, (Tt, H, D)), ("g", g, torch.float32, (Tt, H, D)),
+                               ("beta", beta, torch.float32, (Tt, H))):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous %s CUDA tensor of shape %s (got %s %s)"
+                             % (name, dt, shape, t.dtype, tuple(t.shape)))
+    dev = q.device.index
+    if cu_seqlens_host is None:
+        if cu_seqlens is None:
+            cu_seqlens_host = [0, Tt]
+        elif isinstance(cu_seqlens, (list, tuple)):
+            cu_seqlens_host = list(cu_seqlens)
+        else:
+            cu_seqlens_host = cu_seqlens.tolist()  # host copy for the planner (synchronises)
+    if plan is None:
+        plan = _cached_plan(cu_seqlens_host, H, _cp_mode(use_intracard_cp), dev)
+    if cu_seqlens is None or isinstance(cu_seqlens, (list, tuple)):
+        cu_dev = plan.cu_device()
+    else:
+        cu_dev = cu_seqlens
+        if cu_dev.dtype != torch.int32 or not cu_dev.is_cuda:
+            raise ValueError("cu_seqlens must be an int32 CUDA tensor")
+    N = len(cu_seqlens_host) - 1
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, H, D, D)
+                              or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("%s must be a contiguous fp32 CUDA tensor of shape %s" % (name, (N, H, D, D)))
+    if out is None:
+        out = torch.empty_like(q)
+    if final_state is None and output_final_state:
+        final_state = torch.empty(N, H, D, D, dtype=torch.float32, device=q.device)
+    ctx = context(q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().kda_prefill(ctx.handle, plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state), _ptr(out),
+                             ctypes.c_void_p(stream)), "kda_prefill")
+    return out, final_state

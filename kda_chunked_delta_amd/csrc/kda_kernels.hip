@@ -1,0 +1,279 @@
+// HIP kernels of the KDA forward prefill for gfx950: K1 (chunk preparation),
+// K2 (inter-chunk recurrence, serial or per CP segment), and the intracard
+// context-parallel pre_scan and merge named in the commit summary of
+// "feat(kda/sm90): FlashKDA prefill port + intracard-CP prefill" (cuLA pull
+// request #103): K1 once, pre_scan, merge of segment carries, segment-K2.
+#include "kda_device.hpp"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+// Sequence bounds from the device cu_seqlens, clamped into [0, Tt] so that an
+// inconsistent table can never address outside the inputs.
+__device__ __forceinline__ void seq_bounds(const CommonArgs& c, int seq, int64_t& beg,
+                                           int64_t& end) {
+    int64_t b = c.cu[seq], e = c.cu[seq + 1];
+    b = b < 0 ? 0 : (b > c.Tt ? c.Tt : b);
+    e = e < b ? b : (e > c.Tt ? c.Tt : e);
+    beg = b;
+    end = e;
+}
+
+__device__ __forceinline__ int rows_of(int64_t tok, int64_t end) {
+    const int64_t n = end - tok;
+    return n <= 0 ? 0 : (n >= CH ? CH : (int)n);
+}
+
+template <int NT>
+__device__ __forceinline__ void copy_record_to_lds(const uint8_t* __restrict__ src, uint8_t* dst) {
+    const u32x4* s = (const u32x4*)src;
+    u32x4* d = (u32x4*)dst;
+    for (int i = threadIdx.x; i < REC_VEC; i += NT) d[i] = s[i];
+}
+
+template <int NT>
+struct RecordPrefetch {
+    static constexpr int N = (REC_VEC + NT - 1) / NT;
+    u32x4 r[N];
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ src) {
+        const u32x4* s = (const u32x4*)src;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int i = threadIdx.x + j * NT;
+            if (i < REC_VEC) r[j] = __builtin_nontemporal_load(s + i);
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t* dst) const {
+        u32x4* d = (u32x4*)dst;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int i = threadIdx.x + j * NT;
+            if (i < REC_VEC) d[i] = r[j];
+        }
+    }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// K1: one workgroup per (chunk, head); grid = total_chunks * H, head fastest.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kda_k1_prepare(K1Args a) {
+    __shared__ K1Smem sm;
+    __shared__ __align__(16) uint8_t rec[REC_BYTES];
+    const int H = a.c.H;
+    const int h = blockIdx.x % H;
+    const int gc = blockIdx.x / H;
+    const ChunkDesc cd = a.chunks[gc];
+    int64_t beg, end;
+    seq_bounds(a.c, cd.seq, beg, end);
+    const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
+    k1_chunk(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, tok0, rows_of(tok0, end), sm, rec);
+    u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_BYTES);
+    const u32x4* src = (const u32x4*)rec;
+    for (int i = threadIdx.x; i < REC_VEC; i += 256) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// K2: one workgroup of 4 wavefronts per (unit, head); wavefront w owns value
+// columns 32w..32w+31. Records stream through a double-buffered LDS stage.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kda_k2_recur(K2Args a) {
+    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
+    const int H = a.c.H;
+    const int h = blockIdx.x % H;
+    const UnitDesc u = a.units[blockIdx.x / H];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gg = lane >> 4, m = lane & 15;
+    const int wcol = 2 * wave;
+    int64_t beg, end;
+    seq_bounds(a.c, u.seq, beg, end);
+    const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
+
+    const float* sin = nullptr;
+    if (u.in_slot >= 0)
+        sin = a.carries + ((size_t)u.in_slot * H + h) * (D * D);
+    else if (a.s0)
+        sin = a.s0 + ((size_t)u.seq * H + h) * (D * D);
+    f32x4 S[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                S[t][n][vv] = sin ? sin[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] : 0.f;
+
+    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0) * REC_BYTES;
+    const int nc = u.n_chunks;
+    if (nc > 0) copy_record_to_lds<256>(rb, recs[0]);
+    __syncthreads();
+    RecordPrefetch<256> pf;
+    for (int c = 0; c < nc; ++c) {
+        const bool more = c + 1 < nc;
+        if (more) pf.load(rb + (size_t)(c + 1) * REC_BYTES);
+        f32x4 oacc[2];
+        chain_step<true, true>(recs[c & 1], S, wcol, lane, oacc);
+        const int64_t tk = tok0 + (int64_t)CH * c;
+        if (m < rows_of(tk, end)) {
+            uint16_t* orow = a.out + ((size_t)(tk + m) * H + h) * D;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                u32x2 w;
+                w.x = pack_bf16(a.scale * oacc[n][0], a.scale * oacc[n][1]);
+                w.y = pack_bf16(a.scale * oacc[n][2], a.scale * oacc[n][3]);
+                *(u32x2*)(orow + 16 * (wcol + n) + 4 * gg) = w;
+            }
+        }
+        if (more) pf.store(recs[(c + 1) & 1]);
+        __syncthreads();
+    }
+    if (u.write_final && a.sT) {
+        float* so = a.sT + ((size_t)u.seq * H + h) * (D * D);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int vv = 0; vv < 4; ++vv)
+                    so[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] = S[t][n][vv];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// CP pre_scan: one workgroup of 8 wavefronts per (segment, head). Wavefronts
+// 0..3 run the K2 state update from S = 0 over the segment (B, value columns
+// 32w..), wavefronts 4..7 run it from S = I with U~ := 0 (M, key columns
+// 32(w-4)..). Both use the same chain step as K2, so B follows K2's
+// arithmetic exactly.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void kda_cp_prescan(PrescanArgs a) {
+    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
+    const int H = a.c.H;
+    const int h = blockIdx.x % H;
+    const PrescanDesc it = a.items[blockIdx.x / H];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gg = lane >> 4, m = lane & 15;
+    const bool is_b = wave < 4;
+    const int wcol = 2 * (wave & 3);
+
+    f32x4 S[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                S[t][n][vv] = (!is_b && 16 * t + 4 * gg + vv == 16 * (wcol + n) + m) ? 1.f : 0.f;
+
+    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
+    const int nc = it.n_chunks;
+    if (nc > 0) copy_record_to_lds<512>(rb, recs[0]);
+    __syncthreads();
+    RecordPrefetch<512> pf;
+    f32x4 unused[2];
+    for (int c = 0; c < nc; ++c) {
+        const bool more = c + 1 < nc;
+        if (more) pf.load(rb + (size_t)(c + 1) * REC_BYTES);
+        if (is_b)
+            chain_step<true, false>(recs[c & 1], S, wcol, lane, unused);
+        else
+            chain_step<false, false>(recs[c & 1], S, wcol, lane, unused);
+        if (more) pf.store(recs[(c + 1) & 1]);
+        __syncthreads();
+    }
+    float* dst = (is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                dst[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] = S[t][n][vv];
+}
+
+// ---------------------------------------------------------------------------
+// CP merge: one workgroup of 8 wavefronts per (segmented sequence, head,
+// 16-column value tile). carry_0 = S0 (or 0); carry_{s+1} = M_s carry_s + B_s,
+// in segment order, on fp32 MFMA. Wavefront t owns carry rows 16t..16t+15.
+// Every carry (including carry_0) is written to the carries scratch, so that
+// segment-K2 never reads initial_state while another segment writes
+// final_state in place.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
+    __shared__ float carry[D][16];
+    const int H = a.c.H;
+    const int vt = blockIdx.x & 7;
+    const int h = (blockIdx.x >> 3) % H;
+    const MergeDesc it = a.items[(blockIdx.x >> 3) / H];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gg = lane >> 4, m = lane & 15;
+
+    {
+        const float* s0 = a.s0 ? a.s0 + ((size_t)it.seq * H + h) * (D * D) : nullptr;
+        float* c0 = a.carries + ((size_t)it.carry0 * H + h) * (D * D);
+        for (int i = tid; i < D * 16; i += 512) {
+            const int row = i >> 4, col = i & 15;
+            const float val = s0 ? s0[row * D + 16 * vt + col] : 0.f;
+            carry[row][col] = val;
+            c0[row * D + 16 * vt + col] = val;
+        }
+    }
+    __syncthreads();
+    for (int s = 0; s + 1 < it.n_segments; ++s) {
+        const size_t sum_off = ((size_t)(it.prescan0 + s) * H + h) * (D * D);
+        const float* M = a.m_seg + sum_off;
+        const float* B = a.b_seg + sum_off;
+        f32x4 acc;
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) acc[vv] = B[(16 * wave + 4 * gg + vv) * D + 16 * vt + m];
+        f32x4 mrow[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mrow[j] = *(const f32x4*)(M + (16 * wave + m) * D + 32 * gg + 4 * j);
+#pragma unroll
+        for (int qq = 0; qq < 32; ++qq) acc = mfma_f32_k4(mrow[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc);
+        __syncthreads();
+        float* cn = a.carries + ((size_t)(it.carry0 + s + 1) * H + h) * (D * D);
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+            carry[16 * wave + 4 * gg + vv][m] = acc[vv];
+            cn[(16 * wave + 4 * gg + vv) * D + 16 * vt + m] = acc[vv];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s) {
+    const long long n = (long long)a.c.total_chunks * a.c.H;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_k1_prepare, dim3((unsigned)n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_k2_recur(const K2Args& a, hipStream_t s) {
+    const long long n = (long long)a.n_units * a.c.H;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_k2_recur, dim3((unsigned)n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s) {
+    const long long n = (long long)a.n_items * a.c.H;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_cp_prescan, dim3((unsigned)n), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s) {
+    const long long n = (long long)a.n_items * a.c.H * 8;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_cp_merge, dim3((unsigned)n), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,104 @@
+// Internal interface between the host runtime (kda_runtime.cpp) and the
+// kernels (kda_kernels.hip): plan-table entry types, kernel parameter blocks
+// and launchers. Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// K1 work item: one chunk (a sequence's local chunk index).
+struct ChunkDesc {
+    int32_t seq;
+    int32_t chunk;  // local chunk index within the sequence
+};
+
+// K2 work unit: a whole sequence (serial) or one segment of it (CP).
+struct UnitDesc {
+    int32_t seq;
+    int32_t chunk0;      // first local chunk of the unit
+    int32_t n_chunks;    // chunks to run (may be 0: state copy only)
+    int32_t rec_chunk0;  // global index of the unit's first chunk record
+    int32_t in_slot;     // -1: initial_state[seq] (or zero); >= 0: carries[in_slot]
+    int32_t write_final; // 1: write final_state[seq] at the end
+    int32_t segment;     // segment index within the sequence
+    int32_t n_segments;  // segments of the sequence
+};
+
+// CP pre_scan item: one segment whose (M, B) summary feeds the merge.
+struct PrescanDesc {
+    int32_t seq;
+    int32_t chunk0;
+    int32_t n_chunks;
+    int32_t rec_chunk0;
+    int32_t slot;  // summary slot in b_seg / m_seg
+    int32_t pad[3];
+};
+
+// CP merge item: one segmented sequence.
+struct MergeDesc {
+    int32_t seq;
+    int32_t n_segments;
+    int32_t carry0;    // carries slot of segment 0 (segments use carry0 + s)
+    int32_t prescan0;  // summary slot of segment 0 (segments 0..n-2)
+};
+
+struct CommonArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;
+    const float* beta;
+    const int32_t* cu;  // device cu_seqlens [n_seqs + 1]
+    int64_t Tt;
+    int32_t H;
+    int32_t n_seqs;
+    int32_t total_chunks;
+    uint8_t* rec;  // K1 records [H][total_chunks][REC_BYTES]
+};
+
+struct K2Args {
+    CommonArgs c;
+    const UnitDesc* units;
+    int32_t n_units;
+    const float* s0;     // may be null
+    float* sT;           // may be null
+    const float* carries;
+    uint16_t* out;
+    float scale;
+};
+
+struct PrescanArgs {
+    CommonArgs c;
+    const PrescanDesc* items;
+    int32_t n_items;
+    float* b_seg;  // [slots][H][128][128]
+    float* m_seg;
+};
+
+struct MergeArgs {
+    CommonArgs c;
+    const MergeDesc* items;
+    int32_t n_items;
+    const float* s0;
+    const float* b_seg;
+    const float* m_seg;
+    float* carries;  // [slots][H][128][128]
+};
+
+struct K1Args {
+    CommonArgs c;
+    const ChunkDesc* chunks;
+};
+
+hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s);
+hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
+hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);
+hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);
+
+constexpr int kChunk = 16;                      // tokens per chunk
+constexpr size_t kRecBytes = 17408;            // bytes of one K1 chunk record
+constexpr size_t kStateBytes = 128 * 128 * 4;  // one (sequence, head) state
+
+}  // namespace kda

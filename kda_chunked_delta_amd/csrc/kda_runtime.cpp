@@ -1,0 +1,661 @@
+// Host runtime of the KDA forward-prefill library: context, planner, per-stream
+// workspace arena, argument validation and kernel dispatch behind the C ABI of
+// include/kda.h.
+//
+// Structure follows "feat(kda/sm90): FlashKDA prefill port + intracard-CP
+// prefill" (cuLA pull request #103): the planner returns the plan the executor
+// runs and a trivial plan means serial (reviewer notes); the executor makes no
+// decisions; the workspace arena is reused across calls (description). The
+// review thread of that pull request found a race when scratch buffers are
+// shared across streams, so arenas here are keyed by stream.
+#include "kda.h"
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "kda_launch.h"
+
+using namespace kda;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status fail(kda_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kda_status hip_fail(hipError_t e, const char* what) {
+    return fail(KDA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+double env_double(const char* name, double dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    char* e = nullptr;
+    const double v = strtod(s, &e);
+    return (e && *e == 0 && std::isfinite(v) && v > 0) ? v : dflt;
+}
+
+// Planner constants. Costs are in units of one K2 chunk step of one unit;
+// the two chain-cost ratios play the role of the pull request's two fitted,
+// environment-overridable constants.
+struct PlannerConsts {
+    double prescan_ratio;   // pre_scan chunk step / K2 chunk step
+    double merge_ratio;     // merge cost per segment / K2 chunk step
+    double launch_steps;    // fixed cost of one extra launch, in K2 chunk steps
+    double chunk_us;        // K2 chunk step in microseconds (reporting only)
+    int min_seg_chunks;     // shortest segment the planner will form
+    int units_per_cu;       // concurrent K2 (unit, head) workgroups per CU
+};
+
+PlannerConsts planner_consts() {
+    PlannerConsts c;
+    c.prescan_ratio = env_double("KDA_CP_PRESCAN_RATIO", 1.0);
+    c.merge_ratio = env_double("KDA_CP_MERGE_RATIO", 2.0);
+    c.launch_steps = env_double("KDA_CP_LAUNCH_STEPS", 20.0);
+    c.chunk_us = env_double("KDA_CP_CHUNK_US", 0.25);
+    c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
+    c.units_per_cu = (int)env_double("KDA_CP_UNITS_PER_CU", 2.0);
+    return c;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+struct kda_plan {
+    kda_plan_info info{};
+    std::vector<int32_t> cu;            // host copy of cu_seqlens
+    std::vector<ChunkDesc> chunks;      // K1 items (global chunk order)
+    std::vector<UnitDesc> units;        // K2 units, launch order
+    std::vector<PrescanDesc> prescan;   // CP pre_scan items
+    std::vector<MergeDesc> merges;      // CP merge items
+    // workspace layout (byte offsets into the arena)
+    size_t off_rec = 0, off_b = 0, off_m = 0, off_carry = 0;
+    // device copy of the tables
+    int device = -1;
+    void* dev_tables = nullptr;
+    size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_prescan = 0, dev_off_merges = 0;
+};
+
+namespace {
+
+// Serial chain estimate: the longest unit, or the total work spread over the
+// concurrent workgroups, whichever is larger (in K2 chunk steps).
+double est_serial(const std::vector<int>& nch, int H, int n_cus, const PlannerConsts& pc) {
+    long long tot = 0;
+    int mx = 0;
+    for (int n : nch) { tot += n; mx = std::max(mx, n); }
+    const double width = (double)n_cus * pc.units_per_cu;
+    return std::max((double)mx, std::ceil((double)tot * H / width)) + pc.launch_steps;
+}
+
+// Segmented estimate for segment length `seg` (chunks): pre_scan over every
+// segment but the last of each split sequence, a serial merge over segments,
+// then segment-K2 over all units.
+double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const PlannerConsts& pc) {
+    long long tot = 0, pre_work = 0;
+    int longest_unit = 0, max_segs = 0;
+    for (int n : nch) {
+        tot += n;
+        const int s = (n > seg) ? (n + seg - 1) / seg : 1;
+        if (s > 1) {
+            pre_work += (long long)(s - 1) * seg;
+            max_segs = std::max(max_segs, s);
+            longest_unit = std::max(longest_unit, seg);
+        } else {
+            longest_unit = std::max(longest_unit, n);
+        }
+    }
+    if (max_segs == 0) return 1e300;
+    const double width = (double)n_cus * pc.units_per_cu;
+    // a pre_scan workgroup carries twice the columns of a K2 workgroup
+    const double t_pre = pc.prescan_ratio *
+                         std::max((double)seg, std::ceil(2.0 * (double)pre_work * H / width));
+    const double t_merge = pc.merge_ratio * (max_segs - 1);
+    const double t_k2 = std::max((double)longest_unit, std::ceil((double)tot * H / width));
+    return t_pre + t_merge + t_k2 + 3 * pc.launch_steps;
+}
+
+// seg_chunks > 0 forces that segment length on every longer sequence.
+kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int32_t H,
+                      int32_t dk, int32_t dv, kda_cp_mode mode, int32_t seg_chunks,
+                      kda_plan** out) {
+    if (!out) return fail(KDA_ERR_INVALID, "kda_plan_prefill: out is NULL");
+    *out = nullptr;
+    if (dk != 128 || dv != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_plan_prefill: dk = dv = 128 required (got dk=%d dv=%d)",
+                    dk, dv);
+    if (H < 1) return fail(KDA_ERR_INVALID, "kda_plan_prefill: H must be >= 1 (got %d)", H);
+    if (n_seqs < 1) return fail(KDA_ERR_INVALID, "kda_plan_prefill: n_seqs must be >= 1 (got %d)", n_seqs);
+    if (!cu_host) return fail(KDA_ERR_INVALID, "kda_plan_prefill: cu_seqlens_host is NULL");
+    if (n_cus < 1) return fail(KDA_ERR_INVALID, "kda_plan_prefill: n_cus must be >= 1 (got %d)", n_cus);
+    if (mode != KDA_CP_OFF && mode != KDA_CP_ON && mode != KDA_CP_AUTO)
+        return fail(KDA_ERR_INVALID, "kda_plan_prefill: unknown cp mode %d", (int)mode);
+    if (cu_host[0] != 0)
+        return fail(KDA_ERR_INVALID, "kda_plan_prefill: cu_seqlens[0] must be 0 (got %d)", cu_host[0]);
+    for (int i = 0; i < n_seqs; ++i)
+        if (cu_host[i + 1] < cu_host[i])
+            return fail(KDA_ERR_INVALID, "kda_plan_prefill: cu_seqlens decreases at index %d (%d -> %d)",
+                        i, cu_host[i], cu_host[i + 1]);
+
+    const PlannerConsts pc = planner_consts();
+    kda_plan* p = new kda_plan();
+    p->cu.assign(cu_host, cu_host + n_seqs + 1);
+    std::vector<int> nch(n_seqs), chunk_base(n_seqs);
+    long long total_chunks = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        const int L = cu_host[i + 1] - cu_host[i];
+        nch[i] = (L + kChunk - 1) / kChunk;
+        chunk_base[i] = (int)total_chunks;
+        total_chunks += nch[i];
+    }
+    if (total_chunks > (1LL << 30)) {
+        delete p;
+        return fail(KDA_ERR_INVALID, "kda_plan_prefill: too many chunks (%lld)", total_chunks);
+    }
+    p->chunks.reserve(total_chunks);
+    for (int i = 0; i < n_seqs; ++i)
+        for (int c = 0; c < nch[i]; ++c) p->chunks.push_back(ChunkDesc{i, c});
+
+    // segment length decision
+    const double t_serial = est_serial(nch, H, n_cus, pc);
+    double t_cp = 1e300;
+    int seg = 0;
+    if (seg_chunks > 0) {
+        seg = seg_chunks;
+        t_cp = est_cp(nch, H, n_cus, seg, pc);
+    } else if (mode != KDA_CP_OFF) {
+        const int mx = *std::max_element(nch.begin(), nch.end());
+        for (int s = std::max(1, pc.min_seg_chunks); s < mx; s *= 2) {
+            const double t = est_cp(nch, H, n_cus, s, pc);
+            if (t < t_cp) { t_cp = t; seg = s; }
+        }
+        if (mode == KDA_CP_AUTO && !(t_cp < 0.9 * t_serial)) seg = 0;
+    }
+
+    // units
+    int n_cp_seqs = 0, n_prescan = 0, n_carry = 0;
+    std::vector<int> order(n_seqs);
+    for (int i = 0; i < n_seqs; ++i) order[i] = i;
+    for (int i : order) {
+        const int s = (seg > 0 && nch[i] > seg) ? (nch[i] + seg - 1) / seg : 1;
+        if (s == 1) {
+            p->units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1});
+            continue;
+        }
+        MergeDesc md{i, s, n_carry, n_prescan};
+        p->merges.push_back(md);
+        for (int j = 0; j < s; ++j) {
+            const int c0 = j * seg, n = std::min(seg, nch[i] - c0);
+            p->units.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, n_carry + j, j == s - 1, j, s});
+            if (j < s - 1)
+                p->prescan.push_back(PrescanDesc{i, c0, n, chunk_base[i] + c0, n_prescan + j, {0, 0, 0}});
+        }
+        n_cp_seqs++;
+        n_prescan += s - 1;
+        n_carry += s;
+    }
+    // longest chains first
+    std::stable_sort(p->units.begin(), p->units.end(),
+                     [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
+    std::stable_sort(p->prescan.begin(), p->prescan.end(),
+                     [](const PrescanDesc& a, const PrescanDesc& b) { return a.n_chunks > b.n_chunks; });
+
+    // workspace layout
+    size_t off = 0;
+    p->off_rec = off;
+    off = align_up(off + (size_t)total_chunks * H * kRecBytes, 256);
+    p->off_b = off;
+    off = align_up(off + (size_t)n_prescan * H * kStateBytes, 256);
+    p->off_m = off;
+    off = align_up(off + (size_t)n_prescan * H * kStateBytes, 256);
+    p->off_carry = off;
+    off = align_up(off + (size_t)n_carry * H * kStateBytes, 256);
+
+    kda_plan_info& in = p->info;
+    in.n_seqs = n_seqs;
+    in.H = H;
+    in.dk = dk;
+    in.dv = dv;
+    in.total_tokens = cu_host[n_seqs];
+    in.total_chunks = (int32_t)total_chunks;
+    in.uses_cp = n_cp_seqs > 0;
+    in.n_units = (int32_t)p->units.size();
+    in.n_cp_seqs = n_cp_seqs;
+    in.n_prescan = n_prescan;
+    in.n_carry_slots = n_carry;
+    in.max_unit_chunks = 0;
+    for (const auto& u : p->units) in.max_unit_chunks = std::max(in.max_unit_chunks, u.n_chunks);
+    in.n_cus = n_cus;
+    in.workspace_bytes = off;
+    in.est_serial_us = t_serial * pc.chunk_us;
+    in.est_cp_us = (t_cp < 1e299 ? t_cp : -1.0) * pc.chunk_us;
+    *out = p;
+    return KDA_OK;
+}
+
+kda_status upload_plan(kda_plan* p, int device) {
+    size_t off = 0;
+    p->dev_off_chunks = off;
+    off = align_up(off + p->chunks.size() * sizeof(ChunkDesc), 256);
+    p->dev_off_units = off;
+    off = align_up(off + p->units.size() * sizeof(UnitDesc), 256);
+    p->dev_off_prescan = off;
+    off = align_up(off + p->prescan.size() * sizeof(PrescanDesc), 256);
+    p->dev_off_merges = off;
+    off = align_up(off + p->merges.size() * sizeof(MergeDesc), 256);
+    std::vector<uint8_t> host(off, 0);
+    if (!p->chunks.empty()) memcpy(&host[p->dev_off_chunks], p->chunks.data(), p->chunks.size() * sizeof(ChunkDesc));
+    if (!p->units.empty()) memcpy(&host[p->dev_off_units], p->units.data(), p->units.size() * sizeof(UnitDesc));
+    if (!p->prescan.empty()) memcpy(&host[p->dev_off_prescan], p->prescan.data(), p->prescan.size() * sizeof(PrescanDesc));
+    if (!p->merges.empty()) memcpy(&host[p->dev_off_merges], p->merges.data(), p->merges.size() * sizeof(MergeDesc));
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* d = nullptr;
+    e = hipMalloc(&d, off);
+    if (e == hipSuccess) e = hipMemcpy(d, host.data(), off, hipMemcpyHostToDevice);
+    (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+        if (d) (void)hipFree(d);
+        return hip_fail(e, "kda_plan_prefill: uploading plan tables");
+    }
+    p->dev_tables = d;
+    p->device = device;
+    return KDA_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// context and arena
+// ---------------------------------------------------------------------------
+struct Arena {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+struct TimedLaunch {
+    const char* name;
+    hipEvent_t beg, end;
+};
+
+struct kda_ctx {
+    int device = 0;
+    int n_cus = 0;
+    hipDeviceProp_t prop{};
+    std::mutex mu;
+    std::unordered_map<hipStream_t, Arena> arenas;
+    bool poison = false;
+    bool timing = false;
+    std::vector<TimedLaunch> events;  // pool, reused across calls
+    int n_timed = 0;
+};
+
+static const size_t kMaxArenas = 16;
+static const int kMaxTimedLaunches = 4096;
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+const char* kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
+
+kda_status kda_create(int device, kda_ctx** out) {
+    if (!out) return fail(KDA_ERR_INVALID, "kda_create: out is NULL");
+    *out = nullptr;
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (device < 0 || device >= n)
+        return fail(KDA_ERR_INVALID, "kda_create: device %d out of range (%d devices)", device, n);
+    kda_ctx* c = new kda_ctx();
+    c->device = device;
+    e = hipGetDeviceProperties(&c->prop, device);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "hipGetDeviceProperties");
+    }
+    c->n_cus = c->prop.multiProcessorCount;
+    const char* pz = getenv("KDA_DEBUG_POISON");
+    c->poison = pz && *pz && strcmp(pz, "0") != 0;
+    *out = c;
+    return KDA_OK;
+}
+
+void kda_destroy(kda_ctx* c) {
+    if (!c) return;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    for (auto& kv : c->arenas)
+        if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    for (auto& t : c->events) {
+        (void)hipEventDestroy(t.beg);
+        (void)hipEventDestroy(t.end);
+    }
+    if (prev >= 0) (void)hipSetDevice(prev);
+    delete c;
+}
+
+kda_status kda_plan_prefill_host(int32_t n_cus, const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t H,
+                                 int32_t dk, int32_t dv, kda_cp_mode mode, kda_plan** out) {
+    return build_plan(n_cus, cu_seqlens_host, n_seqs, H, dk, dv, mode, 0, out);
+}
+
+kda_status kda_plan_prefill(kda_ctx* ctx, const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t H,
+                            int32_t dk, int32_t dv, kda_cp_mode mode, kda_plan** out) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_plan_prefill: ctx is NULL");
+    kda_status st = build_plan(ctx->n_cus, cu_seqlens_host, n_seqs, H, dk, dv, mode, 0, out);
+    if (st != KDA_OK) return st;
+    st = upload_plan(*out, ctx->device);
+    if (st != KDA_OK) {
+        delete *out;
+        *out = nullptr;
+    }
+    return st;
+}
+
+kda_status kda_plan_prefill_segments(kda_ctx* ctx, const int32_t* cu_seqlens_host, int32_t n_seqs,
+                                     int32_t H, int32_t dk, int32_t dv, int32_t seg_chunks,
+                                     kda_plan** out) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_plan_prefill_segments: ctx is NULL");
+    if (seg_chunks < 1)
+        return fail(KDA_ERR_INVALID, "kda_plan_prefill_segments: seg_chunks must be >= 1 (got %d)", seg_chunks);
+    kda_status st = build_plan(ctx->n_cus, cu_seqlens_host, n_seqs, H, dk, dv, KDA_CP_ON, seg_chunks, out);
+    if (st != KDA_OK) return st;
+    st = upload_plan(*out, ctx->device);
+    if (st != KDA_OK) {
+        delete *out;
+        *out = nullptr;
+    }
+    return st;
+}
+
+void kda_plan_destroy(kda_plan* p) {
+    if (!p) return;
+    if (p->dev_tables) {
+        int prev = -1;
+        (void)hipGetDevice(&prev);
+        (void)hipSetDevice(p->device);
+        (void)hipFree(p->dev_tables);
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+    delete p;
+}
+
+kda_status kda_plan_get_info(const kda_plan* p, kda_plan_info* info) {
+    if (!p || !info) return fail(KDA_ERR_INVALID, "kda_plan_get_info: NULL argument");
+    *info = p->info;
+    return KDA_OK;
+}
+
+kda_status kda_plan_get_units(const kda_plan* p, kda_unit_info* units, int32_t max_units) {
+    if (!p || (!units && max_units > 0)) return fail(KDA_ERR_INVALID, "kda_plan_get_units: NULL argument");
+    const int n = std::min<int>(max_units, (int)p->units.size());
+    for (int i = 0; i < n; ++i) {
+        const UnitDesc& u = p->units[i];
+        units[i] = kda_unit_info{u.seq, u.chunk0, u.n_chunks, u.segment, u.n_segments};
+    }
+    return KDA_OK;
+}
+
+kda_status kda_prefill_validate(const kda_plan* p, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const int32_t* cu_dev, float scale,
+                                const float* s0, const float* sT, const void* out) {
+    if (!p) return fail(KDA_ERR_INVALID, "kda_prefill: plan is NULL");
+    const kda_plan_info& in = p->info;
+    const size_t Tt = (size_t)in.total_tokens, H = (size_t)in.H, N = (size_t)in.n_seqs;
+    const size_t n_act = Tt * H * 128 * 2, n_g = Tt * H * 128 * 4, n_beta = Tt * H * 4;
+    const size_t n_state = N * H * kStateBytes, n_cu = (N + 1) * 4;
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID, "kda_prefill: scale is not finite");
+    if (!cu_dev) return fail(KDA_ERR_INVALID, "kda_prefill: cu_seqlens is NULL");
+    if (Tt > 0) {
+        const void* need[] = {q, k, v, g, beta, out};
+        const char* names[] = {"q", "k", "v", "g", "beta", "out"};
+        for (int i = 0; i < 6; ++i) {
+            if (!need[i]) return fail(KDA_ERR_INVALID, "kda_prefill: %s is NULL", names[i]);
+            if ((uintptr_t)need[i] % (i == 4 ? 4 : 16))
+                return fail(KDA_ERR_INVALID, "kda_prefill: %s is not %d-byte aligned", names[i], i == 4 ? 4 : 16);
+        }
+    }
+    if ((uintptr_t)cu_dev % 4) return fail(KDA_ERR_INVALID, "kda_prefill: cu_seqlens is not 4-byte aligned");
+    if (s0 && (uintptr_t)s0 % 16) return fail(KDA_ERR_INVALID, "kda_prefill: initial_state is not 16-byte aligned");
+    if (sT && (uintptr_t)sT % 16) return fail(KDA_ERR_INVALID, "kda_prefill: final_state is not 16-byte aligned");
+    // out may not overlap anything
+    struct B { const void* p; size_t n; const char* name; };
+    const B ins[] = {{q, n_act, "q"}, {k, n_act, "k"}, {v, n_act, "v"}, {g, n_g, "g"},
+                     {beta, n_beta, "beta"}, {cu_dev, n_cu, "cu_seqlens"}};
+    for (const B& b : ins) {
+        if (overlap(out, n_act, b.p, b.n))
+            return fail(KDA_ERR_ALIAS, "kda_prefill: out overlaps %s", b.name);
+        if (overlap(sT, n_state, b.p, b.n))
+            return fail(KDA_ERR_ALIAS, "kda_prefill: final_state overlaps %s", b.name);
+    }
+    if (overlap(out, n_act, s0, n_state)) return fail(KDA_ERR_ALIAS, "kda_prefill: out overlaps initial_state");
+    if (overlap(out, n_act, sT, n_state)) return fail(KDA_ERR_ALIAS, "kda_prefill: out overlaps final_state");
+    if (s0 && sT && s0 != sT && overlap(s0, n_state, sT, n_state))
+        return fail(KDA_ERR_ALIAS, "kda_prefill: final_state partially overlaps initial_state "
+                                   "(must be the same buffer or disjoint)");
+    return KDA_OK;
+}
+
+kda_status kda_set_timing(kda_ctx* ctx, int enable) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_set_timing: ctx is NULL");
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->timing = enable != 0;
+    ctx->n_timed = 0;
+    return KDA_OK;
+}
+
+int32_t kda_get_timing(kda_ctx* ctx, const char** names, double* total_ms, int32_t* launches, int32_t max) {
+    if (!ctx) {
+        fail(KDA_ERR_INVALID, "kda_get_timing: ctx is NULL");
+        return -1;
+    }
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    std::vector<const char*> order;
+    std::vector<double> tot;
+    std::vector<int32_t> cnt;
+    for (int i = 0; i < ctx->n_timed; ++i) {
+        TimedLaunch& t = ctx->events[i];
+        hipError_t e = hipEventSynchronize(t.end);
+        float v = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&v, t.beg, t.end);
+        if (e != hipSuccess) {
+            ctx->n_timed = 0;
+            hip_fail(e, "kda_get_timing");
+            return -1;
+        }
+        size_t j = 0;
+        while (j < order.size() && strcmp(order[j], t.name) != 0) ++j;
+        if (j == order.size()) {
+            order.push_back(t.name);
+            tot.push_back(0.0);
+            cnt.push_back(0);
+        }
+        tot[j] += v;
+        cnt[j] += 1;
+    }
+    ctx->n_timed = 0;
+    const int n = std::min((int)order.size(), (int)max);
+    for (int i = 0; i < n; ++i) {
+        if (names) names[i] = order[i];
+        if (total_ms) total_ms[i] = tot[i];
+        if (launches) launches[i] = cnt[i];
+    }
+    return n;
+}
+
+kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const int32_t* cu_dev, float scale,
+                       const float* s0, float* sT, void* out, hipStream_t stream) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_prefill: ctx is NULL");
+    kda_status st = kda_prefill_validate(p, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
+    if (st != KDA_OK) return st;
+    if (!p->dev_tables)
+        return fail(KDA_ERR_INVALID, "kda_prefill: plan has no device tables (built by kda_plan_prefill_host?)");
+    if (p->device != ctx->device)
+        return fail(KDA_ERR_INVALID, "kda_prefill: plan is for device %d, context for device %d", p->device,
+                    ctx->device);
+
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (prev != ctx->device && (e = hipSetDevice(ctx->device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    struct Restore {
+        int prev, cur;
+        ~Restore() { if (prev >= 0 && prev != cur) (void)hipSetDevice(prev); }
+    } restore{prev, ctx->device};
+
+    // workspace arena of this stream
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    const size_t need = p->info.workspace_bytes;
+    auto it = ctx->arenas.find(stream);
+    if (it == ctx->arenas.end() || it->second.bytes < need) {
+        if (cap != hipStreamCaptureStatusNone)
+            return fail(KDA_ERR_CAPTURE, "kda_prefill: the workspace arena of this stream must grow to %zu bytes, "
+                                         "which is not allowed while the stream is capturing; run once uncaptured first",
+                        need);
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        if (it == ctx->arenas.end() && ctx->arenas.size() >= kMaxArenas) {
+            // evict one arena (the device is idle after the synchronise)
+            auto victim = ctx->arenas.begin();
+            if (victim->second.ptr) (void)hipFree(victim->second.ptr);
+            ctx->arenas.erase(victim);
+        }
+        Arena& a = ctx->arenas[stream];
+        if (a.ptr) (void)hipFree(a.ptr);
+        a.ptr = nullptr;
+        a.bytes = 0;
+        if (need > 0) {
+            const size_t bytes = align_up(need + need / 8, 1 << 20);
+            e = hipMalloc(&a.ptr, bytes);
+            if (e != hipSuccess) return hip_fail(e, "hipMalloc (workspace arena)");
+            a.bytes = bytes;
+            if (ctx->poison) {
+                e = hipMemset(a.ptr, 0xff, bytes);  // NaN in both bf16 and fp32
+                if (e != hipSuccess) return hip_fail(e, "hipMemset (poison)");
+            }
+        }
+        it = ctx->arenas.find(stream);
+    }
+    uint8_t* ws = (uint8_t*)it->second.ptr;
+
+    const uint8_t* tabs = (const uint8_t*)p->dev_tables;
+    CommonArgs c{};
+    c.q = (const uint16_t*)q;
+    c.k = (const uint16_t*)k;
+    c.v = (const uint16_t*)v;
+    c.g = g;
+    c.beta = beta;
+    c.cu = cu_dev;
+    c.Tt = p->info.total_tokens;
+    c.H = p->info.H;
+    c.n_seqs = p->info.n_seqs;
+    c.total_chunks = p->info.total_chunks;
+    c.rec = ws + p->off_rec;
+
+    auto timed = [&](const char* name, auto&& launch) -> hipError_t {
+        if (!ctx->timing) return launch();
+        if (ctx->n_timed >= kMaxTimedLaunches) return launch();  // log full: run untimed
+        if ((int)ctx->events.size() <= ctx->n_timed) {
+            TimedLaunch t{name, nullptr, nullptr};
+            hipError_t ee = hipEventCreate(&t.beg);
+            if (ee == hipSuccess) ee = hipEventCreate(&t.end);
+            if (ee != hipSuccess) return ee;
+            ctx->events.push_back(t);
+        }
+        TimedLaunch& t = ctx->events[ctx->n_timed++];
+        t.name = name;
+        hipError_t ee = hipEventRecord(t.beg, stream);
+        if (ee == hipSuccess) ee = launch();
+        if (ee == hipSuccess) ee = hipEventRecord(t.end, stream);
+        return ee;
+    };
+
+    K1Args k1{c, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
+    e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
+    if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+
+    if (p->info.n_prescan > 0) {
+        PrescanArgs pa{c, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
+                       (float*)(ws + p->off_b), (float*)(ws + p->off_m)};
+        e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
+        if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
+    }
+    if (p->info.n_cp_seqs > 0) {
+        MergeArgs ma{c, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
+                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry)};
+        e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
+        if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
+    }
+    K2Args ka{c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(), s0, sT,
+              (const float*)(ws + p->off_carry), (uint16_t*)out, scale};
+    e = timed(p->info.uses_cp ? "k2_segment" : "k2_recur", [&] { return launch_k2_recur(ka, stream); });
+    if (e != hipSuccess) return hip_fail(e, "k2_recur launch");
+    return KDA_OK;
+}
+
+kda_status kda_debug_k1_records(kda_ctx* ctx, const kda_plan* p, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta, const int32_t* cu_dev,
+                                void* records, hipStream_t stream) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_debug_k1_records: ctx is NULL");
+    if (!records && p && p->info.total_chunks > 0)
+        return fail(KDA_ERR_INVALID, "kda_debug_k1_records: records is NULL");
+    // reuse the prefill checks with records standing in for out
+    kda_status st = kda_prefill_validate(p, q, k, v, g, beta, cu_dev, 1.0f, nullptr, nullptr, records);
+    if (st != KDA_OK) return st;
+    if (!p->dev_tables || p->device != ctx->device)
+        return fail(KDA_ERR_INVALID, "kda_debug_k1_records: plan not executable on this context");
+    CommonArgs c{};
+    c.q = (const uint16_t*)q;
+    c.k = (const uint16_t*)k;
+    c.v = (const uint16_t*)v;
+    c.g = g;
+    c.beta = beta;
+    c.cu = cu_dev;
+    c.Tt = p->info.total_tokens;
+    c.H = p->info.H;
+    c.n_seqs = p->info.n_seqs;
+    c.total_chunks = p->info.total_chunks;
+    c.rec = (uint8_t*)records;
+    K1Args k1{c, (const ChunkDesc*)((const uint8_t*)p->dev_tables + p->dev_off_chunks)};
+    const hipError_t e = launch_k1_prepare(k1, stream);
+    if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,377 @@
+"""GPU parity of the HIP prefill against the fp64 CPU oracle.
+
+Bar: bf16 output and the complete fp32 final state within atol = rtol = 1e-2
+of the oracle (the correctness gate of "fix(cake_kda): support non-aligned
+recurrent prefill head counts", FlashInfer pull request #4351, description),
+and bitwise equality where the arithmetic is identical by construction:
+intracard CP vs serial ("feat(kda/sm90): FlashKDA prefill port +
+intracard-CP prefill", cuLA pull request #103, commit summary and tests),
+packing, head permutation, chunk-aligned carry, repetition.
+All calls go through the C ABI (libkda.so) via the ctypes binding.
+"""
+import os
+
+os.environ.setdefault("KDA_DEBUG_POISON", "1")  # NaN-filled workspace catches uninitialised reads
+
+import numpy as np
+import pytest
+import torch
+
+import kda_chunked_delta_amd as kda
+from kda_inputs import draw, workload
+from oracle import reference as ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = dict(atol=1e-2, rtol=1e-2)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def assert_close(name, gpu, expect, atol=1e-2, rtol=1e-2):
+    g = gpu.double().cpu().numpy() if hasattr(gpu, "cpu") else np.asarray(gpu, dtype=np.float64)
+    e = np.asarray(expect, dtype=np.float64)
+    assert g.shape == e.shape, (name, g.shape, e.shape)
+    bad = np.abs(g - e) > atol + rtol * np.abs(e)
+    err = np.abs(g - e)
+    say("  %-14s max|err| %.3e  max rel-to-tol %.3f" % (name, err.max() if err.size else 0.0,
+                                                        (err / (atol + rtol * np.abs(e))).max() if err.size else 0.0))
+    if bad.any() or not np.isfinite(g).all():
+        idx = np.unravel_index(np.argmax(np.where(np.isfinite(g), err, np.inf)), g.shape)
+        raise AssertionError("%s: %d elements out of tolerance; worst at %s: gpu %r oracle %r"
+                             % (name, int(bad.sum()) + int((~np.isfinite(g)).sum()), idx, g[idx], e[idx]))
+
+
+def run(d, mode=False, s0="given", final=True, plan=None, scale=1.0):
+    init = d["initial_state"] if s0 == "given" else None
+    o, s = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                       cu_seqlens_host=d["cu_seqlens_host"], initial_state=init,
+                       output_final_state=final, use_intracard_cp=mode, plan=plan, scale=scale)
+    torch.cuda.synchronize()
+    return o, s
+
+
+def oracle(d, s0="given", scale=1.0, heads=None):
+    init = d["initial_state"] if s0 == "given" else None
+    return ref.recurrent_c(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens_host"], init,
+                           scale=scale, heads=heads)
+
+
+@pytest.mark.parametrize("name", ["t64_h1", "h12_2x32", "h12_2x33", "h12_32_3"])
+def test_small_workloads_match_oracle(name):
+    say("case", name)
+    d = workload(name, device=DEV)
+    o, s = run(d)
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+@pytest.mark.parametrize("lengths", [[1], [15], [16], [17], [0, 5, 0, 31, 48, 0], [3, 100, 257]])
+def test_short_and_ragged_lengths(lengths):
+    say("case lengths", lengths)
+    d = draw(lengths, 5, seed=sum(lengths) + 11, state_std=0.1, device=DEV)
+    o, s = run(d)
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+@pytest.mark.parametrize("s0,final", [("given", True), ("given", False), (None, True), (None, False)])
+def test_state_in_out_combinations(s0, final):
+    say("case s0", s0, "final", final)
+    d = workload("h12_2x33", device=DEV)
+    o, s = run(d, s0=s0, final=final)
+    o_ref, s_ref = oracle(d, s0=s0)
+    assert_close("out", o, o_ref)
+    if final:
+        assert_close("final_state", s, s_ref)
+    else:
+        assert s is None
+
+
+def test_in_place_state_update():
+    d = workload("h12_32_3", device=DEV)
+    o_ref, s_ref = oracle(d)
+    st = d["initial_state"].clone()
+    o, s = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                       cu_seqlens_host=d["cu_seqlens_host"], initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == st.data_ptr()
+    assert_close("out", o, o_ref)
+    assert_close("final_state", st, s_ref)
+
+
+def test_zero_state_equals_no_state():
+    d = workload("h12_2x33", device=DEV)
+    o1, s1 = run(d, s0=None)
+    d2 = dict(d, initial_state=torch.zeros_like(d["initial_state"]))
+    o2, s2 = run(d2)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_scale():
+    d = workload("h12_2x32", device=DEV)
+    o, _ = run(d, scale=0.5)
+    o_ref, _ = oracle(d, scale=0.5)
+    assert_close("out(scale=0.5)", o, o_ref)
+
+
+# ---------------------------------------------------------------------------
+# K1 records against the chunked fp64 oracle
+# ---------------------------------------------------------------------------
+def decode_records(rec):
+    """uint8 [17408] record -> dict of fp32 numpy arrays (layout of include/kda.h)."""
+    r = rec.cpu().numpy()
+    bf = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    lanes = np.arange(64)
+    gg, m = lanes // 16, lanes % 16
+    out = {}
+    for name, off in (("Qt", 0), ("W", 4096)):
+        a = bf(r[off:off + 4096].view(np.uint16).reshape(4, 64, 8))
+        x = np.zeros((16, 128), np.float32)
+        for p in range(4):
+            for j in range(8):
+                x[m, 32 * p + 16 * (j // 4) + 4 * gg + j % 4] = a[p, :, j]
+        out[name] = x
+    a = bf(r[8192:12288].view(np.uint16).reshape(8, 64, 4))
+    x = np.zeros((16, 128), np.float32)
+    for t in range(8):
+        for j in range(4):
+            x[4 * gg + j, 16 * t + m] = a[t, :, j]
+    out["Kt"] = x
+    a = bf(r[12288:16384].view(np.uint16).reshape(8, 64, 4))
+    x = np.zeros((16, 128), np.float32)
+    for n in range(8):
+        for j in range(4):
+            x[4 * gg + j, 16 * n + m] = a[n, :, j]
+    out["U"] = x
+    a = bf(r[16384:16896].view(np.uint16).reshape(64, 4))
+    x = np.zeros((16, 16), np.float32)
+    for j in range(4):
+        x[m, 4 * gg + j] = a[:, j]
+    out["A_qk"] = x
+    out["gC"] = r[16896:17408].view(np.float32).copy()
+    return out
+
+
+@pytest.mark.parametrize("lengths", [[16], [33, 3], [64, 21]])
+def test_k1_records_match_chunked_oracle(lengths):
+    say("case lengths", lengths)
+    H = 3
+    d = draw(lengths, H, seed=77 + sum(lengths), state_std=None, device=DEV)
+    p = kda.plan(d["cu_seqlens_host"], H, device=DEV)
+    recs = kda.k1_records(d["q"], d["k"], d["v"], d["g"], d["beta"], p)
+    torch.cuda.synchronize()
+    _, _, ks = ref.chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens_host"], None,
+                           intermediates=True)
+    gidx = 0
+    for i, L in enumerate(lengths):
+        for c in range((L + 15) // 16):
+            for h in range(H):
+                got = decode_records(recs[h, gidx])
+                exp = ks[(i, c, h)]
+                n = exp["Qt"].shape[0]
+                for key in ("Qt", "W", "Kt", "U"):
+                    assert_close("%s[%d,%d,%d]" % (key, i, c, h), got[key][:n], exp[key])
+                    assert np.all(got[key][n:] == 0), "%s rows past the tail must be zero" % key
+                aq = np.zeros((16, 16))
+                aq[:n, :n] = exp["A_qk"]
+                assert_close("A_qk", got["A_qk"], aq)
+                assert_close("gC", got["gC"], exp["gC"], atol=1e-6, rtol=1e-5)
+            gidx += 1
+
+
+# ---------------------------------------------------------------------------
+# bitwise properties of the serial path
+# ---------------------------------------------------------------------------
+def test_chunk_aligned_carry_is_bitwise():
+    """run([a; b]) == run(b, run(a).final) bitwise when |a| is a multiple of 16."""
+    d = draw([160], 4, seed=5, state_std=0.1, device=DEV)
+    o, s = run(d)
+    cut = 96
+    sl = lambda x, a, b: x[a:b].contiguous()
+    da = dict(d, q=sl(d["q"], 0, cut), k=sl(d["k"], 0, cut), v=sl(d["v"], 0, cut), g=sl(d["g"], 0, cut),
+              beta=sl(d["beta"], 0, cut), cu_seqlens=None, cu_seqlens_host=[0, cut])
+    oa, sa = run(da)
+    db = dict(d, q=sl(d["q"], cut, 160), k=sl(d["k"], cut, 160), v=sl(d["v"], cut, 160),
+              g=sl(d["g"], cut, 160), beta=sl(d["beta"], cut, 160), cu_seqlens=None,
+              cu_seqlens_host=[0, 160 - cut], initial_state=sa)
+    ob, sb = run(db)
+    assert torch.equal(torch.cat([oa, ob]), o)
+    assert torch.equal(sb, s)
+
+
+def test_varlen_packing_is_bitwise():
+    lengths = [40, 7, 130]
+    d = draw(lengths, 6, seed=8, state_std=0.1, device=DEV)
+    o, s = run(d)
+    cu = d["cu_seqlens_host"]
+    for i in range(len(lengths)):
+        a, b = cu[i], cu[i + 1]
+        di = dict(d, q=d["q"][a:b].contiguous(), k=d["k"][a:b].contiguous(), v=d["v"][a:b].contiguous(),
+                  g=d["g"][a:b].contiguous(), beta=d["beta"][a:b].contiguous(), cu_seqlens=None,
+                  cu_seqlens_host=[0, b - a], initial_state=d["initial_state"][i:i + 1].contiguous())
+        oi, si = run(di)
+        assert torch.equal(oi, o[a:b]) and torch.equal(si, s[i:i + 1])
+
+
+def test_head_permutation_is_bitwise():
+    d = draw([70, 33], 5, seed=9, state_std=0.1, device=DEV)
+    o, s = run(d)
+    perm = torch.tensor([3, 0, 4, 1, 2], device=DEV)
+    dp = dict(d)
+    for key in ("q", "k", "v", "g", "beta"):
+        dp[key] = d[key].index_select(1, perm).contiguous()
+    dp["initial_state"] = d["initial_state"].index_select(1, perm).contiguous()
+    op, sp = run(dp)
+    assert torch.equal(op, o.index_select(1, perm)) and torch.equal(sp, s.index_select(1, perm))
+
+
+def test_repeated_runs_are_bitwise_deterministic():
+    d = draw([300, 77], 4, seed=10, state_std=0.1, device=DEV)
+    o0, s0 = run(d)
+    for _ in range(20):
+        o, s = run(d)
+        assert torch.equal(o, o0) and torch.equal(s, s0)
+
+
+# ---------------------------------------------------------------------------
+# intracard CP
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seg_chunks,lengths", [(2, [200]), (3, [100, 35, 260]), (8, [1000, 20])])
+def test_forced_cp_accuracy(seg_chunks, lengths):
+    say("case seg_chunks", seg_chunks, "lengths", lengths)
+    d = draw(lengths, 4, seed=seg_chunks * 100 + len(lengths), state_std=0.1, device=DEV)
+    p = kda.plan_segments(d["cu_seqlens_host"], 4, seg_chunks, device=DEV)
+    assert p.info()["uses_cp"] == 1
+    o, s = run(d, plan=p)
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+def test_forced_cp_in_place_state():
+    d = draw([400, 50], 3, seed=3, state_std=0.1, device=DEV)
+    o_ref, s_ref = oracle(d)
+    p = kda.plan_segments(d["cu_seqlens_host"], 3, 4, device=DEV)
+    st = d["initial_state"].clone()
+    o, _ = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                       cu_seqlens_host=d["cu_seqlens_host"], initial_state=st, final_state=st, plan=p)
+    torch.cuda.synchronize()
+    assert_close("out", o, o_ref)
+    assert_close("final_state", st, s_ref)
+
+
+def test_cp_bitwise_on_long_sequence_and_oracle():
+    """One 65536-token sequence, 8 heads: the auto plan splits it; the result
+    must equal the serial path bitwise and the oracle within 1e-2."""
+    say("case long65536_h8")
+    d = workload("long65536_h8", device=DEV)
+    p_auto = kda.plan(d["cu_seqlens_host"], 8, "auto", device=DEV)
+    assert p_auto.info()["uses_cp"] == 1
+    o_ser, s_ser = run(d, mode=False)
+    o_cp, s_cp = run(d, plan=p_auto)
+    assert torch.equal(o_cp, o_ser), "CP output differs from serial"
+    assert torch.equal(s_cp, s_ser), "CP final state differs from serial"
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o_cp, o_ref)
+    assert_close("final_state", s_cp, s_ref)
+
+
+def test_cp_weak_decay_within_tolerance():
+    """With weak decay the carried state is not forgotten inside a segment, so
+    CP equals serial only within rounding; both match the oracle."""
+    d = draw([4096], 2, seed=12, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * 0.05
+    p = kda.plan_segments(d["cu_seqlens_host"], 2, 64, device=DEV)
+    o_cp, s_cp = run(d, plan=p)
+    o_ser, s_ser = run(d)
+    o_ref, s_ref = oracle(d)
+    assert_close("out(cp)", o_cp, o_ref)
+    assert_close("final(cp)", s_cp, s_ref)
+    assert_close("out(serial)", o_ser, o_ref)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+def test_headline_varlen_h32_full_parity():
+    say("case varlen8_h32 (auto plan, as benchmarked)")
+    d = workload("varlen8_h32", device=DEV)
+    o, s = run(d, mode="auto")
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+def test_batch16_h64_sampled_parity():
+    say("case batch16x8192_h64 (sampled sequences and heads)")
+    d = workload("batch16x8192_h64", device=DEV)
+    o, s = run(d, mode="auto", s0=None)
+    heads = [0, 17, 63]
+    for i in (0, 9, 15):
+        a, b = i * 8192, (i + 1) * 8192
+        sub = {key: d[key][a:b, heads].contiguous() for key in ("q", "k", "v", "g", "beta")}
+        o_ref, s_ref = ref.recurrent_c(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], [0, 8192])
+        assert_close("out[seq %d]" % i, o[a:b, heads], o_ref)
+        assert_close("final[seq %d]" % i, s[i:i + 1, heads], s_ref)
+
+
+# ---------------------------------------------------------------------------
+# runtime behaviour
+# ---------------------------------------------------------------------------
+def test_graph_replay_picks_up_changed_beta():
+    d = workload("h12_2x33", device=DEV)
+    run(d)  # grow the arena outside capture
+    o_buf = torch.empty_like(d["q"])
+    s_buf = torch.empty_like(d["initial_state"])
+    p = kda.plan(d["cu_seqlens_host"], 12, device=DEV)
+    cu = p.cu_device()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):  # warm the side stream's arena
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=d["cu_seqlens_host"],
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=d["cu_seqlens_host"],
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    for trial in range(3):
+        d["beta"].copy_(torch.sigmoid(torch.randn(d["beta"].shape, device=DEV, generator=torch.Generator(DEV).manual_seed(trial))))
+        graph.replay()
+        torch.cuda.synchronize()
+        o_e, s_e = run(d)
+        assert torch.equal(o_buf, o_e) and torch.equal(s_buf, s_e), "replay %d differs from eager" % trial
+    o_ref, s_ref = oracle(d)
+    assert_close("out(replay)", o_buf, o_ref)
+
+
+def test_arena_reuse_across_shape_changes():
+    big = draw([3000, 1000], 8, seed=1, state_std=0.1, device=DEV)
+    small = draw([40], 2, seed=2, state_std=0.1, device=DEV)
+    ob1, sb1 = run(big)
+    os1, ss1 = run(small)
+    ob2, sb2 = run(big)
+    os2, ss2 = run(small)
+    assert torch.equal(ob1, ob2) and torch.equal(sb1, sb2)
+    assert torch.equal(os1, os2) and torch.equal(ss1, ss2)
+    o_ref, s_ref = oracle(small)
+    assert_close("out(small)", os2, o_ref)
+
+
+def test_validation_errors_reach_python():
+    d = workload("h12_2x32", device=DEV)
+    with pytest.raises(kda.KDAError) as e:
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                    cu_seqlens_host=d["cu_seqlens_host"], out=d["q"])
+    assert e.value.status == 3
+    st = d["initial_state"]
+    bad_final = torch.empty(st.numel() + 4096, device=DEV)[4096:].view(st.shape)
+    with pytest.raises(ValueError):
+        kda.prefill(d["q"], d["k"], d["v"], d["g"].to(torch.bfloat16), d["beta"], cu_seqlens=d["cu_seqlens"])
+    del bad_final

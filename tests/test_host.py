@@ -1,0 +1,196 @@
+"""Host-side tests of the C-ABI library (no GPU needed): exported symbols,
+the planner and argument validation. No compute entry point is called."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kda_chunked_delta_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kda_create", "kda_destroy", "kda_plan_prefill", "kda_prefill", "kda_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(kda_lib):
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, "declared in include/kda.h but not exported: %s" % missing
+
+
+def test_version(kda_lib):
+    assert b"gfx950" in kda_lib.kda_version()
+
+
+# ---------------------------------------------------------------------------
+# planner
+# ---------------------------------------------------------------------------
+def cu_of(lengths):
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    return cu
+
+
+def test_serial_plan_orders_longest_first(kda_lib):
+    lengths = [100, 4096, 17, 0, 2000]
+    p = kda.plan_host(cu_of(lengths), H=4, n_cus=256)
+    info = p.info()
+    assert info["uses_cp"] == 0
+    assert info["total_chunks"] == sum((L + 15) // 16 for L in lengths)
+    units = p.units()
+    assert sorted(u["seq"] for u in units) == list(range(len(lengths)))
+    chunks = [u["n_chunks"] for u in units]
+    assert chunks == sorted(chunks, reverse=True)
+    assert all(u["n_segments"] == 1 for u in units)
+    # workspace holds one 17408-byte record per (chunk, head)
+    assert info["workspace_bytes"] >= info["total_chunks"] * 4 * 17408
+
+
+def test_auto_plan_splits_few_head_long_sequence(kda_lib):
+    p = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp="auto")
+    info = p.info()
+    assert info["uses_cp"] == 1 and info["n_cp_seqs"] == 1
+    units = p.units()
+    segs = sorted((u["chunk0"], u["n_chunks"]) for u in units)
+    # chunk-aligned, contiguous, covering all 4096 chunks
+    pos = 0
+    for c0, n in segs:
+        assert c0 == pos and n >= 1
+        pos += n
+    assert pos == 4096
+    assert min(n for _, n in segs[:-1]) >= 64  # minimum segment length
+    assert info["n_prescan"] == len(segs) - 1
+    assert info["est_cp_us"] < info["est_serial_us"]
+
+
+def test_auto_plan_declines_saturated_and_short(kda_lib):
+    # batch x heads already fills the machine
+    assert kda.plan_host(cu_of([8192] * 16), H=64, n_cus=256, use_intracard_cp="auto").info()["uses_cp"] == 0
+    # sequences too short to split
+    assert kda.plan_host(cu_of([512] * 4), H=2, n_cus=256, use_intracard_cp="auto").info()["uses_cp"] == 0
+    # off means off
+    assert kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=False).info()["uses_cp"] == 0
+
+
+def test_plan_depends_on_cu_count(kda_lib):
+    small = kda.plan_host([0, 32768], H=16, n_cus=32, use_intracard_cp="auto").info()
+    big = kda.plan_host([0, 32768], H=16, n_cus=256, use_intracard_cp="auto").info()
+    assert big["n_units"] >= small["n_units"]
+    assert big["n_cus"] == 256 and small["n_cus"] == 32
+
+
+def test_ragged_batch_splits_only_long_sequences(kda_lib):
+    lengths = [32768, 300, 50, 20000]
+    p = kda.plan_host(cu_of(lengths), H=4, n_cus=256, use_intracard_cp=True)
+    units = p.units()
+    by_seq = {}
+    for u in units:
+        by_seq.setdefault(u["seq"], []).append(u)
+    assert len(by_seq[1]) == 1 and len(by_seq[2]) == 1
+    assert len(by_seq[0]) > 1
+
+
+def test_planner_constants_are_env_overridable(kda_lib, monkeypatch):
+    base = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=True).info()
+    monkeypatch.setenv("KDA_CP_MIN_SEG_CHUNKS", "1024")
+    big = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=True).info()
+    assert big["max_unit_chunks"] >= 1024 > base["max_unit_chunks"]
+
+
+@pytest.mark.parametrize("cu,H,err", [
+    ([1, 5], 2, "cu_seqlens[0]"),
+    ([0, 5, 3], 2, "decreases"),
+    ([0, 5], 0, "H must be"),
+])
+def test_plan_rejects_bad_input(kda_lib, cu, H, err):
+    with pytest.raises(kda.KDAError, match=re.escape(err)) as e:
+        kda.plan_host(cu, H=H, n_cus=256)
+    assert e.value.status == 1
+
+
+def test_plan_rejects_other_head_dims(kda_lib):
+    arr = (ctypes.c_int32 * 2)(0, 16)
+    h = ctypes.c_void_p()
+    st = kda_lib.kda_plan_prefill_host(256, arr, 1, 2, 64, 64, 0, ctypes.byref(h))
+    assert st == 2 and b"128" in kda_lib.kda_last_error()
+
+
+# ---------------------------------------------------------------------------
+# validation (addresses only; never dereferenced)
+# ---------------------------------------------------------------------------
+class FakeBuffers:
+    def __init__(self, Tt, H, N):
+        act = Tt * H * 128 * 2
+        self.size = dict(act=act, g=Tt * H * 128 * 4, beta=Tt * H * 4, state=N * H * 128 * 128 * 4,
+                         cu=(N + 1) * 4)
+        base = 1 << 40
+        self.addr = {}
+        for name, kind in (("q", "act"), ("k", "act"), ("v", "act"), ("g", "g"), ("beta", "beta"),
+                           ("cu", "cu"), ("s0", "state"), ("sT", "state"), ("out", "act")):
+            self.addr[name] = base
+            base += (self.size[kind] + 4096) // 256 * 256
+
+    def call(self, lib, plan, **over):
+        a = dict(self.addr)
+        a.update(over)
+        P = lambda x: ctypes.c_void_p(x) if x else None
+        return lib.kda_prefill_validate(plan.handle, P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]),
+                                        P(a["beta"]), P(a["cu"]), ctypes.c_float(a.get("scale", 1.0)),
+                                        P(a["s0"]), P(a["sT"]), P(a["out"]))
+
+
+@pytest.fixture
+def setup(kda_lib):
+    p = kda.plan_host([0, 40, 100], H=3, n_cus=256)
+    return kda_lib, p, FakeBuffers(100, 3, 2)
+
+
+def test_validate_accepts_good_call(setup):
+    lib, p, fb = setup
+    assert fb.call(lib, p) == 0
+    assert fb.call(lib, p, s0=0) == 0                      # no initial state
+    assert fb.call(lib, p, sT=0) == 0                      # no final state
+    assert fb.call(lib, p, s0=0, sT=0) == 0                # neither
+    assert fb.call(lib, p, sT=fb.addr["s0"]) == 0          # in place
+
+
+def test_validate_rejects_aliasing(setup):
+    lib, p, fb = setup
+    assert fb.call(lib, p, out=fb.addr["q"]) == 3
+    assert fb.call(lib, p, out=fb.addr["v"] + 256) == 3
+    assert fb.call(lib, p, sT=fb.addr["s0"] + 4096) == 3   # partial state overlap
+    assert b"partially overlaps" in lib.kda_last_error()
+    assert fb.call(lib, p, sT=fb.addr["g"]) == 3
+    assert fb.call(lib, p, out=fb.addr["sT"]) == 3
+
+
+def test_validate_rejects_null_and_misaligned(setup):
+    lib, p, fb = setup
+    assert fb.call(lib, p, q=0) == 1
+    assert fb.call(lib, p, cu=0) == 1
+    assert fb.call(lib, p, k=fb.addr["k"] + 8) == 1
+    assert b"aligned" in lib.kda_last_error()
+    assert fb.call(lib, p, scale=float("nan")) == 1
+
+
+def test_host_plan_cannot_execute(setup):
+    lib, p, fb = setup
+    # kda_prefill needs a context; with a NULL context it fails before any HIP call
+    P = lambda x: ctypes.c_void_p(x)
+    a = fb.addr
+    st = lib.kda_prefill(None, p.handle, P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                         P(a["cu"]), ctypes.c_float(1.0), P(a["s0"]), P(a["sT"]), P(a["out"]), None)
+    assert st == 1 and b"ctx" in lib.kda_last_error()
