@@ -78,6 +78,10 @@ typedef struct {
     size_t  workspace_bytes;   /* arena bytes kda_prefill needs for this plan */
     double  est_serial_us;     /* planner's cost estimate of the serial path */
     double  est_cp_us;         /* planner's cost estimate of the segmented path */
+    int32_t k1_materialized;   /* 1: K1 writes chunk records to the workspace once and
+                                  K2 / pre_scan read them; 0: K1 is recomputed per chunk
+                                  inside the K2 and pre_scan kernels (default; set
+                                  KDA_MATERIALIZE_K1=1 at plan time for the other form) */
 } kda_plan_info;
 
 /* One K2 work unit of a plan (a whole sequence, or one segment of it). */
@@ -157,8 +161,10 @@ kda_status kda_prefill_validate(const kda_plan *plan, const void *q, const void 
  *                  initial_state (updated in place) but may not partly
  *                  overlap it; may not overlap any input or out
  *   out          : may not overlap any input or state
- * Serial plans launch K1 (per chunk) then K2 (per unit); segmented plans
- * launch K1, pre_scan, merge and segment-K2. Results of a segmented plan are
+ * Serial plans launch one fused K1+K2 kernel (or K1 then K2 when the plan
+ * materialises K1); segmented plans launch pre_scan, merge and segment-K2
+ * (preceded by K1 when it is materialised). Every form runs the same K1 and
+ * K2 arithmetic, so their results are bitwise equal. Results of a segmented plan are
  * bitwise equal to the serial plan's whenever the carried-in state is
  * forgotten within a segment (strong decay); otherwise equal within fp32
  * rounding. */
@@ -172,14 +178,17 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
  * of (chunk c, head h) at index h * total_chunks + c; layout in
  * KDA_RECORD_* below). Arguments as in kda_prefill. */
 #define KDA_RECORD_BYTES 17408
-/* Record layout (lane l of a 64-wide wavefront: gg = l / 16, m = l % 16;
- * dkperm(p, gg, j) = 32p + 16(j / 4) + 4gg + j % 4):
- *   [0, 4096)      Qt = q * exp(G): bf16 [p 4][lane 64][j 8] = Qt[m][dkperm(p, gg, j)]
- *   [4096, 8192)   W (WY keys):     same layout as Qt
- *   [8192, 12288)  Kt = k * exp(G_C - G): bf16 [t 8][lane 64][j 4] = Kt[4gg + j][16t + m]
- *   [12288, 16384) U~ (WY values):  bf16 [n 8][lane 64][j 4] = U~[4gg + j][16n + m]
- *   [16384, 16896) A_qk (i <= r):   bf16 [lane 64][j 4] = A_qk[m][4gg + j]
- *   [16896, 17408) exp(G_C):        fp32 [128]
+/* Record layout (bf16 unless noted; r = token row 0..15 of the chunk, c =
+ * channel 0..127; rows past the end of a short chunk are zero):
+ *   [0, 4096)      Qt = q * exp(G): row-major 256-byte rows whose 16-byte
+ *                  chunks are XOR-swizzled by the row: element (r, c) at byte
+ *                  r*256 + ((((c / 8) ^ r) % 16) * 16) + 2 * (c % 8)
+ *   [4096, 8192)   W (WY-transformed keys): same layout as Qt
+ *   [8192, 12288)  Kt = k * exp(G_C - G): column-major, (r, c) at byte 32c + 2r
+ *   [12288, 16384) U~ (WY-transformed values): column-major, (r, c) at 32c + 2r
+ *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4], lane l = 16g + i,
+ *                  element j = A_qk[i][4g + j]
+ *   [16896, 17408) exp(G_C): fp32 [128]
  */
 kda_status kda_debug_k1_records(kda_ctx *ctx, const kda_plan *plan, const void *q, const void *k,
                                 const void *v, const float *g, const float *beta,

@@ -49,7 +49,7 @@ class PlanInfo(ctypes.Structure):
                 ("n_prescan", ctypes.c_int32), ("n_carry_slots", ctypes.c_int32),
                 ("max_unit_chunks", ctypes.c_int32), ("n_cus", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t), ("est_serial_us", ctypes.c_double),
-                ("est_cp_us", ctypes.c_double)]
+                ("est_cp_us", ctypes.c_double), ("k1_materialized", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -24,18 +24,17 @@ constexpr int D = 128;   // head dimension (dk = dv)
 constexpr int CH = 16;   // chunk length
 
 // ---------------------------------------------------------------------------
-// K1 -> K2 chunk record: everything K2 needs for one (chunk, head), laid out
-// so that each wavefront lane reads its MFMA fragment with one vector load.
-// Lane l has group gg = l >> 4 and index m = l & 15.
-//   REC_Q  : Qt  fragments [p 0..3][lane][8 bf16]: Qt[m][dkperm(p, gg, j)]
-//   REC_W  : W   fragments, same layout as REC_Q
-//   REC_KT : Kt^T fragments [t 0..7][lane][4 bf16]: Kt[4gg + j][16t + m]
-//   REC_U  : U~ in accumulator layout [n 0..7][lane][4 bf16]: U~[4gg + j][16n + m]
-//   REC_AQK: A_qk^T fragment [lane][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
+// K1 -> K2 chunk record: everything K2 needs for one (chunk, head). Layouts
+// are chosen so that K1 writes and K2's MFMA fragment reads are both free of
+// heavy LDS bank conflicts (all bf16 unless noted):
+//   REC_Q  : Qt[token r][channel c], row-major 256 B rows, 16-byte chunks of a
+//            row XOR-swizzled by the row: byte r*256 + (((c>>3) ^ r) << 4) + 2(c&7)
+//   REC_W  : W, same layout as REC_Q
+//   REC_KT : Kt column-major: byte 32c + 2r holds Kt[r][c]
+//   REC_U  : U~ column-major: byte 32c + 2r holds U~[r][c]
+//   REC_AQK: A_qk^T fragment [lane 64][4]: A_qk[m][4gg + j] (masked i <= r)
 //   REC_GC : exp(G_C) [128] fp32
-// dkperm(p, gg, j) = 32p + 16(j >> 2) + 4gg + (j & 3): the key-channel order
-// of a 16x16x32 MFMA step that lets the fp32 state, held in 16x16
-// accumulator tiles, feed the next MFMA as an operand without any shuffle.
+// Lane l of a wavefront has group gg = l >> 4 and index m = l & 15.
 // ---------------------------------------------------------------------------
 constexpr int REC_Q = 0;
 constexpr int REC_W = 4096;
@@ -45,6 +44,9 @@ constexpr int REC_AQK = 16384;
 constexpr int REC_GC = 16896;
 constexpr int REC_BYTES = 17408;
 constexpr int REC_VEC = REC_BYTES / 16;  // 1088 16-byte vectors
+
+// byte offset of element (row r, channel c) in a swizzled row-major block
+__host__ __device__ constexpr int swz(int r, int c) { return r * 256 + ((((c >> 3) ^ r) & 15) << 4) + 2 * (c & 7); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -88,6 +90,7 @@ struct __align__(16) K1Smem {
     uint16_t qa[CH][D + 8];  // Gram operands (bf16), rows padded
     uint16_t ka[CH][D + 8];
     uint16_t kb[CH][D + 8];
+    uint16_t kt[CH * D];     // Kt = k * exp(G_C - G), swizzled row-major (transposed later)
     float L[CH][CH];         // strict-lower(diag(beta) A_kk)
     float eref[D];           // exp(G_ref), G_ref = G at row 7
     float ecr[D];            // exp(G_C - G_ref)
@@ -95,55 +98,84 @@ struct __align__(16) K1Smem {
     float beta[CH];
 };
 
-// Rows [tok0, tok0 + nrows) of head h (nrows in 0..16; rows beyond are
-// treated as k = q = v = 0, g = 0, beta = 0, which leaves them inert).
-__device__ __forceinline__ void k1_chunk(const uint16_t* __restrict__ q,
-                                         const uint16_t* __restrict__ k,
-                                         const uint16_t* __restrict__ v,
-                                         const float* __restrict__ g,
-                                         const float* __restrict__ beta, int H, int h,
-                                         int64_t tok0, int nrows, K1Smem& sm, uint8_t* rec) {
+// Workgroup barrier that waits only for this wavefront's LDS traffic, so
+// global loads issued earlier (prefetch of later chunks) stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Raw inputs of one chunk held by K1 thread tid < 256: row r = tid >> 4,
+// channels 8c..8c+7 with c = tid & 15 (16-byte loads). Rows at or beyond
+// nrows are zero (k = q = v = 0, g = 0, beta = 0), which leaves them inert.
+struct RawChunk {
+    u32x4 q8, k8, v8;
+    f32x4 ga, gb;
+    float br;
+};
+
+__device__ __forceinline__ void k1_load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                        const uint16_t* __restrict__ v, const float* __restrict__ g,
+                                        const float* __restrict__ beta, int H, int h, int64_t tok0,
+                                        int nrows, RawChunk& raw) {
     const int tid = threadIdx.x;
-    // -- load: thread owns row r, channels 8c..8c+7 (16-byte loads) --------
-    const int r = tid >> 4, c = tid & 15;
-    u32x4 q8 = {0u, 0u, 0u, 0u}, k8 = q8, v8 = q8;
-    f32x4 ga = {0.f, 0.f, 0.f, 0.f}, gb = ga;
-    float br = 0.f;
-    if (r < nrows) {
+    const int r = (tid >> 4) & 15, c = tid & 15;
+    raw.q8 = u32x4{0u, 0u, 0u, 0u};
+    raw.k8 = raw.q8;
+    raw.v8 = raw.q8;
+    raw.ga = f32x4{0.f, 0.f, 0.f, 0.f};
+    raw.gb = raw.ga;
+    raw.br = 0.f;
+    if (tid < 256 && r < nrows) {
         const size_t row = (size_t)(tok0 + r) * H + h;
         const size_t off = row * D + 8 * c;
-        q8 = *(const u32x4*)(q + off);
-        k8 = *(const u32x4*)(k + off);
-        v8 = *(const u32x4*)(v + off);
-        ga = *(const f32x4*)(g + off);
-        gb = *(const f32x4*)(g + off + 4);
-        br = beta[row];
+        raw.q8 = __builtin_nontemporal_load((const u32x4*)(q + off));
+        raw.k8 = __builtin_nontemporal_load((const u32x4*)(k + off));
+        raw.v8 = __builtin_nontemporal_load((const u32x4*)(v + off));
+        raw.ga = __builtin_nontemporal_load((const f32x4*)(g + off));
+        raw.gb = __builtin_nontemporal_load((const f32x4*)(g + off + 4));
+        raw.br = beta[row];
     }
-    *(f32x4*)&sm.G[r][8 * c] = ga;
-    *(f32x4*)&sm.G[r][8 * c + 4] = gb;
-    if (c == 0) sm.beta[r] = br;
-    __syncthreads();
+}
+
+// K1 on one chunk of one head: threads 0..255 compute, every thread of the
+// workgroup (any multiple of 64 threads >= 256) must call it, since it holds
+// workgroup barriers. The record is complete in `rec` (LDS) on return.
+__device__ __forceinline__ void k1_compute(const RawChunk& raw, K1Smem& sm, uint8_t* rec) {
+    const int tid = threadIdx.x;
+    const bool act = tid < 256;
+    const int r = (tid >> 4) & 15, c = tid & 15;
+    if (act) {
+        *(f32x4*)&sm.G[r][8 * c] = raw.ga;
+        *(f32x4*)&sm.G[r][8 * c + 4] = raw.gb;
+        if (c == 0) sm.beta[r] = raw.br;
+    }
+    lds_barrier();
 
     // -- in-chunk cumulative sum per key channel, per-channel decays -------
     if (tid < D) {
-        float acc = 0.f, gref = 0.f;
+        float gv[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) gv[i] = sm.G[i][tid];
+        float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            acc += sm.G[i][tid];
-            sm.G[i][tid] = acc;
-            if (i == 7) gref = acc;
+            acc += gv[i];
+            gv[i] = acc;
         }
-        sm.eref[tid] = __expf(gref);
-        sm.ecr[tid] = __expf(acc - gref);
-        sm.gc[tid] = __expf(acc);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) sm.G[i][tid] = gv[i];
+        sm.eref[tid] = __expf(gv[7]);
+        sm.ecr[tid] = __expf(gv[15] - gv[7]);
+        sm.gc[tid] = __expf(gv[15]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // -- decayed operands (thread: row r, channels 8c..8c+7) ---------------
-    {
-        const uint32_t qw[4] = {q8.x, q8.y, q8.z, q8.w};
-        const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
-        const uint32_t vw[4] = {v8.x, v8.y, v8.z, v8.w};
+    if (act) {
+        const float br = raw.br;
+        const uint32_t qw[4] = {raw.q8.x, raw.q8.y, raw.q8.z, raw.q8.w};
+        const uint32_t kw[4] = {raw.k8.x, raw.k8.y, raw.k8.z, raw.k8.w};
+        const uint32_t vw[4] = {raw.v8.x, raw.v8.y, raw.v8.z, raw.v8.w};
         float qt[8], kt[8], qa[8], ka[8], kb[8], X[8], Y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -178,29 +210,19 @@ __device__ __forceinline__ void k1_chunk(const uint16_t* __restrict__ q,
         *(f32x4*)&sm.XY[r][8 * c + 4] = f32x4{X[4], X[5], X[6], X[7]};
         *(f32x4*)&sm.XY[r][D + 8 * c] = f32x4{Y[0], Y[1], Y[2], Y[3]};
         *(f32x4*)&sm.XY[r][D + 8 * c + 4] = f32x4{Y[4], Y[5], Y[6], Y[7]};
-        // Qt fragments: two runs of four channels
-#pragma unroll
-        for (int j4 = 0; j4 < 2; ++j4) {
-            const int dd = 8 * c + 4 * j4;
-            const int p = dd >> 5, half = (dd >> 4) & 1, gq = (dd >> 2) & 3;
-            u32x2 w;
-            w.x = pack_bf16(qt[4 * j4], qt[4 * j4 + 1]);
-            w.y = pack_bf16(qt[4 * j4 + 2], qt[4 * j4 + 3]);
-            *(u32x2*)(rec + REC_Q + p * 1024 + (gq * 16 + r) * 16 + half * 8) = w;
-        }
-        // Kt^T fragments: element (r, d) -> tile d>>4, lane (r>>2, d&15), slot r&3
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = 8 * c + e;
-            *(uint16_t*)(rec + REC_KT + (d >> 4) * 512 + ((r >> 2) * 16 + (d & 15)) * 8 +
-                         (r & 3) * 2) = (uint16_t)bf16_bits(kt[e]);
-        }
+        u32x4 wqt, wkt;
+        wqt.x = pack_bf16(qt[0], qt[1]); wqt.y = pack_bf16(qt[2], qt[3]);
+        wqt.z = pack_bf16(qt[4], qt[5]); wqt.w = pack_bf16(qt[6], qt[7]);
+        wkt.x = pack_bf16(kt[0], kt[1]); wkt.y = pack_bf16(kt[2], kt[3]);
+        wkt.z = pack_bf16(kt[4], kt[5]); wkt.w = pack_bf16(kt[6], kt[7]);
+        *(u32x4*)(rec + REC_Q + swz(r, 8 * c)) = wqt;
+        *(u32x4*)((uint8_t*)sm.kt + swz(r, 8 * c)) = wkt;
         if (r == 0) {
             *(f32x4*)(rec + REC_GC + 32 * c) = *(const f32x4*)&sm.gc[8 * c];
             *(f32x4*)(rec + REC_GC + 32 * c + 16) = *(const f32x4*)&sm.gc[8 * c + 4];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // -- Grams on MFMA: wave 0 A_kk -> L, wave 1 A_qk -> record ------------
     {
@@ -216,10 +238,12 @@ __device__ __forceinline__ void k1_chunk(const uint16_t* __restrict__ q,
             }
             // acc[vv] = Gram[row 4gg + vv][col m]
             if (wave == 0) {
+                const f32x4 b4 = *(const f32x4*)&sm.beta[4 * gg];
 #pragma unroll
                 for (int vv = 0; vv < 4; ++vv) {
                     const int rr = 4 * gg + vv;
-                    sm.L[rr][m] = (m < rr) ? sm.beta[rr] * acc[vv] : 0.f;
+                    const float lv = b4[vv] * acc[vv];
+                    sm.L[rr][m] = (m < rr) ? lv : 0.f;
                 }
             } else {
 #pragma unroll
@@ -232,36 +256,60 @@ __device__ __forceinline__ void k1_chunk(const uint16_t* __restrict__ q,
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // -- WY inverse applied by forward substitution, one column per thread --
-    {
+    if (act) {
         const int col = tid;  // 0..127: column of W, 128..255: column of U~
         float x[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) x[i] = sm.XY[i][col];
+        // row rr of L is read one row ahead of its use
+        f32x4 lnext[4], lcur[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) lnext[q4] = *(const f32x4*)&sm.L[1][4 * q4];
 #pragma unroll
         for (int rr = 1; rr < CH; ++rr) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) lcur[q4] = lnext[q4];
+            if (rr + 1 < CH) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    if (4 * q4 < rr + 1) lnext[q4] = *(const f32x4*)&sm.L[rr + 1][4 * q4];
+            }
             float acc = x[rr];
 #pragma unroll
-            for (int i = 0; i < rr; ++i) acc = __builtin_fmaf(-sm.L[rr][i], x[i], acc);
+            for (int i = 0; i < rr; ++i) acc = __builtin_fmaf(-lcur[i >> 2][i & 3], x[i], acc);
             x[rr] = acc;
         }
         if (col < D) {
-            const int p = col >> 5, half = (col >> 4) & 1, gq = (col >> 2) & 3, jj = col & 3;
+            // W row-major (swizzled), one column per thread
 #pragma unroll
             for (int rr = 0; rr < CH; ++rr)
-                *(uint16_t*)(rec + REC_W + p * 1024 + (gq * 16 + rr) * 16 + half * 8 + jj * 2) =
-                    (uint16_t)bf16_bits(x[rr]);
+                *(uint16_t*)(rec + REC_W + swz(rr, col)) = (uint16_t)bf16_bits(x[rr]);
+            // Kt: transpose column `col` of the row-major scratch into column-major
+            uint32_t kw[8];
+#pragma unroll
+            for (int rr = 0; rr < CH; rr += 2) {
+                const uint32_t lo = *(const uint16_t*)((const uint8_t*)sm.kt + swz(rr, col));
+                const uint32_t hi = *(const uint16_t*)((const uint8_t*)sm.kt + swz(rr + 1, col));
+                kw[rr >> 1] = lo | (hi << 16);
+            }
+            *(u32x4*)(rec + REC_KT + 32 * col) = u32x4{kw[0], kw[1], kw[2], kw[3]};
+            *(u32x4*)(rec + REC_KT + 32 * col + 16) = u32x4{kw[4], kw[5], kw[6], kw[7]};
         } else {
-            const int j = col - D, n16 = j >> 4, mm = j & 15;
-#pragma unroll
-            for (int rr = 0; rr < CH; ++rr)
-                *(uint16_t*)(rec + REC_U + n16 * 512 + ((rr >> 2) * 16 + mm) * 8 + (rr & 3) * 2) =
-                    (uint16_t)bf16_bits(x[rr]);
+            // U~ column-major, one column per thread
+            const int j = col - D;
+            u32x4 w0, w1;
+            w0.x = pack_bf16(x[0], x[1]);   w0.y = pack_bf16(x[2], x[3]);
+            w0.z = pack_bf16(x[4], x[5]);   w0.w = pack_bf16(x[6], x[7]);
+            w1.x = pack_bf16(x[8], x[9]);   w1.y = pack_bf16(x[10], x[11]);
+            w1.z = pack_bf16(x[12], x[13]); w1.w = pack_bf16(x[14], x[15]);
+            *(u32x4*)(rec + REC_U + 32 * j) = w0;
+            *(u32x4*)(rec + REC_U + 32 * j + 16) = w1;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -288,11 +336,18 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][2],
             Sb[p][n].z = pack_bf16(S[2 * p + 1][n][0], S[2 * p + 1][n][1]);
             Sb[p][n].w = pack_bf16(S[2 * p + 1][n][2], S[2 * p + 1][n][3]);
         }
+    const int m = lane & 15;
+    // fragment of a swizzled row-major block: row m, channels dkperm(p, gg, 0..7)
+    auto row_frag = [&](int base, int p) {
+        const u32x2 a0 = *(const u32x2*)(rec + base + swz(m, 32 * p + 4 * gg));
+        const u32x2 a1 = *(const u32x2*)(rec + base + swz(m, 32 * p + 16 + 4 * gg));
+        return u32x4{a0.x, a0.y, a1.x, a1.y};
+    };
     // W S0
     f32x4 ws[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const u32x4 wf = *(const u32x4*)(rec + REC_W + p * 1024 + lane * 16);
+        const u32x4 wf = row_frag(REC_W, p);
 #pragma unroll
         for (int n = 0; n < 2; ++n) ws[n] = mfma_k32(wf, Sb[p][n], ws[n]);
     }
@@ -302,7 +357,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][2],
     for (int n = 0; n < 2; ++n) {
         f32x4 u;
         if constexpr (WITH_U) {
-            const u32x2 uw = *(const u32x2*)(rec + REC_U + (wcol + n) * 512 + lane * 8);
+            const u32x2 uw = *(const u32x2*)(rec + REC_U + 32 * (16 * (wcol + n) + m) + 8 * gg);
             u[0] = bf16_lo(uw.x) - ws[n][0];
             u[1] = bf16_hi(uw.x) - ws[n][1];
             u[2] = bf16_lo(uw.y) - ws[n][2];
@@ -320,7 +375,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][2],
         for (int n = 0; n < 2; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const u32x4 qf = *(const u32x4*)(rec + REC_Q + p * 1024 + lane * 16);
+            const u32x4 qf = row_frag(REC_Q, p);
 #pragma unroll
             for (int n = 0; n < 2; ++n) oacc[n] = mfma_k32(Sb[p][n], qf, oacc[n]);
         }
@@ -331,7 +386,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][2],
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const f32x4 gcv = *(const f32x4*)(rec + REC_GC + (16 * t + 4 * gg) * 4);
-        const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + lane * 8);
+        const u32x2 kt = *(const u32x2*)(rec + REC_KT + 32 * (16 * t + m) + 8 * gg);
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             S[t][n] = gcv * S[t][n];

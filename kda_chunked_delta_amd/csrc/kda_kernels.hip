@@ -26,13 +26,7 @@ __device__ __forceinline__ int rows_of(int64_t tok, int64_t end) {
     return n <= 0 ? 0 : (n >= CH ? CH : (int)n);
 }
 
-template <int NT>
-__device__ __forceinline__ void copy_record_to_lds(const uint8_t* __restrict__ src, uint8_t* dst) {
-    const u32x4* s = (const u32x4*)src;
-    u32x4* d = (u32x4*)dst;
-    for (int i = threadIdx.x; i < REC_VEC; i += NT) d[i] = s[i];
-}
-
+// Record prefetch through registers: NT threads each hold N 16-byte vectors.
 template <int NT>
 struct RecordPrefetch {
     static constexpr int N = (REC_VEC + NT - 1) / NT;
@@ -55,6 +49,109 @@ struct RecordPrefetch {
     }
 };
 
+// Stream nc materialised records (starting at rb) through a double-buffered
+// LDS stage; records are fetched two chunks ahead. step(ci, rec) runs once
+// per chunk with the record in LDS, by every thread.
+template <int NT, class Step>
+__device__ __forceinline__ void record_loop(const uint8_t* __restrict__ rb, int nc,
+                                            uint8_t (*recs)[REC_BYTES], Step&& step) {
+    RecordPrefetch<NT> p0, p1;
+    if (nc > 0) p0.load(rb);
+    if (nc > 1) p1.load(rb + REC_BYTES);
+    if (nc > 0) p0.store(recs[0]);
+    lds_barrier();
+    for (int ci = 0; ci < nc; ci += 2) {
+        if (ci + 2 < nc) p0.load(rb + (size_t)(ci + 2) * REC_BYTES);
+        step(ci, recs[0]);
+        if (ci + 1 < nc) p1.store(recs[1]);
+        lds_barrier();
+        if (ci + 1 < nc) {
+            if (ci + 3 < nc) p1.load(rb + (size_t)(ci + 3) * REC_BYTES);
+            step(ci + 1, recs[1]);
+            if (ci + 2 < nc) p0.store(recs[0]);
+            lds_barrier();
+        }
+    }
+}
+
+// Recompute K1 for nc chunks starting at token tok0 (sequence end `end`),
+// raw inputs fetched two chunks ahead; step(ci, rec) runs once per chunk
+// with the chunk's record in LDS, by every thread.
+template <class Step>
+__device__ __forceinline__ void fused_loop(const CommonArgs& c, int h, int64_t tok0, int64_t end,
+                                           int nc, K1Smem& sm, uint8_t* rec, Step&& step) {
+    RawChunk r0, r1;
+    auto load = [&](int ci, RawChunk& raw) {
+        const int64_t t = tok0 + (int64_t)CH * ci;
+        k1_load(c.q, c.k, c.v, c.g, c.beta, c.H, h, t, rows_of(t, end), raw);
+    };
+    if (nc > 0) load(0, r0);
+    if (nc > 1) load(1, r1);
+    for (int ci = 0; ci < nc; ci += 2) {
+        k1_compute(r0, sm, rec);
+        if (ci + 2 < nc) load(ci + 2, r0);
+        step(ci, rec);
+        lds_barrier();
+        if (ci + 1 < nc) {
+            k1_compute(r1, sm, rec);
+            if (ci + 3 < nc) load(ci + 3, r1);
+            step(ci + 1, rec);
+            lds_barrier();
+        }
+    }
+}
+
+__device__ __forceinline__ void load_state(const float* sin, f32x4 (&S)[8][2], int wcol, int gg, int m) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                S[t][n][vv] = sin ? sin[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] : 0.f;
+}
+
+__device__ __forceinline__ void store_state(float* so, const f32x4 (&S)[8][2], int wcol, int gg, int m) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                so[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] = S[t][n][vv];
+}
+
+__device__ __forceinline__ void identity_state(f32x4 (&S)[8][2], int wcol, int gg, int m) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                S[t][n][vv] = (16 * t + 4 * gg + vv == 16 * (wcol + n) + m) ? 1.f : 0.f;
+}
+
+// Output rows of one chunk: oacc[n][v] is o[token m][16(wcol + n) + 4gg + v].
+__device__ __forceinline__ void store_output(const K2Args& a, int h, int64_t tk, int64_t end,
+                                             const f32x4 (&oacc)[2], int wcol, int gg, int m) {
+    if (m < rows_of(tk, end)) {
+        uint16_t* orow = a.out + ((size_t)(tk + m) * a.c.H + h) * D;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            u32x2 w;
+            w.x = pack_bf16(a.scale * oacc[n][0], a.scale * oacc[n][1]);
+            w.y = pack_bf16(a.scale * oacc[n][2], a.scale * oacc[n][3]);
+            *(u32x2*)(orow + 16 * (wcol + n) + 4 * gg) = w;
+        }
+    }
+}
+
+__device__ __forceinline__ const float* unit_state_in(const K2Args& a, const UnitDesc& u, int h) {
+    if (u.in_slot >= 0) return a.carries + ((size_t)u.in_slot * a.c.H + h) * (D * D);
+    if (a.s0) return a.s0 + ((size_t)u.seq * a.c.H + h) * (D * D);
+    return nullptr;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -70,17 +167,46 @@ __global__ __launch_bounds__(256) void kda_k1_prepare(K1Args a) {
     int64_t beg, end;
     seq_bounds(a.c, cd.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
-    k1_chunk(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, tok0, rows_of(tok0, end), sm, rec);
+    RawChunk raw;
+    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, tok0, rows_of(tok0, end), raw);
+    k1_compute(raw, sm, rec);
     u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_BYTES);
     const u32x4* src = (const u32x4*)rec;
     for (int i = threadIdx.x; i < REC_VEC; i += 256) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
-// K2: one workgroup of 4 wavefronts per (unit, head); wavefront w owns value
-// columns 32w..32w+31. Records stream through a double-buffered LDS stage.
+// Fused K1 + K2 (the serial path, and segment-K2 of CP): one workgroup of 4
+// wavefronts per (unit, head). Each chunk's record is computed into LDS by
+// the whole workgroup, then wavefront w advances value columns 32w..32w+31
+// of the state, held in MFMA accumulators for the whole unit.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kda_k2_recur(K2Args a) {
+__global__ __launch_bounds__(256) void kda_fused(K2Args a) {
+    __shared__ K1Smem sm;
+    __shared__ __align__(16) uint8_t rec[REC_BYTES];
+    const int H = a.c.H;
+    const int h = blockIdx.x % H;
+    const UnitDesc u = a.units[blockIdx.x / H];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gg = lane >> 4, m = lane & 15;
+    const int wcol = 2 * wave;
+    int64_t beg, end;
+    seq_bounds(a.c, u.seq, beg, end);
+    const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
+    f32x4 S[8][2];
+    load_state(unit_state_in(a, u, h), S, wcol, gg, m);
+    fused_loop(a.c, h, tok0, end, u.n_chunks, sm, rec, [&](int ci, const uint8_t* r) {
+        f32x4 oacc[2];
+        chain_step<true, true>(r, S, wcol, lane, oacc);
+        store_output(a, h, tok0 + (int64_t)CH * ci, end, oacc, wcol, gg, m);
+    });
+    if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wcol, gg, m);
+}
+
+// ---------------------------------------------------------------------------
+// K2 over materialised K1 records (segment-K2 of the record-based CP path).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void kda_k2_recur(K2Args a) {
     __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
@@ -91,66 +217,27 @@ __global__ __launch_bounds__(256) void kda_k2_recur(K2Args a) {
     int64_t beg, end;
     seq_bounds(a.c, u.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
-
-    const float* sin = nullptr;
-    if (u.in_slot >= 0)
-        sin = a.carries + ((size_t)u.in_slot * H + h) * (D * D);
-    else if (a.s0)
-        sin = a.s0 + ((size_t)u.seq * H + h) * (D * D);
     f32x4 S[8][2];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv)
-                S[t][n][vv] = sin ? sin[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] : 0.f;
-
+    load_state(unit_state_in(a, u, h), S, wcol, gg, m);
     const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0) * REC_BYTES;
-    const int nc = u.n_chunks;
-    if (nc > 0) copy_record_to_lds<256>(rb, recs[0]);
-    __syncthreads();
-    RecordPrefetch<256> pf;
-    for (int c = 0; c < nc; ++c) {
-        const bool more = c + 1 < nc;
-        if (more) pf.load(rb + (size_t)(c + 1) * REC_BYTES);
+    record_loop<256>(rb, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
         f32x4 oacc[2];
-        chain_step<true, true>(recs[c & 1], S, wcol, lane, oacc);
-        const int64_t tk = tok0 + (int64_t)CH * c;
-        if (m < rows_of(tk, end)) {
-            uint16_t* orow = a.out + ((size_t)(tk + m) * H + h) * D;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                u32x2 w;
-                w.x = pack_bf16(a.scale * oacc[n][0], a.scale * oacc[n][1]);
-                w.y = pack_bf16(a.scale * oacc[n][2], a.scale * oacc[n][3]);
-                *(u32x2*)(orow + 16 * (wcol + n) + 4 * gg) = w;
-            }
-        }
-        if (more) pf.store(recs[(c + 1) & 1]);
-        __syncthreads();
-    }
-    if (u.write_final && a.sT) {
-        float* so = a.sT + ((size_t)u.seq * H + h) * (D * D);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-                for (int vv = 0; vv < 4; ++vv)
-                    so[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] = S[t][n][vv];
-    }
+        chain_step<true, true>(r, S, wcol, lane, oacc);
+        store_output(a, h, tok0 + (int64_t)CH * ci, end, oacc, wcol, gg, m);
+    });
+    if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wcol, gg, m);
 }
 
 // ---------------------------------------------------------------------------
 // CP pre_scan: one workgroup of 8 wavefronts per (segment, head). Wavefronts
 // 0..3 run the K2 state update from S = 0 over the segment (B, value columns
 // 32w..), wavefronts 4..7 run it from S = I with U~ := 0 (M, key columns
-// 32(w-4)..). Both use the same chain step as K2, so B follows K2's
-// arithmetic exactly.
+// 32(w-4)..). Both use K2's chain step, so B follows K2's arithmetic exactly.
+// The fused form recomputes each chunk's K1 record; the record form reads the
+// records K1 materialised.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void kda_cp_prescan(PrescanArgs a) {
-    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
+template <bool FUSED>
+__device__ __forceinline__ void prescan_body(const PrescanArgs& a, K1Smem* sm, uint8_t (*recs)[REC_BYTES]) {
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const PrescanDesc it = a.items[blockIdx.x / H];
@@ -158,40 +245,38 @@ __global__ __launch_bounds__(512) void kda_cp_prescan(PrescanArgs a) {
     const int gg = lane >> 4, m = lane & 15;
     const bool is_b = wave < 4;
     const int wcol = 2 * (wave & 3);
-
     f32x4 S[8][2];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv)
-                S[t][n][vv] = (!is_b && 16 * t + 4 * gg + vv == 16 * (wcol + n) + m) ? 1.f : 0.f;
-
-    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
-    const int nc = it.n_chunks;
-    if (nc > 0) copy_record_to_lds<512>(rb, recs[0]);
-    __syncthreads();
-    RecordPrefetch<512> pf;
+    if (is_b)
+        load_state(nullptr, S, wcol, gg, m);
+    else
+        identity_state(S, wcol, gg, m);
     f32x4 unused[2];
-    for (int c = 0; c < nc; ++c) {
-        const bool more = c + 1 < nc;
-        if (more) pf.load(rb + (size_t)(c + 1) * REC_BYTES);
+    auto step = [&](int, const uint8_t* r) {
         if (is_b)
-            chain_step<true, false>(recs[c & 1], S, wcol, lane, unused);
+            chain_step<true, false>(r, S, wcol, lane, unused);
         else
-            chain_step<false, false>(recs[c & 1], S, wcol, lane, unused);
-        if (more) pf.store(recs[(c + 1) & 1]);
-        __syncthreads();
+            chain_step<false, false>(r, S, wcol, lane, unused);
+    };
+    if constexpr (FUSED) {
+        int64_t beg, end;
+        seq_bounds(a.c, it.seq, beg, end);
+        fused_loop(a.c, h, beg + (int64_t)CH * it.chunk0, end, it.n_chunks, *sm, recs[0], step);
+    } else {
+        const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
+        record_loop<512>(rb, it.n_chunks, recs, step);
     }
-    float* dst = (is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D);
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv)
-                dst[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] = S[t][n][vv];
+    store_state((is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D), S, wcol, gg, m);
+}
+
+__global__ __launch_bounds__(512) void kda_cp_prescan(PrescanArgs a) {
+    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
+    prescan_body<false>(a, nullptr, recs);
+}
+
+__global__ __launch_bounds__(512) void kda_cp_prescan_fused(PrescanArgs a) {
+    __shared__ K1Smem sm;
+    __shared__ __align__(16) uint8_t recs[1][REC_BYTES];
+    prescan_body<true>(a, &sm, recs);
 }
 
 // ---------------------------------------------------------------------------
@@ -248,6 +333,20 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_fused(const K2Args& a, hipStream_t s) {
+    const long long n = (long long)a.n_units * a.c.H;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_fused, dim3((unsigned)n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cp_prescan_fused(const PrescanArgs& a, hipStream_t s) {
+    const long long n = (long long)a.n_items * a.c.H;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_cp_prescan_fused, dim3((unsigned)n), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s) {
     const long long n = (long long)a.c.total_chunks * a.c.H;
     if (n <= 0) return hipSuccess;

@@ -222,9 +222,10 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
                      [](const PrescanDesc& a, const PrescanDesc& b) { return a.n_chunks > b.n_chunks; });
 
     // workspace layout
+    const bool materialize = env_double("KDA_MATERIALIZE_K1", 0.0) > 0.5;
     size_t off = 0;
     p->off_rec = off;
-    off = align_up(off + (size_t)total_chunks * H * kRecBytes, 256);
+    if (materialize) off = align_up(off + (size_t)total_chunks * H * kRecBytes, 256);
     p->off_b = off;
     off = align_up(off + (size_t)n_prescan * H * kStateBytes, 256);
     p->off_m = off;
@@ -250,6 +251,7 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     in.workspace_bytes = off;
     in.est_serial_us = t_serial * pc.chunk_us;
     in.est_cp_us = (t_cp < 1e299 ? t_cp : -1.0) * pc.chunk_us;
+    in.k1_materialized = materialize ? 1 : 0;
     *out = p;
     return KDA_OK;
 }
@@ -606,14 +608,17 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
         return ee;
     };
 
-    K1Args k1{c, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
-    e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
-    if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
-
+    const bool mat = p->info.k1_materialized != 0;
+    if (mat) {
+        K1Args k1{c, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
+        e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
+        if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+    }
     if (p->info.n_prescan > 0) {
         PrescanArgs pa{c, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
                        (float*)(ws + p->off_b), (float*)(ws + p->off_m)};
-        e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
+        e = mat ? timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); })
+                : timed("cp_prescan_fused", [&] { return launch_cp_prescan_fused(pa, stream); });
         if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
     }
     if (p->info.n_cp_seqs > 0) {
@@ -624,8 +629,10 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
     }
     K2Args ka{c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(), s0, sT,
               (const float*)(ws + p->off_carry), (uint16_t*)out, scale};
-    e = timed(p->info.uses_cp ? "k2_segment" : "k2_recur", [&] { return launch_k2_recur(ka, stream); });
-    if (e != hipSuccess) return hip_fail(e, "k2_recur launch");
+    const char* k2name = mat ? (p->info.uses_cp ? "k2_segment" : "k2_recur")
+                             : (p->info.uses_cp ? "fused_segment" : "fused_serial");
+    e = timed(k2name, [&] { return mat ? launch_k2_recur(ka, stream) : launch_fused(ka, stream); });
+    if (e != hipSuccess) return hip_fail(e, "k2 launch");
     return KDA_OK;
 }
 
@@ -635,7 +642,7 @@ kda_status kda_debug_k1_records(kda_ctx* ctx, const kda_plan* p, const void* q, 
     if (!ctx) return fail(KDA_ERR_INVALID, "kda_debug_k1_records: ctx is NULL");
     if (!records && p && p->info.total_chunks > 0)
         return fail(KDA_ERR_INVALID, "kda_debug_k1_records: records is NULL");
-    // reuse the prefill checks with records standing in for out
+    // the prefill checks, with records standing in for out
     kda_status st = kda_prefill_validate(p, q, k, v, g, beta, cu_dev, 1.0f, nullptr, nullptr, records);
     if (st != KDA_OK) return st;
     if (!p->dev_tables || p->device != ctx->device)

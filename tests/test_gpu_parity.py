@@ -126,32 +126,20 @@ def decode_records(rec):
     """uint8 [17408] record -> dict of fp32 numpy arrays (layout of include/kda.h)."""
     r = rec.cpu().numpy()
     bf = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
-    lanes = np.arange(64)
-    gg, m = lanes // 16, lanes % 16
+    rows, cols = np.meshgrid(np.arange(16), np.arange(128), indexing="ij")
+    swz = rows * 256 + ((((cols // 8) ^ rows) % 16) * 16) + 2 * (cols % 8)
     out = {}
     for name, off in (("Qt", 0), ("W", 4096)):
-        a = bf(r[off:off + 4096].view(np.uint16).reshape(4, 64, 8))
-        x = np.zeros((16, 128), np.float32)
-        for p in range(4):
-            for j in range(8):
-                x[m, 32 * p + 16 * (j // 4) + 4 * gg + j % 4] = a[p, :, j]
-        out[name] = x
-    a = bf(r[8192:12288].view(np.uint16).reshape(8, 64, 4))
-    x = np.zeros((16, 128), np.float32)
-    for t in range(8):
-        for j in range(4):
-            x[4 * gg + j, 16 * t + m] = a[t, :, j]
-    out["Kt"] = x
-    a = bf(r[12288:16384].view(np.uint16).reshape(8, 64, 4))
-    x = np.zeros((16, 128), np.float32)
-    for n in range(8):
-        for j in range(4):
-            x[4 * gg + j, 16 * n + m] = a[n, :, j]
-    out["U"] = x
+        u16 = r[off:off + 4096].view(np.uint16)
+        out[name] = bf(u16[swz // 2])
+    for name, off in (("Kt", 8192), ("U", 12288)):
+        out[name] = bf(r[off:off + 4096].view(np.uint16).reshape(128, 16).T)
     a = bf(r[16384:16896].view(np.uint16).reshape(64, 4))
     x = np.zeros((16, 16), np.float32)
+    lanes = np.arange(64)
+    g, m = lanes // 16, lanes % 16
     for j in range(4):
-        x[m, 4 * gg + j] = a[:, j]
+        x[m, 4 * g + j] = a[:, j]
     out["A_qk"] = x
     out["gC"] = r[16896:17408].view(np.float32).copy()
     return out
@@ -279,6 +267,23 @@ def test_cp_bitwise_on_long_sequence_and_oracle():
     o_ref, s_ref = oracle(d)
     assert_close("out", o_cp, o_ref)
     assert_close("final_state", s_cp, s_ref)
+
+
+def test_materialized_k1_paths_are_bitwise_equal_to_fused(monkeypatch):
+    """The two-kernel form (K1 writes records once; K2, pre_scan read them)
+    runs the same arithmetic as the fused form: serial and CP results match
+    the fused serial path bitwise."""
+    d = draw([1500, 300, 2100], 4, seed=21, state_std=0.1, device=DEV)
+    o_ref, s_ref = run(d, mode=False)
+    monkeypatch.setenv("KDA_MATERIALIZE_K1", "1")
+    p_ser = kda.plan(d["cu_seqlens_host"], 4, False, device=DEV)
+    p_cp = kda.plan_segments(d["cu_seqlens_host"], 4, 64, device=DEV)
+    monkeypatch.delenv("KDA_MATERIALIZE_K1")
+    assert p_ser.info()["k1_materialized"] == 1 and p_cp.info()["k1_materialized"] == 1
+    o1, s1 = run(d, plan=p_ser)
+    assert torch.equal(o1, o_ref) and torch.equal(s1, s_ref)
+    o2, s2 = run(d, plan=p_cp)
+    assert torch.equal(o2, o_ref) and torch.equal(s2, s_ref)
 
 
 def test_cp_weak_decay_within_tolerance():

@@ -55,7 +55,15 @@ def test_serial_plan_orders_longest_first(kda_lib):
     chunks = [u["n_chunks"] for u in units]
     assert chunks == sorted(chunks, reverse=True)
     assert all(u["n_segments"] == 1 for u in units)
-    # workspace holds one 17408-byte record per (chunk, head)
+    # the fused serial path needs no workspace
+    assert info["k1_materialized"] == 0 and info["workspace_bytes"] == 0
+
+
+def test_materialized_plan_sizes_records(kda_lib, monkeypatch):
+    monkeypatch.setenv("KDA_MATERIALIZE_K1", "1")
+    info = kda.plan_host(cu_of([100, 4096]), H=4, n_cus=256).info()
+    # one 17408-byte record per (chunk, head)
+    assert info["k1_materialized"] == 1
     assert info["workspace_bytes"] >= info["total_chunks"] * 4 * 17408
 
 
