@@ -178,16 +178,15 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
  * of (chunk c, head h) at index h * total_chunks + c; layout in
  * KDA_RECORD_* below). Arguments as in kda_prefill. */
 #define KDA_RECORD_BYTES 17408
-/* Record layout (bf16 unless noted; r = token row 0..15 of the chunk, c =
- * channel 0..127; rows past the end of a short chunk are zero):
- *   [0, 4096)      Qt = q * exp(G): row-major 256-byte rows whose 16-byte
- *                  chunks are XOR-swizzled by the row: element (r, c) at byte
- *                  r*256 + ((((c / 8) ^ r) % 16) * 16) + 2 * (c % 8)
+/* Record layout: the order in which a 64-wide wavefront reads its MFMA
+ * fragments (bf16 unless noted). Lane l has g = l / 16, i = l % 16;
+ * dkperm(p, g, j) = 32p + 16(j / 4) + 4g + j % 4. r = token row 0..15 of the
+ * chunk (rows past the end of a short chunk are zero), c = channel.
+ *   [0, 4096)      Qt = q * exp(G): [p 4][lane 64][j 8] = Qt[i][dkperm(p, g, j)]
  *   [4096, 8192)   W (WY-transformed keys): same layout as Qt
- *   [8192, 12288)  Kt = k * exp(G_C - G): column-major, (r, c) at byte 32c + 2r
- *   [12288, 16384) U~ (WY-transformed values): column-major, (r, c) at 32c + 2r
- *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4], lane l = 16g + i,
- *                  element j = A_qk[i][4g + j]
+ *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][lane 64][j 4] = Kt[4g + j][16t + i]
+ *   [12288, 16384) U~ (WY-transformed values): [n 8][lane 64][j 4] = U~[4g + j][16n + i]
+ *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]
  *   [16896, 17408) exp(G_C): fp32 [128]
  */
 kda_status kda_debug_k1_records(kda_ctx *ctx, const kda_plan *plan, const void *q, const void *k,

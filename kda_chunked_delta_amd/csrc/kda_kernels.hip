@@ -74,31 +74,14 @@ __device__ __forceinline__ void record_loop(const uint8_t* __restrict__ rb, int 
     }
 }
 
-// Recompute K1 for nc chunks starting at token tok0 (sequence end `end`),
-// raw inputs fetched two chunks ahead; step(ci, rec) runs once per chunk
-// with the chunk's record in LDS, by every thread.
-template <class Step>
-__device__ __forceinline__ void fused_loop(const CommonArgs& c, int h, int64_t tok0, int64_t end,
-                                           int nc, K1Smem& sm, uint8_t* rec, Step&& step) {
-    RawChunk r0, r1;
-    auto load = [&](int ci, RawChunk& raw) {
-        const int64_t t = tok0 + (int64_t)CH * ci;
-        k1_load(c.q, c.k, c.v, c.g, c.beta, c.H, h, t, rows_of(t, end), raw);
-    };
-    if (nc > 0) load(0, r0);
-    if (nc > 1) load(1, r1);
-    for (int ci = 0; ci < nc; ci += 2) {
-        k1_compute(r0, sm, rec);
-        if (ci + 2 < nc) load(ci + 2, r0);
-        step(ci, rec);
-        lds_barrier();
-        if (ci + 1 < nc) {
-            k1_compute(r1, sm, rec);
-            if (ci + 3 < nc) load(ci + 3, r1);
-            step(ci + 1, rec);
-            lds_barrier();
-        }
-    }
+// Make every register of x live here: its loads complete before this point,
+// so no wait for them is left inside the chunk loop that follows (where it
+// would also wait for the prefetches issued there).
+__device__ __forceinline__ void settle(const f32x4 (&S)[8][2]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) asm volatile("" ::"v"(S[t][n]));
 }
 
 __device__ __forceinline__ void load_state(const float* sin, f32x4 (&S)[8][2], int wcol, int gg, int m) {
@@ -109,6 +92,7 @@ __device__ __forceinline__ void load_state(const float* sin, f32x4 (&S)[8][2], i
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv)
                 S[t][n][vv] = sin ? sin[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] : 0.f;
+    settle(S);
 }
 
 __device__ __forceinline__ void store_state(float* so, const f32x4 (&S)[8][2], int wcol, int gg, int m) {
@@ -155,56 +139,88 @@ __device__ __forceinline__ const float* unit_state_in(const K2Args& a, const Uni
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// K1: one workgroup per (chunk, head); grid = total_chunks * H, head fastest.
+// K1 (materialised form): one workgroup of 8 wavefronts per (chunk, head);
+// grid = total_chunks * H, head fastest. Same two phases as the fused kernel.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kda_k1_prepare(K1Args a) {
-    __shared__ K1Smem sm;
+__global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     __shared__ __align__(16) uint8_t rec[REC_BYTES];
+    __shared__ __align__(16) uint8_t ws[K1_BYTES];
+    __shared__ __align__(16) float lw[4][K1_LBYTES / 4];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const int gc = blockIdx.x / H;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const ChunkDesc cd = a.chunks[gc];
     int64_t beg, end;
     seq_bounds(a.c, cd.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
     RawChunk raw;
-    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, tok0, rows_of(tok0, end), raw);
-    k1_compute(raw, sm, rec);
+    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, tok0, rows_of(tok0, end), wave, lane, raw);
+    k1_phase1(raw, wave, lane, rec, ws);
+    lds_barrier();
+    if (wave < 4) k1_phase2(wave, lane, rec, ws, lw[wave]);
+    lds_barrier();
     u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_BYTES);
     const u32x4* src = (const u32x4*)rec;
-    for (int i = threadIdx.x; i < REC_VEC; i += 256) dst[i] = src[i];
+    for (int i = threadIdx.x; i < REC_VEC; i += 512) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
-// Fused K1 + K2 (the serial path, and segment-K2 of CP): one workgroup of 4
-// wavefronts per (unit, head). Each chunk's record is computed into LDS by
-// the whole workgroup, then wavefront w advances value columns 32w..32w+31
-// of the state, held in MFMA accumulators for the whole unit.
+// Fused K1 + K2 (the serial path): one workgroup of 8 wavefronts per (unit,
+// head), software-pipelined with one barrier per chunk. In the interval that
+// ends with barrier i, all 8 wavefronts run K1 phase 1 of chunk i+2,
+// wavefronts 0..3 run K1 phase 2 of chunk i+1, and wavefronts 4..7 advance
+// the state over chunk i (wavefront 4+w owns value columns 32w..32w+31, held
+// in MFMA accumulators for the whole unit). Records live in a 3-deep LDS
+// ring, K1 scratch in a 2-deep one; raw inputs are prefetched one chunk ahead.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kda_fused(K2Args a) {
-    __shared__ K1Smem sm;
-    __shared__ __align__(16) uint8_t rec[REC_BYTES];
+constexpr int FUSED_LDS = 3 * REC_BYTES + 2 * K1_BYTES + 4 * K1_LBYTES;
+
+__global__ __launch_bounds__(512) void kda_fused(K2Args a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t* recs = smem;
+    uint8_t* wss = smem + 3 * REC_BYTES;
+    float* lws = (float*)(wss + 2 * K1_BYTES);
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const UnitDesc u = a.units[blockIdx.x / H];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int gg = lane >> 4, m = lane & 15;
-    const int wcol = 2 * wave;
+    const bool chain = wave >= 4;
+    const int wcol = 2 * (wave & 3);
     int64_t beg, end;
     seq_bounds(a.c, u.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
+    const int nc = u.n_chunks;
     f32x4 S[8][2];
-    load_state(unit_state_in(a, u, h), S, wcol, gg, m);
-    fused_loop(a.c, h, tok0, end, u.n_chunks, sm, rec, [&](int ci, const uint8_t* r) {
-        f32x4 oacc[2];
-        chain_step<true, true>(r, S, wcol, lane, oacc);
-        store_output(a, h, tok0 + (int64_t)CH * ci, end, oacc, wcol, gg, m);
-    });
-    if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wcol, gg, m);
+    if (chain) load_state(unit_state_in(a, u, h), S, wcol, gg, m);
+    RawChunk raw;
+    auto load = [&](int ci) {
+        const int64_t t = tok0 + (int64_t)CH * ci;
+        k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, t, rows_of(t, end), wave, lane, raw);
+    };
+    if (nc > 0) load(0);
+    for (int i = -2; i < nc; ++i) {
+        if (i + 2 < nc) {
+            k1_phase1(raw, wave, lane, recs + ((i + 2) % 3) * REC_BYTES, wss + ((i + 2) & 1) * K1_BYTES);
+            if (i + 3 < nc) load(i + 3);
+        }
+        if (!chain) {
+            if (i + 1 >= 0 && i + 1 < nc)
+                k1_phase2(wave, lane, recs + ((i + 1) % 3) * REC_BYTES, wss + ((i + 1) & 1) * K1_BYTES,
+                          lws + wave * (K1_LBYTES / 4));
+        } else if (i >= 0) {
+            f32x4 oacc[2];
+            chain_step<true, true>(recs + (i % 3) * REC_BYTES, S, wcol, lane, oacc);
+            store_output(a, h, tok0 + (int64_t)CH * i, end, oacc, wcol, gg, m);
+        }
+        lds_barrier();
+    }
+    if (chain && u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wcol, gg, m);
 }
 
 // ---------------------------------------------------------------------------
-// K2 over materialised K1 records (segment-K2 of the record-based CP path).
+// K2 over materialised K1 records (two-kernel serial form and CP segment-K2).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void kda_k2_recur(K2Args a) {
     __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
@@ -229,15 +245,14 @@ __global__ __launch_bounds__(256, 2) void kda_k2_recur(K2Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// CP pre_scan: one workgroup of 8 wavefronts per (segment, head). Wavefronts
-// 0..3 run the K2 state update from S = 0 over the segment (B, value columns
-// 32w..), wavefronts 4..7 run it from S = I with U~ := 0 (M, key columns
-// 32(w-4)..). Both use K2's chain step, so B follows K2's arithmetic exactly.
-// The fused form recomputes each chunk's K1 record; the record form reads the
-// records K1 materialised.
+// CP pre_scan over materialised K1 records: one workgroup of 8 wavefronts per
+// (segment, head). Wavefronts 0..3 run the K2 state update from S = 0 over
+// the segment (B, value columns 32w..), wavefronts 4..7 run it from S = I
+// with U~ := 0 (M, key columns 32(w-4)..). Both use K2's chain step, so B
+// follows K2's arithmetic exactly.
 // ---------------------------------------------------------------------------
-template <bool FUSED>
-__device__ __forceinline__ void prescan_body(const PrescanArgs& a, K1Smem* sm, uint8_t (*recs)[REC_BYTES]) {
+__global__ __launch_bounds__(512) void kda_cp_prescan(PrescanArgs a) {
+    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const PrescanDesc it = a.items[blockIdx.x / H];
@@ -251,32 +266,14 @@ __device__ __forceinline__ void prescan_body(const PrescanArgs& a, K1Smem* sm, u
     else
         identity_state(S, wcol, gg, m);
     f32x4 unused[2];
-    auto step = [&](int, const uint8_t* r) {
+    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
+    record_loop<512>(rb, it.n_chunks, recs, [&](int, const uint8_t* r) {
         if (is_b)
             chain_step<true, false>(r, S, wcol, lane, unused);
         else
             chain_step<false, false>(r, S, wcol, lane, unused);
-    };
-    if constexpr (FUSED) {
-        int64_t beg, end;
-        seq_bounds(a.c, it.seq, beg, end);
-        fused_loop(a.c, h, beg + (int64_t)CH * it.chunk0, end, it.n_chunks, *sm, recs[0], step);
-    } else {
-        const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
-        record_loop<512>(rb, it.n_chunks, recs, step);
-    }
+    });
     store_state((is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D), S, wcol, gg, m);
-}
-
-__global__ __launch_bounds__(512) void kda_cp_prescan(PrescanArgs a) {
-    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
-    prescan_body<false>(a, nullptr, recs);
-}
-
-__global__ __launch_bounds__(512) void kda_cp_prescan_fused(PrescanArgs a) {
-    __shared__ K1Smem sm;
-    __shared__ __align__(16) uint8_t recs[1][REC_BYTES];
-    prescan_body<true>(a, &sm, recs);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,21 +333,17 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
 hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     const long long n = (long long)a.n_units * a.c.H;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_fused, dim3((unsigned)n), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_cp_prescan_fused(const PrescanArgs& a, hipStream_t s) {
-    const long long n = (long long)a.n_items * a.c.H;
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_cp_prescan_fused, dim3((unsigned)n), dim3(512), 0, s, a);
+    static hipError_t attr = hipFuncSetAttribute((const void*)kda_fused,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kda_fused, dim3((unsigned)n), dim3(512), FUSED_LDS, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s) {
     const long long n = (long long)a.c.total_chunks * a.c.H;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_k1_prepare, dim3((unsigned)n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(kda_k1_prepare, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

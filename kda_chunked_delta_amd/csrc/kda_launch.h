@@ -94,7 +94,6 @@ struct K1Args {
 
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s);
 hipError_t launch_fused(const K2Args& a, hipStream_t s);
-hipError_t launch_cp_prescan_fused(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
 hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);

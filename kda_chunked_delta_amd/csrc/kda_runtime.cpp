@@ -222,7 +222,9 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
                      [](const PrescanDesc& a, const PrescanDesc& b) { return a.n_chunks > b.n_chunks; });
 
     // workspace layout
-    const bool materialize = env_double("KDA_MATERIALIZE_K1", 0.0) > 0.5;
+    // CP plans always materialise K1 (K1 once, then pre_scan and segment-K2
+    // read its records); serial plans run the fused kernel unless asked not to.
+    const bool materialize = n_cp_seqs > 0 || env_double("KDA_MATERIALIZE_K1", 0.0) > 0.5;
     size_t off = 0;
     p->off_rec = off;
     if (materialize) off = align_up(off + (size_t)total_chunks * H * kRecBytes, 256);
@@ -617,8 +619,7 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
     if (p->info.n_prescan > 0) {
         PrescanArgs pa{c, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
                        (float*)(ws + p->off_b), (float*)(ws + p->off_m)};
-        e = mat ? timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); })
-                : timed("cp_prescan_fused", [&] { return launch_cp_prescan_fused(pa, stream); });
+        e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
         if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
     }
     if (p->info.n_cp_seqs > 0) {

@@ -126,20 +126,27 @@ def decode_records(rec):
     """uint8 [17408] record -> dict of fp32 numpy arrays (layout of include/kda.h)."""
     r = rec.cpu().numpy()
     bf = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
-    rows, cols = np.meshgrid(np.arange(16), np.arange(128), indexing="ij")
-    swz = rows * 256 + ((((cols // 8) ^ rows) % 16) * 16) + 2 * (cols % 8)
+    lanes = np.arange(64)
+    g, i = lanes // 16, lanes % 16
     out = {}
     for name, off in (("Qt", 0), ("W", 4096)):
-        u16 = r[off:off + 4096].view(np.uint16)
-        out[name] = bf(u16[swz // 2])
+        a = bf(r[off:off + 4096].view(np.uint16).reshape(4, 64, 8))
+        x = np.zeros((16, 128), np.float32)
+        for p in range(4):
+            for j in range(8):
+                x[i, 32 * p + 16 * (j // 4) + 4 * g + j % 4] = a[p, :, j]
+        out[name] = x
     for name, off in (("Kt", 8192), ("U", 12288)):
-        out[name] = bf(r[off:off + 4096].view(np.uint16).reshape(128, 16).T)
+        a = bf(r[off:off + 4096].view(np.uint16).reshape(8, 64, 4))
+        x = np.zeros((16, 128), np.float32)
+        for t in range(8):
+            for j in range(4):
+                x[4 * g + j, 16 * t + i] = a[t, :, j]
+        out[name] = x
     a = bf(r[16384:16896].view(np.uint16).reshape(64, 4))
     x = np.zeros((16, 16), np.float32)
-    lanes = np.arange(64)
-    g, m = lanes // 16, lanes % 16
     for j in range(4):
-        x[m, 4 * g + j] = a[:, j]
+        x[i, 4 * g + j] = a[:, j]
     out["A_qk"] = x
     out["gC"] = r[16896:17408].view(np.float32).copy()
     return out
