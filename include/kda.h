@@ -177,17 +177,21 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
  * into `records` (device, total_chunks * H * KDA_RECORD_BYTES bytes, record
  * of (chunk c, head h) at index h * total_chunks + c; layout in
  * KDA_RECORD_* below). Arguments as in kda_prefill. */
-#define KDA_RECORD_BYTES 17408
+#define KDA_RECORD_BYTES 18432
 /* Record layout: the order in which a 64-wide wavefront reads its MFMA
  * fragments (bf16 unless noted). Lane l has g = l / 16, i = l % 16;
  * dkperm(p, g, j) = 32p + 16(j / 4) + 4g + j % 4. r = token row 0..15 of the
  * chunk (rows past the end of a short chunk are zero), c = channel.
  *   [0, 4096)      Qt = q * exp(G): [p 4][lane 64][j 8] = Qt[i][dkperm(p, g, j)]
- *   [4096, 8192)   W (WY-transformed keys): same layout as Qt
+ *   [4096, 8192)   X = k * exp(G): same layout as Qt
  *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][lane 64][j 4] = Kt[4g + j][16t + i]
- *   [12288, 16384) U~ (WY-transformed values): [n 8][lane 64][j 4] = U~[4g + j][16n + i]
+ *   [12288, 16384) V (the chunk's values): [n 8][lane 64][j 4] = V[4g + j][16n + i]
  *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]
  *   [16896, 17408) exp(G_C): fp32 [128]
+ *   [17408, 18432) T' = (I + L)^-1 diag(beta), L = strict-lower(diag(beta) A_kk),
+ *                  as a bf16 pair hi + lo: [2][lane 64][j 4] = T'[i][4g + j]
+ * K2 forms U = T' (V - X S) (= U~ - W S in WY terms), then O = Qt S + A_qk U
+ * and S <- Diag(exp G_C) S + Kt^T U.
  */
 kda_status kda_debug_k1_records(kda_ctx *ctx, const kda_plan *plan, const void *q, const void *k,
                                 const void *v, const float *g, const float *beta,

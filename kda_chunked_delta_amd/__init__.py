@@ -279,7 +279,7 @@ def k1_records(q, k, v, g, beta, plan):
     return rec
 
 
-RECORD_BYTES = 17408
+RECORD_BYTES = 18432
 
 
 def _ptr(t):

@@ -8,13 +8,15 @@
 // cumulative log-decay G_r (per key channel) and G_C = G at the last row:
 //   A_kk[r,i] = sum_d k_rd k_id exp(G_rd - G_id)   (i < r)
 //   A_qk[r,i] = sum_d q_rd k_id exp(G_rd - G_id)   (i <= r)
-//   L  = strict-lower(diag(beta) A_kk)
-//   W  = (I + L)^-1 diag(beta) (k * exp G),   U~ = (I + L)^-1 diag(beta) v
-//   Qt = q * exp G,   Kt = k * exp(G_C - G)
-//   U  = U~ - W S0;   O = Qt S0 + A_qk U;   S_next = Diag(exp G_C) S0 + Kt^T U
-// All matrix products run on bf16 MFMA with fp32 accumulation; the state
-// and the decays stay fp32, and the WY inverse is formed in fp32 and applied
-// as a hi/lo pair of bf16 MFMA operands.
+//   L  = strict-lower(diag(beta) A_kk),   T' = (I + L)^-1 diag(beta)
+//   X  = k * exp G,   Qt = q * exp G,   Kt = k * exp(G_C - G)
+//   U  = T' (V - X S0)
+//   O  = Qt S0 + A_qk U,   S_next = Diag(exp G_C) S0 + Kt^T U
+// U is the WY form U~ - W S0 with W = T' X and U~ = T' V regrouped, so K1
+// never forms W or U~ and K2 applies T' to the 16 x 16 tile V - X S0.
+// All matrix products run on bf16 MFMA with fp32 accumulation; the state and
+// the decays stay fp32, and T' is formed in fp32 and applied as a hi/lo pair
+// of bf16 MFMA operands.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,33 +36,41 @@ constexpr int CH = 16;   // chunk length
 // MFMA step, chosen so the fp32 state, held in 16x16 accumulator tiles,
 // feeds the next MFMA as an operand without any shuffle.
 //   REC_Q  : Qt fragments [p 4][lane 64][8 bf16]: Qt[m][dkperm(p, gg, j)]
-//   REC_W  : W fragments, same layout as REC_Q
+//   REC_X  : X fragments, same layout as REC_Q
 //   REC_KT : Kt^T fragments [t 8][lane 64][4 bf16]: Kt[4gg + j][16t + m]
-//   REC_U  : U~ in accumulator layout [n 8][lane 64][4 bf16]: U~[4gg + j][16n + m]
-//   REC_AQK: A_qk^T fragment [lane 64][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
+//   REC_V  : V in accumulator layout [n 8][lane 64][4 bf16]: V[4gg + j][16n + m]
+//   REC_AQK: A_qk fragment [lane 64][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
 //   REC_GC : exp(G_C) [128] fp32
+//   REC_T  : T' fragments, hi then lo [2][lane 64][4 bf16]: T'[m][4gg + j]
 // The same bytes are used in LDS and, when K1 is materialised, in HBM.
 // ---------------------------------------------------------------------------
 constexpr int REC_Q = 0;
-constexpr int REC_W = 4096;
+constexpr int REC_X = 4096;
 constexpr int REC_KT = 8192;
-constexpr int REC_U = 12288;
+constexpr int REC_V = 12288;
 constexpr int REC_AQK = 16384;
 constexpr int REC_GC = 16896;
-constexpr int REC_BYTES = 17408;
-constexpr int REC_VEC = REC_BYTES / 16;  // 1088 16-byte vectors
+constexpr int REC_T = 17408;
+constexpr int REC_BYTES = 18432;
+constexpr int REC_VEC = REC_BYTES / 16;  // 1152 16-byte vectors
 
-// K1 scratch of one chunk (LDS only), shared between its two phases:
-//   K1_XCT : X = beta k exp(G) (bf16) in Kt^T fragment layout: X[4gg + j][16t + m]
-//   K1_YCT : Y = beta v (bf16), same layout
-//   K1_GP  : partial Grams fp32 [wavefront 8][A_kk, A_qk][lane 64][4] over its 16 channels
-//   K1_BETA: beta of the chunk's 16 rows, fp32
-constexpr int K1_XCT = 0;
-constexpr int K1_YCT = 4096;
-constexpr int K1_GP = 8192;
-constexpr int K1_BETA = 8192 + 16384;
+// K1 scratch of one chunk (LDS only), from phase 1 to phase 2:
+//   K1_KA, K1_KB, K1_QA: beta k exp(G - G_7), k exp(G_7 - G), q exp(G - G_7)
+//                        as fragments in the REC_Q layout
+//   K1_BETA            : beta of the chunk's 16 rows, fp32
+constexpr int K1_KA = 0;
+constexpr int K1_KB = 4096;
+constexpr int K1_QA = 8192;
+constexpr int K1_BETA = 12288;
 constexpr int K1_BYTES = K1_BETA + 64;
-constexpr int K1_LBYTES = 1024;  // per phase-2 wavefront: L as fp32 [16][16]
+constexpr int K1_LBYTES = 1024;  // per T' wavefront, private LDS: L as fp32 [16][16]
+
+// Phase-2 roles: wavefronts 0..3 (one per SIMD) each form four rows of T',
+// wavefront WAVE_QK forms A_qk.
+constexpr int N_WAVE_T = 4;
+constexpr int WAVE_QK = 5;
+
+constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -76,13 +86,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
-// fp32 -> bf16 bits in the low half.
-__device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16(x, x) & 0xffffu; }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
     return u32x2{pack_bf16(a, b), pack_bf16(c, d)};
 }
+__device__ __forceinline__ u32x2 pack4(const f32x4& x) { return pack4(x[0], x[1], x[2], x[3]); }
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // D(16x16) += A(16x32) B(32x16), bf16 in, fp32 accumulate.
 // A: lane holds A[m][8gg + j]; B: lane holds B[8gg + j][m]; C: lane holds C[4gg + v][m].
@@ -106,31 +118,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// x from lane (m - n) of the same 16-lane row, 0 for m < n (DPP row shift).
+// x from lane (m - n) of the same 16-lane row, 0 for m < n (DPP row shift;
+// folds into the consuming add).
 template <int N>
 __device__ __forceinline__ float row_shr(float x) {
-    return __builtin_amdgcn_update_dpp(0.0f, x, 0x110 + N, 0xF, 0xF, false);
+    return __builtin_amdgcn_update_dpp(0.0f, x, 0x110 + N, 0xF, 0xF, true);
 }
 // x from lane I of the same 16-lane row (swizzle broadcast).
 template <int I>
 __device__ __forceinline__ float row_bcast(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (I << 5)));
 }
-// x from the same lane index m of 16-lane row R, in every row (two permlane swaps).
-template <int R>
-__device__ __forceinline__ float rows_from(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const uint32_t pr = (R & 1) ? s16[1] : s16[0];  // rows (R & 2), (R & 2) + 1 now hold row R
-    const auto s32 = __builtin_amdgcn_permlane32_swap(pr, pr, false, false);
-    return __uint_as_float((R & 2) ? s32[1] : s32[0]);
+// x from lane K of the same 16-lane row (DPP row broadcast; folds into the
+// consuming multiply).
+template <int K>
+__device__ __forceinline__ float row_newbcast(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, 0x150 + K, 0xF, 0xF, true);
 }
 
+// Byte offset of element (row m, column 4gg + j) of a 16-column tile in the
+// transposed 4-element fragment layout [lane (m >> 2) * 16 + 4gg + j][m & 3].
+__device__ __forceinline__ int tfrag_off(int gg, int m) { return ((m >> 2) * 16 + 4 * gg) * 8 + (m & 3) * 2; }
+
 // ---------------------------------------------------------------------------
-// K1, phase 1 (8 wavefronts). Wavefront p (0..7) owns key channels 16p..16p+15
-// and value columns 16p..16p+15; lane (gg, m) holds token m of the chunk and
-// channels 16p + 4gg + j, j = 0..3. Rows past nrows are zero (k = q = v = 0,
-// g = 0, beta = 0), which leaves them inert.
+// K1, phase 1 (8 wavefronts). Wavefront w owns key channels and value
+// columns 16w..16w+15; lane (gg, m) holds token m of the chunk and channels
+// 16w + 4gg + j, j = 0..3. Rows past nrows are zero (k = q = v = 0, g = 0,
+// beta = 0), which leaves them inert.
 // ---------------------------------------------------------------------------
 struct RawChunk {
     u32x2 q, k, v;
@@ -160,114 +174,110 @@ __device__ __forceinline__ void k1_load(const uint16_t* __restrict__ q, const ui
 }
 
 __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lane, uint8_t* rec,
-                                          uint8_t* ws) {
+                                          uint8_t* scr) {
     const int gg = lane >> 4, m = lane & 15;
-    // in-chunk cumulative log-decay per channel: inclusive scan over the tokens
+    // in-chunk cumulative log2-decay per channel: inclusive scan over the tokens
     float G[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        float x = raw.g[j];
+        float x = raw.g[j] * LOG2E;
         x += row_shr<1>(x);
         x += row_shr<2>(x);
         x += row_shr<4>(x);
         x += row_shr<8>(x);
         G[j] = x;
     }
-    // decays relative to the reference row 7: E = exp(G - G_7), F = exp(G_7 - G)
-    float E[4], F[4], c7[4], e15[4];
+    float g7[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g7[j] = row_bcast<7>(G[j]);
+    // decays relative to the reference row 7: E = exp(G - G_7), F = exp(G_7 - G);
+    // gam = exp(G)
+    float E[4], F[4], gam[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float g7 = row_bcast<7>(G[j]);
-        E[j] = __expf(G[j] - g7);
-        F[j] = __expf(g7 - G[j]);
-        c7[j] = __expf(g7);  // exp(G_7)
+        E[j] = exp2_hw(G[j] - g7[j]);
+        F[j] = exp2_hw(g7[j] - G[j]);
+        gam[j] = exp2_hw(G[j]);
     }
+    float e15[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) e15[j] = row_bcast<15>(E[j]);  // exp(G_C - G_7)
     const float qf[4] = {bf16_lo(raw.q.x), bf16_hi(raw.q.x), bf16_lo(raw.q.y), bf16_hi(raw.q.y)};
     const float kf[4] = {bf16_lo(raw.k.x), bf16_hi(raw.k.x), bf16_lo(raw.k.y), bf16_hi(raw.k.y)};
-    const float vf[4] = {bf16_lo(raw.v.x), bf16_hi(raw.v.x), bf16_lo(raw.v.y), bf16_hi(raw.v.y)};
-    float ka[4], kb[4], qa[4], qt[4], kt[4], X[4], Y[4];
+    f32x4 ka, kb, qa, qt, xk, kt;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float gam = E[j] * c7[j];  // exp(G_r)
-        const float kc = F[j] * e15[j];  // exp(G_C - G_r)
-        ka[j] = kf[j] * E[j];
+        ka[j] = raw.b * (kf[j] * E[j]);
         kb[j] = kf[j] * F[j];
         qa[j] = qf[j] * E[j];
-        qt[j] = qf[j] * gam;
-        kt[j] = kf[j] * kc;
-        X[j] = raw.b * (kf[j] * gam);
-        Y[j] = raw.b * vf[j];
+        qt[j] = qf[j] * gam[j];
+        xk[j] = kf[j] * gam[j];
+        kt[j] = kb[j] * e15[j];  // k exp(G_C - G)
     }
-    // partial Grams over this wavefront's 16 channels (A: token m, B: token m)
-    const u32x2 fa = pack4(ka[0], ka[1], ka[2], ka[3]);
-    const u32x2 fb = pack4(kb[0], kb[1], kb[2], kb[3]);
-    const u32x2 fq = pack4(qa[0], qa[1], qa[2], qa[3]);
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 pkk = mfma_k16(fa, fb, zero);
-    const f32x4 pqk = mfma_k16(fq, fb, zero);
-    *(f32x4*)(ws + K1_GP + ((wave * 2 + 0) * 64 + lane) * 16) = pkk;
-    *(f32x4*)(ws + K1_GP + ((wave * 2 + 1) * 64 + lane) * 16) = pqk;
-    // Qt: half (wave & 1) of K-step (wave >> 1)
-    *(u32x2*)(rec + REC_Q + (wave >> 1) * 1024 + lane * 16 + (wave & 1) * 8) = pack4(qt[0], qt[1], qt[2], qt[3]);
-    // Kt^T, X, Y: element (token m, channel 16 wave + 4gg + j) -> tile wave,
+    // fragments in the REC_Q layout: half (wave & 1) of K-step (wave >> 1)
+    const int fo = (wave >> 1) * 1024 + lane * 16 + (wave & 1) * 8;
+    *(u32x2*)(scr + K1_KA + fo) = pack4(ka);
+    *(u32x2*)(scr + K1_KB + fo) = pack4(kb);
+    *(u32x2*)(scr + K1_QA + fo) = pack4(qa);
+    *(u32x2*)(rec + REC_Q + fo) = pack4(qt);
+    *(u32x2*)(rec + REC_X + fo) = pack4(xk);
+    // Kt^T and V: element (token m, channel 16 wave + 4gg + j) -> tile wave,
     // lane (m >> 2) * 16 + 4gg + j, slot m & 3
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int o = wave * 512 + ((m >> 2) * 16 + 4 * gg + j) * 8 + (m & 3) * 2;
-        *(uint16_t*)(rec + REC_KT + o) = (uint16_t)bf16_bits(kt[j]);
-        *(uint16_t*)(ws + K1_XCT + o) = (uint16_t)bf16_bits(X[j]);
-        *(uint16_t*)(ws + K1_YCT + o) = (uint16_t)bf16_bits(Y[j]);
-    }
-    if (m == 0)
-        *(f32x4*)(rec + REC_GC + (16 * wave + 4 * gg) * 4) =
-            f32x4{c7[0] * e15[0], c7[1] * e15[1], c7[2] * e15[2], c7[3] * e15[3]};
-    if (wave == 0 && gg == 0) *(float*)(ws + K1_BETA + 4 * m) = raw.b;
+    const int to = wave * 512 + tfrag_off(gg, m);
+    const u32x2 ktp = pack4(kt);
+    uint8_t* kd = rec + REC_KT + to;
+    uint8_t* vd = rec + REC_V + to;
+    *(uint16_t*)(kd + 0) = (uint16_t)ktp.x;
+    *(uint16_t*)(kd + 8) = (uint16_t)(ktp.x >> 16);
+    *(uint16_t*)(kd + 16) = (uint16_t)ktp.y;
+    *(uint16_t*)(kd + 24) = (uint16_t)(ktp.y >> 16);
+    *(uint16_t*)(vd + 0) = (uint16_t)raw.v.x;
+    *(uint16_t*)(vd + 8) = (uint16_t)(raw.v.x >> 16);
+    *(uint16_t*)(vd + 16) = (uint16_t)raw.v.y;
+    *(uint16_t*)(vd + 24) = (uint16_t)(raw.v.y >> 16);
+    // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
+    if (m == 15) *(f32x4*)(rec + REC_GC + (16 * wave + 4 * gg) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
+    if (wave == 0 && gg == 0) *(float*)(scr + K1_BETA + 4 * m) = raw.b;
 }
 
 // ---------------------------------------------------------------------------
-// K1, phase 2 (4 wavefronts, after a barrier that publishes phase 1): the
-// Grams, L = strict-lower(diag(beta) A_kk), the WY inverse T = (I + L)^-1
-// and the WY-transformed keys and values of tiles 2w, 2w+1. Each wavefront
-// forms T itself (no further barrier); lw is its private 1 KiB of LDS.
+// K1, phase 2 (after a barrier that publishes phase 1). Wavefront s < 4
+// forms L = strict-lower(diag(beta) A_kk) and rows 4s + gg of
+// T' = (I + L)^-1 diag(beta); wavefront WAVE_QK forms the masked A_qk. Both Grams run over all 128 channels on MFMA from the phase-1
+// fragments (each T' wavefront forms its own copy of L, in its private 1 KiB
+// lw, so phase 2 needs no barrier of its own). The inverse is a
+// substitution over 15 dependent steps, each one DPP-broadcast
+// multiply-subtract.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void k1_phase2(int w, int lane, uint8_t* rec, const uint8_t* ws, float* lw) {
+__device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, const uint8_t* scr, float* lw) {
     const int gg = lane >> 4, m = lane & 15;
-    f32x4 akk = *(const f32x4*)(ws + K1_GP + (0 * 64 + lane) * 16);
-    f32x4 aqk = *(const f32x4*)(ws + K1_GP + (1 * 64 + lane) * 16);
+    // (beta k exp(G - G_7)) (k exp(G_7 - G))^T: lane holds beta_r A_kk[r][m], r = 4gg + v
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 1; p < 8; ++p) {
-        akk += *(const f32x4*)(ws + K1_GP + ((p * 2 + 0) * 64 + lane) * 16);
-        aqk += *(const f32x4*)(ws + K1_GP + ((p * 2 + 1) * 64 + lane) * 16);
+    for (int p = 0; p < 4; ++p)
+        a = mfma_k32(*(const u32x4*)(scr + K1_KA + p * 1024 + lane * 16),
+                     *(const u32x4*)(scr + K1_KB + p * 1024 + lane * 16), a);
+    f32x4 l;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) l[v] = (m < 4 * gg + v) ? a[v] : 0.f;
+    // through LDS as L^T (lw[c * 16 + r] = L[r][c]): lane (gg, i) then holds
+    // column i of L, lc[K] = L[K][i]
+    *(f32x4*)(lw + m * 16 + 4 * gg) = l;
+    float lc[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 c = *(const f32x4*)(lw + m * 16 + 4 * q);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lc[4 * q + v] = c[v];
     }
-    // lane holds rows r = 4gg + v, column m
-    const f32x4 b4 = *(const f32x4*)(ws + K1_BETA + 16 * gg);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int r = 4 * gg + v;
-        const float lv = b4[v] * akk[v];
-        lw[r * 16 + m] = (m < r) ? lv : 0.f;
-    }
-    if (w == 0) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = 4 * gg + v;
-            const float val = (m <= r) ? aqk[v] : 0.f;
-            *(uint16_t*)(rec + REC_AQK + ((m >> 2) * 16 + r) * 8 + (m & 3) * 2) = (uint16_t)bf16_bits(val);
-        }
-    }
-    // T^T = (I + L^T)^-1 by back substitution; lane holds T^T[4gg + v][m].
-    // Row k is final once rows k+1..15 are applied; L[k][i] = 0 for i >= k.
-    float tt[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) tt[v] = (4 * gg + v == m) ? 1.f : 0.f;
+    // Rows of T = (I + L)^-1 are independent: T[r][c] = [r = c] -
+    // sum_{K > c} T[r][K] L[K][c]. Row r = 4 s4 + gg lives in 16-lane row gg,
+    // column i in lane i; for K = 15..1, T[r][K] is final and is broadcast
+    // along the row to update the columns c < K (L[K][c] = 0 for c >= K).
+    float t = (4 * s4 + gg == m) ? 1.f : 0.f;
     auto step = [&](auto kc) {
         constexpr int K = decltype(kc)::value;
-        const f32x4 lk = *(const f32x4*)(lw + K * 16 + 4 * gg);  // L[K][4gg .. 4gg+3]
-        const float rowk = rows_from<(K >> 2)>(tt[K & 3]);         // T^T[K][m]
-#pragma unroll
-        for (int v = 0; v < 4; ++v) tt[v] = __builtin_fmaf(-lk[v], rowk, tt[v]);
+        t -= lc[K] * row_newbcast<K>(t);
     };
     step(std::integral_constant<int, 15>{}); step(std::integral_constant<int, 14>{});
     step(std::integral_constant<int, 13>{}); step(std::integral_constant<int, 12>{});
@@ -277,89 +287,104 @@ __device__ __forceinline__ void k1_phase2(int w, int lane, uint8_t* rec, const u
     step(std::integral_constant<int, 5>{});  step(std::integral_constant<int, 4>{});
     step(std::integral_constant<int, 3>{});  step(std::integral_constant<int, 2>{});
     step(std::integral_constant<int, 1>{});
-    // hi/lo bf16 split of T^T: B operand of W^T = X^T T^T and A operand of U~ = T Y
-    const u32x2 th = pack4(tt[0], tt[1], tt[2], tt[3]);
-    const u32x2 tl = pack4(tt[0] - bf16_lo(th.x), tt[1] - bf16_hi(th.x), tt[2] - bf16_lo(th.y),
-                           tt[3] - bf16_hi(th.y));
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // T'[r][i] = T[r][i] beta_i, split into bf16 hi + lo, to the A-fragment
+    // layout T'[m'][4gg' + j] at lane (gg', m') = (i >> 2, r), j = i & 3
+    const float tb = t * *(const float*)(scr + K1_BETA + 4 * m);
+    const uint32_t th = pack_bf16(tb, tb);
+    const uint32_t tl = pack_bf16(tb - bf16_lo(th), tb - bf16_lo(th));
+    uint8_t* td = rec + REC_T + ((16 * (m >> 2) + 4 * s4 + gg) * 4 + (m & 3)) * 2;
+    *(uint16_t*)(td + 0) = (uint16_t)th;
+    *(uint16_t*)(td + 512) = (uint16_t)tl;
+}
+
+__device__ __forceinline__ void k1_phase2_qk(int lane, uint8_t* rec, const uint8_t* scr) {
+    const int gg = lane >> 4, m = lane & 15;
+    // A_qk^T = (k exp(G_7 - G)) (q exp(G - G_7))^T: lane holds A_qk[m][4gg + v]
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-        const int n = 2 * w + nn;
-        // W^T tile n: lane (gg, m) gets W[m][16n + 4gg + v]
-        const u32x2 xf = *(const u32x2*)(ws + K1_XCT + n * 512 + lane * 8);
-        f32x4 wt = mfma_k16(xf, th, zero);
-        wt = mfma_k16(xf, tl, wt);
-        *(u32x2*)(rec + REC_W + (n >> 1) * 1024 + lane * 16 + (n & 1) * 8) = pack4(wt[0], wt[1], wt[2], wt[3]);
-        // U~ tile n: lane (gg, m) gets U~[4gg + v][16n + m]
-        const u32x2 yf = *(const u32x2*)(ws + K1_YCT + n * 512 + lane * 8);
-        f32x4 ut = mfma_k16(th, yf, zero);
-        ut = mfma_k16(tl, yf, ut);
-        *(u32x2*)(rec + REC_U + n * 512 + lane * 8) = pack4(ut[0], ut[1], ut[2], ut[3]);
-    }
+    for (int p = 0; p < 4; ++p)
+        a = mfma_k32(*(const u32x4*)(scr + K1_KB + p * 1024 + lane * 16),
+                     *(const u32x4*)(scr + K1_QA + p * 1024 + lane * 16), a);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) a[v] = (4 * gg + v <= m) ? a[v] : 0.f;
+    *(u32x2*)(rec + REC_AQK + lane * 8) = pack4(a);
+}
+
+// Phase 2 by role; other wavefronts have nothing to do in it. lw is the
+// N_WAVE_T * K1_LBYTES of LDS that the T' wavefronts use privately.
+__device__ __forceinline__ void k1_phase2(int wave, int lane, uint8_t* rec, const uint8_t* scr, float* lw) {
+    if (wave < N_WAVE_T) k1_phase2_t(lane, wave, rec, scr, lw + wave * (K1_LBYTES / 4));
+    else if (wave == WAVE_QK) k1_phase2_qk(lane, rec, scr);
 }
 
 // ---------------------------------------------------------------------------
-// K2 chain step: one wavefront advances its 128 x 32 slice of the state
-// (value-column tiles wcol, wcol + 1) over one chunk record held in LDS.
-// State tile S[t][n] holds S[16t + 4gg + v][16(wcol + n) + m], v = 0..3.
-// WITH_U = false runs the same update with U~ := 0 (the segment transfer of
+// K2 chain step: one wavefront advances NT value-column tiles n0..n0+NT-1 of
+// the state (16 columns each) over one chunk record held in LDS.
+// State tile S[t][n] holds S[16t + 4gg + v][16(n0 + n) + m], v = 0..3.
+// WITH_V = false runs the same update with V := 0 (the segment transfer of
 // the CP pre_scan). WITH_OUT also forms O^T = S0^T Qt^T + U^T A_qk^T, whose
-// accumulator oacc[n][v] is o[token m][16(wcol + n) + 4gg + v].
-// The state-update arithmetic is identical in every instantiation.
+// accumulator oacc[n][v] is o[token m][16(n0 + n) + 4gg + v].
+// The arithmetic of a tile is identical in every instantiation.
 // ---------------------------------------------------------------------------
-template <bool WITH_U, bool WITH_OUT>
-__device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][2], int wcol,
-                                           int lane, f32x4 (&oacc)[2]) {
+template <int NT, bool WITH_V, bool WITH_OUT>
+__device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT], int n0, int lane,
+                                           f32x4 (&oacc)[NT]) {
     const int gg = lane >> 4;
     // bf16 copy of the chunk-start state, as K=32 operands
-    u32x4 Sb[4][2];
+    u32x4 Sb[4][NT];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
+        for (int n = 0; n < NT; ++n) {
             Sb[p][n].x = pack_bf16(S[2 * p][n][0], S[2 * p][n][1]);
             Sb[p][n].y = pack_bf16(S[2 * p][n][2], S[2 * p][n][3]);
             Sb[p][n].z = pack_bf16(S[2 * p + 1][n][0], S[2 * p + 1][n][1]);
             Sb[p][n].w = pack_bf16(S[2 * p + 1][n][2], S[2 * p + 1][n][3]);
         }
-    // W S0
-    f32x4 ws[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // P = X S0
+    f32x4 P[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) P[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const u32x4 wf = *(const u32x4*)(rec + REC_W + p * 1024 + lane * 16);
+        const u32x4 xf = *(const u32x4*)(rec + REC_X + p * 1024 + lane * 16);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) ws[n] = mfma_k32(wf, Sb[p][n], ws[n]);
+        for (int n = 0; n < NT; ++n) P[n] = mfma_k32(xf, Sb[p][n], P[n]);
     }
-    // U = U~ - W S0 (fp32), bf16 operand copy
-    u32x2 Ub[2];
+    // U = T' (V - P): hi and lo halves of T'
+    const u32x2 th = *(const u32x2*)(rec + REC_T + lane * 8);
+    const u32x2 tl = *(const u32x2*)(rec + REC_T + 512 + lane * 8);
+    u32x2 Ub[NT];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        f32x4 u;
-        if constexpr (WITH_U) {
-            const u32x2 uw = *(const u32x2*)(rec + REC_U + (wcol + n) * 512 + lane * 8);
-            u[0] = bf16_lo(uw.x) - ws[n][0];
-            u[1] = bf16_hi(uw.x) - ws[n][1];
-            u[2] = bf16_lo(uw.y) - ws[n][2];
-            u[3] = bf16_hi(uw.y) - ws[n][3];
+    for (int n = 0; n < NT; ++n) {
+        f32x4 r;
+        if constexpr (WITH_V) {
+            const u32x2 vw = *(const u32x2*)(rec + REC_V + (n0 + n) * 512 + lane * 8);
+            r[0] = bf16_lo(vw.x) - P[n][0];
+            r[1] = bf16_hi(vw.x) - P[n][1];
+            r[2] = bf16_lo(vw.y) - P[n][2];
+            r[3] = bf16_hi(vw.y) - P[n][3];
         } else {
-            u = -ws[n];
+            r = -P[n];
         }
-        Ub[n].x = pack_bf16(u[0], u[1]);
-        Ub[n].y = pack_bf16(u[2], u[3]);
+        const u32x2 rb = pack4(r);
+        f32x4 u = mfma_k16(th, rb, f32x4{0.f, 0.f, 0.f, 0.f});
+        u = mfma_k16(tl, rb, u);
+        Ub[n] = pack4(u);
     }
     // O^T = S0^T Qt^T + U^T A_qk^T
     if constexpr (WITH_OUT) {
         const u32x2 aq = *(const u32x2*)(rec + REC_AQK + lane * 8);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NT; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const u32x4 qf = *(const u32x4*)(rec + REC_Q + p * 1024 + lane * 16);
 #pragma unroll
-            for (int n = 0; n < 2; ++n) oacc[n] = mfma_k32(Sb[p][n], qf, oacc[n]);
+            for (int n = 0; n < NT; ++n) oacc[n] = mfma_k32(Sb[p][n], qf, oacc[n]);
         }
 #pragma unroll
-        for (int n = 0; n < 2; ++n) oacc[n] = mfma_k16(Ub[n], aq, oacc[n]);
+        for (int n = 0; n < NT; ++n) oacc[n] = mfma_k16(Ub[n], aq, oacc[n]);
     }
     // S_next = Diag(exp G_C) S0 + Kt^T U
 #pragma unroll
@@ -367,7 +392,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][2],
         const f32x4 gcv = *(const f32x4*)(rec + REC_GC + (16 * t + 4 * gg) * 4);
         const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + lane * 8);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
+        for (int n = 0; n < NT; ++n) {
             S[t][n] = gcv * S[t][n];
             S[t][n] = mfma_k16(kt, Ub[n], S[t][n]);
         }

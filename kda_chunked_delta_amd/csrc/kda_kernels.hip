@@ -8,6 +8,8 @@
 
 namespace kda {
 
+static_assert(REC_BYTES == kRecBytes, "record size differs between host and device");
+
 namespace {
 
 // Sequence bounds from the device cu_seqlens, clamped into [0, Tt] so that an
@@ -77,56 +79,58 @@ __device__ __forceinline__ void record_loop(const uint8_t* __restrict__ rb, int 
 // Make every register of x live here: its loads complete before this point,
 // so no wait for them is left inside the chunk loop that follows (where it
 // would also wait for the prefetches issued there).
-__device__ __forceinline__ void settle(const f32x4 (&S)[8][2]) {
+template <int NT>
+__device__ __forceinline__ void settle(const f32x4 (&S)[8][NT]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) asm volatile("" ::"v"(S[t][n]));
+        for (int n = 0; n < NT; ++n) asm volatile("" ::"v"(S[t][n]));
 }
 
-__device__ __forceinline__ void load_state(const float* sin, f32x4 (&S)[8][2], int wcol, int gg, int m) {
+// State tiles of value columns 16(n0 + n) .. +15 (see chain_step).
+template <int NT>
+__device__ __forceinline__ void load_state(const float* sin, f32x4 (&S)[8][NT], int n0, int gg, int m) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv)
-                S[t][n][vv] = sin ? sin[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] : 0.f;
+                S[t][n][vv] = sin ? sin[(16 * t + 4 * gg + vv) * D + 16 * (n0 + n) + m] : 0.f;
     settle(S);
 }
 
-__device__ __forceinline__ void store_state(float* so, const f32x4 (&S)[8][2], int wcol, int gg, int m) {
+template <int NT>
+__device__ __forceinline__ void store_state(float* so, const f32x4 (&S)[8][NT], int n0, int gg, int m) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv)
-                so[(16 * t + 4 * gg + vv) * D + 16 * (wcol + n) + m] = S[t][n][vv];
+                so[(16 * t + 4 * gg + vv) * D + 16 * (n0 + n) + m] = S[t][n][vv];
 }
 
-__device__ __forceinline__ void identity_state(f32x4 (&S)[8][2], int wcol, int gg, int m) {
+template <int NT>
+__device__ __forceinline__ void identity_state(f32x4 (&S)[8][NT], int n0, int gg, int m) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv)
-                S[t][n][vv] = (16 * t + 4 * gg + vv == 16 * (wcol + n) + m) ? 1.f : 0.f;
+                S[t][n][vv] = (16 * t + 4 * gg + vv == 16 * (n0 + n) + m) ? 1.f : 0.f;
 }
 
-// Output rows of one chunk: oacc[n][v] is o[token m][16(wcol + n) + 4gg + v].
+// Output rows of one chunk: oacc[v] is o[token m][16 n + 4gg + v].
 __device__ __forceinline__ void store_output(const K2Args& a, int h, int64_t tk, int64_t end,
-                                             const f32x4 (&oacc)[2], int wcol, int gg, int m) {
+                                             const f32x4& oacc, int n, int gg, int m) {
     if (m < rows_of(tk, end)) {
         uint16_t* orow = a.out + ((size_t)(tk + m) * a.c.H + h) * D;
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            u32x2 w;
-            w.x = pack_bf16(a.scale * oacc[n][0], a.scale * oacc[n][1]);
-            w.y = pack_bf16(a.scale * oacc[n][2], a.scale * oacc[n][3]);
-            *(u32x2*)(orow + 16 * (wcol + n) + 4 * gg) = w;
-        }
+        u32x2 w;
+        w.x = pack_bf16(a.scale * oacc[0], a.scale * oacc[1]);
+        w.y = pack_bf16(a.scale * oacc[2], a.scale * oacc[3]);
+        *(u32x2*)(orow + 16 * n + 4 * gg) = w;
     }
 }
 
@@ -144,8 +148,8 @@ __device__ __forceinline__ const float* unit_state_in(const K2Args& a, const Uni
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     __shared__ __align__(16) uint8_t rec[REC_BYTES];
-    __shared__ __align__(16) uint8_t ws[K1_BYTES];
-    __shared__ __align__(16) float lw[4][K1_LBYTES / 4];
+    __shared__ __align__(16) uint8_t scr[K1_BYTES];
+    __shared__ __align__(16) float lw[N_WAVE_T * K1_LBYTES / 4];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const int gc = blockIdx.x / H;
@@ -156,9 +160,9 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
     RawChunk raw;
     k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, tok0, rows_of(tok0, end), wave, lane, raw);
-    k1_phase1(raw, wave, lane, rec, ws);
+    k1_phase1(raw, wave, lane, rec, scr);
     lds_barrier();
-    if (wave < 4) k1_phase2(wave, lane, rec, ws, lw[wave]);
+    k1_phase2(wave, lane, rec, scr, lw);
     lds_barrier();
     u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_BYTES);
     const u32x4* src = (const u32x4*)rec;
@@ -166,114 +170,127 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused K1 + K2 (the serial path): one workgroup of 8 wavefronts per (unit,
-// head), software-pipelined with one barrier per chunk. In the interval that
-// ends with barrier i, all 8 wavefronts run K1 phase 1 of chunk i+2,
-// wavefronts 0..3 run K1 phase 2 of chunk i+1, and wavefronts 4..7 advance
-// the state over chunk i (wavefront 4+w owns value columns 32w..32w+31, held
-// in MFMA accumulators for the whole unit). Records live in a 3-deep LDS
-// ring, K1 scratch in a 2-deep one; raw inputs are prefetched one chunk ahead.
+// Fused K1 + K2 (the serial path): one workgroup of 16 wavefronts per (unit,
+// head), software-pipelined with one barrier per chunk. Wavefronts 0..7
+// hold the state (wavefront w: value columns 16w..16w+15, in MFMA
+// accumulators for the whole unit) and in the interval that ends with
+// barrier i advance it over chunk i and store that chunk's output.
+// Wavefronts 8 + w run K1 phase 1 of chunk i+2 on key channels and value
+// columns 16w..16w+15 and prefetch chunk i+3; of them, w < 4 and w = WAVE_QK
+// also run K1 phase 2 of chunk i+1. Every SIMD thus holds two state
+// wavefronts and two K1 wavefronts, whose latency-bound and arithmetic-bound
+// work interleave. Records live in a 3-deep LDS ring, K1 scratch in a 2-deep
+// one.
 // ---------------------------------------------------------------------------
-constexpr int FUSED_LDS = 3 * REC_BYTES + 2 * K1_BYTES + 4 * K1_LBYTES;
+constexpr int FUSED_LDS = 3 * REC_BYTES + 2 * K1_BYTES + N_WAVE_T * K1_LBYTES;
 
-__global__ __launch_bounds__(512) void kda_fused(K2Args a) {
+__global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* recs = smem;
-    uint8_t* wss = smem + 3 * REC_BYTES;
-    float* lws = (float*)(wss + 2 * K1_BYTES);
+    uint8_t* scrs = smem + 3 * REC_BYTES;
+    float* lw = (float*)(scrs + 2 * K1_BYTES);
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const UnitDesc u = a.units[blockIdx.x / H];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int gg = lane >> 4, m = lane & 15;
-    const bool chain = wave >= 4;
-    const int wcol = 2 * (wave & 3);
+    const int w8 = wave & 7;
     int64_t beg, end;
     seq_bounds(a.c, u.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
     const int nc = u.n_chunks;
-    f32x4 S[8][2];
-    if (chain) load_state(unit_state_in(a, u, h), S, wcol, gg, m);
-    RawChunk raw;
-    auto load = [&](int ci) {
-        const int64_t t = tok0 + (int64_t)CH * ci;
-        k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, t, rows_of(t, end), wave, lane, raw);
-    };
-    if (nc > 0) load(0);
-    for (int i = -2; i < nc; ++i) {
-        if (i + 2 < nc) {
-            k1_phase1(raw, wave, lane, recs + ((i + 2) % 3) * REC_BYTES, wss + ((i + 2) & 1) * K1_BYTES);
-            if (i + 3 < nc) load(i + 3);
+    if (wave < 8) {
+        // state wavefronts
+        f32x4 S[8][1];
+        load_state(unit_state_in(a, u, h), S, w8, gg, m);
+        for (int i = -2; i < nc; ++i) {
+            if (i >= 0) {
+                f32x4 oacc[1];
+                chain_step<1, true, true>(recs + (i % 3) * REC_BYTES, S, w8, lane, oacc);
+                store_output(a, h, tok0 + (int64_t)CH * i, end, oacc[0], w8, gg, m);
+            }
+            lds_barrier();
         }
-        if (!chain) {
-            if (i + 1 >= 0 && i + 1 < nc)
-                k1_phase2(wave, lane, recs + ((i + 1) % 3) * REC_BYTES, wss + ((i + 1) & 1) * K1_BYTES,
-                          lws + wave * (K1_LBYTES / 4));
-        } else if (i >= 0) {
-            f32x4 oacc[2];
-            chain_step<true, true>(recs + (i % 3) * REC_BYTES, S, wcol, lane, oacc);
-            store_output(a, h, tok0 + (int64_t)CH * i, end, oacc, wcol, gg, m);
-        }
-        lds_barrier();
+        if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, w8, gg, m);
+    } else {
+        // K1 wavefronts
+        RawChunk raw;
+        auto load = [&](int ci) {
+            const int64_t t = tok0 + (int64_t)CH * ci;
+            k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, t, rows_of(t, end), w8, lane, raw);
+        };
+        auto interval = [&](int i, bool p1, bool ld, bool p2) __attribute__((always_inline)) {
+            if (p1) k1_phase1(raw, w8, lane, recs + ((i + 2) % 3) * REC_BYTES, scrs + ((i + 2) & 1) * K1_BYTES);
+            if (ld) load(i + 3);
+            if (p2) k1_phase2(w8, lane, recs + ((i + 1) % 3) * REC_BYTES, scrs + ((i + 1) & 1) * K1_BYTES, lw);
+            lds_barrier();
+        };
+        if (nc > 0) load(0);
+        // the steady-state intervals run every step unconditionally, which
+        // keeps the compiler's wait analysis for the prefetch exact there
+        int i = -2;
+        interval(i, i + 2 < nc, i + 3 < nc, false);
+        for (i = -1; i + 3 < nc; ++i) interval(i, true, true, true);
+        for (; i < nc; ++i) interval(i, i + 2 < nc, i + 3 < nc, i + 1 >= 0 && i + 1 < nc);
     }
-    if (chain && u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wcol, gg, m);
 }
 
 // ---------------------------------------------------------------------------
-// K2 over materialised K1 records (two-kernel serial form and CP segment-K2).
+// K2 over materialised K1 records (two-kernel serial form and CP segment-K2):
+// one workgroup of 8 wavefronts per (unit, head), wavefront w on value
+// columns 16w..16w+15.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void kda_k2_recur(K2Args a) {
+__global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
     __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const UnitDesc u = a.units[blockIdx.x / H];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gg = lane >> 4, m = lane & 15;
-    const int wcol = 2 * wave;
     int64_t beg, end;
     seq_bounds(a.c, u.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
-    f32x4 S[8][2];
-    load_state(unit_state_in(a, u, h), S, wcol, gg, m);
+    f32x4 S[8][1];
+    load_state(unit_state_in(a, u, h), S, wave, gg, m);
     const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0) * REC_BYTES;
-    record_loop<256>(rb, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
-        f32x4 oacc[2];
-        chain_step<true, true>(r, S, wcol, lane, oacc);
-        store_output(a, h, tok0 + (int64_t)CH * ci, end, oacc, wcol, gg, m);
+    record_loop<512>(rb, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
+        f32x4 oacc[1];
+        chain_step<1, true, true>(r, S, wave, lane, oacc);
+        store_output(a, h, tok0 + (int64_t)CH * ci, end, oacc[0], wave, gg, m);
     });
-    if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wcol, gg, m);
+    if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wave, gg, m);
 }
 
 // ---------------------------------------------------------------------------
-// CP pre_scan over materialised K1 records: one workgroup of 8 wavefronts per
-// (segment, head). Wavefronts 0..3 run the K2 state update from S = 0 over
-// the segment (B, value columns 32w..), wavefronts 4..7 run it from S = I
-// with U~ := 0 (M, key columns 32(w-4)..). Both use K2's chain step, so B
-// follows K2's arithmetic exactly.
+// CP pre_scan over materialised K1 records: one workgroup of 16 wavefronts
+// per (segment, head). Wavefronts 0..7 run the K2 state update from S = 0
+// over the segment (B, value columns 16w..), wavefronts 8..15 run it from
+// S = I with V := 0 (M, key columns 16(w-8)..). Both use K2's chain step, so
+// B follows K2's arithmetic exactly.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void kda_cp_prescan(PrescanArgs a) {
+__global__ __launch_bounds__(1024) void kda_cp_prescan(PrescanArgs a) {
     __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const PrescanDesc it = a.items[blockIdx.x / H];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gg = lane >> 4, m = lane & 15;
-    const bool is_b = wave < 4;
-    const int wcol = 2 * (wave & 3);
-    f32x4 S[8][2];
+    const bool is_b = wave < 8;
+    const int n0 = wave & 7;
+    f32x4 S[8][1];
     if (is_b)
-        load_state(nullptr, S, wcol, gg, m);
+        load_state(nullptr, S, n0, gg, m);
     else
-        identity_state(S, wcol, gg, m);
-    f32x4 unused[2];
+        identity_state(S, n0, gg, m);
+    f32x4 unused[1];
     const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
-    record_loop<512>(rb, it.n_chunks, recs, [&](int, const uint8_t* r) {
+    record_loop<1024>(rb, it.n_chunks, recs, [&](int, const uint8_t* r) {
         if (is_b)
-            chain_step<true, false>(r, S, wcol, lane, unused);
+            chain_step<1, true, false>(r, S, n0, lane, unused);
         else
-            chain_step<false, false>(r, S, wcol, lane, unused);
+            chain_step<1, false, false>(r, S, n0, lane, unused);
     });
-    store_state((is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D), S, wcol, gg, m);
+    store_state((is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D), S, n0, gg, m);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,7 +353,7 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     static hipError_t attr = hipFuncSetAttribute((const void*)kda_fused,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kda_fused, dim3((unsigned)n), dim3(512), FUSED_LDS, s, a);
+    hipLaunchKernelGGL(kda_fused, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
     return hipGetLastError();
 }
 
@@ -350,14 +367,14 @@ hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s) {
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s) {
     const long long n = (long long)a.n_units * a.c.H;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_k2_recur, dim3((unsigned)n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(kda_k2_recur, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s) {
     const long long n = (long long)a.n_items * a.c.H;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_cp_prescan, dim3((unsigned)n), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(kda_cp_prescan, dim3((unsigned)n), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 

@@ -99,7 +99,7 @@ hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);
 
 constexpr int kChunk = 16;                      // tokens per chunk
-constexpr size_t kRecBytes = 17408;            // bytes of one K1 chunk record
+constexpr size_t kRecBytes = 18432;            // bytes of one K1 chunk record
 constexpr size_t kStateBytes = 128 * 128 * 4;  // one (sequence, head) state
 
 }  // namespace kda

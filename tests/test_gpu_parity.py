@@ -123,20 +123,20 @@ def test_scale():
 # K1 records against the chunked fp64 oracle
 # ---------------------------------------------------------------------------
 def decode_records(rec):
-    """uint8 [17408] record -> dict of fp32 numpy arrays (layout of include/kda.h)."""
+    """uint8 [KDA_RECORD_BYTES] record -> dict of fp32 numpy arrays (layout of include/kda.h)."""
     r = rec.cpu().numpy()
     bf = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
     lanes = np.arange(64)
     g, i = lanes // 16, lanes % 16
     out = {}
-    for name, off in (("Qt", 0), ("W", 4096)):
+    for name, off in (("Qt", 0), ("X", 4096)):
         a = bf(r[off:off + 4096].view(np.uint16).reshape(4, 64, 8))
         x = np.zeros((16, 128), np.float32)
         for p in range(4):
             for j in range(8):
                 x[i, 32 * p + 16 * (j // 4) + 4 * g + j % 4] = a[p, :, j]
         out[name] = x
-    for name, off in (("Kt", 8192), ("U", 12288)):
+    for name, off in (("Kt", 8192), ("V", 12288)):
         a = bf(r[off:off + 4096].view(np.uint16).reshape(8, 64, 4))
         x = np.zeros((16, 128), np.float32)
         for t in range(8):
@@ -149,11 +149,18 @@ def decode_records(rec):
         x[i, 4 * g + j] = a[:, j]
     out["A_qk"] = x
     out["gC"] = r[16896:17408].view(np.float32).copy()
+    t = bf(r[17408:18432].view(np.uint16).reshape(2, 64, 4)).astype(np.float64)
+    x = np.zeros((16, 16))
+    for j in range(4):
+        x[i, 4 * g + j] = t[0, :, j] + t[1, :, j]
+    out["Tb"] = x
     return out
 
 
 @pytest.mark.parametrize("lengths", [[16], [33, 3], [64, 21]])
 def test_k1_records_match_chunked_oracle(lengths):
+    """Each record field against the fp64 chunked oracle's K1 of that chunk:
+    X = k exp(G) and T' = Tinv diag(beta) are formed from its G and Tinv."""
     say("case lengths", lengths)
     H = 3
     d = draw(lengths, H, seed=77 + sum(lengths), state_std=None, device=DEV)
@@ -162,19 +169,28 @@ def test_k1_records_match_chunked_oracle(lengths):
     torch.cuda.synchronize()
     _, _, ks = ref.chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens_host"], None,
                            intermediates=True)
+    k64, v64, b64 = (ref.to_f64(d[n]) for n in ("k", "v", "beta"))
+    cu = d["cu_seqlens_host"]
     gidx = 0
     for i, L in enumerate(lengths):
         for c in range((L + 15) // 16):
+            t0 = cu[i] + 16 * c
             for h in range(H):
                 got = decode_records(recs[h, gidx])
                 exp = ks[(i, c, h)]
                 n = exp["Qt"].shape[0]
-                for key in ("Qt", "W", "Kt", "U"):
-                    assert_close("%s[%d,%d,%d]" % (key, i, c, h), got[key][:n], exp[key])
+                want = dict(Qt=exp["Qt"], Kt=exp["Kt"], X=k64[t0:t0 + n, h] * np.exp(exp["G"]),
+                            V=v64[t0:t0 + n, h])
+                for key in ("Qt", "X", "Kt", "V"):
+                    assert_close("%s[%d,%d,%d]" % (key, i, c, h), got[key][:n], want[key])
                     assert np.all(got[key][n:] == 0), "%s rows past the tail must be zero" % key
+                assert np.array_equal(got["V"][:n], want["V"]), "V is the input, moved exactly"
                 aq = np.zeros((16, 16))
                 aq[:n, :n] = exp["A_qk"]
                 assert_close("A_qk", got["A_qk"], aq)
+                tb = exp["Tinv"] * b64[t0:t0 + n, h][None, :]
+                assert_close("T'", got["Tb"][:n, :n], tb)
+                assert np.all(got["Tb"][n:, :] == 0) and np.all(got["Tb"][:, n:] == 0)
                 assert_close("gC", got["gC"], exp["gC"], atol=1e-6, rtol=1e-5)
             gidx += 1
 

@@ -30,6 +30,11 @@ def test_library_exports_every_declared_symbol(kda_lib):
     assert not missing, "declared in include/kda.h but not exported: %s" % missing
 
 
+def test_record_size_matches_header(kda_lib):
+    m = re.search(r"#define KDA_RECORD_BYTES (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == kda.RECORD_BYTES
+
+
 def test_version(kda_lib):
     assert b"gfx950" in kda_lib.kda_version()
 
@@ -62,9 +67,9 @@ def test_serial_plan_orders_longest_first(kda_lib):
 def test_materialized_plan_sizes_records(kda_lib, monkeypatch):
     monkeypatch.setenv("KDA_MATERIALIZE_K1", "1")
     info = kda.plan_host(cu_of([100, 4096]), H=4, n_cus=256).info()
-    # one 17408-byte record per (chunk, head)
+    # one record per (chunk, head)
     assert info["k1_materialized"] == 1
-    assert info["workspace_bytes"] >= info["total_chunks"] * 4 * 17408
+    assert info["workspace_bytes"] >= info["total_chunks"] * 4 * kda.RECORD_BYTES
 
 
 def test_auto_plan_splits_few_head_long_sequence(kda_lib):
