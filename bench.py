@@ -23,10 +23,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # Algorithmic work per token-head of the path (D = 128, chunk 16):
 #   bytes: q 256 + k 256 + v 256 (bf16) + g 512 (fp32) + beta 4 + o 256 (bf16)
-#   flops: K1 16384 (four 16x16x128 products per chunk) + K2 102400
-#          (three 16x128x128 products plus one 16x16x128 per chunk)
+#   flops, per 16-token chunk: X S0, Qt S0 and Kt^T U (16x128x128 each),
+#          T'(V - X S0) and A_qk U (16x16x128 each), the Grams A_kk and A_qk
+#          (16x16x128 each): 2 * (3 * 262144 + 4 * 32768) / 16 per token
 BYTES_PER_TOKEN_HEAD = 1540
-FLOPS_PER_TOKEN_HEAD = 118784
+FLOPS_PER_TOKEN_HEAD = 114688
 STATE_BYTES = 128 * 128 * 4
 
 WORKLOAD_TEXT = {
@@ -47,9 +48,11 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel, digest):
-    """HBM bytes per launch measured by rocprofv3 counters, if the committed
-    measurement was taken on the current kernel sources."""
+def traffic_from_profiles(kernel, digest, workload_name):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, each scaled by its reading on a copy of known size), if the
+    committed measurement was taken on the current kernel sources and on this
+    workload."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
@@ -57,7 +60,7 @@ def traffic_from_profiles(kernel, digest):
     except (OSError, ValueError):
         return None
     ent = data.get(kernel)
-    if not ent or ent.get("source_digest") != digest:
+    if not ent or ent.get("source_digest") != digest or ent.get("workload") != workload_name:
         return None
     return ent.get("bytes_per_launch")
 
@@ -103,10 +106,14 @@ def main():
     ap.add_argument("--cp", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target duration of the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run `steps` launches of a plain elementwise copy of "
+                         "MIB MiB (fp32 negation: MIB MiB read, MIB MiB written); the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
-              "(the path shards by sequence or head with no communication, see DESIGN.md)" % args.gpus,
+        print("bench.py: measures one GPU only; --gpus %d is not supported (the prefill shards by "
+              "sequence or head with no communication, so N GPUs each run this on their share)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
@@ -116,6 +123,16 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                          "launches": max(1, args.steps)}), flush=True)
+        return
     d = workload(args.workload, device=dev)
     H, cu = d["H"], d["cu_seqlens_host"]
     Tt, N = cu[-1], len(cu) - 1
@@ -161,7 +178,7 @@ def main():
     names = "+".join(per_kernel.keys())
     achieved = alg_bytes / (path_ms * 1e-3) / 1e9
     digest = source_digest()
-    traffic = traffic_from_profiles(names, digest)
+    traffic = traffic_from_profiles(names, digest, args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": names, "dominant": dominant, "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},

@@ -54,26 +54,33 @@ double env_double(const char* name, double dflt) {
     return (e && *e == 0 && std::isfinite(v) && v > 0) ? v : dflt;
 }
 
-// Planner constants. Costs are in units of one K2 chunk step of one unit;
-// the two chain-cost ratios play the role of the pull request's two fitted,
-// environment-overridable constants.
+// Planner cost model, in microseconds. The constants were fitted on MI355X
+// from per-kernel timings of this library's kernels (environment-
+// overridable, as the pull request's planner constants are):
+//   fused      one chunk step of a fused serial workgroup (one per CU)
+//   k1         materialised K1 of one (chunk, head), per CU, at full load
+//   prescan    one chunk step of a pre_scan workgroup
+//   rec        one chunk step of a K2 workgroup over materialised records
+//   merge      one segment step of the carry merge
+//   launch     one kernel launch
 struct PlannerConsts {
-    double prescan_ratio;   // pre_scan chunk step / K2 chunk step
-    double merge_ratio;     // merge cost per segment / K2 chunk step
-    double launch_steps;    // fixed cost of one extra launch, in K2 chunk steps
-    double chunk_us;        // K2 chunk step in microseconds (reporting only)
-    int min_seg_chunks;     // shortest segment the planner will form
-    int units_per_cu;       // concurrent K2 (unit, head) workgroups per CU
+    double fused_us, k1_us, prescan_us, rec_us, merge_us, launch_us;
+    int min_seg_chunks;  // shortest segment the planner will form
+    int prescan_per_cu;  // concurrent pre_scan workgroups per CU
+    int rec_per_cu;      // concurrent K2-over-records workgroups per CU
 };
 
 PlannerConsts planner_consts() {
     PlannerConsts c;
-    c.prescan_ratio = env_double("KDA_CP_PRESCAN_RATIO", 1.0);
-    c.merge_ratio = env_double("KDA_CP_MERGE_RATIO", 2.0);
-    c.launch_steps = env_double("KDA_CP_LAUNCH_STEPS", 20.0);
-    c.chunk_us = env_double("KDA_CP_CHUNK_US", 0.25);
+    c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.8);
+    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 2.0);
+    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 2.65);
+    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.1);
+    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 3.2);
+    c.launch_us = env_double("KDA_CP_LAUNCH_US", 5.0);
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
-    c.units_per_cu = (int)env_double("KDA_CP_UNITS_PER_CU", 2.0);
+    c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
+    c.rec_per_cu = (int)env_double("KDA_CP_REC_PER_CU", 2.0);
     return c;
 }
 
@@ -99,19 +106,19 @@ struct kda_plan {
 
 namespace {
 
-// Serial chain estimate: the longest unit, or the total work spread over the
-// concurrent workgroups, whichever is larger (in K2 chunk steps).
+// Serial estimate (fused kernel, one (sequence, head) workgroup per CU):
+// the longest sequence, or the total work spread over the CUs, whichever is
+// larger.
 double est_serial(const std::vector<int>& nch, int H, int n_cus, const PlannerConsts& pc) {
     long long tot = 0;
     int mx = 0;
     for (int n : nch) { tot += n; mx = std::max(mx, n); }
-    const double width = (double)n_cus * pc.units_per_cu;
-    return std::max((double)mx, std::ceil((double)tot * H / width)) + pc.launch_steps;
+    return pc.fused_us * std::max((double)mx, std::ceil((double)tot * H / n_cus)) + pc.launch_us;
 }
 
-// Segmented estimate for segment length `seg` (chunks): pre_scan over every
-// segment but the last of each split sequence, a serial merge over segments,
-// then segment-K2 over all units.
+// Segmented estimate for segment length `seg` (chunks): K1 materialised for
+// every chunk, pre_scan over every segment but the last of each split
+// sequence, a serial merge over segments, then K2 over all units.
 double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const PlannerConsts& pc) {
     long long tot = 0, pre_work = 0;
     int longest_unit = 0, max_segs = 0;
@@ -127,13 +134,13 @@ double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const Plan
         }
     }
     if (max_segs == 0) return 1e300;
-    const double width = (double)n_cus * pc.units_per_cu;
-    // a pre_scan workgroup carries twice the columns of a K2 workgroup
-    const double t_pre = pc.prescan_ratio *
-                         std::max((double)seg, std::ceil(2.0 * (double)pre_work * H / width));
-    const double t_merge = pc.merge_ratio * (max_segs - 1);
-    const double t_k2 = std::max((double)longest_unit, std::ceil((double)tot * H / width));
-    return t_pre + t_merge + t_k2 + 3 * pc.launch_steps;
+    const double t_k1 = pc.k1_us * std::ceil((double)tot * H / n_cus);
+    const double t_pre = pc.prescan_us *
+                         std::max((double)seg, std::ceil((double)pre_work * H / ((double)n_cus * pc.prescan_per_cu)));
+    const double t_merge = pc.merge_us * (max_segs - 1);
+    const double t_k2 = pc.rec_us *
+                        std::max((double)longest_unit, std::ceil((double)tot * H / ((double)n_cus * pc.rec_per_cu)));
+    return t_k1 + t_pre + t_merge + t_k2 + 4 * pc.launch_us;
 }
 
 // seg_chunks > 0 forces that segment length on every longer sequence.
@@ -251,8 +258,8 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     for (const auto& u : p->units) in.max_unit_chunks = std::max(in.max_unit_chunks, u.n_chunks);
     in.n_cus = n_cus;
     in.workspace_bytes = off;
-    in.est_serial_us = t_serial * pc.chunk_us;
-    in.est_cp_us = (t_cp < 1e299 ? t_cp : -1.0) * pc.chunk_us;
+    in.est_serial_us = t_serial;
+    in.est_cp_us = t_cp < 1e299 ? t_cp : -1.0;
     in.k1_materialized = materialize ? 1 : 0;
     *out = p;
     return KDA_OK;

@@ -4,15 +4,17 @@ This module only draws random tensors with the workloads' shapes and value
 distributions; it holds none of the method's arithmetic, so both the GPU
 library's tests and the CPU oracle may consume what it produces.
 
-Recipe (one torch.Generator on the generating device, seeded per workload,
-tensors drawn in this order: lengths, q, k, v, g, beta, initial state):
+Recipe (per workload seed s): sequence lengths drawn first by a CPU
+torch.Generator seeded with s, so a workload's batch structure is the same on
+every device; then one torch.Generator on the generating device, seeded with
+s, draws in this order q, k, v, g, beta, initial state:
   q, k  : randn fp32, L2-normalised per (token, head) over D, rounded to bf16
   v     : randn, rounded to bf16
   g     : -softplus(g_scale * randn) fp32 log-decay per key channel
   beta  : sigmoid(randn) fp32
   S0    : state_std * randn fp32, shape [N, H, D, D], or None
 "N(0, s)" is read as s * randn (a standard deviation).
-Random streams differ between a CPU and a GPU generator; the oracle always
+Tensor values differ between a CPU and a GPU generator; the oracle always
 evaluates the exact tensors the library consumed, so parity does not depend
 on where the inputs were drawn.
 """
@@ -47,15 +49,17 @@ def draw(lengths, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D):
     """Draw one packed-varlen input set.
 
     lengths: list of sequence lengths, or ("uniform", n, lo, hi) for n lengths
-    drawn uniformly from [lo, hi] inclusive with the same generator.
+    drawn uniformly from [lo, hi] inclusive by a CPU generator seeded with seed.
     Returns a dict with q, k, v (bf16), g, beta (fp32), cu_seqlens (int32, on
     the device), cu_seqlens_host (python list), initial_state (fp32 or None).
     """
-    gen = torch.Generator(device=device)
-    gen.manual_seed(int(seed))
     if isinstance(lengths, tuple) and lengths[0] == "uniform":
         _, n, lo, hi = lengths
-        lengths = torch.randint(lo, hi + 1, (n,), generator=gen, device=device).tolist()
+        lgen = torch.Generator(device="cpu")
+        lgen.manual_seed(int(seed))
+        lengths = torch.randint(lo, hi + 1, (n,), generator=lgen).tolist()
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
     lengths = [int(x) for x in lengths]
     Tt = sum(lengths)
     cu = [0]
