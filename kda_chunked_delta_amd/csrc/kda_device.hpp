@@ -124,11 +124,6 @@ template <int N>
 __device__ __forceinline__ float row_shr(float x) {
     return __builtin_amdgcn_update_dpp(0.0f, x, 0x110 + N, 0xF, 0xF, true);
 }
-// x from lane I of the same 16-lane row (swizzle broadcast).
-template <int I>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (I << 5)));
-}
 // x from lane K of the same 16-lane row (DPP row broadcast; folds into the
 // consuming multiply).
 template <int K>
@@ -152,24 +147,40 @@ struct RawChunk {
     float b;
 };
 
+// Per-lane byte offsets of a K1 load from the start of a chunk's first row
+// (row m of the chunk, channels 16 wave + 4gg ..), fixed for a kernel.
+struct K1LaneOffsets {
+    uint32_t act;   // into a bf16 [., H, D] tensor
+    uint32_t g;     // into the fp32 g tensor
+    uint32_t beta;  // into the fp32 beta [., H] tensor
+};
+
+__device__ __forceinline__ K1LaneOffsets k1_lane_offsets(int H, int wave, int lane) {
+    const int gg = lane >> 4, m = lane & 15;
+    const uint32_t el = (uint32_t)m * (uint32_t)H * D + 16 * wave + 4 * gg;
+    return K1LaneOffsets{2 * el, 4 * el, 4 * (uint32_t)m * (uint32_t)H};
+}
+
+// Load the chunk whose first token-head row is crow = t0 * H + h (uniform),
+// nrows valid rows. The addresses are a uniform base plus the lane's fixed
+// offset, so the per-chunk address arithmetic is scalar.
 __device__ __forceinline__ void k1_load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                         const uint16_t* __restrict__ v, const float* __restrict__ g,
-                                        const float* __restrict__ beta, int H, int h, int64_t tok0,
-                                        int nrows, int wave, int lane, RawChunk& raw) {
-    const int gg = lane >> 4, m = lane & 15;
+                                        const float* __restrict__ beta, int64_t crow, int nrows,
+                                        const K1LaneOffsets& lo, int lane, RawChunk& raw) {
+    const int m = lane & 15;
     raw.q = u32x2{0u, 0u};
     raw.k = raw.q;
     raw.v = raw.q;
     raw.g = f32x4{0.f, 0.f, 0.f, 0.f};
     raw.b = 0.f;
     if (m < nrows) {
-        const size_t row = (size_t)(tok0 + m) * H + h;
-        const size_t off = row * D + 16 * wave + 4 * gg;
-        raw.q = __builtin_nontemporal_load((const u32x2*)(q + off));
-        raw.k = __builtin_nontemporal_load((const u32x2*)(k + off));
-        raw.v = __builtin_nontemporal_load((const u32x2*)(v + off));
-        raw.g = __builtin_nontemporal_load((const f32x4*)(g + off));
-        raw.b = beta[row];
+        const size_t act = (size_t)crow * (D * 2), gb = (size_t)crow * (D * 4), bb = (size_t)crow * 4;
+        raw.q = __builtin_nontemporal_load((const u32x2*)((const uint8_t*)q + act + lo.act));
+        raw.k = __builtin_nontemporal_load((const u32x2*)((const uint8_t*)k + act + lo.act));
+        raw.v = __builtin_nontemporal_load((const u32x2*)((const uint8_t*)v + act + lo.act));
+        raw.g = __builtin_nontemporal_load((const f32x4*)((const uint8_t*)g + gb + lo.g));
+        raw.b = *(const float*)((const uint8_t*)beta + bb + lo.beta);
     }
 }
 
@@ -189,7 +200,7 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     }
     float g7[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) g7[j] = row_bcast<7>(G[j]);
+    for (int j = 0; j < 4; ++j) g7[j] = row_newbcast<7>(G[j]);
     // decays relative to the reference row 7: E = exp(G - G_7), F = exp(G_7 - G);
     // gam = exp(G)
     float E[4], F[4], gam[4];
@@ -201,7 +212,7 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     }
     float e15[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) e15[j] = row_bcast<15>(E[j]);  // exp(G_C - G_7)
+    for (int j = 0; j < 4; ++j) e15[j] = row_newbcast<15>(E[j]);  // exp(G_C - G_7)
     const float qf[4] = {bf16_lo(raw.q.x), bf16_hi(raw.q.x), bf16_lo(raw.q.y), bf16_hi(raw.q.y)};
     const float kf[4] = {bf16_lo(raw.k.x), bf16_hi(raw.k.x), bf16_lo(raw.k.y), bf16_hi(raw.k.y)};
     f32x4 ka, kb, qa, qt, xk, kt;

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     seq_bounds(a.c, cd.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
     RawChunk raw;
-    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, tok0, rows_of(tok0, end), wave, lane, raw);
+    const K1LaneOffsets lo = k1_lane_offsets(H, wave, lane);
+    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, tok0 * H + h, rows_of(tok0, end), lo, lane, raw);
     k1_phase1(raw, wave, lane, rec, scr);
     lds_barrier();
     k1_phase2(wave, lane, rec, scr, lw);
@@ -215,9 +216,10 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     } else {
         // K1 wavefronts
         RawChunk raw;
+        const K1LaneOffsets lo = k1_lane_offsets(H, w8, lane);
         auto load = [&](int ci) {
             const int64_t t = tok0 + (int64_t)CH * ci;
-            k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, h, t, rows_of(t, end), w8, lane, raw);
+            k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, t * H + h, rows_of(t, end), lo, lane, raw);
         };
         auto interval = [&](int i, bool p1, bool ld, bool p2) __attribute__((always_inline)) {
             if (p1) k1_phase1(raw, w8, lane, recs + ((i + 2) % 3) * REC_BYTES, scrs + ((i + 2) & 1) * K1_BYTES);
