@@ -184,8 +184,10 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
  * chunk (rows past the end of a short chunk are zero), c = channel.
  *   [0, 4096)      Qt = q * exp(G): [p 4][lane 64][j 8] = Qt[i][dkperm(p, g, j)]
  *   [4096, 8192)   X = k * exp(G): same layout as Qt
- *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][lane 64][j 4] = Kt[4g + j][16t + i]
- *   [12288, 16384) V (the chunk's values): [n 8][lane 64][j 4] = V[4g + j][16n + i]
+ *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][slot 64][j 4]; slot s(l) holds
+ *                  lane l's Kt[4g + j][16t + i], s(l) = (l & ~3) | (((l & 3) + (l >> 4)) & 3)
+ *   [12288, 16384) V (the chunk's values): [n 8][slot 64][j 4]; slot s(l) holds
+ *                  lane l's V[4g + j][16n + i]
  *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]
  *   [16896, 17408) exp(G_C): fp32 [128]
  *   [17408, 18432) T' = (I + L)^-1 diag(beta), L = strict-lower(diag(beta) A_kk),

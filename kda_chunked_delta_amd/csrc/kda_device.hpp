@@ -37,8 +37,10 @@ constexpr int CH = 16;   // chunk length
 // feeds the next MFMA as an operand without any shuffle.
 //   REC_Q  : Qt fragments [p 4][lane 64][8 bf16]: Qt[m][dkperm(p, gg, j)]
 //   REC_X  : X fragments, same layout as REC_Q
-//   REC_KT : Kt^T fragments [t 8][lane 64][4 bf16]: Kt[4gg + j][16t + m]
-//   REC_V  : V in accumulator layout [n 8][lane 64][4 bf16]: V[4gg + j][16n + m]
+//   REC_KT : Kt^T fragments [t 8][slot 64][4 bf16]: lane l's fragment
+//            Kt[4gg + j][16t + m] in slot kv_slot(l)
+//   REC_V  : V in accumulator layout [n 8][slot 64][4 bf16]: lane l's
+//            V[4gg + j][16n + m] in slot kv_slot(l)
 //   REC_AQK: A_qk fragment [lane 64][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
 //   REC_GC : exp(G_C) [128] fp32
 //   REC_T  : T' fragments, hi then lo [2][lane 64][4 bf16]: T'[m][4gg + j]
@@ -63,7 +65,10 @@ constexpr int K1_KB = 4096;
 constexpr int K1_QA = 8192;
 constexpr int K1_BETA = 12288;
 constexpr int K1_BYTES = K1_BETA + 64;
-constexpr int K1_LBYTES = 1024;  // per T' wavefront, private LDS: L as fp32 [16][16]
+// per T' wavefront, private LDS: L^T as fp32 [16][K1_LSTRIDE] (a 20-float row
+// stride puts the 16 lanes of each b128 phase on distinct banks)
+constexpr int K1_LSTRIDE = 20;
+constexpr int K1_LBYTES = 16 * K1_LSTRIDE * 4;
 
 // Phase-2 roles: wavefronts 0..3 (one per SIMD) each form four rows of T',
 // wavefront WAVE_QK forms A_qk.
@@ -135,6 +140,12 @@ __device__ __forceinline__ float row_newbcast(float x) {
 // transposed 4-element fragment layout [lane (m >> 2) * 16 + 4gg + j][m & 3].
 __device__ __forceinline__ int tfrag_off(int gg, int m) { return ((m >> 2) * 16 + 4 * gg) * 8 + (m & 3) * 2; }
 
+// Slot of lane l's 8-byte fragment in the Kt and V tiles: the low two bits
+// are rotated by l >> 4. The reads stay one contiguous 512-byte tile, and
+// the 16-bit scatter that K1 writes them with (for a fixed j, lanes
+// (gg, m) -> lane (m >> 2) * 16 + 4gg + j) then lands on distinct banks.
+__device__ __forceinline__ int kv_slot(int l) { return (l & ~3) | (((l & 3) + (l >> 4)) & 3); }
+
 // ---------------------------------------------------------------------------
 // K1, phase 1 (8 wavefronts). Wavefront w owns key channels and value
 // columns 16w..16w+15; lane (gg, m) holds token m of the chunk and channels
@@ -161,27 +172,140 @@ __device__ __forceinline__ K1LaneOffsets k1_lane_offsets(int H, int wave, int la
     return K1LaneOffsets{2 * el, 4 * el, 4 * (uint32_t)m * (uint32_t)H};
 }
 
+// Buffer descriptor over [base, base + bytes): raw (unstrided) addressing,
+// 32-bit data format. A load whose byte range ends past `bytes` returns
+// zeros and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Cache policy of the input loads: default. (The streaming hint keeps a line
+// out of L1 although the four wavefronts that read its quarters want it
+// there, and measured slower.)
+constexpr int BUF_POLICY = 0;
+
 // Load the chunk whose first token-head row is crow = t0 * H + h (uniform),
-// nrows valid rows. The addresses are a uniform base plus the lane's fixed
-// offset, so the per-chunk address arithmetic is scalar.
+// 1 <= nrows <= 16 valid rows. Each tensor is read through a descriptor
+// based at the chunk's first row whose range ends after row nrows - 1, so
+// the lanes of rows nrows..15 read zeros (k = q = v = 0, g = 0, beta = 0)
+// without a branch; the per-chunk address arithmetic is scalar.
 __device__ __forceinline__ void k1_load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                         const uint16_t* __restrict__ v, const float* __restrict__ g,
-                                        const float* __restrict__ beta, int64_t crow, int nrows,
-                                        const K1LaneOffsets& lo, int lane, RawChunk& raw) {
-    const int m = lane & 15;
-    raw.q = u32x2{0u, 0u};
-    raw.k = raw.q;
-    raw.v = raw.q;
-    raw.g = f32x4{0.f, 0.f, 0.f, 0.f};
-    raw.b = 0.f;
-    if (m < nrows) {
-        const size_t act = (size_t)crow * (D * 2), gb = (size_t)crow * (D * 4), bb = (size_t)crow * 4;
-        raw.q = __builtin_nontemporal_load((const u32x2*)((const uint8_t*)q + act + lo.act));
-        raw.k = __builtin_nontemporal_load((const u32x2*)((const uint8_t*)k + act + lo.act));
-        raw.v = __builtin_nontemporal_load((const u32x2*)((const uint8_t*)v + act + lo.act));
-        raw.g = __builtin_nontemporal_load((const f32x4*)((const uint8_t*)g + gb + lo.g));
-        raw.b = *(const float*)((const uint8_t*)beta + bb + lo.beta);
-    }
+                                        const float* __restrict__ beta, int H, int64_t crow, int nrows,
+                                        const K1LaneOffsets& lo, RawChunk& raw) {
+    const size_t act = (size_t)crow * (D * 2), gb = (size_t)crow * (D * 4), bb = (size_t)crow * 4;
+    // byte ranges end with row nrows - 1 of head h; nrows <= 0 gives empty ranges
+    const uint32_t last = nrows > 0 ? (uint32_t)(nrows - 1) * (uint32_t)H : 0u;
+    const uint32_t live = nrows > 0 ? 1u : 0u;
+    const uint32_t n_act = (last * (D * 2) + D * 2) * live, n_g = (last * (D * 4) + D * 4) * live,
+                   n_b = (last * 4 + 4) * live;
+    raw.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc((const uint8_t*)q + act, n_act), (int)lo.act, 0, BUF_POLICY));
+    raw.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc((const uint8_t*)k + act, n_act), (int)lo.act, 0, BUF_POLICY));
+    raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc((const uint8_t*)v + act, n_act), (int)lo.act, 0, BUF_POLICY));
+    raw.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        chunk_rsrc((const uint8_t*)g + gb, n_g), (int)lo.g, 0, BUF_POLICY));
+    raw.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        chunk_rsrc((const uint8_t*)beta + bb, n_b), (int)lo.beta, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Row-coalesced K1 input path (fused kernel). A per-lane load of phase 1's
+// layout touches 16 rows with 32-64 bytes each and four wavefronts fetch
+// every line; measured, that runs at about a third of the rate of whole-row
+// loads. So wavefront w loads whole rows 2w and 2w + 1 of q, k, v and g
+// into registers (RowChunk), writes them to an LDS staging area, and after
+// the next barrier each wavefront reads its phase-1 fragments from there.
+// Staging of one chunk: rows in order; the 16-byte granules of row r are
+// XOR-swizzled with r & 15, so both the row writes and phase 1's column
+// reads (16 rows, one granule each) spread over all banks.
+// ---------------------------------------------------------------------------
+constexpr int STG_Q = 0;       // q  [16][256 B]
+constexpr int STG_K = 4096;    // k  [16][256 B]
+constexpr int STG_V = 8192;    // v  [16][256 B]
+constexpr int STG_G = 12288;   // g  [16][512 B]
+constexpr int STG_B = 20480;   // beta [16] fp32
+constexpr int STG_BYTES = 20544;
+
+// Staging byte offset of byte `byte` of row r of a 256-byte (bf16) row.
+__device__ __forceinline__ int stg_act_off(int r, int byte) {
+    return r * 256 + ((((byte >> 4) ^ r) & 15) << 4) + (byte & 15);
+}
+// Staging byte offset of byte `byte` of row r of a 512-byte (fp32) row.
+__device__ __forceinline__ int stg_g_off(int r, int byte) {
+    const int c = byte >> 4;
+    return r * 512 + (((c & 16) | ((c ^ r) & 15)) << 4) + (byte & 15);
+}
+
+struct RowChunk {
+    u32x2 q, k, v;  // 8 bytes of row 2w + (lane >> 5) at byte 8 (lane & 31)
+    f32x4 g;        // 16 bytes of that row of g at byte 16 (lane & 31)
+    float b;        // beta of row lane & 15 (wavefront 0 only)
+};
+
+// Per-lane constants of the row path of wavefront w.
+struct RowLaneOffsets {
+    uint32_t act, g, beta;  // global byte offsets from the chunk's first row
+    int st_act, st_g;       // staging offsets of the row writes
+    int rd_act, rd_g;       // staging offsets of phase 1's reads
+};
+
+__device__ __forceinline__ RowLaneOffsets row_lane_offsets(int H, int wave, int lane) {
+    const int r = 2 * wave + (lane >> 5), gg = lane >> 4, m = lane & 15;
+    RowLaneOffsets o;
+    o.act = (uint32_t)r * (uint32_t)H * (D * 2) + (lane & 31) * 8;
+    o.g = (uint32_t)r * (uint32_t)H * (D * 4) + (lane & 31) * 16;
+    o.beta = (uint32_t)m * (uint32_t)H * 4;
+    o.st_act = stg_act_off(r, (lane & 31) * 8);
+    o.st_g = stg_g_off(r, (lane & 31) * 16);
+    o.rd_act = stg_act_off(m, 32 * wave + 8 * gg);
+    o.rd_g = stg_g_off(m, 64 * wave + 16 * gg);
+    return o;
+}
+
+// Loads of the chunk whose first token-head row is crow (uniform), nrows
+// valid rows (rows past them, and every row when nrows <= 0, read as
+// zeros). Only wavefront 0 reads beta: the others' beta range is empty.
+__device__ __forceinline__ void k1_load_rows(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                             const uint16_t* __restrict__ v, const float* __restrict__ g,
+                                             const float* __restrict__ beta, int H, int64_t crow, int nrows,
+                                             int wave, const RowLaneOffsets& lo, RowChunk& rc) {
+    const size_t act = (size_t)crow * (D * 2), gb = (size_t)crow * (D * 4), bb = (size_t)crow * 4;
+    const uint32_t last = nrows > 0 ? (uint32_t)(nrows - 1) * (uint32_t)H : 0u;
+    const uint32_t live = nrows > 0 ? 1u : 0u;
+    const uint32_t n_act = (last * (D * 2) + D * 2) * live, n_g = (last * (D * 4) + D * 4) * live,
+                   n_b = (last * 4 + 4) * live * (wave == 0 ? 1u : 0u);
+    rc.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc((const uint8_t*)q + act, n_act), (int)lo.act, 0, BUF_POLICY));
+    rc.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc((const uint8_t*)k + act, n_act), (int)lo.act, 0, BUF_POLICY));
+    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc((const uint8_t*)v + act, n_act), (int)lo.act, 0, BUF_POLICY));
+    rc.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        chunk_rsrc((const uint8_t*)g + gb, n_g), (int)lo.g, 0, BUF_POLICY));
+    rc.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        chunk_rsrc((const uint8_t*)beta + bb, n_b), (int)lo.beta, 0, BUF_POLICY));
+}
+
+// Write a loaded RowChunk to the staging area stg.
+__device__ __forceinline__ void k1_stage(const RowChunk& rc, int wave, int lane, const RowLaneOffsets& lo,
+                                         uint8_t* stg) {
+    *(u32x2*)(stg + STG_Q + lo.st_act) = rc.q;
+    *(u32x2*)(stg + STG_K + lo.st_act) = rc.k;
+    *(u32x2*)(stg + STG_V + lo.st_act) = rc.v;
+    *(f32x4*)(stg + STG_G + lo.st_g) = rc.g;
+    if (wave == 0 && lane < 16) *(float*)(stg + STG_B + 4 * lane) = rc.b;
+}
+
+// Phase 1's fragments of wavefront w from a staged chunk.
+__device__ __forceinline__ void k1_read_staged(const uint8_t* stg, int lane, const RowLaneOffsets& lo,
+                                               RawChunk& raw) {
+    raw.q = *(const u32x2*)(stg + STG_Q + lo.rd_act);
+    raw.k = *(const u32x2*)(stg + STG_K + lo.rd_act);
+    raw.v = *(const u32x2*)(stg + STG_V + lo.rd_act);
+    raw.g = *(const f32x4*)(stg + STG_G + lo.rd_g);
+    raw.b = *(const float*)(stg + STG_B + 4 * (lane & 15));
 }
 
 __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lane, uint8_t* rec,
@@ -234,18 +358,22 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     *(u32x2*)(rec + REC_X + fo) = pack4(xk);
     // Kt^T and V: element (token m, channel 16 wave + 4gg + j) -> tile wave,
     // lane (m >> 2) * 16 + 4gg + j, slot m & 3
+    // lane (m >> 2) * 16 + 4gg + j sits in slot kv_slot of that lane:
+    // j rotated by m >> 2
+    const int a4 = m >> 2;
     const int to = wave * 512 + tfrag_off(gg, m);
+    const int s0 = (a4 & 3) * 8, s1 = ((a4 + 1) & 3) * 8, s2 = ((a4 + 2) & 3) * 8, s3 = ((a4 + 3) & 3) * 8;
     const u32x2 ktp = pack4(kt);
     uint8_t* kd = rec + REC_KT + to;
     uint8_t* vd = rec + REC_V + to;
-    *(uint16_t*)(kd + 0) = (uint16_t)ktp.x;
-    *(uint16_t*)(kd + 8) = (uint16_t)(ktp.x >> 16);
-    *(uint16_t*)(kd + 16) = (uint16_t)ktp.y;
-    *(uint16_t*)(kd + 24) = (uint16_t)(ktp.y >> 16);
-    *(uint16_t*)(vd + 0) = (uint16_t)raw.v.x;
-    *(uint16_t*)(vd + 8) = (uint16_t)(raw.v.x >> 16);
-    *(uint16_t*)(vd + 16) = (uint16_t)raw.v.y;
-    *(uint16_t*)(vd + 24) = (uint16_t)(raw.v.y >> 16);
+    *(uint16_t*)(kd + s0) = (uint16_t)ktp.x;
+    *(uint16_t*)(kd + s1) = (uint16_t)(ktp.x >> 16);
+    *(uint16_t*)(kd + s2) = (uint16_t)ktp.y;
+    *(uint16_t*)(kd + s3) = (uint16_t)(ktp.y >> 16);
+    *(uint16_t*)(vd + s0) = (uint16_t)raw.v.x;
+    *(uint16_t*)(vd + s1) = (uint16_t)(raw.v.x >> 16);
+    *(uint16_t*)(vd + s2) = (uint16_t)raw.v.y;
+    *(uint16_t*)(vd + s3) = (uint16_t)(raw.v.y >> 16);
     // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
     if (m == 15) *(f32x4*)(rec + REC_GC + (16 * wave + 4 * gg) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     if (wave == 0 && gg == 0) *(float*)(scr + K1_BETA + 4 * m) = raw.b;
@@ -271,13 +399,13 @@ __device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, cons
     f32x4 l;
 #pragma unroll
     for (int v = 0; v < 4; ++v) l[v] = (m < 4 * gg + v) ? a[v] : 0.f;
-    // through LDS as L^T (lw[c * 16 + r] = L[r][c]): lane (gg, i) then holds
+    // through LDS as L^T (lw[c * K1_LSTRIDE + r] = L[r][c]): lane (gg, i) then holds
     // column i of L, lc[K] = L[K][i]
-    *(f32x4*)(lw + m * 16 + 4 * gg) = l;
+    *(f32x4*)(lw + m * K1_LSTRIDE + 4 * gg) = l;
     float lc[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const f32x4 c = *(const f32x4*)(lw + m * 16 + 4 * q);
+        const f32x4 c = *(const f32x4*)(lw + m * K1_LSTRIDE + 4 * q);
 #pragma unroll
         for (int v = 0; v < 4; ++v) lc[4 * q + v] = c[v];
     }
@@ -370,7 +498,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
     for (int n = 0; n < NT; ++n) {
         f32x4 r;
         if constexpr (WITH_V) {
-            const u32x2 vw = *(const u32x2*)(rec + REC_V + (n0 + n) * 512 + lane * 8);
+            const u32x2 vw = *(const u32x2*)(rec + REC_V + (n0 + n) * 512 + kv_slot(lane) * 8);
             r[0] = bf16_lo(vw.x) - P[n][0];
             r[1] = bf16_hi(vw.x) - P[n][1];
             r[2] = bf16_lo(vw.y) - P[n][2];
@@ -401,7 +529,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const f32x4 gcv = *(const f32x4*)(rec + REC_GC + (16 * t + 4 * gg) * 4);
-        const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + lane * 8);
+        const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + kv_slot(lane) * 8);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             S[t][n] = gcv * S[t][n];

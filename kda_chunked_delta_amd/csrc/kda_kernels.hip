@@ -23,6 +23,10 @@ __device__ __forceinline__ void seq_bounds(const CommonArgs& c, int seq, int64_t
     end = e;
 }
 
+// A uniform byte offset that the compiler treats as opaque (no strength
+// reduction of the addresses built on it across loop iterations).
+__device__ __forceinline__ int ring_off(int off) { return __builtin_amdgcn_readfirstlane(off); }
+
 __device__ __forceinline__ int rows_of(int64_t tok, int64_t end) {
     const int64_t n = end - tok;
     return n <= 0 ? 0 : (n >= CH ? CH : (int)n);
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
     RawChunk raw;
     const K1LaneOffsets lo = k1_lane_offsets(H, wave, lane);
-    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, tok0 * H + h, rows_of(tok0, end), lo, lane, raw);
+    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, tok0 * H + h, rows_of(tok0, end), lo, raw);
     k1_phase1(raw, wave, lane, rec, scr);
     lds_barrier();
     k1_phase2(wave, lane, rec, scr, lw);
@@ -172,68 +176,105 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 
 // ---------------------------------------------------------------------------
 // Fused K1 + K2 (the serial path): one workgroup of 16 wavefronts per (unit,
-// head), software-pipelined with one barrier per chunk. Wavefronts 0..7
-// hold the state (wavefront w: value columns 16w..16w+15, in MFMA
-// accumulators for the whole unit) and in the interval that ends with
-// barrier i advance it over chunk i and store that chunk's output.
-// Wavefronts 8 + w run K1 phase 1 of chunk i+2 on key channels and value
-// columns 16w..16w+15 and prefetch chunk i+3; of them, w < 4 and w = WAVE_QK
-// also run K1 phase 2 of chunk i+1. Every SIMD thus holds two state
-// wavefronts and two K1 wavefronts, whose latency-bound and arithmetic-bound
-// work interleave. Records live in a 3-deep LDS ring, K1 scratch in a 2-deep
-// one.
+// head), software-pipelined with one barrier per chunk. In the interval that
+// ends with barrier i:
+//   - wavefronts 0..7 hold the state (wavefront w: value columns
+//     16w..16w+15, in MFMA accumulators for the whole unit), advance it over
+//     chunk i and store that chunk's output; with P2_ON_STATE they also run
+//     K1 phase 2 (T' on w < 4, A_qk on w = WAVE_QK) of chunk i+1;
+//   - wavefronts 8 + w run K1 phase 1 of chunk i+2 (key channels and value
+//     columns 16w..16w+15) from the staged rows, stage the rows of chunk i+3
+//     that they loaded two intervals earlier, and issue the row loads of
+//     chunk i+5 (rows 2w, 2w+1; into the register set just staged).
+// Each SIMD holds two state wavefronts and two K1 wavefronts. Records live in
+// a 3-deep LDS ring, K1 scratch and the staged rows in 2-deep ones. Both
+// roles run the same even number of intervals, nc + 2 rounded up, after one
+// start-up barrier: the trailing K1 work on chunks past the end reads zeros
+// (a buffer load of a chunk with no rows touches no memory) and fills slots
+// nobody reads, so the K1 loop body is unconditional and the compiler's wait
+// for a register set covers only that set's loads.
 // ---------------------------------------------------------------------------
-constexpr int FUSED_LDS = 3 * REC_BYTES + 2 * K1_BYTES + N_WAVE_T * K1_LBYTES;
+constexpr bool P2_ON_STATE = true;
+constexpr int FUSED_LDS = 3 * REC_BYTES + 2 * K1_BYTES + N_WAVE_T * K1_LBYTES + 2 * STG_BYTES;
 
 __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* recs = smem;
     uint8_t* scrs = smem + 3 * REC_BYTES;
     float* lw = (float*)(scrs + 2 * K1_BYTES);
+    uint8_t* stgs = smem + 3 * REC_BYTES + 2 * K1_BYTES + N_WAVE_T * K1_LBYTES;
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const UnitDesc u = a.units[blockIdx.x / H];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int gg = lane >> 4, m = lane & 15;
-    const int w8 = wave & 7;
+    // uniform by construction; said explicitly so that buffer descriptors
+    // built from it stay scalar
+    const int w8 = __builtin_amdgcn_readfirstlane(wave & 7);
     int64_t beg, end;
     seq_bounds(a.c, u.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
     const int nc = u.n_chunks;
+    const int n_int = (nc + 3) & ~1;  // barrier intervals i = -2 .. n_int - 3
     if (wave < 8) {
         // state wavefronts
         f32x4 S[8][1];
         load_state(unit_state_in(a, u, h), S, w8, gg, m);
-        for (int i = -2; i < nc; ++i) {
-            if (i >= 0) {
+        lds_barrier();  // start-up: the first chunk is staged
+        for (int i = -2; i < n_int - 2; ++i) {
+            if (i >= 0 && i < nc) {
                 f32x4 oacc[1];
                 chain_step<1, true, true>(recs + (i % 3) * REC_BYTES, S, w8, lane, oacc);
                 store_output(a, h, tok0 + (int64_t)CH * i, end, oacc[0], w8, gg, m);
             }
+            if (P2_ON_STATE && i >= -1)
+                k1_phase2(w8, lane, recs + ring_off(((i + 1) % 3) * REC_BYTES),
+                          scrs + ring_off(((i + 1) & 1) * K1_BYTES), lw);
             lds_barrier();
         }
         if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, w8, gg, m);
     } else {
-        // K1 wavefronts
-        RawChunk raw;
-        const K1LaneOffsets lo = k1_lane_offsets(H, w8, lane);
-        auto load = [&](int ci) {
+        // K1 wavefronts: chunk c is loaded into register set c & 1
+        RowChunk r0, r1;
+        const RowLaneOffsets lo = row_lane_offsets(H, w8, lane);
+        auto load = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
             const int64_t t = tok0 + (int64_t)CH * ci;
-            k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, t * H + h, rows_of(t, end), lo, lane, raw);
+            k1_load_rows(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, t * H + h, rows_of(t, end), w8, lo, rc);
         };
-        auto interval = [&](int i, bool p1, bool ld, bool p2) __attribute__((always_inline)) {
-            if (p1) k1_phase1(raw, w8, lane, recs + ((i + 2) % 3) * REC_BYTES, scrs + ((i + 2) & 1) * K1_BYTES);
-            if (ld) load(i + 3);
-            if (p2) k1_phase2(w8, lane, recs + ((i + 1) % 3) * REC_BYTES, scrs + ((i + 1) & 1) * K1_BYTES, lw);
+        auto stage = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
+            // the register set is read only from here on (see below)
+            asm volatile("" : "+v"(rc.q), "+v"(rc.k), "+v"(rc.v), "+v"(rc.g), "+v"(rc.b));
+            k1_stage(rc, w8, lane, lo, stgs + ring_off((ci & 1) * STG_BYTES));
+        };
+        auto interval = [&](int i, RowChunk& rc, bool p2) __attribute__((always_inline)) {
+            // Phase 1 reads LDS only after the barrier that ends the previous
+            // interval, and the staging of rc waits for its loads there too:
+            // the empty redefinitions keep the compiler from hoisting
+            // either above that barrier.
+            RawChunk raw;
+            k1_read_staged(stgs + ring_off(((i + 2) & 1) * STG_BYTES), lane, lo, raw);
+            // ring slots as opaque uniform offsets, so every LDS access of a
+            // phase is one per-lane base plus immediate offsets
+            k1_phase1(raw, w8, lane, recs + ring_off(((i + 2) % 3) * REC_BYTES),
+                      scrs + ring_off(((i + 2) & 1) * K1_BYTES));
+            stage(rc, i + 3);
+            load(rc, i + 5);
+            if (!P2_ON_STATE && p2)
+                k1_phase2(w8, lane, recs + ring_off(((i + 1) % 3) * REC_BYTES),
+                          scrs + ring_off(((i + 1) & 1) * K1_BYTES), lw);
             lds_barrier();
         };
-        if (nc > 0) load(0);
-        // the steady-state intervals run every step unconditionally, which
-        // keeps the compiler's wait analysis for the prefetch exact there
-        int i = -2;
-        interval(i, i + 2 < nc, i + 3 < nc, false);
-        for (i = -1; i + 3 < nc; ++i) interval(i, true, true, true);
-        for (; i < nc; ++i) interval(i, i + 2 < nc, i + 3 < nc, i + 1 >= 0 && i + 1 < nc);
+        load(r0, 0);
+        load(r1, 1);
+        stage(r0, 0);
+        load(r0, 2);
+        lds_barrier();  // start-up: chunk 0 staged
+        interval(-2, r1, false);
+        interval(-1, r0, true);
+        for (int i = 0; i < n_int - 2; i += 2) {
+            interval(i, r1, true);
+            interval(i + 1, r0, true);
+        }
     }
 }
 
