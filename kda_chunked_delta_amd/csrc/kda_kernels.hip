@@ -129,13 +129,18 @@ __device__ __forceinline__ void identity_state(f32x4 (&S)[8][NT], int n0, int gg
 // Output rows of one chunk: oacc[v] is o[token m][16 n + 4gg + v].
 __device__ __forceinline__ void store_output(const K2Args& a, int h, int64_t tk, int64_t end,
                                              const f32x4& oacc, int n, int gg, int m) {
-    if (m < rows_of(tk, end)) {
-        uint16_t* orow = a.out + ((size_t)(tk + m) * a.c.H + h) * D;
-        u32x2 w;
-        w.x = pack_bf16(a.scale * oacc[0], a.scale * oacc[1]);
-        w.y = pack_bf16(a.scale * oacc[2], a.scale * oacc[3]);
-        *(u32x2*)(orow + 16 * n + 4 * gg) = w;
-    }
+    // a buffer store whose range ends with row rows_of - 1 of head h: the
+    // lanes of rows past the end are dropped without a branch
+    const int nrows = rows_of(tk, end);
+    const uint32_t rowb = (uint32_t)a.c.H * (D * 2);
+    const uint32_t n_out = nrows > 0 ? (uint32_t)(nrows - 1) * rowb + D * 2 : 0u;
+    u32x2 w;
+    w.x = pack_bf16(a.scale * oacc[0], a.scale * oacc[1]);
+    w.y = pack_bf16(a.scale * oacc[2], a.scale * oacc[3]);
+    __builtin_amdgcn_raw_buffer_store_b64(
+        __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, w),
+        chunk_rsrc(a.out + ((size_t)tk * a.c.H + h) * D, n_out),
+        (int)((uint32_t)m * rowb + (16 * n + 4 * gg) * 2), 0, 0);
 }
 
 __device__ __forceinline__ const float* unit_state_in(const K2Args& a, const UnitDesc& u, int h) {
@@ -221,17 +226,36 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         f32x4 S[8][1];
         load_state(unit_state_in(a, u, h), S, w8, gg, m);
         lds_barrier();  // start-up: the first chunk is staged
-        for (int i = -2; i < n_int - 2; ++i) {
-            if (i >= 0 && i < nc) {
-                f32x4 oacc[1];
-                chain_step<1, true, true>(recs + (i % 3) * REC_BYTES, S, w8, lane, oacc);
-                store_output(a, h, tok0 + (int64_t)CH * i, end, oacc[0], w8, gg, m);
+        auto step = [&](int i) __attribute__((always_inline)) {
+            f32x4 oacc[1];
+            chain_step<1, true, true>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, oacc);
+            store_output(a, h, tok0 + (int64_t)CH * i, end, oacc[0], w8, gg, m);
+        };
+        // one loop per phase-2 role (0: none, 1: rows 4 w8.. of T', 2: A_qk),
+        // so that each loop body is one block in which phase 2 of chunk i + 1
+        // (independent of the chain) interleaves with the chain over chunk i
+        auto run = [&](auto role) __attribute__((always_inline)) {
+            constexpr int R = decltype(role)::value;
+            auto p2 = [&](int c) __attribute__((always_inline)) {
+                uint8_t* rec = recs + ring_off((c % 3) * REC_BYTES);
+                const uint8_t* scr = scrs + ring_off((c & 1) * K1_BYTES);
+                if constexpr (R == 1) k1_phase2_t(lane, w8, rec, scr, lw + w8 * (K1_LBYTES / 4));
+                if constexpr (R == 2) k1_phase2_qk(lane, rec, scr);
+            };
+            lds_barrier();  // interval -2: nothing to do yet
+            p2(0);
+            lds_barrier();  // interval -1
+            for (int i = 0; i < nc; ++i) {
+                p2(i + 1);
+                step(i);
+                lds_barrier();
             }
-            if (P2_ON_STATE && i >= -1)
-                k1_phase2(w8, lane, recs + ring_off(((i + 1) % 3) * REC_BYTES),
-                          scrs + ring_off(((i + 1) & 1) * K1_BYTES), lw);
-            lds_barrier();
-        }
+            for (int i = nc; i < n_int - 2; ++i) lds_barrier();
+        };
+        if (!P2_ON_STATE) run(std::integral_constant<int, 0>{});
+        else if (w8 < N_WAVE_T) run(std::integral_constant<int, 1>{});
+        else if (w8 == WAVE_QK) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 0>{});
         if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, w8, gg, m);
     } else {
         // K1 wavefronts: chunk c is loaded into register set c & 1
