@@ -158,20 +158,6 @@ struct RawChunk {
     float b;
 };
 
-// Per-lane byte offsets of a K1 load from the start of a chunk's first row
-// (row m of the chunk, channels 16 wave + 4gg ..), fixed for a kernel.
-struct K1LaneOffsets {
-    uint32_t act;   // into a bf16 [., H, D] tensor
-    uint32_t g;     // into the fp32 g tensor
-    uint32_t beta;  // into the fp32 beta [., H] tensor
-};
-
-__device__ __forceinline__ K1LaneOffsets k1_lane_offsets(int H, int wave, int lane) {
-    const int gg = lane >> 4, m = lane & 15;
-    const uint32_t el = (uint32_t)m * (uint32_t)H * D + 16 * wave + 4 * gg;
-    return K1LaneOffsets{2 * el, 4 * el, 4 * (uint32_t)m * (uint32_t)H};
-}
-
 // Buffer descriptor over [base, base + bytes): raw (unstrided) addressing,
 // 32-bit data format. A load whose byte range ends past `bytes` returns
 // zeros and touches no memory.
@@ -183,35 +169,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, u
 // there, and measured slower.)
 constexpr int BUF_POLICY = 0;
 
-// Load the chunk whose first token-head row is crow = t0 * H + h (uniform),
-// 1 <= nrows <= 16 valid rows. Each tensor is read through a descriptor
-// based at the chunk's first row whose range ends after row nrows - 1, so
-// the lanes of rows nrows..15 read zeros (k = q = v = 0, g = 0, beta = 0)
-// without a branch; the per-chunk address arithmetic is scalar.
-__device__ __forceinline__ void k1_load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                        const uint16_t* __restrict__ v, const float* __restrict__ g,
-                                        const float* __restrict__ beta, int H, int64_t crow, int nrows,
-                                        const K1LaneOffsets& lo, RawChunk& raw) {
-    const size_t act = (size_t)crow * (D * 2), gb = (size_t)crow * (D * 4), bb = (size_t)crow * 4;
-    // byte ranges end with row nrows - 1 of head h; nrows <= 0 gives empty ranges
-    const uint32_t last = nrows > 0 ? (uint32_t)(nrows - 1) * (uint32_t)H : 0u;
-    const uint32_t live = nrows > 0 ? 1u : 0u;
-    const uint32_t n_act = (last * (D * 2) + D * 2) * live, n_g = (last * (D * 4) + D * 4) * live,
-                   n_b = (last * 4 + 4) * live;
-    raw.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)q + act, n_act), (int)lo.act, 0, BUF_POLICY));
-    raw.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)k + act, n_act), (int)lo.act, 0, BUF_POLICY));
-    raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)v + act, n_act), (int)lo.act, 0, BUF_POLICY));
-    raw.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        chunk_rsrc((const uint8_t*)g + gb, n_g), (int)lo.g, 0, BUF_POLICY));
-    raw.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-        chunk_rsrc((const uint8_t*)beta + bb, n_b), (int)lo.beta, 0, 0));
-}
-
 // ---------------------------------------------------------------------------
-// Row-coalesced K1 input path (fused kernel). A per-lane load of phase 1's
+// Row-coalesced K1 input path (both K1 kernels). A per-lane load of phase 1's
 // layout touches 16 rows with 32-64 bytes each and four wavefronts fetch
 // every line; measured, that runs at about a third of the rate of whole-row
 // loads. So wavefront w loads whole rows 2w and 2w + 1 of q, k, v and g

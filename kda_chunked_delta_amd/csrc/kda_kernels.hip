@@ -153,23 +153,37 @@ __device__ __forceinline__ const float* unit_state_in(const K2Args& a, const Uni
 
 // ---------------------------------------------------------------------------
 // K1 (materialised form): one workgroup of 8 wavefronts per (chunk, head);
-// grid = total_chunks * H, head fastest. Same two phases as the fused kernel.
+// grid = total_chunks * H, head fastest. The rows are loaded whole and
+// staged through LDS as in the fused kernel; the staging area overlays the
+// record and scratch, which are written only after every wavefront has read
+// its phase-1 fragments.
 // ---------------------------------------------------------------------------
+constexpr int K1P_LDS = REC_BYTES + K1_BYTES + N_WAVE_T * K1_LBYTES;
+static_assert(STG_BYTES <= K1P_LDS, "staging overlays the record area");
+
 __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
-    __shared__ __align__(16) uint8_t rec[REC_BYTES];
-    __shared__ __align__(16) uint8_t scr[K1_BYTES];
-    __shared__ __align__(16) float lw[N_WAVE_T * K1_LBYTES / 4];
+    __shared__ __align__(16) uint8_t lds[K1P_LDS];
+    uint8_t* rec = lds;
+    uint8_t* scr = lds + REC_BYTES;
+    float* lw = (float*)(lds + REC_BYTES + K1_BYTES);
+    uint8_t* stg = lds;
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const int gc = blockIdx.x / H;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const ChunkDesc cd = a.chunks[gc];
     int64_t beg, end;
     seq_bounds(a.c, cd.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
+    const RowLaneOffsets lo = row_lane_offsets(H, wave, lane);
+    RowChunk rc;
+    k1_load_rows(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, tok0 * H + h, rows_of(tok0, end), wave, lo, rc);
+    k1_stage(rc, wave, lane, lo, stg);
+    lds_barrier();
     RawChunk raw;
-    const K1LaneOffsets lo = k1_lane_offsets(H, wave, lane);
-    k1_load(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, tok0 * H + h, rows_of(tok0, end), lo, raw);
+    k1_read_staged(stg, lane, lo, raw);
+    lds_barrier();  // the staging area is free again
     k1_phase1(raw, wave, lane, rec, scr);
     lds_barrier();
     k1_phase2(wave, lane, rec, scr, lw);
