@@ -380,8 +380,16 @@ __global__ __launch_bounds__(1024) void kda_cp_prescan(PrescanArgs a) {
 // in segment order, on fp32 MFMA. Wavefront t owns carry rows 16t..16t+15.
 // Every carry (including carry_0) is written to the carries scratch, so that
 // segment-K2 never reads initial_state while another segment writes
-// final_state in place.
+// final_state in place. Only the carry is serial: the summaries (M_s, B_s)
+// of the next step are loaded while the current one computes, into the
+// other of two register sets, and each step splits its 32 MFMAs over two
+// accumulators.
 // ---------------------------------------------------------------------------
+struct MergeOperands {
+    f32x4 m[8];  // M_s[16 wave + m][32 gg + 4j .. + 3], j = 0..7
+    f32x4 b;     // B_s[16 wave + 4 gg + v][16 vt + m], v = 0..3
+};
+
 __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
     __shared__ float carry[D][16];
     const int H = a.c.H;
@@ -402,18 +410,31 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
         }
     }
     __syncthreads();
-    for (int s = 0; s + 1 < it.n_segments; ++s) {
-        const size_t sum_off = ((size_t)(it.prescan0 + s) * H + h) * (D * D);
+    const int n_steps = it.n_segments - 1;
+    if (n_steps <= 0) return;
+    // summaries of step s (clamped to the last one, so every load is valid
+    // and unconditional)
+    auto load = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
+        const int ss = s < n_steps ? s : n_steps - 1;
+        const size_t sum_off = ((size_t)(it.prescan0 + ss) * H + h) * (D * D);
         const float* M = a.m_seg + sum_off;
         const float* B = a.b_seg + sum_off;
-        f32x4 acc;
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) acc[vv] = B[(16 * wave + 4 * gg + vv) * D + 16 * vt + m];
-        f32x4 mrow[8];
+        for (int vv = 0; vv < 4; ++vv) x.b[vv] = B[(16 * wave + 4 * gg + vv) * D + 16 * vt + m];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mrow[j] = *(const f32x4*)(M + (16 * wave + m) * D + 32 * gg + 4 * j);
+        for (int j = 0; j < 8; ++j) x.m[j] = *(const f32x4*)(M + (16 * wave + m) * D + 32 * gg + 4 * j);
+    };
+    auto step = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
+        // the operands are read only from here on (keeps their wait here)
+        asm volatile("" : "+v"(x.m[0]), "+v"(x.m[1]), "+v"(x.m[2]), "+v"(x.m[3]), "+v"(x.m[4]),
+                     "+v"(x.m[5]), "+v"(x.m[6]), "+v"(x.m[7]), "+v"(x.b));
+        f32x4 acc0 = x.b, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qq = 0; qq < 32; ++qq) acc = mfma_f32_k4(mrow[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc);
+        for (int qq = 0; qq < 32; qq += 2) {
+            acc0 = mfma_f32_k4(x.m[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc0);
+            acc1 = mfma_f32_k4(x.m[qq >> 2][(qq & 3) + 1], carry[32 * gg + qq + 1][m], acc1);
+        }
+        const f32x4 acc = acc0 + acc1;
         __syncthreads();
         float* cn = a.carries + ((size_t)(it.carry0 + s + 1) * H + h) * (D * D);
 #pragma unroll
@@ -422,7 +443,18 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
             cn[(16 * wave + 4 * gg + vv) * D + 16 * vt + m] = acc[vv];
         }
         __syncthreads();
+    };
+    MergeOperands xa, xb;
+    load(0, xa);
+    load(1, xb);
+    int s = 0;
+    for (; s + 1 < n_steps; s += 2) {
+        step(s, xa);
+        load(s + 2, xa);
+        step(s + 1, xb);
+        load(s + 3, xb);
     }
+    if (s < n_steps) step(s, xa);
 }
 
 // ---------------------------------------------------------------------------

@@ -72,11 +72,11 @@ struct PlannerConsts {
 
 PlannerConsts planner_consts() {
     PlannerConsts c;
-    c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.8);
-    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 2.0);
-    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 2.65);
-    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.1);
-    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 3.2);
+    c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.7);
+    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 1.72);
+    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 2.93);
+    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.3);
+    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 2.63);
     c.launch_us = env_double("KDA_CP_LAUNCH_US", 5.0);
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
     c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
