@@ -481,8 +481,12 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
 #pragma unroll
             for (int n = 0; n < NT; ++n) oacc[n] = mfma_k32(Sb[p][n], qf, oacc[n]);
         }
+        // A_qk U goes to a fresh 16x16x16 accumulator and is added with VALU.
+        // Chaining it onto oacc (a 16x16x32 accumulator handed straight to the
+        // 16x16x16 shape as its C operand) was seen to lose the last 16x16x32
+        // contribution in two of the four output rows.
 #pragma unroll
-        for (int n = 0; n < NT; ++n) oacc[n] = mfma_k16(Ub[n], aq, oacc[n]);
+        for (int n = 0; n < NT; ++n) oacc[n] += mfma_k16(Ub[n], aq, f32x4{0.f, 0.f, 0.f, 0.f});
     }
     // S_next = Diag(exp G_C) S0 + Kt^T U
 #pragma unroll
