@@ -23,6 +23,8 @@ Functions
   chunked      the chunked WY algebra with CHUNK=16, returning the K1
                quantities per chunk (decayed q/k, WY-transformed keys and
                values, masked q-k Gram, chunk decay) and the K2 results
+  decode_step  one token per sequence, the state advanced by one step, in
+               the matrix form (I - beta k k^T) Diag(exp g) S + beta k v^T
 
 Every function takes fp64-convertible arrays (numpy, or torch tensors of any
 float dtype; bf16/fp32 values upcast exactly) in the packed token-major
@@ -285,3 +287,33 @@ def segment_summary(k1_list, dk, dv):
         _, B = chunk_k2(B, k1)
         M = k1["gC"][:, None] * M - k1["Kt"].T @ (k1["W"] @ M)
     return M, B
+
+
+# ---------------------------------------------------------------------------
+# Decode: one new token per sequence, the state advanced by one step
+# ---------------------------------------------------------------------------
+def decode_step(q, k, v, g, beta, state, scale=1.0):
+    """One decode step for a batch of N sequences, each receiving one token.
+
+    "feat(cake_kda): share recurrent prefill kernels across SM100 family"
+    (FlashInfer pull request #4313, its AOT registration notes) keeps a KDA
+    decode entry beside the prefill; the step is the recurrence of [P1]'s
+    commit summary for a single token, written here in its matrix form:
+      S' = (I - beta k k^T) Diag(exp g) S + beta k v^T,   o = scale S'^T q.
+    Inputs q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H]; state [N, H, dk, dv]
+    (rows are key channels). Returns (o [N, H, dv], new_state); the input
+    state is not modified.
+    """
+    q, k, v, g, beta, S = map(to_f64, (q, k, v, g, beta, state))
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((N, H, dv))
+    S_new = np.zeros((N, H, dk, dv))
+    for n in range(N):
+        for h in range(H):
+            kk = k[n, h]
+            P = np.eye(dk) - beta[n, h] * np.outer(kk, kk)
+            S1 = P @ (np.diag(np.exp(g[n, h])) @ S[n, h]) + beta[n, h] * np.outer(kk, v[n, h])
+            S_new[n, h] = S1
+            o[n, h] = scale * (S1.T @ q[n, h])
+    return o, S_new

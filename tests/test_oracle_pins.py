@@ -369,3 +369,94 @@ def test_planted_chunk_mistakes_are_caught(kind, monkeypatch):
     o1, s1 = ref.recurrent(**c)
     o2, s2 = ref.chunked(**c)
     assert not (np.allclose(o1, o2, rtol=1e-9, atol=1e-10) and np.allclose(s1, s2, rtol=1e-9, atol=1e-10))
+
+
+# ---------------------------------------------------------------------------
+# decode step (one token per sequence, matrix form of the update)
+# ---------------------------------------------------------------------------
+def _decode_tokens(step, c):
+    """Feed each sequence of a packed case through `step` one token at a time
+    (all sequences advance together; shorter ones stop early)."""
+    q, k, v, g, beta = (np.asarray(c[x], dtype=np.float64) for x in ("q", "k", "v", "g", "beta"))
+    cu = np.asarray(c["cu_seqlens"])
+    n = len(cu) - 1
+    H, dk, dv = k.shape[1], k.shape[2], v.shape[2]
+    S = np.zeros((n, H, dk, dv)) if c["initial_state"] is None else np.array(c["initial_state"], dtype=float)
+    o = np.zeros((cu[-1], H, dv))
+    for t in range(int(np.max(np.diff(cu))) if n else 0):
+        live = [i for i in range(n) if cu[i] + t < cu[i + 1]]
+        rows = [cu[i] + t for i in live]
+        ot, St = step(q[rows], k[rows], v[rows], g[rows], beta[rows], S[live])
+        o[rows] = ot
+        S[live] = St
+    return o, S
+
+
+def test_decode_golden_hand_example():
+    c, gv = golden_inputs()
+    o, sT = _decode_tokens(ref.decode_step, c)
+    np.testing.assert_allclose(o.reshape(-1), gv["o"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sT.reshape(-1), gv["ST"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("lengths,dk,dv", [([1], 8, 8), ([5, 1, 9], 8, 4), ([12, 7], 16, 16), ([3], 128, 128)])
+def test_decode_matches_recurrent(lengths, dk, dv):
+    """The matrix form, stepped token by token, equals the residual form of
+    the recurrence over whole sequences (two different algebraic forms)."""
+    c = rand_case(lengths, H=3, dk=dk, dv=dv, seed=sum(lengths) + dk)
+    o1, s1 = ref.recurrent(**c)
+    o2, s2 = _decode_tokens(ref.decode_step, c)
+    np.testing.assert_allclose(o2, o1, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s2, s1, rtol=1e-11, atol=1e-12)
+
+
+def test_decode_closed_forms():
+    r = np.random.default_rng(11)
+    N, H, dk, dv = 4, 2, 8, 6
+    q, k = r.standard_normal((N, H, dk)), r.standard_normal((N, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v, g = r.standard_normal((N, H, dv)), -r.random((N, H, dk))
+    beta, S = r.random((N, H)), r.standard_normal((N, H, dk, dv))
+    # beta = 0: pure per-key-channel decay
+    o, S1 = ref.decode_step(q, k, v, g, np.zeros((N, H)), S, scale=0.5)
+    np.testing.assert_allclose(S1, np.exp(g)[..., None] * S, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(o, 0.5 * np.einsum("nhkv,nhk->nhv", np.exp(g)[..., None] * S, q), rtol=1e-12)
+    # zero state: S' = beta k v^T, o = scale beta (q.k) v
+    o, S1 = ref.decode_step(q, k, v, g, beta, np.zeros_like(S), scale=2.0)
+    np.testing.assert_allclose(S1, beta[..., None, None] * k[..., :, None] * v[..., None, :], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(o, 2.0 * (beta * np.einsum("nhk,nhk->nh", q, k))[..., None] * v, rtol=1e-12, atol=1e-14)
+    # g = 0, beta = 1, |k| = 1: the new state maps k to v exactly
+    _, S1 = ref.decode_step(q, k, v, np.zeros_like(g), np.ones((N, H)), S)
+    np.testing.assert_allclose(np.einsum("nhkv,nhk->nhv", S1, k), v, rtol=1e-12, atol=1e-12)
+
+
+DECODE_MUTANTS = {
+    # decay applied after the projection instead of before it
+    "decay_after": lambda P, Dg, S, w: Dg @ (P @ S) + w,
+    # projection skipped (plain additive update)
+    "no_projection": lambda P, Dg, S, w: Dg @ S + w,
+    # state decayed along the value axis
+    "decay_axis": lambda P, Dg, S, w: P @ (S @ Dg[:S.shape[1], :S.shape[1]]) + w,
+}
+
+
+@pytest.mark.parametrize("kind", sorted(DECODE_MUTANTS))
+def test_planted_decode_mistakes_are_caught(kind):
+    def step(q, k, v, g, beta, S):
+        N, H, dk = k.shape
+        o, S_new = np.zeros((N, H, v.shape[-1])), np.zeros_like(S)
+        for n in range(N):
+            for h in range(H):
+                P = np.eye(dk) - beta[n, h] * np.outer(k[n, h], k[n, h])
+                S_new[n, h] = DECODE_MUTANTS[kind](P, np.diag(np.exp(g[n, h])), S[n, h],
+                                                   beta[n, h] * np.outer(k[n, h], v[n, h]))
+                o[n, h] = S_new[n, h].T @ q[n, h]
+        return o, S_new
+    c, gv = golden_inputs()
+    o, sT = _decode_tokens(step, c)
+    golden_ok = np.allclose(o.reshape(-1), gv["o"], atol=1e-9) and np.allclose(sT.reshape(-1), gv["ST"], atol=1e-9)
+    c = rand_case([6, 3], H=2, dk=8, dv=8, seed=5)
+    o1, s1 = ref.recurrent(**c)
+    o2, s2 = _decode_tokens(step, c)
+    rec_ok = np.allclose(o1, o2, rtol=1e-9, atol=1e-10) and np.allclose(s1, s2, rtol=1e-9, atol=1e-10)
+    assert not (golden_ok and rec_ok), "planted decode mistake %r went unnoticed" % kind
