@@ -7,6 +7,9 @@ measured with HIP events on the launch stream, and the CPU oracle timed on the
 host cores as a reported baseline.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload varlen8_h32]
+
+With --workload decode_n256_h32 a step is instead one kda_decode call: one
+token for each of 256 sequences x 32 heads, the fp32 states advanced in place.
 """
 import argparse
 import hashlib
@@ -40,9 +43,21 @@ WORKLOAD_TEXT = {
 }
 
 
-def source_digest():
+DECODE_METRIC = "KDA decode tokens/sec (one token per sequence, H=32, D=128, fp32 state in place) + % of HBM roofline"
+# Algorithmic bytes of one decode step per (sequence, head): the fp32 state
+# read and written (2 x 65536), q, k, v (bf16, 3 x 256), g (fp32, 512),
+# beta (4) and o (bf16, 256).
+DECODE_BYTES_PER_SEQ_HEAD = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256
+DECODE_TEXT = {
+    "decode_n256_h32": "decode step: 256 sequences x 32 heads, one token each, D=128, bf16 q/k/v, "
+                       "fp32 g=-softplus(N(0,1)) and beta=sigmoid(N(0,1)), fp32 state N(0, 0.1) "
+                       "updated in place",
+}
+
+
+def source_digest(files=("kda_device.hpp", "kda_kernels.hip", "kda_launch.h")):
     h = hashlib.sha256()
-    for f in ("kda_device.hpp", "kda_kernels.hip", "kda_launch.h"):
+    for f in files:
         with open(os.path.join(ROOT, "kda_chunked_delta_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -102,7 +117,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="varlen8_h32", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="varlen8_h32", choices=sorted(WORKLOAD_TEXT) + sorted(DECODE_TEXT))
     ap.add_argument("--cp", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target duration of the CPU-oracle baseline sample (0 disables it)")
@@ -132,6 +147,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
                           "launches": max(1, args.steps)}), flush=True)
+        return
+    if args.workload in DECODE_TEXT:
+        bench_decode(args, dev)
         return
     d = workload(args.workload, device=dev)
     H, cu = d["H"], d["cu_seqlens_host"]
@@ -208,6 +226,91 @@ def main():
     if args.cpu_seconds > 0:
         print("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_decode(d, max_seconds):
+    """The fp64 oracle decode step (numpy, one BLAS thread) on a bounded
+    sample: whole sequences, all heads, added until the estimated time
+    reaches max_seconds."""
+    from threadpoolctl import threadpool_limits
+    from oracle import reference as ref
+    N, H = d["N"], d["H"]
+    cpu = {k: d[k].cpu() for k in ("q", "k", "v", "g", "beta", "state")}
+    with threadpool_limits(limits=1):
+        t = time.time()
+        ref.decode_step(*(cpu[k][:1] for k in ("q", "k", "v", "g", "beta", "state")))
+        per_seq = max(time.time() - t, 1e-6)
+        n = max(1, min(N, int(max_seconds / per_seq)))
+        t = time.time()
+        ref.decode_step(*(cpu[k][:n] for k in ("q", "k", "v", "g", "beta", "state")))
+        dt = time.time() - t
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d sequences, all %d heads, one decode step; fp64 matrix-form update "
+                      "in numpy with one BLAS thread; %.1f s" % (n, N, H, dt)}
+
+
+def bench_decode(args, dev):
+    import torch
+    import kda_chunked_delta_amd as kda
+    from kda_inputs import decode_workload
+
+    d = decode_workload(args.workload, device=dev)
+    N, H = d["N"], d["H"]
+    state = d["state"].clone()
+    o = torch.empty_like(d["q"])
+
+    def step():
+        kda.decode(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=o)
+
+    print("bench: workload %s N=%d H=%d" % (args.workload, N, H), file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    ctx = kda.context(dev)
+    torch.cuda.synchronize()
+    ctx.set_timing(True)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    per_kernel = ctx.timing()
+    ctx.set_timing(False)
+    kern_ms = per_kernel["decode"][0] / per_kernel["decode"][1]
+    print("bench: %.4f ms/step; decode kernel %.4f ms" % (ms_step, kern_ms), file=sys.stderr, flush=True)
+    alg_bytes = N * H * DECODE_BYTES_PER_SEQ_HEAD
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    digest = source_digest(("kda_decode.hip", "kda_launch.h"))
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profiles("decode", digest, args.workload),
+                "kernel": "decode", "dominant": "decode", "kernel_ms": {"decode": round(kern_ms, 4)},
+                "alg_bytes_per_step": alg_bytes, "source_digest": digest}
+    line = {
+        "metric": DECODE_METRIC,
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %s" % (args.workload, DECODE_TEXT[args.workload]), "sequences": N,
+                   "heads": H, "head_dim": 128},
+        "roofline": roofline,
+    }
+    if args.cpu_seconds > 0:
+        print("bench: timing the CPU oracle (~%.0f s)" % min(args.cpu_seconds, 10.0), file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_decode(d, min(args.cpu_seconds, 10.0))
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -1,5 +1,5 @@
 /*
- * kda.h -- C ABI of the MI355X (gfx950) KDA forward-prefill library.
+ * kda.h -- C ABI of the MI355X (gfx950) KDA forward prefill and decode library.
  *
  * Operation. Kimi Delta Attention (KDA) forward prefill: for every packed
  * sequence and head, the gated delta rule with per-key-channel decay
@@ -24,7 +24,7 @@
  *      beta      : fp32 [Tt, H]
  *      states    : fp32 [N, H, 128 (key channel), 128 (value channel)]
  *      cu_seqlens: int32 [N + 1], 0 = cu[0] <= cu[1] <= ... <= cu[N] = Tt
- *    Device pointers must be 16-byte aligned (states: 4-byte aligned).
+ *    Device pointers must be 16-byte aligned (beta: 4-byte aligned).
  *  - Ownership: the caller owns every tensor, stream and plan. The context
  *    owns only its workspace arenas (one per stream), which it frees in
  *    kda_destroy.
@@ -173,6 +173,34 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
                        const int32_t *cu_seqlens_dev, float scale, const float *initial_state,
                        float *final_state, void *out, hipStream_t stream);
 
+/* Decode step: each of n_seqs sequences receives one new token, and its state
+ * is advanced by one step of the recurrence, in place:
+ *   S' = (I - beta k k^T) Diag(exp g) S + beta k v^T,   o = scale S'^T q.
+ * This is the single-token case of the recurrence in the commit summary of
+ * "feat(kda/sm90): FlashKDA prefill port + intracard-CP prefill" (cuLA pull
+ * request #103); "feat(cake_kda): share recurrent prefill kernels across
+ * SM100 family" (FlashInfer pull request #4313, AOT registration notes) keeps
+ * a KDA decode entry of this kind beside the prefill.
+ *   q, k, v, out : bf16 [n_seqs, H, 128] (device, 16-byte aligned)
+ *   g            : fp32 [n_seqs, H, 128] raw log-decay (device, 16-byte aligned)
+ *   beta         : fp32 [n_seqs, H] (device, 4-byte aligned)
+ *   state        : fp32 [n_seqs, H, 128, 128] (device, 16-byte aligned), read
+ *                  and overwritten with the advanced state; may not overlap
+ *                  any input or out
+ *   out          : may not overlap any input or state
+ * dk and dv must be 128. n_seqs = 0 is a no-op. One kernel launch on `stream`,
+ * no allocation, no synchronisation; results are bitwise reproducible. The
+ * step reads and writes each (sequence, head) state once. */
+kda_status kda_decode(kda_ctx *ctx, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void *q,
+                      const void *k, const void *v, const float *g, const float *beta, float scale,
+                      float *state, void *out, hipStream_t stream);
+
+/* The argument checks of kda_decode, without launching anything. Pointers are
+ * compared as addresses only and never dereferenced. Needs no GPU. */
+kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void *q,
+                               const void *k, const void *v, const float *g, const float *beta,
+                               float scale, const float *state, const void *out);
+
 /* K1 alone, for inspection and tests: write every chunk record of the plan
  * into `records` (device, total_chunks * H * KDA_RECORD_BYTES bytes, record
  * of (chunk c, head h) at index h * total_chunks + c; layout in
@@ -199,7 +227,7 @@ kda_status kda_debug_k1_records(kda_ctx *ctx, const kda_plan *plan, const void *
                                 const void *v, const float *g, const float *beta,
                                 const int32_t *cu_seqlens_dev, void *records, hipStream_t stream);
 
-/* Per-kernel timing of kda_prefill calls on this context: while enabled,
+/* Per-kernel timing of kda_prefill and kda_decode calls on this context: while enabled,
  * every call records HIP events around each of its launches on its stream.
  * kda_get_timing waits for all recorded events, and returns, per kernel name
  * (in order of first launch), the summed elapsed milliseconds and the number

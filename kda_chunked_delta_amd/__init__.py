@@ -1,13 +1,14 @@
-"""KDA forward prefill on MI355X (gfx950): Python binding of libkda.so.
+"""KDA forward prefill and decode on MI355X (gfx950): Python binding of libkda.so.
 
-Argument marshalling only: every step of the prefill runs in the library's HIP
-kernels, reached through the C ABI of include/kda.h. PyTorch provides device
-memory and the current HIP stream. There is no fallback: if the library is not
-built, every entry point raises.
+Argument marshalling only: every step runs in the library's HIP kernels,
+reached through the C ABI of include/kda.h. PyTorch provides device memory and
+the current HIP stream. There is no fallback: if the library is not built,
+every entry point raises.
 
     import kda_chunked_delta_amd as kda
     o, s = kda.prefill(q, k, v, g, beta, cu_seqlens=cu, initial_state=s0,
                        output_final_state=True, use_intracard_cp="auto")
+    o_t = kda.decode(q_t, k_t, v_t, g_t, beta_t, s)   # one token each, s in place
 
 The interface follows the FLA-compatible prefill of "feat(kda/sm90): FlashKDA
 prefill port + intracard-CP prefill" (cuLA pull request #103, description:
@@ -24,7 +25,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["prefill", "plan", "plan_host", "plan_segments", "Plan", "Context", "context",
+__all__ = ["prefill", "decode", "plan", "plan_host", "plan_segments", "Plan", "Context", "context",
            "KDAError", "lib", "LIB_PATH", "CP_OFF", "CP_ON", "CP_AUTO"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +90,8 @@ def lib():
                 "kda_prefill_validate": (ctypes.c_int, [P, P, P, P, P, P, P, F32, P, P, P]),
                 "kda_prefill": (ctypes.c_int, [P, P, P, P, P, P, P, P, F32, P, P, P, P]),
                 "kda_debug_k1_records": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
+                "kda_decode": (ctypes.c_int, [P, I32, I32, I32, I32, P, P, P, P, P, F32, P, P, P]),
+                "kda_decode_validate": (ctypes.c_int, [I32, I32, I32, I32, P, P, P, P, P, F32, P, P]),
                 "kda_set_timing": (ctypes.c_int, [P, ctypes.c_int]),
                 "kda_get_timing": (I32, [P, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(I32), I32]),
@@ -351,3 +354,38 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
                              _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state), _ptr(out),
                              ctypes.c_void_p(stream)), "kda_prefill")
     return out, final_state
+
+
+def decode(q, k, v, g, beta, state, scale=1.0, out=None):
+    """KDA decode step: one new token per sequence, state advanced in place.
+
+    q, k, v: bf16 [N, H, 128] (or [N, 1, H, 128]); g: fp32 log-decay, same
+    shape; beta: fp32 [N, H] (or [N, 1, H]); state: fp32 [N, H, 128, 128],
+    overwritten with the advanced state. Returns o, shaped like q.
+    """
+    import torch
+    shape = q.shape
+    if q.dim() == 4:
+        if q.shape[1] != 1:
+            raise ValueError("4-D decode inputs must have one token per sequence, got %s" % (tuple(q.shape),))
+        sq = lambda x: x.reshape(x.shape[0], *x.shape[2:])
+        q, k, v, g, beta = sq(q), sq(k), sq(v), sq(g), sq(beta)
+        if out is not None:
+            out = sq(out)
+    if q.dim() != 3 or q.shape[-1] != D:
+        raise ValueError("q must be [N, H, 128] or [N, 1, H, 128], got %s" % (tuple(shape),))
+    N, H = q.shape[0], q.shape[1]
+    for name, t, dt, shp in (("q", q, torch.bfloat16, (N, H, D)), ("k", k, torch.bfloat16, (N, H, D)),
+                             ("v", v, torch.bfloat16, (N, H, D)), ("g", g, torch.float32, (N, H, D)),
+                             ("beta", beta, torch.float32, (N, H)),
+                             ("state", state, torch.float32, (N, H, D, D))):
+        if t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous %s CUDA tensor of shape %s (got %s %s)"
+                             % (name, dt, shp, t.dtype, tuple(t.shape)))
+    if out is None:
+        out = torch.empty_like(q)
+    ctx = context(q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().kda_decode(ctx.handle, N, H, D, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            float(scale), _ptr(state), _ptr(out), ctypes.c_void_p(stream)), "kda_decode")
+    return out.view(shape)

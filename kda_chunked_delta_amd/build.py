@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kda_kernels.hip", "kda_runtime.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kda_kernels.hip", "kda_decode.hip", "kda_runtime.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <climits>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -333,6 +334,27 @@ struct kda_ctx {
 static const size_t kMaxArenas = 16;
 static const int kMaxTimedLaunches = 4096;
 
+// Run `launch` on `stream`; while the context's timing is on, bracket it with
+// a pair of HIP events from the context's pool (ctx->mu held by the caller).
+template <class F>
+static hipError_t timed_launch(kda_ctx* ctx, hipStream_t stream, const char* name, F&& launch) {
+    if (!ctx->timing) return launch();
+    if (ctx->n_timed >= kMaxTimedLaunches) return launch();  // log full: run untimed
+    if ((int)ctx->events.size() <= ctx->n_timed) {
+        TimedLaunch t{name, nullptr, nullptr};
+        hipError_t ee = hipEventCreate(&t.beg);
+        if (ee == hipSuccess) ee = hipEventCreate(&t.end);
+        if (ee != hipSuccess) return ee;
+        ctx->events.push_back(t);
+    }
+    TimedLaunch& t = ctx->events[ctx->n_timed++];
+    t.name = name;
+    hipError_t ee = hipEventRecord(t.beg, stream);
+    if (ee == hipSuccess) ee = launch();
+    if (ee == hipSuccess) ee = hipEventRecord(t.end, stream);
+    return ee;
+}
+
 extern "C" {
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
@@ -599,23 +621,7 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
     c.total_chunks = p->info.total_chunks;
     c.rec = ws + p->off_rec;
 
-    auto timed = [&](const char* name, auto&& launch) -> hipError_t {
-        if (!ctx->timing) return launch();
-        if (ctx->n_timed >= kMaxTimedLaunches) return launch();  // log full: run untimed
-        if ((int)ctx->events.size() <= ctx->n_timed) {
-            TimedLaunch t{name, nullptr, nullptr};
-            hipError_t ee = hipEventCreate(&t.beg);
-            if (ee == hipSuccess) ee = hipEventCreate(&t.end);
-            if (ee != hipSuccess) return ee;
-            ctx->events.push_back(t);
-        }
-        TimedLaunch& t = ctx->events[ctx->n_timed++];
-        t.name = name;
-        hipError_t ee = hipEventRecord(t.beg, stream);
-        if (ee == hipSuccess) ee = launch();
-        if (ee == hipSuccess) ee = hipEventRecord(t.end, stream);
-        return ee;
-    };
+    auto timed = [&](const char* name, auto&& launch) { return timed_launch(ctx, stream, name, launch); };
 
     const bool mat = p->info.k1_materialized != 0;
     if (mat) {
@@ -641,6 +647,56 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
                              : (p->info.uses_cp ? "fused_segment" : "fused_serial");
     e = timed(k2name, [&] { return mat ? launch_k2_recur(ka, stream) : launch_fused(ka, stream); });
     if (e != hipSuccess) return hip_fail(e, "k2 launch");
+    return KDA_OK;
+}
+
+kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void* q,
+                               const void* k, const void* v, const float* g, const float* beta, float scale,
+                               const float* state, const void* out) {
+    if (dk != 128 || dv != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode: dk = dv = 128 required (got dk=%d dv=%d)", dk, dv);
+    if (n_seqs < 0 || H < 1)
+        return fail(KDA_ERR_INVALID, "kda_decode: n_seqs must be >= 0 and H >= 1 (got n_seqs=%d H=%d)", n_seqs, H);
+    if ((int64_t)n_seqs * H * 2 > (int64_t)INT32_MAX)
+        return fail(KDA_ERR_INVALID, "kda_decode: n_seqs * H too large (%lld)", (long long)n_seqs * H);
+    if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID, "kda_decode: scale is not finite");
+    if (n_seqs == 0) return KDA_OK;
+    const size_t NH = (size_t)n_seqs * H;
+    const size_t n_act = NH * 128 * 2, n_g = NH * 128 * 4, n_beta = NH * 4, n_state = NH * kStateBytes;
+    const void* need[] = {q, k, v, g, beta, state, out};
+    const char* names[] = {"q", "k", "v", "g", "beta", "state", "out"};
+    for (int i = 0; i < 7; ++i) {
+        if (!need[i]) return fail(KDA_ERR_INVALID, "kda_decode: %s is NULL", names[i]);
+        const int al = i == 4 ? 4 : 16;
+        if ((uintptr_t)need[i] % al)
+            return fail(KDA_ERR_INVALID, "kda_decode: %s is not %d-byte aligned", names[i], al);
+    }
+    struct B { const void* p; size_t n; const char* name; };
+    const B ins[] = {{q, n_act, "q"}, {k, n_act, "k"}, {v, n_act, "v"}, {g, n_g, "g"}, {beta, n_beta, "beta"}};
+    for (const B& b : ins) {
+        if (overlap(out, n_act, b.p, b.n)) return fail(KDA_ERR_ALIAS, "kda_decode: out overlaps %s", b.name);
+        if (overlap(state, n_state, b.p, b.n)) return fail(KDA_ERR_ALIAS, "kda_decode: state overlaps %s", b.name);
+    }
+    if (overlap(out, n_act, state, n_state)) return fail(KDA_ERR_ALIAS, "kda_decode: out overlaps state");
+    return KDA_OK;
+}
+
+kda_status kda_decode(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void* q,
+                      const void* k, const void* v, const float* g, const float* beta, float scale,
+                      float* state, void* out, hipStream_t stream) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_decode: ctx is NULL");
+    kda_status st = kda_decode_validate(n_seqs, H, dk, dv, q, k, v, g, beta, scale, state, out);
+    if (st != KDA_OK || n_seqs == 0) return st;
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (prev != ctx->device && (e = hipSetDevice(ctx->device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    DecodeArgs a{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, beta, state, (uint16_t*)out,
+                 n_seqs, H, scale};
+    e = timed_launch(ctx, stream, "decode", [&] { return launch_decode(a, stream); });
+    if (prev >= 0 && prev != ctx->device) (void)hipSetDevice(prev);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
     return KDA_OK;
 }
 

@@ -14,6 +14,9 @@ s, draws in this order q, k, v, g, beta, initial state:
   beta  : sigmoid(randn) fp32
   S0    : state_std * randn fp32, shape [N, H, D, D], or None
 "N(0, s)" is read as s * randn (a standard deviation).
+Decode inputs (draw_decode) follow the same recipe for one token per
+sequence: q, k, v, g, beta shaped [N, H, D] / [N, H], then the state
+[N, H, D, D].
 Tensor values differ between a CPU and a GPU generator; the oracle always
 evaluates the exact tensors the library consumed, so parity does not depend
 on where the inputs were drawn.
@@ -83,6 +86,45 @@ def draw(lengths, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D):
     return dict(q=q, k=k, v=v, g=g, beta=beta,
                 cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=device),
                 cu_seqlens_host=cu, initial_state=s0, H=H, lengths=lengths)
+
+
+# name -> spec of a decode batch (one token per sequence)
+DECODE_WORKLOADS = {
+    # 256 sequences x 32 heads, state N(0, 0.1): a serving-size decode batch
+    "decode_n256_h32": dict(seed=1005, N=256, H=32, state_std=0.1, g_scale=1.0),
+}
+
+
+def draw_decode(N, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D):
+    """One decode batch: q, k, v (bf16) [N, H, D], g (fp32) [N, H, D],
+    beta (fp32) [N, H], state (fp32) [N, H, D, D] (zeros if state_std is None)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit_rows(x):
+        return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+    q = unit_rows(normal(N, H, D)).to(torch.bfloat16)
+    k = unit_rows(normal(N, H, D)).to(torch.bfloat16)
+    v = normal(N, H, D).to(torch.bfloat16)
+    g = -torch.nn.functional.softplus(g_scale * normal(N, H, D))
+    beta = torch.sigmoid(normal(N, H))
+    if state_std is None:
+        state = torch.zeros(N, H, D, D, device=device, dtype=torch.float32)
+    else:
+        state = state_std * normal(N, H, D, D)
+    return dict(q=q, k=k, v=v, g=g, beta=beta, state=state, N=N, H=H)
+
+
+def decode_workload(name, device="cpu"):
+    """Inputs of a named decode batch (see DECODE_WORKLOADS)."""
+    spec = dict(DECODE_WORKLOADS[name])
+    out = draw_decode(spec.pop("N"), spec.pop("H"), seed=spec.pop("seed"), device=device, **spec)
+    out["name"] = name
+    return out
 
 
 def workload(name, device="cpu"):

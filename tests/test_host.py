@@ -207,3 +207,46 @@ def test_host_plan_cannot_execute(setup):
     st = lib.kda_prefill(None, p.handle, P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
                          P(a["cu"]), ctypes.c_float(1.0), P(a["s0"]), P(a["sT"]), P(a["out"]), None)
     assert st == 1 and b"ctx" in lib.kda_last_error()
+
+
+# ---------------------------------------------------------------------------
+# decode validation (addresses only; never dereferenced)
+# ---------------------------------------------------------------------------
+def decode_validate(lib, N, H, over=None, dk=128, dv=128):
+    NH = N * H
+    size = dict(q=NH * 256, k=NH * 256, v=NH * 256, g=NH * 512, beta=NH * 4, state=NH * 65536, out=NH * 256)
+    base, addr = 1 << 40, {}
+    for name in ("q", "k", "v", "g", "beta", "state", "out"):
+        addr[name] = base
+        base += (size[name] + 4096) // 256 * 256
+    addr.update(over or {})
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.kda_decode_validate(N, H, dk, dv, P(addr["q"]), P(addr["k"]), P(addr["v"]), P(addr["g"]),
+                                   P(addr["beta"]), ctypes.c_float(addr.get("scale", 1.0)), P(addr["state"]),
+                                   P(addr["out"])), addr
+
+
+def test_decode_validate(kda_lib):
+    lib = kda_lib
+    st, a = decode_validate(lib, 64, 12)
+    assert st == 0
+    assert decode_validate(lib, 0, 12, dict(q=0, state=0))[0] == 0        # empty batch: nothing to check
+    assert decode_validate(lib, 4, 2, dk=64)[0] == 2
+    assert decode_validate(lib, -1, 2)[0] == 1
+    assert decode_validate(lib, 4, 0)[0] == 1
+    assert decode_validate(lib, 4, 2, dict(state=0))[0] == 1
+    assert decode_validate(lib, 4, 2, dict(scale=float("inf")))[0] == 1
+    assert decode_validate(lib, 4, 2, dict(g=a["g"] + 8))[0] == 1
+    assert b"aligned" in lib.kda_last_error()
+    _, a = decode_validate(lib, 4, 2)
+    assert decode_validate(lib, 4, 2, dict(out=a["q"]))[0] == 3
+    assert decode_validate(lib, 4, 2, dict(state=a["beta"]))[0] == 3
+    assert decode_validate(lib, 4, 2, dict(out=a["state"] + 1024))[0] == 3
+
+
+def test_decode_needs_context(kda_lib):
+    _, a = decode_validate(kda_lib, 4, 2)
+    P = lambda x: ctypes.c_void_p(x)
+    st = kda_lib.kda_decode(None, 4, 2, 128, 128, P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                            ctypes.c_float(1.0), P(a["state"]), P(a["out"]), None)
+    assert st == 1 and b"ctx" in kda_lib.kda_last_error()
