@@ -23,6 +23,13 @@
 // i = 0..7, held in registers between the two passes; one load instruction of
 // a wavefront covers four whole 256-byte row segments. Every sum runs in a
 // fixed order, so results are bitwise reproducible.
+//
+// When the batch's states are larger than half the 256 MiB last-level cache
+// (MALL), the state is read and written with the nontemporal hint: it cannot
+// stay cached until the next step anyway, and the hinted stream ran 10%
+// faster, at the rate of a hinted plain copy of the same bytes. Smaller
+// batches keep the default policy, under which back-to-back steps find their
+// states in the MALL.
 #include "kda_launch.h"
 
 namespace kda {
@@ -50,6 +57,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, 64); }
 
+template <bool NT>
+__device__ __forceinline__ f32x4 load_state(const f32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void store_state(f32x4* p, f32x4 x) {
+    if constexpr (NT) __builtin_nontemporal_store(x, p);
+    else *p = x;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(DEC_THREADS) void kda_decode_step(DecodeArgs a) {
     __shared__ float s_d[128], s_kd[128], s_qd[128], s_bk[128];
     __shared__ float s_qk[2];
@@ -67,7 +86,7 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode_step(DecodeArgs a) {
     f32x4* st = (f32x4*)(a.state + nh * (128 * 128) + col);
     f32x4 s[DEC_ROWS];
 #pragma unroll
-    for (int i = 0; i < DEC_ROWS; ++i) s[i] = st[(rs + DEC_ROWSETS * i) * (128 / 4)];
+    for (int i = 0; i < DEC_ROWS; ++i) s[i] = load_state<NT>(st + (rs + DEC_ROWSETS * i) * (128 / 4));
     const uint2 vb = *(const uint2*)(a.v + nh * 128 + col);
     const f32x4 vv = {bf16_bits_to_f32(vb.x & 0xffffu), bf16_bits_to_f32(vb.x >> 16),
                       bf16_bits_to_f32(vb.y & 0xffffu), bf16_bits_to_f32(vb.y >> 16)};
@@ -125,7 +144,7 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode_step(DecodeArgs a) {
         f32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = __builtin_fmaf(d, s[i][j], bk * e[j]);
-        st[r * (128 / 4)] = o;
+        store_state<NT>(st + r * (128 / 4), o);
     }
     if (rs == 0) {
         const float bqk = beta * (s_qk[0] + s_qk[1]);
@@ -141,7 +160,9 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode_step(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     const int64_t blocks = (int64_t)a.n_seqs * a.H * DEC_TILES;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_decode_step, dim3((unsigned)blocks), dim3(DEC_THREADS), 0, s, a);
+    const bool nt = (size_t)a.n_seqs * a.H * (128 * 128 * 4) > ((size_t)128 << 20);
+    if (nt) hipLaunchKernelGGL(kda_decode_step<true>, dim3((unsigned)blocks), dim3(DEC_THREADS), 0, s, a);
+    else hipLaunchKernelGGL(kda_decode_step<false>, dim3((unsigned)blocks), dim3(DEC_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
