@@ -285,7 +285,7 @@ def bench_decode(args, dev):
     print("bench: %.4f ms/step; decode kernel %.4f ms" % (ms_step, kern_ms), file=sys.stderr, flush=True)
     alg_bytes = N * H * DECODE_BYTES_PER_SEQ_HEAD
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    digest = source_digest(("kda_decode.hip", "kda_launch.h"))
+    digest = source_digest(("kda_decode.hip", "kda_decode_launch.h"))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles("decode", digest, args.workload),

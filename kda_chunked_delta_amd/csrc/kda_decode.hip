@@ -30,7 +30,7 @@
 // faster, at the rate of a hinted plain copy of the same bytes. Smaller
 // batches keep the default policy, under which back-to-back steps find their
 // states in the MALL.
-#include "kda_launch.h"
+#include "kda_decode_launch.h"
 
 namespace kda {
 namespace {

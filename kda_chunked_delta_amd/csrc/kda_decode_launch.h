@@ -1,0 +1,25 @@
+// Internal interface between the host runtime (kda_runtime.cpp) and the
+// decode kernel (kda_decode.hip). Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Decode step: one token per sequence, state [n_seqs][H][128][128] in place.
+struct DecodeArgs {
+    const uint16_t* q;     // [n_seqs][H][128] bf16
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;        // [n_seqs][H][128]
+    const float* beta;     // [n_seqs][H]
+    float* state;          // [n_seqs][H][128][128], read and written
+    uint16_t* out;         // [n_seqs][H][128] bf16
+    int32_t n_seqs;
+    int32_t H;
+    float scale;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace kda

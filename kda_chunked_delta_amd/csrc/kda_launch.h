@@ -1,6 +1,6 @@
 // Internal interface between the host runtime (kda_runtime.cpp) and the
-// kernels (kda_kernels.hip, kda_decode.hip): plan-table entry types, kernel
-// parameter blocks and launchers. Not part of the public C ABI.
+// kernels (kda_kernels.hip): plan-table entry types, kernel parameter blocks
+// and launchers. Not part of the public C ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -92,22 +92,7 @@ struct K1Args {
     const ChunkDesc* chunks;
 };
 
-// Decode step: one token per sequence, state [n_seqs][H][128][128] in place.
-struct DecodeArgs {
-    const uint16_t* q;     // [n_seqs][H][128] bf16
-    const uint16_t* k;
-    const uint16_t* v;
-    const float* g;        // [n_seqs][H][128]
-    const float* beta;     // [n_seqs][H]
-    float* state;          // [n_seqs][H][128][128], read and written
-    uint16_t* out;         // [n_seqs][H][128] bf16
-    int32_t n_seqs;
-    int32_t H;
-    float scale;
-};
-
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fused(const K2Args& a, hipStream_t s);
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
 hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);

@@ -23,6 +23,7 @@
 #include <vector>
 
 #include "kda_launch.h"
+#include "kda_decode_launch.h"
 
 using namespace kda;
 
