@@ -25,6 +25,7 @@ Functions
                values, masked q-k Gram, chunk decay) and the K2 results
   decode_step  one token per sequence, the state advanced by one step, in
                the matrix form (I - beta k k^T) Diag(exp g) S + beta k v^T
+  gva_expand   grouped value heads: the q/k heads each value head reads
 
 Every function takes fp64-convertible arrays (numpy, or torch tensors of any
 float dtype; bf16/fp32 values upcast exactly) in the packed token-major
@@ -317,3 +318,24 @@ def decode_step(q, k, v, g, beta, state, scale=1.0):
             S_new[n, h] = S1
             o[n, h] = scale * (S1.T @ q[n, h])
     return o, S_new
+
+
+# ---------------------------------------------------------------------------
+# Grouped value heads (GVA): fewer q/k heads than value heads
+# ---------------------------------------------------------------------------
+def gva_expand(q, k, H):
+    """q, k with Hk heads -> the [.., H, dk] q, k that the H value heads read.
+
+    [P1]'s reviewer notes restrict the prefill to num_kv_heads ==
+    num_qk_heads and name grouped value heads (GVA) as a follow-up. Read
+    here as the grouped layout: H = G * Hk value heads, value head h (its v,
+    g, beta, state and output) reads q/k head floor(h / G), so each q/k head
+    serves G consecutive value heads. Every other function then runs
+    unchanged on the expanded q, k.
+    """
+    q, k = to_f64(q), to_f64(k)
+    Hk = k.shape[-2]
+    if H % Hk:
+        raise ValueError("value heads %d not a multiple of q/k heads %d" % (H, Hk))
+    G = H // Hk
+    return np.repeat(q, G, axis=-2), np.repeat(k, G, axis=-2)

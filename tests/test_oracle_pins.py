@@ -460,3 +460,49 @@ def test_planted_decode_mistakes_are_caught(kind):
     o2, s2 = _decode_tokens(step, c)
     rec_ok = np.allclose(o1, o2, rtol=1e-9, atol=1e-10) and np.allclose(s1, s2, rtol=1e-9, atol=1e-10)
     assert not (golden_ok and rec_ok), "planted decode mistake %r went unnoticed" % kind
+
+
+# ---------------------------------------------------------------------------
+# grouped value heads: the head mapping
+# ---------------------------------------------------------------------------
+def _gva_case(Hk, G, seed):
+    """Value heads of one group share v, g, beta and S0, so only the q/k head
+    they read can tell them apart."""
+    c = rand_case([9, 4], H=Hk, dk=8, dv=8, seed=seed)
+    rep = lambda x, axis: np.repeat(x, G, axis=axis)
+    return dict(q=c["q"], k=c["k"], v=rep(c["v"], 1), g=rep(c["g"], 1), beta=rep(c["beta"], 1),
+                cu_seqlens=c["cu_seqlens"], initial_state=rep(c["initial_state"], 1))
+
+
+def _gva_run(c, expand):
+    H = c["v"].shape[1]
+    q, k = expand(c["q"], c["k"], H)
+    return ref.recurrent(q, k, c["v"], c["g"], c["beta"], c["cu_seqlens"], c["initial_state"])
+
+
+def _gva_pins_pass(expand):
+    c = _gva_case(3, 4, seed=12)
+    o, sT = _gva_run(c, expand)
+    # value heads 4j .. 4j+3 form one group: identical results inside it ...
+    same = all(np.allclose(o[:, 4 * j], o[:, 4 * j + i]) and np.allclose(sT[:, 4 * j], sT[:, 4 * j + i])
+               for j in range(3) for i in range(1, 4))
+    # ... and each equals the plain single-head run of its q/k head
+    plain_o, plain_s = ref.recurrent(c["q"], c["k"], c["v"][:, ::4], c["g"][:, ::4], c["beta"][:, ::4],
+                                     c["cu_seqlens"], c["initial_state"][:, ::4])
+    return same and np.allclose(o[:, ::4], plain_o, rtol=1e-12, atol=1e-13) and np.allclose(
+        sT[:, ::4], plain_s, rtol=1e-12, atol=1e-13)
+
+
+def test_gva_grouping_pins():
+    assert _gva_pins_pass(ref.gva_expand)
+    c = rand_case([5], H=4, dk=8, dv=8, seed=3)
+    q, k = ref.gva_expand(c["q"], c["k"], 4)  # one value head per q/k head: unchanged
+    assert np.array_equal(q, c["q"]) and np.array_equal(k, c["k"])
+    with pytest.raises(ValueError):
+        ref.gva_expand(c["q"], c["k"], 6)
+
+
+def test_planted_gva_mapping_is_caught():
+    # value head h reading q/k head h mod Hk (interleaved groups) instead of floor(h / G)
+    interleaved = lambda q, k, H: (np.tile(q, (1, H // q.shape[1], 1)), np.tile(k, (1, H // k.shape[1], 1)))
+    assert not _gva_pins_pass(interleaved)
