@@ -181,7 +181,11 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
  * request #103); "feat(cake_kda): share recurrent prefill kernels across
  * SM100 family" (FlashInfer pull request #4313, AOT registration notes) keeps
  * a KDA decode entry of this kind beside the prefill.
- *   q, k, v, out : bf16 [n_seqs, H, 128] (device, 16-byte aligned)
+ *   q, k         : bf16 [n_seqs, qk_heads, 128] (device, 16-byte aligned); H
+ *                  must be a multiple of qk_heads, and value head h reads q/k
+ *                  head h / (H / qk_heads) (grouped value heads, as in
+ *                  kda_prefill_gva; qk_heads = H is the plain case)
+ *   v, out       : bf16 [n_seqs, H, 128] (device, 16-byte aligned)
  *   g            : fp32 [n_seqs, H, 128] raw log-decay (device, 16-byte aligned)
  *   beta         : fp32 [n_seqs, H] (device, 4-byte aligned)
  *   state        : fp32 [n_seqs, H, 128, 128] (device, 16-byte aligned), read
@@ -191,15 +195,38 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
  * dk and dv must be 128. n_seqs = 0 is a no-op. One kernel launch on `stream`,
  * no allocation, no synchronisation; results are bitwise reproducible. The
  * step reads and writes each (sequence, head) state once. */
-kda_status kda_decode(kda_ctx *ctx, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void *q,
-                      const void *k, const void *v, const float *g, const float *beta, float scale,
-                      float *state, void *out, hipStream_t stream);
+kda_status kda_decode(kda_ctx *ctx, int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                      const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      float scale, float *state, void *out, hipStream_t stream);
 
 /* The argument checks of kda_decode, without launching anything. Pointers are
  * compared as addresses only and never dereferenced. Needs no GPU. */
-kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void *q,
-                               const void *k, const void *v, const float *g, const float *beta,
-                               float scale, const float *state, const void *out);
+kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                               const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float scale, const float *state, const void *out);
+
+/* kda_prefill with grouped value heads (GVA): q and k have qk_heads heads,
+ * while v, g, beta, the states and out have the plan's H heads, H a multiple
+ * of qk_heads. Value head h reads q/k head h / (H / qk_heads), so each q/k
+ * head serves that many consecutive value heads; with qk_heads = H this is
+ * kda_prefill. The reviewer notes of "feat(kda/sm90): FlashKDA prefill port +
+ * intracard-CP prefill" (cuLA pull request #103) restrict that prefill to
+ * num_kv_heads == num_qk_heads and name GVA as its follow-up.
+ *   q, k : bf16 [Tt, qk_heads, 128] (device); everything else as in kda_prefill.
+ * Errors as kda_prefill, plus KDA_ERR_INVALID when H is not a multiple of
+ * qk_heads. */
+kda_status kda_prefill_gva(kda_ctx *ctx, const kda_plan *plan, int32_t qk_heads, const void *q,
+                           const void *k, const void *v, const float *g, const float *beta,
+                           const int32_t *cu_seqlens_dev, float scale, const float *initial_state,
+                           float *final_state, void *out, hipStream_t stream);
+
+/* The argument checks of kda_prefill_gva, without launching anything
+ * (addresses only, never dereferenced; needs no GPU). */
+kda_status kda_prefill_gva_validate(const kda_plan *plan, int32_t qk_heads, const void *q, const void *k,
+                                    const void *v, const float *g, const float *beta,
+                                    const int32_t *cu_seqlens_dev, float scale,
+                                    const float *initial_state, const float *final_state,
+                                    const void *out);
 
 /* K1 alone, for inspection and tests: write every chunk record of the plan
  * into `records` (device, total_chunks * H * KDA_RECORD_BYTES bytes, record

@@ -90,8 +90,10 @@ def lib():
                 "kda_prefill_validate": (ctypes.c_int, [P, P, P, P, P, P, P, F32, P, P, P]),
                 "kda_prefill": (ctypes.c_int, [P, P, P, P, P, P, P, P, F32, P, P, P, P]),
                 "kda_debug_k1_records": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
-                "kda_decode": (ctypes.c_int, [P, I32, I32, I32, I32, P, P, P, P, P, F32, P, P, P]),
-                "kda_decode_validate": (ctypes.c_int, [I32, I32, I32, I32, P, P, P, P, P, F32, P, P]),
+                "kda_prefill_gva": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P, F32, P, P, P, P]),
+                "kda_prefill_gva_validate": (ctypes.c_int, [P, I32, P, P, P, P, P, P, F32, P, P, P]),
+                "kda_decode": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P, P]),
+                "kda_decode_validate": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P]),
                 "kda_set_timing": (ctypes.c_int, [P, ctypes.c_int]),
                 "kda_get_timing": (I32, [P, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(I32), I32]),
@@ -296,7 +298,9 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
 
     q, k, v: bf16 [Tt, H, 128] packed, or [B, T, H, 128] (B equal-length
     sequences when cu_seqlens is None); g: fp32 log-decay, same shape;
-    beta: fp32 [Tt, H] (or [B, T, H]). cu_seqlens: int32 [N + 1] (device
+    beta: fp32 [Tt, H] (or [B, T, H]). q and k may have fewer heads Hk than
+    v (grouped value heads, H a multiple of Hk: value head h reads q/k head
+    h // (H // Hk)). cu_seqlens: int32 [N + 1] (device
     tensor, host list, or None). initial_state: fp32 [N, H, 128, 128] or None.
     final_state: a tensor to write the final state into (may be
     initial_state: in-place update); with output_final_state=True and no
@@ -313,11 +317,13 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
         o, s = prefill(flat(q), flat(k), flat(v), flat(g), flat(beta), cu_seqlens, initial_state,
                        output_final_state, use_intracard_cp, scale, final_state,
                        None if out is None else flat(out), plan, cu_seqlens_host)
-        return o.view(q.shape), s
-    if q.dim() != 3 or q.shape[-1] != D:
+        return o.view(v.shape), s
+    if q.dim() != 3 or q.shape[-1] != D or v.dim() != 3:
         raise ValueError("q must be [Tt, H, 128] or [B, T, H, 128], got %s" % (tuple(q.shape),))
-    Tt, H = q.shape[0], q.shape[1]
-    for name, t, dt, shape in (("q", q, torch.bfloat16, (Tt, H, D)), ("k", k, torch.bfloat16, (Tt, H, D)),
+    Tt, Hk, H = q.shape[0], q.shape[1], v.shape[1]
+    if H % Hk:
+        raise ValueError("v has %d heads, not a multiple of the %d q/k heads" % (H, Hk))
+    for name, t, dt, shape in (("q", q, torch.bfloat16, (Tt, Hk, D)), ("k", k, torch.bfloat16, (Tt, Hk, D)),
                                ("v", v, torch.bfloat16, (Tt, H, D)), ("g", g, torch.float32, (Tt, H, D)),
                                ("beta", beta, torch.float32, (Tt, H))):
         if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
@@ -345,14 +351,14 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
                               or not t.is_contiguous() or not t.is_cuda):
             raise ValueError("%s must be a contiguous fp32 CUDA tensor of shape %s" % (name, (N, H, D, D)))
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(v)
     if final_state is None and output_final_state:
         final_state = torch.empty(N, H, D, D, dtype=torch.float32, device=q.device)
     ctx = context(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(lib().kda_prefill(ctx.handle, plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                             _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state), _ptr(out),
-                             ctypes.c_void_p(stream)), "kda_prefill")
+    _check(lib().kda_prefill_gva(ctx.handle, plan.handle, Hk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                 ctypes.c_void_p(stream)), "kda_prefill")
     return out, final_state
 
 
@@ -360,11 +366,12 @@ def decode(q, k, v, g, beta, state, scale=1.0, out=None):
     """KDA decode step: one new token per sequence, state advanced in place.
 
     q, k, v: bf16 [N, H, 128] (or [N, 1, H, 128]); g: fp32 log-decay, same
-    shape; beta: fp32 [N, H] (or [N, 1, H]); state: fp32 [N, H, 128, 128],
-    overwritten with the advanced state. Returns o, shaped like q.
+    shape as v; beta: fp32 [N, H] (or [N, 1, H]); state: fp32 [N, H, 128, 128],
+    overwritten with the advanced state. q and k may have fewer heads than v
+    (grouped value heads, as in prefill). Returns o, shaped like v.
     """
     import torch
-    shape = q.shape
+    shape = v.shape
     if q.dim() == 4:
         if q.shape[1] != 1:
             raise ValueError("4-D decode inputs must have one token per sequence, got %s" % (tuple(q.shape),))
@@ -374,8 +381,10 @@ def decode(q, k, v, g, beta, state, scale=1.0, out=None):
             out = sq(out)
     if q.dim() != 3 or q.shape[-1] != D:
         raise ValueError("q must be [N, H, 128] or [N, 1, H, 128], got %s" % (tuple(shape),))
-    N, H = q.shape[0], q.shape[1]
-    for name, t, dt, shp in (("q", q, torch.bfloat16, (N, H, D)), ("k", k, torch.bfloat16, (N, H, D)),
+    N, Hk, H = q.shape[0], q.shape[1], v.shape[1]
+    if H % Hk:
+        raise ValueError("v has %d heads, not a multiple of the %d q/k heads" % (H, Hk))
+    for name, t, dt, shp in (("q", q, torch.bfloat16, (N, Hk, D)), ("k", k, torch.bfloat16, (N, Hk, D)),
                              ("v", v, torch.bfloat16, (N, H, D)), ("g", g, torch.float32, (N, H, D)),
                              ("beta", beta, torch.float32, (N, H)),
                              ("state", state, torch.float32, (N, H, D, D))):
@@ -383,9 +392,9 @@ def decode(q, k, v, g, beta, state, scale=1.0, out=None):
             raise ValueError("%s must be a contiguous %s CUDA tensor of shape %s (got %s %s)"
                              % (name, dt, shp, t.dtype, tuple(t.shape)))
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(v)
     ctx = context(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(lib().kda_decode(ctx.handle, N, H, D, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    _check(lib().kda_decode(ctx.handle, N, H, Hk, D, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             float(scale), _ptr(state), _ptr(out), ctypes.c_void_p(stream)), "kda_decode")
     return out.view(shape)

@@ -17,6 +17,8 @@
 // and written once. The step is bound by HBM bandwidth: 2 x 64 KiB of state
 // per (sequence, head) against 1.3 KiB of token data.
 //
+// With grouped value heads, value head h reads q/k head h / group.
+//
 // Launch: one workgroup of 256 threads per (sequence, head, 64-column tile),
 // the two tiles of one (sequence, head) adjacent in the grid. Thread t owns
 // the four columns 4 (t & 15) .. +3 of its tile and the rows (t >> 4) + 16 i,
@@ -77,6 +79,8 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode_step(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile = blockIdx.x % DEC_TILES;
     const int64_t nh = blockIdx.x / DEC_TILES;  // n * H + h
+    // q/k row of the value head's group: n * Hk + h / group
+    const int64_t nq = (nh / a.H) * a.Hk + (int)(nh % a.H) / a.group;
     const int cg = tid % DEC_CG, rs = tid / DEC_CG;
     const int col = tile * DEC_COLS + 4 * cg;
     const float beta = a.beta[nh];
@@ -92,8 +96,8 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode_step(DecodeArgs a) {
                       bf16_bits_to_f32(vb.y & 0xffffu), bf16_bits_to_f32(vb.y >> 16)};
 
     if (tid < 128) {
-        const float kr = bf16_bits_to_f32(a.k[nh * 128 + tid]);
-        const float qr = bf16_bits_to_f32(a.q[nh * 128 + tid]);
+        const float kr = bf16_bits_to_f32(a.k[nq * 128 + tid]);
+        const float qr = bf16_bits_to_f32(a.q[nq * 128 + tid]);
         const float d = __builtin_amdgcn_exp2f(a.g[nh * 128 + tid] * DEC_LOG2E);
         s_d[tid] = d;
         s_kd[tid] = kr * d;

@@ -8,15 +8,17 @@ namespace kda {
 
 // Decode step: one token per sequence, state [n_seqs][H][128][128] in place.
 struct DecodeArgs {
-    const uint16_t* q;     // [n_seqs][H][128] bf16
+    const uint16_t* q;     // [n_seqs][Hk][128] bf16
     const uint16_t* k;
     const uint16_t* v;
     const float* g;        // [n_seqs][H][128]
     const float* beta;     // [n_seqs][H]
     float* state;          // [n_seqs][H][128][128], read and written
-    uint16_t* out;         // [n_seqs][H][128] bf16
+    uint16_t* out;         // [n_seqs][H][128] bf16 (v too)
     int32_t n_seqs;
-    int32_t H;
+    int32_t H;             // value heads
+    int32_t Hk;            // q/k heads; value head h reads q/k head h / group
+    int32_t group;
     float scale;
 };
 

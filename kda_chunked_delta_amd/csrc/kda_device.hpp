@@ -205,14 +205,16 @@ struct RowChunk {
 
 // Per-lane constants of the row path of wavefront w.
 struct RowLaneOffsets {
-    uint32_t act, g, beta;  // global byte offsets from the chunk's first row
+    uint32_t qk, act, g, beta;  // global byte offsets from the chunk's first row (qk: of q and k)
     int st_act, st_g;       // staging offsets of the row writes
     int rd_act, rd_g;       // staging offsets of phase 1's reads
 };
 
-__device__ __forceinline__ RowLaneOffsets row_lane_offsets(int H, int wave, int lane) {
+// H value heads (v, g, beta rows), Hk q/k heads (q, k rows)
+__device__ __forceinline__ RowLaneOffsets row_lane_offsets(int H, int Hk, int wave, int lane) {
     const int r = 2 * wave + (lane >> 5), gg = lane >> 4, m = lane & 15;
     RowLaneOffsets o;
+    o.qk = (uint32_t)r * (uint32_t)Hk * (D * 2) + (lane & 31) * 8;
     o.act = (uint32_t)r * (uint32_t)H * (D * 2) + (lane & 31) * 8;
     o.g = (uint32_t)r * (uint32_t)H * (D * 4) + (lane & 31) * 16;
     o.beta = (uint32_t)m * (uint32_t)H * 4;
@@ -223,22 +225,33 @@ __device__ __forceinline__ RowLaneOffsets row_lane_offsets(int H, int wave, int 
     return o;
 }
 
-// Loads of the chunk whose first token-head row is crow (uniform), nrows
-// valid rows (rows past them, and every row when nrows <= 0, read as
-// zeros). Only wavefront 0 reads beta: the others' beta range is empty.
+// Loads of the chunk whose first value-head row is crow and first q/k-head
+// row is crow_qk (both uniform), nrows valid rows (rows past them, and every
+// row when nrows <= 0, read as zeros). Only wavefront 0 reads beta: the
+// others' beta range is empty. GVA = false: q/k heads are the value heads
+// (Hk = H, crow_qk = crow), and q/k share v's offsets and ranges.
+template <bool GVA>
 __device__ __forceinline__ void k1_load_rows(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                              const uint16_t* __restrict__ v, const float* __restrict__ g,
-                                             const float* __restrict__ beta, int H, int64_t crow, int nrows,
-                                             int wave, const RowLaneOffsets& lo, RowChunk& rc) {
+                                             const float* __restrict__ beta, int H, int Hk, int64_t crow,
+                                             int64_t crow_qk, int nrows, int wave, const RowLaneOffsets& lo,
+                                             RowChunk& rc) {
     const size_t act = (size_t)crow * (D * 2), gb = (size_t)crow * (D * 4), bb = (size_t)crow * 4;
     const uint32_t last = nrows > 0 ? (uint32_t)(nrows - 1) * (uint32_t)H : 0u;
     const uint32_t live = nrows > 0 ? 1u : 0u;
     const uint32_t n_act = (last * (D * 2) + D * 2) * live, n_g = (last * (D * 4) + D * 4) * live,
                    n_b = (last * 4 + 4) * live * (wave == 0 ? 1u : 0u);
+    size_t aqk = act;
+    uint32_t n_qk = n_act, o_qk = lo.act;
+    if constexpr (GVA) {
+        aqk = (size_t)crow_qk * (D * 2);
+        n_qk = ((nrows > 0 ? (uint32_t)(nrows - 1) * (uint32_t)Hk : 0u) * (D * 2) + D * 2) * live;
+        o_qk = lo.qk;
+    }
     rc.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)q + act, n_act), (int)lo.act, 0, BUF_POLICY));
+        chunk_rsrc((const uint8_t*)q + aqk, n_qk), (int)o_qk, 0, BUF_POLICY));
     rc.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)k + act, n_act), (int)lo.act, 0, BUF_POLICY));
+        chunk_rsrc((const uint8_t*)k + aqk, n_qk), (int)o_qk, 0, BUF_POLICY));
     rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
         chunk_rsrc((const uint8_t*)v + act, n_act), (int)lo.act, 0, BUF_POLICY));
     rc.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(

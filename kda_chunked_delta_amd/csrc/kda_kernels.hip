@@ -161,6 +161,7 @@ __device__ __forceinline__ const float* unit_state_in(const K2Args& a, const Uni
 constexpr int K1P_LDS = REC_BYTES + K1_BYTES + N_WAVE_T * K1_LBYTES;
 static_assert(STG_BYTES <= K1P_LDS, "staging overlays the record area");
 
+template <bool GVA>
 __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     __shared__ __align__(16) uint8_t lds[K1P_LDS];
     uint8_t* rec = lds;
@@ -176,9 +177,10 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     int64_t beg, end;
     seq_bounds(a.c, cd.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
-    const RowLaneOffsets lo = row_lane_offsets(H, wave, lane);
+    const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, wave, lane);
     RowChunk rc;
-    k1_load_rows(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, tok0 * H + h, rows_of(tok0, end), wave, lo, rc);
+    k1_load_rows<GVA>(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0 * H + h,
+                      tok0 * a.c.Hk + h / a.c.group, rows_of(tok0, end), wave, lo, rc);
     k1_stage(rc, wave, lane, lo, stg);
     lds_barrier();
     RawChunk raw;
@@ -216,6 +218,9 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 constexpr bool P2_ON_STATE = true;
 constexpr int FUSED_LDS = 3 * REC_BYTES + 2 * K1_BYTES + N_WAVE_T * K1_LBYTES + 2 * STG_BYTES;
 
+// GVA: q/k heads differ from the value heads (value head h reads q/k head
+// h / group); the plain instance keeps the q/k loads on v's offsets.
+template <bool GVA>
 __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* recs = smem;
@@ -274,10 +279,12 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     } else {
         // K1 wavefronts: chunk c is loaded into register set c & 1
         RowChunk r0, r1;
-        const RowLaneOffsets lo = row_lane_offsets(H, w8, lane);
+        const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, w8, lane);
+        const int hq = h / a.c.group;
         auto load = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
             const int64_t t = tok0 + (int64_t)CH * ci;
-            k1_load_rows(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, t * H + h, rows_of(t, end), w8, lo, rc);
+            k1_load_rows<GVA>(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, t * H + h, t * a.c.Hk + hq,
+                              rows_of(t, end), w8, lo, rc);
         };
         auto stage = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
             // the register set is read only from here on (see below)
@@ -463,17 +470,22 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
 hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     const long long n = (long long)a.n_units * a.c.H;
     if (n <= 0) return hipSuccess;
-    static hipError_t attr = hipFuncSetAttribute((const void*)kda_fused,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kda_fused, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
+    static hipError_t attr0 = hipFuncSetAttribute((const void*)kda_fused<false>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
+    static hipError_t attr1 = hipFuncSetAttribute((const void*)kda_fused<true>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
+    if (attr0 != hipSuccess) return attr0;
+    if (attr1 != hipSuccess) return attr1;
+    if (a.c.group > 1) hipLaunchKernelGGL(kda_fused<true>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
+    else hipLaunchKernelGGL(kda_fused<false>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s) {
     const long long n = (long long)a.c.total_chunks * a.c.H;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_k1_prepare, dim3((unsigned)n), dim3(512), 0, s, a);
+    if (a.c.group > 1) hipLaunchKernelGGL(kda_k1_prepare<true>, dim3((unsigned)n), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL(kda_k1_prepare<false>, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -52,7 +52,9 @@ struct CommonArgs {
     const float* beta;
     const int32_t* cu;  // device cu_seqlens [n_seqs + 1]
     int64_t Tt;
-    int32_t H;
+    int32_t H;       // value heads (v, g, beta, states, out)
+    int32_t Hk;      // q/k heads; H = group * Hk
+    int32_t group;   // value heads per q/k head (value head h reads q/k head h / group)
     int32_t n_seqs;
     int32_t total_chunks;
     uint8_t* rec;  // K1 records [H][total_chunks][REC_BYTES]

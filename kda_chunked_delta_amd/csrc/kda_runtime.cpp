@@ -462,13 +462,17 @@ kda_status kda_plan_get_units(const kda_plan* p, kda_unit_info* units, int32_t m
     return KDA_OK;
 }
 
-kda_status kda_prefill_validate(const kda_plan* p, const void* q, const void* k, const void* v,
-                                const float* g, const float* beta, const int32_t* cu_dev, float scale,
-                                const float* s0, const float* sT, const void* out) {
+kda_status kda_prefill_gva_validate(const kda_plan* p, int32_t qk_heads, const void* q, const void* k,
+                                    const void* v, const float* g, const float* beta, const int32_t* cu_dev,
+                                    float scale, const float* s0, const float* sT, const void* out) {
     if (!p) return fail(KDA_ERR_INVALID, "kda_prefill: plan is NULL");
     const kda_plan_info& in = p->info;
+    if (qk_heads < 1 || in.H % qk_heads != 0)
+        return fail(KDA_ERR_INVALID, "kda_prefill: the plan's %d value heads are not a multiple of %d q/k heads",
+                    in.H, qk_heads);
     const size_t Tt = (size_t)in.total_tokens, H = (size_t)in.H, N = (size_t)in.n_seqs;
     const size_t n_act = Tt * H * 128 * 2, n_g = Tt * H * 128 * 4, n_beta = Tt * H * 4;
+    const size_t n_qk = Tt * (size_t)qk_heads * 128 * 2;
     const size_t n_state = N * H * kStateBytes, n_cu = (N + 1) * 4;
     if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID, "kda_prefill: scale is not finite");
     if (!cu_dev) return fail(KDA_ERR_INVALID, "kda_prefill: cu_seqlens is NULL");
@@ -486,7 +490,7 @@ kda_status kda_prefill_validate(const kda_plan* p, const void* q, const void* k,
     if (sT && (uintptr_t)sT % 16) return fail(KDA_ERR_INVALID, "kda_prefill: final_state is not 16-byte aligned");
     // out may not overlap anything
     struct B { const void* p; size_t n; const char* name; };
-    const B ins[] = {{q, n_act, "q"}, {k, n_act, "k"}, {v, n_act, "v"}, {g, n_g, "g"},
+    const B ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_act, "v"}, {g, n_g, "g"},
                      {beta, n_beta, "beta"}, {cu_dev, n_cu, "cu_seqlens"}};
     for (const B& b : ins) {
         if (overlap(out, n_act, b.p, b.n))
@@ -500,6 +504,13 @@ kda_status kda_prefill_validate(const kda_plan* p, const void* q, const void* k,
         return fail(KDA_ERR_ALIAS, "kda_prefill: final_state partially overlaps initial_state "
                                    "(must be the same buffer or disjoint)");
     return KDA_OK;
+}
+
+kda_status kda_prefill_validate(const kda_plan* p, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const int32_t* cu_dev, float scale,
+                                const float* s0, const float* sT, const void* out) {
+    if (!p) return fail(KDA_ERR_INVALID, "kda_prefill: plan is NULL");
+    return kda_prefill_gva_validate(p, p->info.H, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
 }
 
 kda_status kda_set_timing(kda_ctx* ctx, int enable) {
@@ -552,8 +563,15 @@ int32_t kda_get_timing(kda_ctx* ctx, const char** names, double* total_ms, int32
 kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const int32_t* cu_dev, float scale,
                        const float* s0, float* sT, void* out, hipStream_t stream) {
+    if (!p) return fail(KDA_ERR_INVALID, "kda_prefill: plan is NULL");
+    return kda_prefill_gva(ctx, p, p->info.H, q, k, v, g, beta, cu_dev, scale, s0, sT, out, stream);
+}
+
+kda_status kda_prefill_gva(kda_ctx* ctx, const kda_plan* p, int32_t qk_heads, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta, const int32_t* cu_dev,
+                           float scale, const float* s0, float* sT, void* out, hipStream_t stream) {
     if (!ctx) return fail(KDA_ERR_INVALID, "kda_prefill: ctx is NULL");
-    kda_status st = kda_prefill_validate(p, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
+    kda_status st = kda_prefill_gva_validate(p, qk_heads, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
     if (st != KDA_OK) return st;
     if (!p->dev_tables)
         return fail(KDA_ERR_INVALID, "kda_prefill: plan has no device tables (built by kda_plan_prefill_host?)");
@@ -618,6 +636,8 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
     c.cu = cu_dev;
     c.Tt = p->info.total_tokens;
     c.H = p->info.H;
+    c.Hk = qk_heads;
+    c.group = p->info.H / qk_heads;
     c.n_seqs = p->info.n_seqs;
     c.total_chunks = p->info.total_chunks;
     c.rec = ws + p->off_rec;
@@ -651,19 +671,22 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
     return KDA_OK;
 }
 
-kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void* q,
-                               const void* k, const void* v, const float* g, const float* beta, float scale,
-                               const float* state, const void* out) {
+kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                               const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               float scale, const float* state, const void* out) {
     if (dk != 128 || dv != 128)
         return fail(KDA_ERR_UNSUPPORTED, "kda_decode: dk = dv = 128 required (got dk=%d dv=%d)", dk, dv);
     if (n_seqs < 0 || H < 1)
         return fail(KDA_ERR_INVALID, "kda_decode: n_seqs must be >= 0 and H >= 1 (got n_seqs=%d H=%d)", n_seqs, H);
+    if (qk_heads < 1 || H % qk_heads != 0)
+        return fail(KDA_ERR_INVALID, "kda_decode: %d value heads are not a multiple of %d q/k heads", H, qk_heads);
     if ((int64_t)n_seqs * H * 2 > (int64_t)INT32_MAX)
         return fail(KDA_ERR_INVALID, "kda_decode: n_seqs * H too large (%lld)", (long long)n_seqs * H);
     if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID, "kda_decode: scale is not finite");
     if (n_seqs == 0) return KDA_OK;
     const size_t NH = (size_t)n_seqs * H;
     const size_t n_act = NH * 128 * 2, n_g = NH * 128 * 4, n_beta = NH * 4, n_state = NH * kStateBytes;
+    const size_t n_qk = (size_t)n_seqs * qk_heads * 128 * 2;
     const void* need[] = {q, k, v, g, beta, state, out};
     const char* names[] = {"q", "k", "v", "g", "beta", "state", "out"};
     for (int i = 0; i < 7; ++i) {
@@ -673,7 +696,7 @@ kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv
             return fail(KDA_ERR_INVALID, "kda_decode: %s is not %d-byte aligned", names[i], al);
     }
     struct B { const void* p; size_t n; const char* name; };
-    const B ins[] = {{q, n_act, "q"}, {k, n_act, "k"}, {v, n_act, "v"}, {g, n_g, "g"}, {beta, n_beta, "beta"}};
+    const B ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_act, "v"}, {g, n_g, "g"}, {beta, n_beta, "beta"}};
     for (const B& b : ins) {
         if (overlap(out, n_act, b.p, b.n)) return fail(KDA_ERR_ALIAS, "kda_decode: out overlaps %s", b.name);
         if (overlap(state, n_state, b.p, b.n)) return fail(KDA_ERR_ALIAS, "kda_decode: state overlaps %s", b.name);
@@ -682,11 +705,11 @@ kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv
     return KDA_OK;
 }
 
-kda_status kda_decode(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, const void* q,
-                      const void* k, const void* v, const float* g, const float* beta, float scale,
+kda_status kda_decode(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                      const void* q, const void* k, const void* v, const float* g, const float* beta, float scale,
                       float* state, void* out, hipStream_t stream) {
     if (!ctx) return fail(KDA_ERR_INVALID, "kda_decode: ctx is NULL");
-    kda_status st = kda_decode_validate(n_seqs, H, dk, dv, q, k, v, g, beta, scale, state, out);
+    kda_status st = kda_decode_validate(n_seqs, H, qk_heads, dk, dv, q, k, v, g, beta, scale, state, out);
     if (st != KDA_OK || n_seqs == 0) return st;
     std::lock_guard<std::mutex> lk(ctx->mu);
     int prev = -1;
@@ -694,7 +717,7 @@ kda_status kda_decode(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t dk, int32
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (prev != ctx->device && (e = hipSetDevice(ctx->device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
     DecodeArgs a{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, beta, state, (uint16_t*)out,
-                 n_seqs, H, scale};
+                 n_seqs, H, qk_heads, H / qk_heads, scale};
     e = timed_launch(ctx, stream, "decode", [&] { return launch_decode(a, stream); });
     if (prev >= 0 && prev != ctx->device) (void)hipSetDevice(prev);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -721,6 +744,8 @@ kda_status kda_debug_k1_records(kda_ctx* ctx, const kda_plan* p, const void* q, 
     c.cu = cu_dev;
     c.Tt = p->info.total_tokens;
     c.H = p->info.H;
+    c.Hk = p->info.H;
+    c.group = 1;
     c.n_seqs = p->info.n_seqs;
     c.total_chunks = p->info.total_chunks;
     c.rec = (uint8_t*)records;

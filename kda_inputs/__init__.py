@@ -48,13 +48,14 @@ WORKLOADS = {
 }
 
 
-def draw(lengths, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D):
+def draw(lengths, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D, qk_heads=None):
     """Draw one packed-varlen input set.
 
     lengths: list of sequence lengths, or ("uniform", n, lo, hi) for n lengths
     drawn uniformly from [lo, hi] inclusive by a CPU generator seeded with seed.
     Returns a dict with q, k, v (bf16), g, beta (fp32), cu_seqlens (int32, on
     the device), cu_seqlens_host (python list), initial_state (fp32 or None).
+    qk_heads: q and k get that many heads instead of H (grouped value heads).
     """
     if isinstance(lengths, tuple) and lengths[0] == "uniform":
         _, n, lo, hi = lengths
@@ -75,8 +76,9 @@ def draw(lengths, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D):
     def unit_rows(x):
         return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
 
-    q = unit_rows(normal(Tt, H, D)).to(torch.bfloat16)
-    k = unit_rows(normal(Tt, H, D)).to(torch.bfloat16)
+    Hk = H if qk_heads is None else qk_heads
+    q = unit_rows(normal(Tt, Hk, D)).to(torch.bfloat16)
+    k = unit_rows(normal(Tt, Hk, D)).to(torch.bfloat16)
     v = normal(Tt, H, D).to(torch.bfloat16)
     g = -torch.nn.functional.softplus(g_scale * normal(Tt, H, D))
     beta = torch.sigmoid(normal(Tt, H))
@@ -95,7 +97,7 @@ DECODE_WORKLOADS = {
 }
 
 
-def draw_decode(N, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D):
+def draw_decode(N, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D, qk_heads=None):
     """One decode batch: q, k, v (bf16) [N, H, D], g (fp32) [N, H, D],
     beta (fp32) [N, H], state (fp32) [N, H, D, D] (zeros if state_std is None)."""
     gen = torch.Generator(device=device)
@@ -107,8 +109,9 @@ def draw_decode(N, H, *, seed, state_std=0.1, g_scale=1.0, device="cpu", D=D):
     def unit_rows(x):
         return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
 
-    q = unit_rows(normal(N, H, D)).to(torch.bfloat16)
-    k = unit_rows(normal(N, H, D)).to(torch.bfloat16)
+    Hk = H if qk_heads is None else qk_heads
+    q = unit_rows(normal(N, Hk, D)).to(torch.bfloat16)
+    k = unit_rows(normal(N, Hk, D)).to(torch.bfloat16)
     v = normal(N, H, D).to(torch.bfloat16)
     g = -torch.nn.functional.softplus(g_scale * normal(N, H, D))
     beta = torch.sigmoid(normal(N, H))

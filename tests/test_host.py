@@ -212,16 +212,16 @@ def test_host_plan_cannot_execute(setup):
 # ---------------------------------------------------------------------------
 # decode validation (addresses only; never dereferenced)
 # ---------------------------------------------------------------------------
-def decode_validate(lib, N, H, over=None, dk=128, dv=128):
-    NH = N * H
-    size = dict(q=NH * 256, k=NH * 256, v=NH * 256, g=NH * 512, beta=NH * 4, state=NH * 65536, out=NH * 256)
+def decode_validate(lib, N, H, over=None, dk=128, dv=128, Hk=None):
+    NH, Hk = N * H, H if Hk is None else Hk
+    size = dict(q=N * Hk * 256, k=N * Hk * 256, v=NH * 256, g=NH * 512, beta=NH * 4, state=NH * 65536, out=NH * 256)
     base, addr = 1 << 40, {}
     for name in ("q", "k", "v", "g", "beta", "state", "out"):
         addr[name] = base
         base += (size[name] + 4096) // 256 * 256
     addr.update(over or {})
     P = lambda x: ctypes.c_void_p(x) if x else None
-    return lib.kda_decode_validate(N, H, dk, dv, P(addr["q"]), P(addr["k"]), P(addr["v"]), P(addr["g"]),
+    return lib.kda_decode_validate(N, H, Hk, dk, dv, P(addr["q"]), P(addr["k"]), P(addr["v"]), P(addr["g"]),
                                    P(addr["beta"]), ctypes.c_float(addr.get("scale", 1.0)), P(addr["state"]),
                                    P(addr["out"])), addr
 
@@ -242,11 +242,32 @@ def test_decode_validate(kda_lib):
     assert decode_validate(lib, 4, 2, dict(out=a["q"]))[0] == 3
     assert decode_validate(lib, 4, 2, dict(state=a["beta"]))[0] == 3
     assert decode_validate(lib, 4, 2, dict(out=a["state"] + 1024))[0] == 3
+    # grouped value heads: 12 value heads over 4 q/k heads; 5 does not divide 12
+    assert decode_validate(lib, 4, 12, Hk=4)[0] == 0
+    assert decode_validate(lib, 4, 12, Hk=5)[0] == 1
+    assert decode_validate(lib, 4, 12, Hk=0)[0] == 1
 
 
 def test_decode_needs_context(kda_lib):
     _, a = decode_validate(kda_lib, 4, 2)
     P = lambda x: ctypes.c_void_p(x)
-    st = kda_lib.kda_decode(None, 4, 2, 128, 128, P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+    st = kda_lib.kda_decode(None, 4, 2, 2, 128, 128, P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
                             ctypes.c_float(1.0), P(a["state"]), P(a["out"]), None)
     assert st == 1 and b"ctx" in kda_lib.kda_last_error()
+
+
+def test_gva_validate(kda_lib):
+    """kda_prefill_gva_validate sizes q/k by the q/k head count."""
+    lib = kda_lib
+    p = kda.plan_host([0, 40, 100], H=6, n_cus=256)
+    fb = FakeBuffers(100, 6, 2)
+    a = dict(fb.addr)
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    call = lambda Hk, **o: lib.kda_prefill_gva_validate(
+        p.handle, Hk, *(P(dict(a, **o)[n]) for n in ("q", "k", "v", "g", "beta", "cu")), ctypes.c_float(1.0),
+        P(a["s0"]), P(a["sT"]), P(a["out"]))
+    assert call(6) == 0 and call(3) == 0 and call(2) == 0 and call(1) == 0
+    assert call(4) == 1 and b"multiple" in lib.kda_last_error()
+    assert call(0) == 1
+    # q sized for 2 q/k heads still may not overlap out
+    assert call(2, q=a["out"] + 256) == 3
