@@ -184,7 +184,7 @@ kda_status kda_prefill(kda_ctx *ctx, const kda_plan *plan, const void *q, const 
  *   q, k         : bf16 [n_seqs, qk_heads, 128] (device, 16-byte aligned); H
  *                  must be a multiple of qk_heads, and value head h reads q/k
  *                  head h / (H / qk_heads) (grouped value heads, as in
- *                  kda_prefill_gva; qk_heads = H is the plain case)
+ *                  kda_prefill_opts; qk_heads = H is the plain case)
  *   v, out       : bf16 [n_seqs, H, 128] (device, 16-byte aligned)
  *   g            : fp32 [n_seqs, H, 128] raw log-decay (device, 16-byte aligned)
  *   beta         : fp32 [n_seqs, H] (device, 4-byte aligned)
@@ -205,28 +205,47 @@ kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int3
                                const void *q, const void *k, const void *v, const float *g,
                                const float *beta, float scale, const float *state, const void *out);
 
-/* kda_prefill with grouped value heads (GVA): q and k have qk_heads heads,
- * while v, g, beta, the states and out have the plan's H heads, H a multiple
- * of qk_heads. Value head h reads q/k head h / (H / qk_heads), so each q/k
- * head serves that many consecutive value heads; with qk_heads = H this is
- * kda_prefill. The reviewer notes of "feat(kda/sm90): FlashKDA prefill port +
- * intracard-CP prefill" (cuLA pull request #103) restrict that prefill to
- * num_kv_heads == num_qk_heads and name GVA as its follow-up.
- *   q, k : bf16 [Tt, qk_heads, 128] (device); everything else as in kda_prefill.
- * Errors as kda_prefill, plus KDA_ERR_INVALID when H is not a multiple of
- * qk_heads. */
-kda_status kda_prefill_gva(kda_ctx *ctx, const kda_plan *plan, int32_t qk_heads, const void *q,
-                           const void *k, const void *v, const float *g, const float *beta,
-                           const int32_t *cu_seqlens_dev, float scale, const float *initial_state,
-                           float *final_state, void *out, hipStream_t stream);
+/* Options of kda_prefill_ex. A zeroed struct (or NULL) gives kda_prefill. */
+typedef struct {
+    /* Grouped value heads (GVA): q and k have qk_heads heads while v, g,
+     * beta, the states and out have the plan's H heads, H a multiple of
+     * qk_heads; value head h reads q/k head h / (H / qk_heads), so each q/k
+     * head serves that many consecutive value heads. 0 means H (no grouping).
+     * The reviewer notes of "feat(kda/sm90): FlashKDA prefill port +
+     * intracard-CP prefill" (cuLA pull request #103) restrict that prefill to
+     * num_kv_heads == num_qk_heads and name GVA as its follow-up. */
+    int32_t qk_heads;
+    /* 1: beta is bf16 [Tt, H] (2-byte aligned). It is widened to fp32 in the
+     * stream's workspace arena by one extra launch; the results are then
+     * bitwise those of kda_prefill on that fp32 beta. The FlashInfer KDA
+     * facade of "fix(cake_kda): support non-aligned recurrent prefill head
+     * counts" (pull request #4351, description) keeps beta in bf16. */
+    int32_t beta_bf16;
+    /* 1: initial_state and final_state are bf16 [N, H, 128, 128]; the state
+     * is read exactly, carried in fp32 and rounded to nearest even once, when
+     * the final state is written. The same facade allocates its returned
+     * final state in bf16 (review thread of FlashInfer pull request #4313). */
+    int32_t state_bf16;
+} kda_prefill_opts;
 
-/* The argument checks of kda_prefill_gva, without launching anything
+/* kda_prefill with options (grouped value heads, bf16 beta, bf16 states).
+ *   q, k : bf16 [Tt, qk_heads, 128] (device)
+ *   beta : fp32 [Tt, H], or bf16 with beta_bf16
+ *   initial_state, final_state : fp32 [N, H, 128, 128], or bf16 with
+ *          state_bf16 (device, 16-byte aligned)
+ * everything else as in kda_prefill. Errors as kda_prefill, plus
+ * KDA_ERR_INVALID when H is not a multiple of qk_heads. */
+kda_status kda_prefill_ex(kda_ctx *ctx, const kda_plan *plan, const kda_prefill_opts *opts, const void *q,
+                          const void *k, const void *v, const float *g, const void *beta,
+                          const int32_t *cu_seqlens_dev, float scale, const void *initial_state,
+                          void *final_state, void *out, hipStream_t stream);
+
+/* The argument checks of kda_prefill_ex, without launching anything
  * (addresses only, never dereferenced; needs no GPU). */
-kda_status kda_prefill_gva_validate(const kda_plan *plan, int32_t qk_heads, const void *q, const void *k,
-                                    const void *v, const float *g, const float *beta,
-                                    const int32_t *cu_seqlens_dev, float scale,
-                                    const float *initial_state, const float *final_state,
-                                    const void *out);
+kda_status kda_prefill_ex_validate(const kda_plan *plan, const kda_prefill_opts *opts, const void *q,
+                                   const void *k, const void *v, const float *g, const void *beta,
+                                   const int32_t *cu_seqlens_dev, float scale, const void *initial_state,
+                                   const void *final_state, const void *out);
 
 /* K1 alone, for inspection and tests: write every chunk record of the plan
  * into `records` (device, total_chunks * H * KDA_RECORD_BYTES bytes, record

@@ -56,6 +56,10 @@ class PlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class PrefillOpts(ctypes.Structure):
+    _fields_ = [("qk_heads", ctypes.c_int32), ("beta_bf16", ctypes.c_int32), ("state_bf16", ctypes.c_int32)]
+
+
 class UnitInfo(ctypes.Structure):
     _fields_ = [("seq", ctypes.c_int32), ("chunk0", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
                 ("segment", ctypes.c_int32), ("n_segments", ctypes.c_int32)]
@@ -90,8 +94,10 @@ def lib():
                 "kda_prefill_validate": (ctypes.c_int, [P, P, P, P, P, P, P, F32, P, P, P]),
                 "kda_prefill": (ctypes.c_int, [P, P, P, P, P, P, P, P, F32, P, P, P, P]),
                 "kda_debug_k1_records": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
-                "kda_prefill_gva": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P, F32, P, P, P, P]),
-                "kda_prefill_gva_validate": (ctypes.c_int, [P, I32, P, P, P, P, P, P, F32, P, P, P]),
+                "kda_prefill_ex": (ctypes.c_int, [P, P, ctypes.POINTER(PrefillOpts), P, P, P, P, P, P, F32, P, P,
+                                                  P, P]),
+                "kda_prefill_ex_validate": (ctypes.c_int, [P, ctypes.POINTER(PrefillOpts), P, P, P, P, P, P, F32,
+                                                           P, P, P]),
                 "kda_decode": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P, P]),
                 "kda_decode_validate": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P]),
                 "kda_set_timing": (ctypes.c_int, [P, ctypes.c_int]),
@@ -293,18 +299,20 @@ def _ptr(t):
 
 def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=False,
             use_intracard_cp=False, scale=1.0, final_state=None, out=None, plan=None,
-            cu_seqlens_host=None):
+            cu_seqlens_host=None, state_dtype=None):
     """KDA forward prefill.
 
     q, k, v: bf16 [Tt, H, 128] packed, or [B, T, H, 128] (B equal-length
     sequences when cu_seqlens is None); g: fp32 log-decay, same shape;
-    beta: fp32 [Tt, H] (or [B, T, H]). q and k may have fewer heads Hk than
-    v (grouped value heads, H a multiple of Hk: value head h reads q/k head
-    h // (H // Hk)). cu_seqlens: int32 [N + 1] (device
-    tensor, host list, or None). initial_state: fp32 [N, H, 128, 128] or None.
+    beta: fp32 or bf16 [Tt, H] (or [B, T, H]). q and k may have fewer heads
+    Hk than v (grouped value heads, H a multiple of Hk: value head h reads
+    q/k head h // (H // Hk)). cu_seqlens: int32 [N + 1] (device
+    tensor, host list, or None). initial_state: [N, H, 128, 128] or None.
     final_state: a tensor to write the final state into (may be
     initial_state: in-place update); with output_final_state=True and no
-    final_state, a new one is allocated. Returns (o, final_state or None).
+    final_state, a new one is allocated. States are fp32, or all bf16
+    (state_dtype, default: the dtype of the given state, else fp32).
+    Returns (o, final_state or None).
     """
     import torch
     if q.dim() == 4:
@@ -316,16 +324,17 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
         flat = lambda x: x.reshape(B * T, *x.shape[2:])
         o, s = prefill(flat(q), flat(k), flat(v), flat(g), flat(beta), cu_seqlens, initial_state,
                        output_final_state, use_intracard_cp, scale, final_state,
-                       None if out is None else flat(out), plan, cu_seqlens_host)
+                       None if out is None else flat(out), plan, cu_seqlens_host, state_dtype)
         return o.view(v.shape), s
     if q.dim() != 3 or q.shape[-1] != D or v.dim() != 3:
         raise ValueError("q must be [Tt, H, 128] or [B, T, H, 128], got %s" % (tuple(q.shape),))
     Tt, Hk, H = q.shape[0], q.shape[1], v.shape[1]
     if H % Hk:
         raise ValueError("v has %d heads, not a multiple of the %d q/k heads" % (H, Hk))
+    beta16 = beta.dtype == torch.bfloat16
     for name, t, dt, shape in (("q", q, torch.bfloat16, (Tt, Hk, D)), ("k", k, torch.bfloat16, (Tt, Hk, D)),
                                ("v", v, torch.bfloat16, (Tt, H, D)), ("g", g, torch.float32, (Tt, H, D)),
-                               ("beta", beta, torch.float32, (Tt, H))):
+                               ("beta", beta, torch.bfloat16 if beta16 else torch.float32, (Tt, H))):
         if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("%s must be a contiguous %s CUDA tensor of shape %s (got %s %s)"
                              % (name, dt, shape, t.dtype, tuple(t.shape)))
@@ -346,19 +355,26 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
         if cu_dev.dtype != torch.int32 or not cu_dev.is_cuda:
             raise ValueError("cu_seqlens must be an int32 CUDA tensor")
     N = len(cu_seqlens_host) - 1
+    if state_dtype is None:
+        given = initial_state if initial_state is not None else final_state
+        state_dtype = given.dtype if given is not None else torch.float32
+    if state_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("states must be fp32 or bf16, got %s" % (state_dtype,))
     for name, t in (("initial_state", initial_state), ("final_state", final_state)):
-        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, H, D, D)
+        if t is not None and (t.dtype != state_dtype or tuple(t.shape) != (N, H, D, D)
                               or not t.is_contiguous() or not t.is_cuda):
-            raise ValueError("%s must be a contiguous fp32 CUDA tensor of shape %s" % (name, (N, H, D, D)))
+            raise ValueError("%s must be a contiguous %s CUDA tensor of shape %s"
+                             % (name, state_dtype, (N, H, D, D)))
     if out is None:
         out = torch.empty_like(v)
     if final_state is None and output_final_state:
-        final_state = torch.empty(N, H, D, D, dtype=torch.float32, device=q.device)
+        final_state = torch.empty(N, H, D, D, dtype=state_dtype, device=q.device)
     ctx = context(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(lib().kda_prefill_gva(ctx.handle, plan.handle, Hk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state), _ptr(out),
-                                 ctypes.c_void_p(stream)), "kda_prefill")
+    opts = PrefillOpts(Hk, int(beta16), int(state_dtype == torch.bfloat16))
+    _check(lib().kda_prefill_ex(ctx.handle, plan.handle, ctypes.byref(opts), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state),
+                                _ptr(out), ctypes.c_void_p(stream)), "kda_prefill")
     return out, final_state
 
 

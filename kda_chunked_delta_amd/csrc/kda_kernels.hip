@@ -115,6 +115,30 @@ __device__ __forceinline__ void store_state(float* so, const f32x4 (&S)[8][NT], 
                 so[(16 * t + 4 * gg + vv) * D + 16 * (n0 + n) + m] = S[t][n][vv];
 }
 
+// The same for a bf16 state (loaded exactly; stored rounded to nearest even).
+template <int NT>
+__device__ __forceinline__ void load_state_bf16(const uint16_t* sin, f32x4 (&S)[8][NT], int n0, int gg, int m) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                S[t][n][vv] = bf16_lo(sin[(16 * t + 4 * gg + vv) * D + 16 * (n0 + n) + m]);
+    settle(S);
+}
+
+template <int NT>
+__device__ __forceinline__ void store_state_bf16(uint16_t* so, const f32x4 (&S)[8][NT], int n0, int gg, int m) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv)
+                so[(16 * t + 4 * gg + vv) * D + 16 * (n0 + n) + m] = (uint16_t)pack_bf16(S[t][n][vv], 0.f);
+}
+
 template <int NT>
 __device__ __forceinline__ void identity_state(f32x4 (&S)[8][NT], int n0, int gg, int m) {
 #pragma unroll
@@ -143,10 +167,28 @@ __device__ __forceinline__ void store_output(const K2Args& a, int h, int64_t tk,
         (int)((uint32_t)m * rowb + (16 * n + 4 * gg) * 2), 0, 0);
 }
 
-__device__ __forceinline__ const float* unit_state_in(const K2Args& a, const UnitDesc& u, int h) {
-    if (u.in_slot >= 0) return a.carries + ((size_t)u.in_slot * a.c.H + h) * (D * D);
-    if (a.s0) return a.s0 + ((size_t)u.seq * a.c.H + h) * (D * D);
-    return nullptr;
+// Start state of a unit: its carry (fp32, CP segments), else the caller's
+// initial state (fp32 or bf16), else zeros.
+template <int NT>
+__device__ __forceinline__ void load_unit_state(const K2Args& a, const UnitDesc& u, int h, f32x4 (&S)[8][NT],
+                                                int n0, int gg, int m) {
+    const size_t off = ((size_t)u.seq * a.c.H + h) * (D * D);
+    if (u.in_slot >= 0)
+        load_state(a.carries + ((size_t)u.in_slot * a.c.H + h) * (D * D), S, n0, gg, m);
+    else if (a.s0 && a.state_bf16)
+        load_state_bf16((const uint16_t*)a.s0 + off, S, n0, gg, m);
+    else
+        load_state(a.s0 ? (const float*)a.s0 + off : nullptr, S, n0, gg, m);
+}
+
+// Final state of a unit, if it writes one (fp32 or bf16).
+template <int NT>
+__device__ __forceinline__ void store_unit_state(const K2Args& a, const UnitDesc& u, int h,
+                                                 const f32x4 (&S)[8][NT], int n0, int gg, int m) {
+    if (!u.write_final || !a.sT) return;
+    const size_t off = ((size_t)u.seq * a.c.H + h) * (D * D);
+    if (a.state_bf16) store_state_bf16((uint16_t*)a.sT + off, S, n0, gg, m);
+    else store_state((float*)a.sT + off, S, n0, gg, m);
 }
 
 }  // namespace
@@ -243,7 +285,7 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     if (wave < 8) {
         // state wavefronts
         f32x4 S[8][1];
-        load_state(unit_state_in(a, u, h), S, w8, gg, m);
+        load_unit_state(a, u, h, S, w8, gg, m);
         lds_barrier();  // start-up: the first chunk is staged
         auto step = [&](int i) __attribute__((always_inline)) {
             f32x4 oacc[1];
@@ -275,7 +317,7 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         else if (w8 < N_WAVE_T) run(std::integral_constant<int, 1>{});
         else if (w8 == WAVE_QK) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 0>{});
-        if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, w8, gg, m);
+        store_unit_state(a, u, h, S, w8, gg, m);
     } else {
         // K1 wavefronts: chunk c is loaded into register set c & 1
         RowChunk r0, r1;
@@ -339,14 +381,14 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
     seq_bounds(a.c, u.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
     f32x4 S[8][1];
-    load_state(unit_state_in(a, u, h), S, wave, gg, m);
+    load_unit_state(a, u, h, S, wave, gg, m);
     const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0) * REC_BYTES;
     record_loop<512>(rb, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
         f32x4 oacc[1];
         chain_step<1, true, true>(r, S, wave, lane, oacc);
         store_output(a, h, tok0 + (int64_t)CH * ci, end, oacc[0], wave, gg, m);
     });
-    if (u.write_final && a.sT) store_state(a.sT + ((size_t)u.seq * H + h) * (D * D), S, wave, gg, m);
+    store_unit_state(a, u, h, S, wave, gg, m);
 }
 
 // ---------------------------------------------------------------------------
@@ -407,11 +449,13 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
     const int gg = lane >> 4, m = lane & 15;
 
     {
-        const float* s0 = a.s0 ? a.s0 + ((size_t)it.seq * H + h) * (D * D) : nullptr;
+        const size_t s0_off = ((size_t)it.seq * H + h) * (D * D);
+        const float* s0 = (a.s0 && !a.state_bf16) ? (const float*)a.s0 + s0_off : nullptr;
+        const uint16_t* s0h = (a.s0 && a.state_bf16) ? (const uint16_t*)a.s0 + s0_off : nullptr;
         float* c0 = a.carries + ((size_t)it.carry0 * H + h) * (D * D);
         for (int i = tid; i < D * 16; i += 512) {
             const int row = i >> 4, col = i & 15;
-            const float val = s0 ? s0[row * D + 16 * vt + col] : 0.f;
+            const float val = s0 ? s0[row * D + 16 * vt + col] : (s0h ? bf16_lo(s0h[row * D + 16 * vt + col]) : 0.f);
             carry[row][col] = val;
             c0[row * D + 16 * vt + col] = val;
         }
@@ -478,6 +522,20 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     if (attr1 != hipSuccess) return attr1;
     if (a.c.group > 1) hipLaunchKernelGGL(kda_fused<true>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
     else hipLaunchKernelGGL(kda_fused<false>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
+    return hipGetLastError();
+}
+
+// bf16 beta -> fp32 beta (exact), for callers that keep beta in bf16.
+__global__ __launch_bounds__(256) void kda_beta_to_f32(const uint16_t* __restrict__ src, float* __restrict__ dst,
+                                                       int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        dst[i] = bf16_lo(src[i]);
+}
+
+hipError_t launch_beta_to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(kda_beta_to_f32, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, src, dst, n);
     return hipGetLastError();
 }
 

@@ -64,11 +64,12 @@ struct K2Args {
     CommonArgs c;
     const UnitDesc* units;
     int32_t n_units;
-    const float* s0;     // may be null
-    float* sT;           // may be null
+    const void* s0;      // may be null; fp32, or bf16 when state_bf16
+    void* sT;            // may be null; fp32, or bf16 when state_bf16
     const float* carries;
     uint16_t* out;
     float scale;
+    int32_t state_bf16;  // initial and final states are bf16
 };
 
 struct PrescanArgs {
@@ -83,10 +84,11 @@ struct MergeArgs {
     CommonArgs c;
     const MergeDesc* items;
     int32_t n_items;
-    const float* s0;
+    const void* s0;      // fp32, or bf16 when state_bf16
     const float* b_seg;
     const float* m_seg;
     float* carries;  // [slots][H][128][128]
+    int32_t state_bf16;
 };
 
 struct K1Args {
@@ -95,6 +97,7 @@ struct K1Args {
 };
 
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s);
+hipError_t launch_beta_to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_fused(const K2Args& a, hipStream_t s);
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
 hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);

@@ -462,18 +462,22 @@ kda_status kda_plan_get_units(const kda_plan* p, kda_unit_info* units, int32_t m
     return KDA_OK;
 }
 
-kda_status kda_prefill_gva_validate(const kda_plan* p, int32_t qk_heads, const void* q, const void* k,
-                                    const void* v, const float* g, const float* beta, const int32_t* cu_dev,
-                                    float scale, const float* s0, const float* sT, const void* out) {
+kda_status kda_prefill_ex_validate(const kda_plan* p, const kda_prefill_opts* opts, const void* q, const void* k,
+                                   const void* v, const float* g, const void* beta, const int32_t* cu_dev,
+                                   float scale, const void* s0, const void* sT, const void* out) {
     if (!p) return fail(KDA_ERR_INVALID, "kda_prefill: plan is NULL");
     const kda_plan_info& in = p->info;
-    if (qk_heads < 1 || in.H % qk_heads != 0)
+    const int32_t qk_heads = (opts && opts->qk_heads > 0) ? opts->qk_heads : in.H;
+    const bool beta16 = opts && opts->beta_bf16, state16 = opts && opts->state_bf16;
+    if (opts && opts->qk_heads < 0)
+        return fail(KDA_ERR_INVALID, "kda_prefill: qk_heads must be >= 0 (got %d)", opts->qk_heads);
+    if (in.H % qk_heads != 0)
         return fail(KDA_ERR_INVALID, "kda_prefill: the plan's %d value heads are not a multiple of %d q/k heads",
                     in.H, qk_heads);
     const size_t Tt = (size_t)in.total_tokens, H = (size_t)in.H, N = (size_t)in.n_seqs;
-    const size_t n_act = Tt * H * 128 * 2, n_g = Tt * H * 128 * 4, n_beta = Tt * H * 4;
+    const size_t n_act = Tt * H * 128 * 2, n_g = Tt * H * 128 * 4, n_beta = Tt * H * (beta16 ? 2 : 4);
     const size_t n_qk = Tt * (size_t)qk_heads * 128 * 2;
-    const size_t n_state = N * H * kStateBytes, n_cu = (N + 1) * 4;
+    const size_t n_state = N * H * 128 * 128 * (state16 ? 2 : 4), n_cu = (N + 1) * 4;
     if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID, "kda_prefill: scale is not finite");
     if (!cu_dev) return fail(KDA_ERR_INVALID, "kda_prefill: cu_seqlens is NULL");
     if (Tt > 0) {
@@ -481,8 +485,9 @@ kda_status kda_prefill_gva_validate(const kda_plan* p, int32_t qk_heads, const v
         const char* names[] = {"q", "k", "v", "g", "beta", "out"};
         for (int i = 0; i < 6; ++i) {
             if (!need[i]) return fail(KDA_ERR_INVALID, "kda_prefill: %s is NULL", names[i]);
-            if ((uintptr_t)need[i] % (i == 4 ? 4 : 16))
-                return fail(KDA_ERR_INVALID, "kda_prefill: %s is not %d-byte aligned", names[i], i == 4 ? 4 : 16);
+            const int al = i == 4 ? (beta16 ? 2 : 4) : 16;
+            if ((uintptr_t)need[i] % al)
+                return fail(KDA_ERR_INVALID, "kda_prefill: %s is not %d-byte aligned", names[i], al);
         }
     }
     if ((uintptr_t)cu_dev % 4) return fail(KDA_ERR_INVALID, "kda_prefill: cu_seqlens is not 4-byte aligned");
@@ -509,8 +514,7 @@ kda_status kda_prefill_gva_validate(const kda_plan* p, int32_t qk_heads, const v
 kda_status kda_prefill_validate(const kda_plan* p, const void* q, const void* k, const void* v,
                                 const float* g, const float* beta, const int32_t* cu_dev, float scale,
                                 const float* s0, const float* sT, const void* out) {
-    if (!p) return fail(KDA_ERR_INVALID, "kda_prefill: plan is NULL");
-    return kda_prefill_gva_validate(p, p->info.H, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
+    return kda_prefill_ex_validate(p, nullptr, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
 }
 
 kda_status kda_set_timing(kda_ctx* ctx, int enable) {
@@ -563,15 +567,14 @@ int32_t kda_get_timing(kda_ctx* ctx, const char** names, double* total_ms, int32
 kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const int32_t* cu_dev, float scale,
                        const float* s0, float* sT, void* out, hipStream_t stream) {
-    if (!p) return fail(KDA_ERR_INVALID, "kda_prefill: plan is NULL");
-    return kda_prefill_gva(ctx, p, p->info.H, q, k, v, g, beta, cu_dev, scale, s0, sT, out, stream);
+    return kda_prefill_ex(ctx, p, nullptr, q, k, v, g, beta, cu_dev, scale, s0, sT, out, stream);
 }
 
-kda_status kda_prefill_gva(kda_ctx* ctx, const kda_plan* p, int32_t qk_heads, const void* q, const void* k,
-                           const void* v, const float* g, const float* beta, const int32_t* cu_dev,
-                           float scale, const float* s0, float* sT, void* out, hipStream_t stream) {
+kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts* opts, const void* q,
+                          const void* k, const void* v, const float* g, const void* beta, const int32_t* cu_dev,
+                          float scale, const void* s0, void* sT, void* out, hipStream_t stream) {
     if (!ctx) return fail(KDA_ERR_INVALID, "kda_prefill: ctx is NULL");
-    kda_status st = kda_prefill_gva_validate(p, qk_heads, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
+    kda_status st = kda_prefill_ex_validate(p, opts, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
     if (st != KDA_OK) return st;
     if (!p->dev_tables)
         return fail(KDA_ERR_INVALID, "kda_prefill: plan has no device tables (built by kda_plan_prefill_host?)");
@@ -593,7 +596,12 @@ kda_status kda_prefill_gva(kda_ctx* ctx, const kda_plan* p, int32_t qk_heads, co
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     e = hipStreamIsCapturing(stream, &cap);
     if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-    const size_t need = p->info.workspace_bytes;
+    const int32_t qk_heads = (opts && opts->qk_heads > 0) ? opts->qk_heads : p->info.H;
+    const bool beta16 = opts && opts->beta_bf16, state16 = opts && opts->state_bf16;
+    // a bf16 beta is widened to fp32 into the arena, after the plan's part
+    const size_t off_beta = align_up(p->info.workspace_bytes, 256);
+    const size_t n_beta = (size_t)p->info.total_tokens * p->info.H;
+    const size_t need = beta16 ? off_beta + n_beta * 4 : p->info.workspace_bytes;
     auto it = ctx->arenas.find(stream);
     if (it == ctx->arenas.end() || it->second.bytes < need) {
         if (cap != hipStreamCaptureStatusNone)
@@ -632,7 +640,7 @@ kda_status kda_prefill_gva(kda_ctx* ctx, const kda_plan* p, int32_t qk_heads, co
     c.k = (const uint16_t*)k;
     c.v = (const uint16_t*)v;
     c.g = g;
-    c.beta = beta;
+    c.beta = beta16 ? (const float*)(ws + off_beta) : (const float*)beta;
     c.cu = cu_dev;
     c.Tt = p->info.total_tokens;
     c.H = p->info.H;
@@ -644,6 +652,12 @@ kda_status kda_prefill_gva(kda_ctx* ctx, const kda_plan* p, int32_t qk_heads, co
 
     auto timed = [&](const char* name, auto&& launch) { return timed_launch(ctx, stream, name, launch); };
 
+    if (beta16) {
+        e = timed("beta_to_f32", [&] {
+            return launch_beta_to_f32((const uint16_t*)beta, (float*)(ws + off_beta), (int64_t)n_beta, stream);
+        });
+        if (e != hipSuccess) return hip_fail(e, "beta_to_f32 launch");
+    }
     const bool mat = p->info.k1_materialized != 0;
     if (mat) {
         K1Args k1{c, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
@@ -658,12 +672,13 @@ kda_status kda_prefill_gva(kda_ctx* ctx, const kda_plan* p, int32_t qk_heads, co
     }
     if (p->info.n_cp_seqs > 0) {
         MergeArgs ma{c, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
-                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry)};
+                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
+                     state16 ? 1 : 0};
         e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
         if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
     }
     K2Args ka{c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(), s0, sT,
-              (const float*)(ws + p->off_carry), (uint16_t*)out, scale};
+              (const float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0};
     const char* k2name = mat ? (p->info.uses_cp ? "k2_segment" : "k2_recur")
                              : (p->info.uses_cp ? "fused_segment" : "fused_serial");
     e = timed(k2name, [&] { return mat ? launch_k2_recur(ka, stream) : launch_fused(ka, stream); });

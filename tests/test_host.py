@@ -256,18 +256,32 @@ def test_decode_needs_context(kda_lib):
     assert st == 1 and b"ctx" in kda_lib.kda_last_error()
 
 
-def test_gva_validate(kda_lib):
-    """kda_prefill_gva_validate sizes q/k by the q/k head count."""
+def test_prefill_ex_validate(kda_lib):
+    """kda_prefill_ex_validate sizes q/k by the q/k head count, beta and the
+    states by their dtypes."""
     lib = kda_lib
     p = kda.plan_host([0, 40, 100], H=6, n_cus=256)
     fb = FakeBuffers(100, 6, 2)
     a = dict(fb.addr)
     P = lambda x: ctypes.c_void_p(x) if x else None
-    call = lambda Hk, **o: lib.kda_prefill_gva_validate(
-        p.handle, Hk, *(P(dict(a, **o)[n]) for n in ("q", "k", "v", "g", "beta", "cu")), ctypes.c_float(1.0),
-        P(a["s0"]), P(a["sT"]), P(a["out"]))
-    assert call(6) == 0 and call(3) == 0 and call(2) == 0 and call(1) == 0
+
+    def call(Hk, beta16=0, state16=0, **o):
+        b = dict(a, **o)
+        opts = kda.PrefillOpts(Hk, beta16, state16)
+        return lib.kda_prefill_ex_validate(
+            p.handle, ctypes.byref(opts), *(P(b[n]) for n in ("q", "k", "v", "g", "beta", "cu")),
+            ctypes.c_float(1.0), P(b["s0"]), P(b["sT"]), P(b["out"]))
+    assert call(6) == 0 and call(3) == 0 and call(2) == 0 and call(1) == 0 and call(0) == 0
     assert call(4) == 1 and b"multiple" in lib.kda_last_error()
-    assert call(0) == 1
+    assert call(-1) == 1
+    assert lib.kda_prefill_ex_validate(p.handle, None, *(P(a[n]) for n in ("q", "k", "v", "g", "beta", "cu")),
+                                       ctypes.c_float(1.0), P(a["s0"]), P(a["sT"]), P(a["out"])) == 0
     # q sized for 2 q/k heads still may not overlap out
     assert call(2, q=a["out"] + 256) == 3
+    # bf16 beta needs only 2-byte alignment; fp32 beta 4
+    assert call(6, beta16=1, beta=a["beta"] + 2) == 0
+    assert call(6, beta=a["beta"] + 2) == 1
+    # a bf16 state is half the bytes: a final state right behind a bf16 initial state is disjoint
+    half = 2 * 6 * 128 * 128 * 2
+    assert call(6, state16=1, sT=a["s0"] + half) == 0
+    assert call(6, state16=0, sT=a["s0"] + half) == 3
