@@ -225,39 +225,81 @@ __device__ __forceinline__ RowLaneOffsets row_lane_offsets(int H, int Hk, int wa
     return o;
 }
 
-// Loads of the chunk whose first value-head row is crow and first q/k-head
-// row is crow_qk (both uniform), nrows valid rows (rows past them, and every
-// row when nrows <= 0, read as zeros). Only wavefront 0 reads beta: the
-// others' beta range is empty. GVA = false: q/k heads are the value heads
-// (Hk = H, crow_qk = crow), and q/k share v's offsets and ranges.
+// Row streams of one (unit, head): the first chunk's row bases and the bytes
+// per token row of each tensor (all uniform). st_b is 0 on the wavefronts
+// that do not read beta (every wavefront but 0), which makes their beta
+// range empty.
+struct RowStreams {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    const uint8_t* g;
+    const uint8_t* b;
+    uint32_t st_qk, st_act, st_g, st_b;
+};
+
+// H value heads (v, g, beta rows), Hk q/k heads (value head h reads q/k
+// head hq); the unit's first token is tok0.
+__device__ __forceinline__ RowStreams row_streams(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                                  const float* g, const float* beta, int H, int Hk, int64_t tok0,
+                                                  int h, int hq, int wave) {
+    RowStreams r;
+    const int64_t crow = tok0 * H + h, crow_qk = tok0 * Hk + hq;
+    r.q = (const uint8_t*)q + crow_qk * (D * 2);
+    r.k = (const uint8_t*)k + crow_qk * (D * 2);
+    r.v = (const uint8_t*)v + crow * (D * 2);
+    r.g = (const uint8_t*)g + crow * (D * 4);
+    r.b = (const uint8_t*)beta + crow * 4;
+    r.st_qk = (uint32_t)Hk * (D * 2);
+    r.st_act = (uint32_t)H * (D * 2);
+    r.st_g = (uint32_t)H * (D * 4);
+    r.st_b = wave == 0 ? (uint32_t)H * 4 : 0u;
+    return r;
+}
+
+// Loads of chunk ci of the streams with nrows (0..16) valid rows. Each range
+// covers nrows whole token rows, so the lanes of rows past them, and every
+// lane when nrows = 0, read zeros and touch no memory. GVA = false: q/k heads
+// are the value heads, and q/k share v's offsets and ranges.
 template <bool GVA>
-__device__ __forceinline__ void k1_load_rows(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                             const uint16_t* __restrict__ v, const float* __restrict__ g,
-                                             const float* __restrict__ beta, int H, int Hk, int64_t crow,
-                                             int64_t crow_qk, int nrows, int wave, const RowLaneOffsets& lo,
-                                             RowChunk& rc) {
-    const size_t act = (size_t)crow * (D * 2), gb = (size_t)crow * (D * 4), bb = (size_t)crow * 4;
-    const uint32_t last = nrows > 0 ? (uint32_t)(nrows - 1) * (uint32_t)H : 0u;
-    const uint32_t live = nrows > 0 ? 1u : 0u;
-    const uint32_t n_act = (last * (D * 2) + D * 2) * live, n_g = (last * (D * 4) + D * 4) * live,
-                   n_b = (last * 4 + 4) * live * (wave == 0 ? 1u : 0u);
-    size_t aqk = act;
+__device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int nrows, const RowLaneOffsets& lo,
+                                              RowChunk& rc) {
+    const uint32_t n_act = (uint32_t)nrows * rs.st_act;
+    const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
+    const uint8_t* qb = rs.q + c_act;
+    const uint8_t* kb = rs.k + c_act;
     uint32_t n_qk = n_act, o_qk = lo.act;
     if constexpr (GVA) {
-        aqk = (size_t)crow_qk * (D * 2);
-        n_qk = ((nrows > 0 ? (uint32_t)(nrows - 1) * (uint32_t)Hk : 0u) * (D * 2) + D * 2) * live;
+        const size_t c_qk = (size_t)ci * (CH * (size_t)rs.st_qk);
+        qb = rs.q + c_qk;
+        kb = rs.k + c_qk;
+        n_qk = (uint32_t)nrows * rs.st_qk;
         o_qk = lo.qk;
     }
-    rc.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)q + aqk, n_qk), (int)o_qk, 0, BUF_POLICY));
-    rc.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)k + aqk, n_qk), (int)o_qk, 0, BUF_POLICY));
-    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc((const uint8_t*)v + act, n_act), (int)lo.act, 0, BUF_POLICY));
+    rc.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(qb, n_qk), (int)o_qk, 0,
+                                                                          BUF_POLICY));
+    rc.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(kb, n_qk), (int)o_qk, 0,
+                                                                          BUF_POLICY));
+    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(rs.v + c_act, n_act),
+                                                                          (int)lo.act, 0, BUF_POLICY));
+    // g rows are twice as long as v rows, beta rows 1/64 of them
     rc.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        chunk_rsrc((const uint8_t*)g + gb, n_g), (int)lo.g, 0, BUF_POLICY));
+        chunk_rsrc(rs.g + 2 * c_act, (uint32_t)nrows * rs.st_g), (int)lo.g, 0, BUF_POLICY));
     rc.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-        chunk_rsrc((const uint8_t*)beta + bb, n_b), (int)lo.beta, 0, BUF_POLICY));
+        chunk_rsrc(rs.b + (c_act >> 6), (uint32_t)nrows * rs.st_b), (int)lo.beta, 0, BUF_POLICY));
+}
+
+// Valid rows of chunk ci when rem tokens of the sequence start at the unit's
+// first token: clamp(rem - 16 ci, 0, 16), in 32-bit arithmetic. Written as
+// scalar min/max so that the buffer ranges built on it stay in SGPRs (the
+// compiler would otherwise pick the vector v_med3_i32, and every load would
+// then need a waterfall loop over its descriptor). Both instructions write
+// SCC, which the compiler must not keep live across them (a 64-bit address
+// add split around them would lose its carry): hence the clobber.
+__device__ __forceinline__ int chunk_rows(int rem, int ci) {
+    int n = rem - CH * ci;
+    asm("s_max_i32 %0, %0, 0\n\ts_min_i32 %0, %0, %1" : "+s"(n) : "i"(CH) : "scc");
+    return n;
 }
 
 // Write a loaded RowChunk to the staging area stg.

@@ -151,11 +151,10 @@ __device__ __forceinline__ void identity_state(f32x4 (&S)[8][NT], int n0, int gg
 }
 
 // Output rows of one chunk: oacc[v] is o[token m][16 n + 4gg + v].
-__device__ __forceinline__ void store_output(const K2Args& a, int h, int64_t tk, int64_t end,
+__device__ __forceinline__ void store_output(const K2Args& a, int h, int64_t tk, int nrows,
                                              const f32x4& oacc, int n, int gg, int m) {
-    // a buffer store whose range ends with row rows_of - 1 of head h: the
+    // a buffer store whose range ends with row nrows - 1 of head h: the
     // lanes of rows past the end are dropped without a branch
-    const int nrows = rows_of(tk, end);
     const uint32_t rowb = (uint32_t)a.c.H * (D * 2);
     const uint32_t n_out = nrows > 0 ? (uint32_t)(nrows - 1) * rowb + D * 2 : 0u;
     u32x2 w;
@@ -220,9 +219,9 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     seq_bounds(a.c, cd.seq, beg, end);
     const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
     const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, wave, lane);
+    const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0, h, h / a.c.group, wave);
     RowChunk rc;
-    k1_load_rows<GVA>(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0 * H + h,
-                      tok0 * a.c.Hk + h / a.c.group, rows_of(tok0, end), wave, lo, rc);
+    k1_load_chunk<GVA>(rs, 0, rows_of(tok0, end), lo, rc);
     k1_stage(rc, wave, lane, lo, stg);
     lds_barrier();
     RawChunk raw;
@@ -287,10 +286,11 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         f32x4 S[8][1];
         load_unit_state(a, u, h, S, w8, gg, m);
         lds_barrier();  // start-up: the first chunk is staged
+        const int rem = (int)(end - tok0);
         auto step = [&](int i) __attribute__((always_inline)) {
             f32x4 oacc[1];
             chain_step<1, true, true>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, oacc);
-            store_output(a, h, tok0 + (int64_t)CH * i, end, oacc[0], w8, gg, m);
+            store_output(a, h, tok0 + (int64_t)CH * i, chunk_rows(rem, i), oacc[0], w8, gg, m);
         };
         // one loop per phase-2 role (0: none, 1: rows 4 w8.. of T', 2: A_qk),
         // so that each loop body is one block in which phase 2 of chunk i + 1
@@ -322,11 +322,12 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         // K1 wavefronts: chunk c is loaded into register set c & 1
         RowChunk r0, r1;
         const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, w8, lane);
-        const int hq = h / a.c.group;
+        const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0, h,
+                                          h / a.c.group, w8);
+        // tokens of the sequence from the unit's first one (sequences are < 2^31 tokens)
+        const int rem = (int)(end - tok0);
         auto load = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
-            const int64_t t = tok0 + (int64_t)CH * ci;
-            k1_load_rows<GVA>(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, t * H + h, t * a.c.Hk + hq,
-                              rows_of(t, end), w8, lo, rc);
+            k1_load_chunk<GVA>(rs, ci, chunk_rows(rem, ci), lo, rc);
         };
         auto stage = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
             // the register set is read only from here on (see below)
@@ -383,10 +384,11 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
     f32x4 S[8][1];
     load_unit_state(a, u, h, S, wave, gg, m);
     const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0) * REC_BYTES;
+    const int rem = (int)(end - tok0);
     record_loop<512>(rb, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
         f32x4 oacc[1];
         chain_step<1, true, true>(r, S, wave, lane, oacc);
-        store_output(a, h, tok0 + (int64_t)CH * ci, end, oacc[0], wave, gg, m);
+        store_output(a, h, tok0 + (int64_t)CH * ci, chunk_rows(rem, ci), oacc[0], wave, gg, m);
     });
     store_unit_state(a, u, h, S, wave, gg, m);
 }
