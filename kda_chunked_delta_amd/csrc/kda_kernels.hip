@@ -139,6 +139,20 @@ __device__ __forceinline__ void store_state_bf16(uint16_t* so, const f32x4 (&S)[
                 so[(16 * t + 4 * gg + vv) * D + 16 * (n0 + n) + m] = (uint16_t)pack_bf16(S[t][n][vv], 0.f);
 }
 
+// Whether any element of the wavefront's state tile is nonzero (-0 counts
+// as zero); the result is uniform over the wavefront.
+template <int NT>
+__device__ __forceinline__ bool tile_nonzero(const f32x4 (&S)[8][NT]) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) acc |= __float_as_uint(S[t][n][vv]);
+    return __builtin_amdgcn_ballot_w64((acc & 0x7fffffffu) != 0u) != 0;
+}
+
 template <int NT>
 __device__ __forceinline__ void identity_state(f32x4 (&S)[8][NT], int n0, int gg, int m) {
 #pragma unroll
@@ -416,13 +430,23 @@ __global__ __launch_bounds__(1024) void kda_cp_prescan(PrescanArgs a) {
         identity_state(S, n0, gg, m);
     f32x4 unused[1];
     const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
-    record_loop<1024>(rb, it.n_chunks, recs, [&](int, const uint8_t* r) {
-        if (is_b)
+    // An M tile (16 columns of the transfer matrix) that is exactly zero
+    // stays zero: its columns evolve independently, and the update of a zero
+    // column is zero. Under decay the transfer underflows within a few
+    // chunks, so an M wavefront checks its tile every 4 chunks and stops
+    // computing once it is zero (it still takes part in the record loads).
+    bool m_live = true;
+    record_loop<1024>(rb, it.n_chunks, recs, [&](int ci, const uint8_t* r) {
+        if (is_b) {
             chain_step<1, true, false>(r, S, n0, lane, unused);
-        else
+        } else if (m_live) {
             chain_step<1, false, false>(r, S, n0, lane, unused);
+            if ((ci & 3) == 3) m_live = tile_nonzero(S);
+        }
     });
+    if (!is_b) m_live = tile_nonzero(S);
     store_state((is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D), S, n0, gg, m);
+    if (!is_b && lane == 0) a.m_live[((size_t)it.slot * H + h) * 8 + n0] = m_live ? 1 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -439,6 +463,7 @@ __global__ __launch_bounds__(1024) void kda_cp_prescan(PrescanArgs a) {
 struct MergeOperands {
     f32x4 m[8];  // M_s[16 wave + m][32 gg + 4j .. + 3], j = 0..7
     f32x4 b;     // B_s[16 wave + 4 gg + v][16 vt + m], v = 0..3
+    int zero;    // M_s is exactly zero (uniform)
 };
 
 __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
@@ -472,22 +497,35 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
         const size_t sum_off = ((size_t)(it.prescan0 + ss) * H + h) * (D * D);
         const float* M = a.m_seg + sum_off;
         const float* B = a.b_seg + sum_off;
+        // a transfer that underflowed to zero in every tile is not read: the
+        // carry is then B_s itself
+        const int32_t* live = a.m_live + ((size_t)(it.prescan0 + ss) * H + h) * 8;
+        int any = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) any |= live[j];
+        x.zero = __builtin_amdgcn_readfirstlane(any == 0 ? 1 : 0);
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) x.b[vv] = B[(16 * wave + 4 * gg + vv) * D + 16 * vt + m];
+        const __amdgpu_buffer_rsrc_t mr = chunk_rsrc(M, x.zero ? 0u : (uint32_t)(D * D * 4));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x.m[j] = *(const f32x4*)(M + (16 * wave + m) * D + 32 * gg + 4 * j);
+        for (int j = 0; j < 8; ++j)
+            x.m[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                mr, (int)(((16 * wave + m) * D + 32 * gg + 4 * j) * 4), 0, 0));
     };
     auto step = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
         // the operands are read only from here on (keeps their wait here)
         asm volatile("" : "+v"(x.m[0]), "+v"(x.m[1]), "+v"(x.m[2]), "+v"(x.m[3]), "+v"(x.m[4]),
                      "+v"(x.m[5]), "+v"(x.m[6]), "+v"(x.m[7]), "+v"(x.b));
-        f32x4 acc0 = x.b, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = x.b;
+        if (!x.zero) {
+            f32x4 acc0 = x.b, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qq = 0; qq < 32; qq += 2) {
-            acc0 = mfma_f32_k4(x.m[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc0);
-            acc1 = mfma_f32_k4(x.m[qq >> 2][(qq & 3) + 1], carry[32 * gg + qq + 1][m], acc1);
+            for (int qq = 0; qq < 32; qq += 2) {
+                acc0 = mfma_f32_k4(x.m[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc0);
+                acc1 = mfma_f32_k4(x.m[qq >> 2][(qq & 3) + 1], carry[32 * gg + qq + 1][m], acc1);
+            }
+            acc = acc0 + acc1;
         }
-        const f32x4 acc = acc0 + acc1;
         __syncthreads();
         float* cn = a.carries + ((size_t)(it.carry0 + s + 1) * H + h) * (D * D);
 #pragma unroll

@@ -78,6 +78,7 @@ struct PrescanArgs {
     int32_t n_items;
     float* b_seg;  // [slots][H][128][128]
     float* m_seg;
+    int32_t* m_live;  // [slots][H][8]: 0 when that 16-column tile of M is exactly zero
 };
 
 struct MergeArgs {
@@ -89,6 +90,7 @@ struct MergeArgs {
     const float* m_seg;
     float* carries;  // [slots][H][128][128]
     int32_t state_bf16;
+    const int32_t* m_live;  // as PrescanArgs::m_live
 };
 
 struct K1Args {

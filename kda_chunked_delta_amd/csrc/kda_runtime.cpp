@@ -99,7 +99,7 @@ struct kda_plan {
     std::vector<PrescanDesc> prescan;   // CP pre_scan items
     std::vector<MergeDesc> merges;      // CP merge items
     // workspace layout (byte offsets into the arena)
-    size_t off_rec = 0, off_b = 0, off_m = 0, off_carry = 0;
+    size_t off_rec = 0, off_b = 0, off_m = 0, off_mlive = 0, off_carry = 0;
     // device copy of the tables
     int device = -1;
     void* dev_tables = nullptr;
@@ -241,6 +241,8 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     off = align_up(off + (size_t)n_prescan * H * kStateBytes, 256);
     p->off_m = off;
     off = align_up(off + (size_t)n_prescan * H * kStateBytes, 256);
+    p->off_mlive = off;
+    off = align_up(off + (size_t)n_prescan * H * 8 * sizeof(int32_t), 256);
     p->off_carry = off;
     off = align_up(off + (size_t)n_carry * H * kStateBytes, 256);
 
@@ -666,14 +668,14 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     }
     if (p->info.n_prescan > 0) {
         PrescanArgs pa{c, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
-                       (float*)(ws + p->off_b), (float*)(ws + p->off_m)};
+                       (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
         e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
         if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
     }
     if (p->info.n_cp_seqs > 0) {
         MergeArgs ma{c, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
                      (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
-                     state16 ? 1 : 0};
+                     state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
         e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
         if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
     }
