@@ -79,9 +79,11 @@ typedef struct {
     double  est_serial_us;     /* planner's cost estimate of the serial path */
     double  est_cp_us;         /* planner's cost estimate of the segmented path */
     int32_t k1_materialized;   /* 1: K1 writes chunk records to the workspace once and
-                                  K2 / pre_scan read them; 0: K1 is recomputed per chunk
-                                  inside the K2 and pre_scan kernels (default; set
-                                  KDA_MATERIALIZE_K1=1 at plan time for the other form) */
+                                  K2 / pre_scan read them (always so for segmented
+                                  plans, and for serial plans made with
+                                  KDA_MATERIALIZE_K1=1 in the environment); 0: serial
+                                  plan whose fused kernel recomputes K1 per chunk in LDS
+                                  (the default for serial plans) */
 } kda_plan_info;
 
 /* One K2 work unit of a plan (a whole sequence, or one segment of it). */
