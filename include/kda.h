@@ -201,6 +201,24 @@ kda_status kda_decode(kda_ctx *ctx, int32_t n_seqs, int32_t H, int32_t qk_heads,
                       const void *q, const void *k, const void *v, const float *g, const float *beta,
                       float scale, float *state, void *out, hipStream_t stream);
 
+/* kda_decode over a pool of states: sequence n reads and advances state
+ * slot slots[n] of state [n_slots, H, 128, 128] (a continuous-batching
+ * engine keeps such a pool and a slot table per step). slots: device int32
+ * [n_seqs], 4-byte aligned. A sequence whose slot is outside [0, n_slots)
+ * (for instance -1 for a padded entry) is skipped: its output is zero and no
+ * state is touched. Two sequences may not share a slot (their updates would
+ * race). slots = NULL with n_slots = n_seqs is kda_decode. */
+kda_status kda_decode_slots(kda_ctx *ctx, int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                            const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            float scale, float *state, int32_t n_slots, const int32_t *slots, void *out,
+                            hipStream_t stream);
+
+/* The argument checks of kda_decode_slots (addresses only; needs no GPU). */
+kda_status kda_decode_slots_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                                     const void *q, const void *k, const void *v, const float *g,
+                                     const float *beta, float scale, const float *state, int32_t n_slots,
+                                     const int32_t *slots, const void *out);
+
 /* The argument checks of kda_decode, without launching anything. Pointers are
  * compared as addresses only and never dereferenced. Needs no GPU. */
 kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,

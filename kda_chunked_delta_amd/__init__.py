@@ -100,6 +100,9 @@ def lib():
                                                            P, P, P]),
                 "kda_decode": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P, P]),
                 "kda_decode_validate": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P]),
+                "kda_decode_slots": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, I32, P, P, P]),
+                "kda_decode_slots_validate": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, I32, P,
+                                                             P]),
                 "kda_set_timing": (ctypes.c_int, [P, ctypes.c_int]),
                 "kda_get_timing": (I32, [P, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(I32), I32]),
@@ -378,13 +381,16 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
     return out, final_state
 
 
-def decode(q, k, v, g, beta, state, scale=1.0, out=None):
+def decode(q, k, v, g, beta, state, scale=1.0, out=None, slots=None):
     """KDA decode step: one new token per sequence, state advanced in place.
 
     q, k, v: bf16 [N, H, 128] (or [N, 1, H, 128]); g: fp32 log-decay, same
     shape as v; beta: fp32 [N, H] (or [N, 1, H]); state: fp32 [N, H, 128, 128],
     overwritten with the advanced state. q and k may have fewer heads than v
-    (grouped value heads, as in prefill). Returns o, shaped like v.
+    (grouped value heads, as in prefill). With slots (int32 CUDA tensor [N]),
+    state is a pool [n_slots, H, 128, 128] and sequence n uses slot slots[n];
+    a slot outside the pool skips that sequence (zero output). Returns o,
+    shaped like v.
     """
     import torch
     shape = v.shape
@@ -403,7 +409,7 @@ def decode(q, k, v, g, beta, state, scale=1.0, out=None):
     for name, t, dt, shp in (("q", q, torch.bfloat16, (N, Hk, D)), ("k", k, torch.bfloat16, (N, Hk, D)),
                              ("v", v, torch.bfloat16, (N, H, D)), ("g", g, torch.float32, (N, H, D)),
                              ("beta", beta, torch.float32, (N, H)),
-                             ("state", state, torch.float32, (N, H, D, D))):
+                             ("state", state, torch.float32, (state.shape[0] if slots is not None else N, H, D, D))):
         if t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("%s must be a contiguous %s CUDA tensor of shape %s (got %s %s)"
                              % (name, dt, shp, t.dtype, tuple(t.shape)))
@@ -411,6 +417,13 @@ def decode(q, k, v, g, beta, state, scale=1.0, out=None):
         out = torch.empty_like(v)
     ctx = context(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if slots is not None:
+        if slots.dtype != torch.int32 or tuple(slots.shape) != (N,) or not slots.is_contiguous() or not slots.is_cuda:
+            raise ValueError("slots must be a contiguous int32 CUDA tensor of shape (%d,)" % N)
+        _check(lib().kda_decode_slots(ctx.handle, N, H, Hk, D, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      float(scale), _ptr(state), state.shape[0], _ptr(slots), _ptr(out),
+                                      ctypes.c_void_p(stream)), "kda_decode_slots")
+        return out.view(shape)
     _check(lib().kda_decode(ctx.handle, N, H, Hk, D, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             float(scale), _ptr(state), _ptr(out), ctypes.c_void_p(stream)), "kda_decode")
     return out.view(shape)

@@ -17,7 +17,10 @@
 // and written once. The step is bound by HBM bandwidth: 2 x 64 KiB of state
 // per (sequence, head) against 1.3 KiB of token data.
 //
-// With grouped value heads, value head h reads q/k head h / group.
+// With grouped value heads, value head h reads q/k head h / group. With a
+// slot table, sequence n reads and writes the state of pool slot slots[n]
+// (continuous batching keeps a pool of states and a table per step).
+//
 //
 // Launch: one workgroup of 256 threads per (sequence, head, 64-column tile),
 // the two tiles of one (sequence, head) adjacent in the grid. Thread t owns
@@ -79,15 +82,25 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode_step(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile = blockIdx.x % DEC_TILES;
     const int64_t nh = blockIdx.x / DEC_TILES;  // n * H + h
+    const int64_t n = nh / a.H;
+    const int h = (int)(nh % a.H);
     // q/k row of the value head's group: n * Hk + h / group
-    const int64_t nq = (nh / a.H) * a.Hk + (int)(nh % a.H) / a.group;
+    const int64_t nq = n * a.Hk + h / a.group;
     const int cg = tid % DEC_CG, rs = tid / DEC_CG;
     const int col = tile * DEC_COLS + 4 * cg;
+    // state slot of sequence n; a sequence whose slot is outside the pool is
+    // skipped: zero output, no state touched
+    const int64_t slot = a.slots ? (int64_t)a.slots[n] : n;
+    if (slot < 0 || slot >= a.n_slots) {
+        if (rs == 0) *(uint2*)(a.out + nh * 128 + col) = uint2{0u, 0u};
+        return;
+    }
+    const int64_t sh = slot * a.H + h;  // state row of (slot, head)
     const float beta = a.beta[nh];
 
     // the thread's state rows: issued first, they stream while the token's
     // per-row factors are formed
-    f32x4* st = (f32x4*)(a.state + nh * (128 * 128) + col);
+    f32x4* st = (f32x4*)(a.state + sh * (128 * 128) + col);
     f32x4 s[DEC_ROWS];
 #pragma unroll
     for (int i = 0; i < DEC_ROWS; ++i) s[i] = load_state<NT>(st + (rs + DEC_ROWSETS * i) * (128 / 4));

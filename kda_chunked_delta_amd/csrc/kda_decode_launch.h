@@ -20,6 +20,9 @@ struct DecodeArgs {
     int32_t Hk;            // q/k heads; value head h reads q/k head h / group
     int32_t group;
     float scale;
+    const int32_t* slots;  // null: sequence n uses state[n]; else state[slots[n]], skipped when
+                           // slots[n] is outside [0, n_slots)
+    int32_t n_slots;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

@@ -688,32 +688,42 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     return KDA_OK;
 }
 
-kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
-                               const void* q, const void* k, const void* v, const float* g, const float* beta,
-                               float scale, const float* state, const void* out) {
+kda_status kda_decode_slots_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                                     const void* q, const void* k, const void* v, const float* g,
+                                     const float* beta, float scale, const float* state, int32_t n_slots,
+                                     const int32_t* slots, const void* out) {
     if (dk != 128 || dv != 128)
         return fail(KDA_ERR_UNSUPPORTED, "kda_decode: dk = dv = 128 required (got dk=%d dv=%d)", dk, dv);
     if (n_seqs < 0 || H < 1)
         return fail(KDA_ERR_INVALID, "kda_decode: n_seqs must be >= 0 and H >= 1 (got n_seqs=%d H=%d)", n_seqs, H);
     if (qk_heads < 1 || H % qk_heads != 0)
         return fail(KDA_ERR_INVALID, "kda_decode: %d value heads are not a multiple of %d q/k heads", H, qk_heads);
+    if (n_slots < 0) return fail(KDA_ERR_INVALID, "kda_decode: n_slots must be >= 0 (got %d)", n_slots);
+    if (!slots && n_slots != n_seqs)
+        return fail(KDA_ERR_INVALID, "kda_decode: without a slot table the state holds n_seqs = %d states, "
+                                     "not %d", n_seqs, n_slots);
     if ((int64_t)n_seqs * H * 2 > (int64_t)INT32_MAX)
         return fail(KDA_ERR_INVALID, "kda_decode: n_seqs * H too large (%lld)", (long long)n_seqs * H);
     if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID, "kda_decode: scale is not finite");
     if (n_seqs == 0) return KDA_OK;
     const size_t NH = (size_t)n_seqs * H;
-    const size_t n_act = NH * 128 * 2, n_g = NH * 128 * 4, n_beta = NH * 4, n_state = NH * kStateBytes;
+    const size_t n_act = NH * 128 * 2, n_g = NH * 128 * 4, n_beta = NH * 4;
+    const size_t n_state = (size_t)n_slots * H * kStateBytes, n_slot_tab = (size_t)n_seqs * 4;
     const size_t n_qk = (size_t)n_seqs * qk_heads * 128 * 2;
-    const void* need[] = {q, k, v, g, beta, state, out};
-    const char* names[] = {"q", "k", "v", "g", "beta", "state", "out"};
-    for (int i = 0; i < 7; ++i) {
+    const void* need[] = {q, k, v, g, beta, out};
+    const char* names[] = {"q", "k", "v", "g", "beta", "out"};
+    for (int i = 0; i < 6; ++i) {
         if (!need[i]) return fail(KDA_ERR_INVALID, "kda_decode: %s is NULL", names[i]);
         const int al = i == 4 ? 4 : 16;
         if ((uintptr_t)need[i] % al)
             return fail(KDA_ERR_INVALID, "kda_decode: %s is not %d-byte aligned", names[i], al);
     }
+    if (n_slots > 0 && !state) return fail(KDA_ERR_INVALID, "kda_decode: state is NULL");
+    if (state && (uintptr_t)state % 16) return fail(KDA_ERR_INVALID, "kda_decode: state is not 16-byte aligned");
+    if (slots && (uintptr_t)slots % 4) return fail(KDA_ERR_INVALID, "kda_decode: slots is not 4-byte aligned");
     struct B { const void* p; size_t n; const char* name; };
-    const B ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_act, "v"}, {g, n_g, "g"}, {beta, n_beta, "beta"}};
+    const B ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_act, "v"}, {g, n_g, "g"}, {beta, n_beta, "beta"},
+                     {slots, n_slot_tab, "slots"}};
     for (const B& b : ins) {
         if (overlap(out, n_act, b.p, b.n)) return fail(KDA_ERR_ALIAS, "kda_decode: out overlaps %s", b.name);
         if (overlap(state, n_state, b.p, b.n)) return fail(KDA_ERR_ALIAS, "kda_decode: state overlaps %s", b.name);
@@ -722,11 +732,21 @@ kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int3
     return KDA_OK;
 }
 
-kda_status kda_decode(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
-                      const void* q, const void* k, const void* v, const float* g, const float* beta, float scale,
-                      float* state, void* out, hipStream_t stream) {
+kda_status kda_decode_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                               const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               float scale, const float* state, const void* out) {
+    if (n_seqs > 0 && !state) return fail(KDA_ERR_INVALID, "kda_decode: state is NULL");
+    return kda_decode_slots_validate(n_seqs, H, qk_heads, dk, dv, q, k, v, g, beta, scale, state, n_seqs, nullptr,
+                                     out);
+}
+
+kda_status kda_decode_slots(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                            const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            float scale, float* state, int32_t n_slots, const int32_t* slots, void* out,
+                            hipStream_t stream) {
     if (!ctx) return fail(KDA_ERR_INVALID, "kda_decode: ctx is NULL");
-    kda_status st = kda_decode_validate(n_seqs, H, qk_heads, dk, dv, q, k, v, g, beta, scale, state, out);
+    kda_status st = kda_decode_slots_validate(n_seqs, H, qk_heads, dk, dv, q, k, v, g, beta, scale, state, n_slots,
+                                              slots, out);
     if (st != KDA_OK || n_seqs == 0) return st;
     std::lock_guard<std::mutex> lk(ctx->mu);
     int prev = -1;
@@ -734,11 +754,20 @@ kda_status kda_decode(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t qk_heads,
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (prev != ctx->device && (e = hipSetDevice(ctx->device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
     DecodeArgs a{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, beta, state, (uint16_t*)out,
-                 n_seqs, H, qk_heads, H / qk_heads, scale};
+                 n_seqs, H, qk_heads, H / qk_heads, scale, slots, n_slots};
     e = timed_launch(ctx, stream, "decode", [&] { return launch_decode(a, stream); });
     if (prev >= 0 && prev != ctx->device) (void)hipSetDevice(prev);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return KDA_OK;
+}
+
+kda_status kda_decode(kda_ctx* ctx, int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
+                      const void* q, const void* k, const void* v, const float* g, const float* beta, float scale,
+                      float* state, void* out, hipStream_t stream) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_decode: ctx is NULL");
+    if (n_seqs > 0 && !state) return fail(KDA_ERR_INVALID, "kda_decode: state is NULL");
+    return kda_decode_slots(ctx, n_seqs, H, qk_heads, dk, dv, q, k, v, g, beta, scale, state, n_seqs, nullptr, out,
+                            stream);
 }
 
 kda_status kda_debug_k1_records(kda_ctx* ctx, const kda_plan* p, const void* q, const void* k,

@@ -136,3 +136,29 @@ def test_decode_full_size_sampled():
                                    sub(d["state"]))
     assert_close("out", o.cpu()[ns, hs], o_ref[:, 0])
     assert_close("state", s.cpu()[ns, hs], s_ref[:, 0])
+
+
+def test_decode_with_a_state_pool_and_slot_table():
+    """Sequences address a pool of states through a slot table; a slot of -1
+    or past the pool skips its sequence (zero output, no state touched)."""
+    N, H, n_slots = 6, 4, 9
+    say("case decode slots N=%d H=%d pool=%d" % (N, H, n_slots))
+    d = draw_decode(N, H, seed=61, state_std=0.1, device=DEV)
+    pool = 0.1 * torch.randn(n_slots, H, 128, 128, generator=torch.Generator(device=DEV).manual_seed(62),
+                             device=DEV)
+    slots = torch.tensor([7, 2, -1, 0, 9, 4], dtype=torch.int32, device=DEV)
+    before = pool.clone()
+    o = kda.decode(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, slots=slots)
+    torch.cuda.synchronize()
+    live = [n for n, s in enumerate(slots.tolist()) if 0 <= s < n_slots]
+    idx = torch.tensor(live)
+    sl = slots.cpu()[idx].long()
+    sub = lambda x: x.cpu()[idx]
+    o_ref, s_ref = ref.decode_step(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]), sub(d["beta"]),
+                                   before.cpu()[sl])
+    assert_close("out", o.cpu()[idx], o_ref)
+    assert_close("state", pool.cpu()[sl], s_ref)
+    skipped = [n for n in range(N) if n not in live]
+    assert torch.count_nonzero(o[skipped]) == 0
+    untouched = [s for s in range(n_slots) if s not in sl.tolist()]
+    assert torch.equal(pool[untouched], before[untouched])

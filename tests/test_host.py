@@ -285,3 +285,28 @@ def test_prefill_ex_validate(kda_lib):
     half = 2 * 6 * 128 * 128 * 2
     assert call(6, state16=1, sT=a["s0"] + half) == 0
     assert call(6, state16=0, sT=a["s0"] + half) == 3
+
+
+def test_decode_slots_validate(kda_lib):
+    lib = kda_lib
+    N, H, n_slots = 4, 2, 10
+    base, addr = 1 << 40, {}
+    size = dict(q=N * H * 256, k=N * H * 256, v=N * H * 256, g=N * H * 512, beta=N * H * 4,
+                state=n_slots * H * 65536, slots=N * 4, out=N * H * 256)
+    for name in ("q", "k", "v", "g", "beta", "state", "slots", "out"):
+        addr[name] = base
+        base += (size[name] + 4096) // 256 * 256
+    P = lambda x: ctypes.c_void_p(x) if x else None
+
+    def call(ns=n_slots, **o):
+        a = dict(addr, **o)
+        return lib.kda_decode_slots_validate(N, H, H, 128, 128, P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]),
+                                             P(a["beta"]), ctypes.c_float(1.0), P(a["state"]), ns, P(a["slots"]),
+                                             P(a["out"]))
+    assert call() == 0
+    assert call(ns=-1) == 1
+    assert call(slots=0) == 1 and b"without a slot table" in lib.kda_last_error()   # n_slots != N
+    assert call(ns=N, slots=0) == 0
+    assert call(slots=addr["slots"] + 2) == 1
+    assert call(slots=addr["state"] + 4096) == 3      # the table may not live inside the pool
+    assert call(out=addr["state"] + 65536 * 9) == 3
