@@ -310,3 +310,13 @@ def test_decode_slots_validate(kda_lib):
     assert call(slots=addr["slots"] + 2) == 1
     assert call(slots=addr["state"] + 4096) == 3      # the table may not live inside the pool
     assert call(out=addr["state"] + 65536 * 9) == 3
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message before
+    touching any device."""
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr
