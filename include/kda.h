@@ -137,6 +137,12 @@ kda_status kda_plan_prefill_segments(kda_ctx *ctx, const int32_t *cu_seqlens_hos
 
 void kda_plan_destroy(kda_plan *plan);
 
+/* Bytes of the per-stream workspace arena that kda_prefill needs for this
+ * plan (0 for NULL), so that a caller can warm the arena up before graph
+ * capture. kda_prefill_ex with a bf16 beta needs 4 * Tt * H bytes more,
+ * after this much rounded up to 256. */
+size_t kda_plan_workspace_bytes(const kda_plan *plan);
+
 /* Plan summary; returns KDA_ERR_INVALID for NULL arguments. */
 kda_status kda_plan_get_info(const kda_plan *plan, kda_plan_info *info);
 

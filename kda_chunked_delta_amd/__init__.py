@@ -90,6 +90,7 @@ def lib():
                 "kda_plan_prefill_segments": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, PP]),
                 "kda_plan_destroy": (None, [P]),
                 "kda_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(PlanInfo)]),
+                "kda_plan_workspace_bytes": (ctypes.c_size_t, [P]),
                 "kda_plan_get_units": (ctypes.c_int, [P, ctypes.POINTER(UnitInfo), I32]),
                 "kda_prefill_validate": (ctypes.c_int, [P, P, P, P, P, P, P, F32, P, P, P]),
                 "kda_prefill": (ctypes.c_int, [P, P, P, P, P, P, P, P, F32, P, P, P, P]),

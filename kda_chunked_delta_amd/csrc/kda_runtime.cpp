@@ -448,6 +448,8 @@ void kda_plan_destroy(kda_plan* p) {
     delete p;
 }
 
+size_t kda_plan_workspace_bytes(const kda_plan* p) { return p ? p->info.workspace_bytes : 0; }
+
 kda_status kda_plan_get_info(const kda_plan* p, kda_plan_info* info) {
     if (!p || !info) return fail(KDA_ERR_INVALID, "kda_plan_get_info: NULL argument");
     *info = p->info;

@@ -320,3 +320,13 @@ def test_bench_refuses_several_gpus():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_plan_workspace_bytes(kda_lib, monkeypatch):
+    p = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp="auto")
+    info = p.info()
+    assert info["uses_cp"] and info["workspace_bytes"] > 0
+    assert kda_lib.kda_plan_workspace_bytes(p.handle) == info["workspace_bytes"]
+    assert kda_lib.kda_plan_workspace_bytes(None) == 0
+    serial = kda.plan_host([0, 100, 300], H=4, n_cus=256)
+    assert kda_lib.kda_plan_workspace_bytes(serial.handle) == 0
