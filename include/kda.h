@@ -289,7 +289,7 @@ kda_status kda_prefill_ex_validate(const kda_plan *plan, const kda_prefill_opts 
  *   [12288, 16384) V (the chunk's values): [n 8][slot 64][j 4]; slot s(l) holds
  *                  lane l's V[4g + j][16n + i]
  *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]
- *   [16896, 17408) exp(G_C): fp32 [128]
+ *   [16896, 17408) exp(G_C): fp32 [128], channel 16t + 4g + j at position 32g + 4t + j
  *   [17408, 18432) T' = (I + L)^-1 diag(beta), L = strict-lower(diag(beta) A_kk),
  *                  as a bf16 pair hi + lo: [2][lane 64][j 4] = T'[i][4g + j]
  * K2 forms U = T' (V - X S) (= U~ - W S in WY terms), then O = Qt S + A_qk U

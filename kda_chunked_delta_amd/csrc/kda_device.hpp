@@ -42,7 +42,9 @@ constexpr int CH = 16;   // chunk length
 //   REC_V  : V in accumulator layout [n 8][slot 64][4 bf16]: lane l's
 //            V[4gg + j][16n + m] in slot kv_slot(l)
 //   REC_AQK: A_qk fragment [lane 64][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
-//   REC_GC : exp(G_C) [128] fp32
+//   REC_GC : exp(G_C) [128] fp32, channel c = 16t + 4gg + v at position
+//            32gg + 4t + v: lane (gg, m) of a state wavefront reads the pair
+//            at 2 * lane, which holds channels 16(m >> 1) + 4gg + 2(m & 1) + 0..1
 //   REC_T  : T' fragments, hi then lo [2][lane 64][4 bf16]: T'[m][4gg + j]
 // The same bytes are used in LDS and, when K1 is materialised, in HBM.
 // ---------------------------------------------------------------------------
@@ -57,8 +59,9 @@ constexpr int REC_BYTES = 18432;
 constexpr int REC_VEC = REC_BYTES / 16;  // 1152 16-byte vectors
 
 // K1 scratch of one chunk (LDS only), from phase 1 to phase 2:
-//   K1_KA, K1_KB, K1_QA: beta k exp(G - G_7), k exp(G_7 - G), q exp(G - G_7)
-//                        as fragments in the REC_Q layout
+//   K1_KA, K1_KB, K1_QA: the Gram factors k exp(G - G_ref), k exp(G_ref - G),
+//                        q exp(G - G_ref) as fragments in the REC_Q layout,
+//                        with G_ref = 0 (the chunk start) or G_7 (see k1_phase1)
 //   K1_BETA            : beta of the chunk's 16 rows, fp32
 constexpr int K1_KA = 0;
 constexpr int K1_KB = 4096;
@@ -322,6 +325,11 @@ __device__ __forceinline__ void k1_read_staged(const uint8_t* stg, int lane, con
     raw.b = *(const float*)(stg + STG_B + 4 * (lane & 15));
 }
 
+// Largest |G| (log2 units) for which phase 1 factors the decays about the
+// chunk start: exp(G) and exp(-G) are then normal fp32 and bf16 values, and
+// the unmasked Gram terms exp(G_r - G_i) (i <= r) are at most 1.
+constexpr float G_FACTOR0_MAX = 100.0f;
+
 __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lane, uint8_t* rec,
                                           uint8_t* scr) {
     const int gg = lane >> 4, m = lane & 15;
@@ -336,40 +344,72 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
         x += row_shr<8>(x);
         G[j] = x;
     }
-    float g7[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) g7[j] = row_newbcast<7>(G[j]);
-    // decays relative to the reference row 7: E = exp(G - G_7), F = exp(G_7 - G);
-    // gam = exp(G)
-    float E[4], F[4], gam[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        E[j] = exp2_hw(G[j] - g7[j]);
-        F[j] = exp2_hw(g7[j] - G[j]);
-        gam[j] = exp2_hw(G[j]);
-    }
-    float e15[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) e15[j] = row_newbcast<15>(E[j]);  // exp(G_C - G_7)
     const float qf[4] = {bf16_lo(raw.q.x), bf16_hi(raw.q.x), bf16_lo(raw.q.y), bf16_hi(raw.q.y)};
     const float kf[4] = {bf16_lo(raw.k.x), bf16_hi(raw.k.x), bf16_lo(raw.k.y), bf16_hi(raw.k.y)};
-    f32x4 ka, kb, qa, qt, xk, kt;
+    // The Grams need k_r k_i exp(G_r - G_i) (and q_r k_i ...) as a product of
+    // a row factor and a column factor. Factored about the chunk start, the
+    // row factors are the chain's own operands X = k exp(G) and
+    // Qt = q exp(G), and the column factor is k exp(-G): two exponentials
+    // and four products per element. That needs |G| within G_FACTOR0_MAX
+    // over the wavefront's channels; otherwise (decay beyond about e^-69
+    // inside one chunk) the wavefront factors about row 7 instead, which
+    // only needs |G - G_7| within the fp32 exponent range. The choice is
+    // uniform per wavefront and per chunk, and a function of g alone.
+    const float amax = fmaxf(fmaxf(fabsf(G[0]), fabsf(G[1])), fmaxf(fabsf(G[2]), fabsf(G[3])));
+    const bool about_row7 = __builtin_amdgcn_ballot_w64(!(amax <= G_FACTOR0_MAX)) != 0;
+    float gam[4];  // exp(G)
+    u32x2 pka, pkb, pqa, pqt, pxk, pkt;
+    if (!about_row7) {
+        f32x4 kb, qt, xk, kt;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ka[j] = raw.b * (kf[j] * E[j]);
-        kb[j] = kf[j] * F[j];
-        qa[j] = qf[j] * E[j];
-        qt[j] = qf[j] * gam[j];
-        xk[j] = kf[j] * gam[j];
-        kt[j] = kb[j] * e15[j];  // k exp(G_C - G)
+        for (int j = 0; j < 4; ++j) {
+            gam[j] = exp2_hw(G[j]);
+            const float ig = exp2_hw(-G[j]);
+            qt[j] = qf[j] * gam[j];
+            xk[j] = kf[j] * gam[j];
+            kb[j] = kf[j] * ig;
+            kt[j] = kb[j] * row_newbcast<15>(gam[j]);  // k exp(G_C - G)
+        }
+        pqt = pack4(qt);
+        pxk = pack4(xk);
+        pkb = pack4(kb);
+        pkt = pack4(kt);
+        pka = pxk;
+        pqa = pqt;
+    } else {
+        // E = exp(G - G_7), F = exp(G_7 - G)
+        float E[4], F[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float g7 = row_newbcast<7>(G[j]);
+            E[j] = exp2_hw(G[j] - g7);
+            F[j] = exp2_hw(g7 - G[j]);
+            gam[j] = exp2_hw(G[j]);
+        }
+        f32x4 ka, kb, qa, qt, xk, kt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ka[j] = kf[j] * E[j];
+            kb[j] = kf[j] * F[j];
+            qa[j] = qf[j] * E[j];
+            qt[j] = qf[j] * gam[j];
+            xk[j] = kf[j] * gam[j];
+            kt[j] = kb[j] * row_newbcast<15>(E[j]);  // k exp(G_C - G)
+        }
+        pka = pack4(ka);
+        pkb = pack4(kb);
+        pqa = pack4(qa);
+        pqt = pack4(qt);
+        pxk = pack4(xk);
+        pkt = pack4(kt);
     }
     // fragments in the REC_Q layout: half (wave & 1) of K-step (wave >> 1)
     const int fo = (wave >> 1) * 1024 + lane * 16 + (wave & 1) * 8;
-    *(u32x2*)(scr + K1_KA + fo) = pack4(ka);
-    *(u32x2*)(scr + K1_KB + fo) = pack4(kb);
-    *(u32x2*)(scr + K1_QA + fo) = pack4(qa);
-    *(u32x2*)(rec + REC_Q + fo) = pack4(qt);
-    *(u32x2*)(rec + REC_X + fo) = pack4(xk);
+    *(u32x2*)(scr + K1_KA + fo) = pka;
+    *(u32x2*)(scr + K1_KB + fo) = pkb;
+    *(u32x2*)(scr + K1_QA + fo) = pqa;
+    *(u32x2*)(rec + REC_Q + fo) = pqt;
+    *(u32x2*)(rec + REC_X + fo) = pxk;
     // Kt^T and V: element (token m, channel 16 wave + 4gg + j) -> tile wave,
     // lane (m >> 2) * 16 + 4gg + j, slot m & 3
     // lane (m >> 2) * 16 + 4gg + j sits in slot kv_slot of that lane:
@@ -377,7 +417,7 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     const int a4 = m >> 2;
     const int to = wave * 512 + tfrag_off(gg, m);
     const int s0 = (a4 & 3) * 8, s1 = ((a4 + 1) & 3) * 8, s2 = ((a4 + 2) & 3) * 8, s3 = ((a4 + 3) & 3) * 8;
-    const u32x2 ktp = pack4(kt);
+    const u32x2 ktp = pkt;
     uint8_t* kd = rec + REC_KT + to;
     uint8_t* vd = rec + REC_V + to;
     *(uint16_t*)(kd + s0) = (uint16_t)ktp.x;
@@ -389,7 +429,7 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     *(uint16_t*)(vd + s2) = (uint16_t)raw.v.y;
     *(uint16_t*)(vd + s3) = (uint16_t)(raw.v.y >> 16);
     // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
-    if (m == 15) *(f32x4*)(rec + REC_GC + (16 * wave + 4 * gg) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
+    if (m == 15) *(f32x4*)(rec + REC_GC + (32 * gg + 4 * wave) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     if (wave == 0 && gg == 0) *(float*)(scr + K1_BETA + 4 * m) = raw.b;
 }
 
@@ -404,15 +444,17 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, const uint8_t* scr, float* lw) {
     const int gg = lane >> 4, m = lane & 15;
-    // (beta k exp(G - G_7)) (k exp(G_7 - G))^T: lane holds beta_r A_kk[r][m], r = 4gg + v
+    // (k exp(G - G_ref)) (k exp(G_ref - G))^T: lane holds A_kk[r][m], r = 4gg + v,
+    // which the row's beta then scales
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 4; ++p)
         a = mfma_k32(*(const u32x4*)(scr + K1_KA + p * 1024 + lane * 16),
                      *(const u32x4*)(scr + K1_KB + p * 1024 + lane * 16), a);
+    const f32x4 br = *(const f32x4*)(scr + K1_BETA + 16 * gg);
     f32x4 l;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) l[v] = (m < 4 * gg + v) ? a[v] : 0.f;
+    for (int v = 0; v < 4; ++v) l[v] = (m < 4 * gg + v) ? br[v] * a[v] : 0.f;
     // through LDS as L^T (lw[c * K1_LSTRIDE + r] = L[r][c]): lane (gg, i) then holds
     // column i of L, lc[K] = L[K][i]
     *(f32x4*)(lw + m * K1_LSTRIDE + 4 * gg) = l;
@@ -452,7 +494,7 @@ __device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, cons
 
 __device__ __forceinline__ void k1_phase2_qk(int lane, uint8_t* rec, const uint8_t* scr) {
     const int gg = lane >> 4, m = lane & 15;
-    // A_qk^T = (k exp(G_7 - G)) (q exp(G - G_7))^T: lane holds A_qk[m][4gg + v]
+    // A_qk^T = (k exp(G_ref - G)) (q exp(G - G_ref))^T: lane holds A_qk[m][4gg + v]
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -543,17 +585,27 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
 #pragma unroll
         for (int n = 0; n < NT; ++n) oacc[n] += mfma_k16(Ub[n], aq, f32x4{0.f, 0.f, 0.f, 0.f});
     }
-    // S_next = Diag(exp G_C) S0 + Kt^T U
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const f32x4 gcv = *(const f32x4*)(rec + REC_GC + (16 * t + 4 * gg) * 4);
+    // S_next = Diag(exp G_C) S0 + Kt^T U. Lane (gg, m) holds exp(G_C) of
+    // channels 16(m >> 1) + 4gg + 2(m & 1) + 0..1; row 4gg + v of tile t
+    // takes it from lane 2t + (v >> 1) of its 16-lane row (a DPP broadcast
+    // folded into the multiply), so the wavefront reads 512 bytes instead
+    // of 32 values per lane.
+    const f32x2 gcp = *(const f32x2*)(rec + REC_GC + lane * 8);
+    auto decay = [&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        const f32x4 gcv = {row_newbcast<2 * t>(gcp[0]), row_newbcast<2 * t>(gcp[1]),
+                           row_newbcast<2 * t + 1>(gcp[0]), row_newbcast<2 * t + 1>(gcp[1])};
         const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + kv_slot(lane) * 8);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             S[t][n] = gcv * S[t][n];
             S[t][n] = mfma_k16(kt, Ub[n], S[t][n]);
         }
-    }
+    };
+    decay(std::integral_constant<int, 0>{}); decay(std::integral_constant<int, 1>{});
+    decay(std::integral_constant<int, 2>{}); decay(std::integral_constant<int, 3>{});
+    decay(std::integral_constant<int, 4>{}); decay(std::integral_constant<int, 5>{});
+    decay(std::integral_constant<int, 6>{}); decay(std::integral_constant<int, 7>{});
 }
 
 }  // namespace kda

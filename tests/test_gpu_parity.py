@@ -150,7 +150,10 @@ def decode_records(rec):
     for j in range(4):
         x[i, 4 * g + j] = a[:, j]
     out["A_qk"] = x
-    out["gC"] = r[16896:17408].view(np.float32).copy()
+    # exp(G_C): channel c = 16t + 4g + j at position 32g + 4t + j
+    gcp = r[16896:17408].view(np.float32)
+    c = np.arange(128)
+    out["gC"] = gcp[32 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3)].copy()
     t = bf(r[17408:18432].view(np.uint16).reshape(2, 64, 4)).astype(np.float64)
     x = np.zeros((16, 16))
     for j in range(4):
@@ -323,6 +326,40 @@ def test_cp_weak_decay_within_tolerance():
     assert_close("out(cp)", o_cp, o_ref)
     assert_close("final(cp)", s_cp, s_ref)
     assert_close("out(serial)", o_ser, o_ref)
+
+
+def test_steep_in_chunk_decay_matches_oracle(monkeypatch):
+    """Decay steps of e^-40 at rows 0 and 8 of every chunk, on the key
+    channels of two of the eight K1 wavefronts of the second sequence: the
+    in-chunk decay there (e^-80) is past what the chunk-start factoring of
+    the Grams can hold, so those wavefronts factor about row 7, while the
+    rows between the steps still interact fully. The other channels and the
+    first sequence keep ordinary decay. Fused serial, materialised K1 and
+    forced CP all match the oracle."""
+    d = draw([40, 70], 3, seed=31, state_std=0.1, device=DEV)
+    cu = d["cu_seqlens_host"]
+    g = d["g"].clone()
+    t = torch.arange(cu[1], cu[2], device=DEV)
+    steep = ((t - cu[1]) % 8 == 0)
+    rows = t[steep]
+    g[cu[1]:cu[2], :, 16:32] = -0.01
+    g[cu[1]:cu[2], :, 96:112] = -0.02
+    for c0, c1 in ((16, 32), (96, 112)):
+        g[rows, :, c0:c1] = -40.0
+    d["g"] = g
+    o_ref, s_ref = oracle(d)
+    o, s = run(d)
+    assert_close("out(fused)", o, o_ref)
+    assert_close("final(fused)", s, s_ref)
+    monkeypatch.setenv("KDA_MATERIALIZE_K1", "1")
+    p_ser = kda.plan(cu, 3, False, device=DEV)
+    monkeypatch.delenv("KDA_MATERIALIZE_K1")
+    o1, s1 = run(d, plan=p_ser)
+    assert torch.equal(o1, o) and torch.equal(s1, s), "materialised K1 differs from fused"
+    p_cp = kda.plan_segments(cu, 3, 2, device=DEV)
+    o2, s2 = run(d, plan=p_cp)
+    assert_close("out(cp)", o2, o_ref)
+    assert_close("final(cp)", s2, s_ref)
 
 
 # ---------------------------------------------------------------------------
