@@ -112,11 +112,22 @@ def cpu_baseline(d, max_seconds):
                       % (nseq, len(cu) - 1, T, H, dt)}
 
 
+def plan_kind(info):
+    if info["uses_cp"]:
+        return "cp"
+    if info.get("n_split_seqs", 0) > 0:
+        return "split(%d sequences, warm-up %d chunks)" % (info["n_split_seqs"], info["split_warm_chunks"])
+    return "serial"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # a step is well under a millisecond; the GPU's clocks take tens of
+    # milliseconds of work to settle, so the defaults warm up and time a few
+    # hundred steps (still well under a second of GPU time)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="varlen8_h32", choices=sorted(WORKLOAD_TEXT) + sorted(DECODE_TEXT))
     ap.add_argument("--cp", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
@@ -166,7 +177,7 @@ def main():
                     cu_seqlens_host=cu, initial_state=s0, final_state=s_out, out=o, plan=plan)
 
     print("bench: workload %s Tt=%d H=%d plan=%s units=%d" % (args.workload, Tt, H,
-          "cp" if info["uses_cp"] else "serial", info["n_units"]), file=sys.stderr, flush=True)
+          plan_kind(info), info["n_units"]), file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -218,7 +229,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (args.workload, WORKLOAD_TEXT[args.workload]), "tokens": Tt,
                    "heads": H, "head_dim": 128, "sequences": N, "lengths": d["lengths"],
-                   "plan": "cp" if info["uses_cp"] else "serial", "cp_mode": args.cp},
+                   "plan": plan_kind(info), "cp_mode": args.cp},
         "roofline": roofline,
         "mfma_roofline": {"bound": "mfma", "achieved": round(alg_flops / (path_ms * 1e-3) / 1e12, 2),
                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4)},

@@ -84,6 +84,12 @@ typedef struct {
                                   KDA_MATERIALIZE_K1=1 in the environment); 0: serial
                                   plan whose fused kernel recomputes K1 per chunk in LDS
                                   (the default for serial plans) */
+    int32_t n_split_seqs;      /* sequences run as a first segment plus a warm-start
+                                  segment (see kda_plan_prefill_split); AUTO plans
+                                  choose these when the longest sequences would
+                                  otherwise leave the compute units idle at the end */
+    int32_t split_warm_chunks; /* warm-up chunks of each warm-start segment */
+    double  est_split_us;      /* planner's estimate of the split plan (-1: none) */
 } kda_plan_info;
 
 /* One K2 work unit of a plan (a whole sequence, or one segment of it). */
@@ -93,6 +99,7 @@ typedef struct {
     int32_t n_chunks;     /* chunks in the unit (0 for an empty sequence) */
     int32_t segment;      /* segment index within its sequence (0 if serial) */
     int32_t n_segments;   /* segments of its sequence (1 if serial) */
+    int32_t warm_chunks;  /* warm-up chunks run before chunk0 (warm-start segment), else 0 */
 } kda_unit_info;
 
 /* Create a context on HIP device `device`: caches the device properties
@@ -134,6 +141,24 @@ kda_status kda_plan_prefill_host(int32_t n_cus, const int32_t *cu_seqlens_host, 
 kda_status kda_plan_prefill_segments(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
                                      int32_t H, int32_t dk, int32_t dv, int32_t seg_chunks,
                                      kda_plan **out);
+
+/* A plan that splits sequence i at chunk split_chunk[i] (0: not split) into
+ * two segments run side by side in the fused serial kernel, the intracard
+ * context parallelism of "feat(kda/sm90): FlashKDA prefill port +
+ * intracard-CP prefill" (cuLA pull request #103, description) without its
+ * separate pre_scan and merge passes. The first segment runs from the initial
+ * state. The second, a warm-start segment, first runs the warm_chunks chunks
+ * before its start twice: as the transfer M from the identity with V := 0,
+ * and as the state B from zero. Where every tile of M is exactly zero, B is
+ * its carry, exactly as the CP merge takes it; otherwise a fix-up launch
+ * reruns the segment from the first segment's end state. Either way the
+ * result equals the unsplit serial path's bit for bit wherever the CP
+ * path's does. split_chunk[i] must be 0 or in [warm_chunks, chunks of
+ * sequence i). AUTO plans (kda_plan_prefill) pick such splits themselves.
+ * Device tables are uploaded as in kda_plan_prefill. */
+kda_status kda_plan_prefill_split(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
+                                  int32_t H, int32_t dk, int32_t dv, const int32_t *split_chunk,
+                                  int32_t warm_chunks, kda_plan **out);
 
 void kda_plan_destroy(kda_plan *plan);
 

@@ -50,7 +50,9 @@ class PlanInfo(ctypes.Structure):
                 ("n_prescan", ctypes.c_int32), ("n_carry_slots", ctypes.c_int32),
                 ("max_unit_chunks", ctypes.c_int32), ("n_cus", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t), ("est_serial_us", ctypes.c_double),
-                ("est_cp_us", ctypes.c_double), ("k1_materialized", ctypes.c_int32)]
+                ("est_cp_us", ctypes.c_double), ("k1_materialized", ctypes.c_int32),
+                ("n_split_seqs", ctypes.c_int32), ("split_warm_chunks", ctypes.c_int32),
+                ("est_split_us", ctypes.c_double)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -62,7 +64,8 @@ class PrefillOpts(ctypes.Structure):
 
 class UnitInfo(ctypes.Structure):
     _fields_ = [("seq", ctypes.c_int32), ("chunk0", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
-                ("segment", ctypes.c_int32), ("n_segments", ctypes.c_int32)]
+                ("segment", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("warm_chunks", ctypes.c_int32)]
 
 
 _lib = None
@@ -88,6 +91,7 @@ def lib():
                 "kda_plan_prefill": (ctypes.c_int, [P, P, I32, I32, I32, I32, ctypes.c_int, PP]),
                 "kda_plan_prefill_host": (ctypes.c_int, [I32, P, I32, I32, I32, I32, ctypes.c_int, PP]),
                 "kda_plan_prefill_segments": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, PP]),
+                "kda_plan_prefill_split": (ctypes.c_int, [P, P, I32, I32, I32, I32, P, I32, PP]),
                 "kda_plan_destroy": (None, [P]),
                 "kda_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(PlanInfo)]),
                 "kda_plan_workspace_bytes": (ctypes.c_size_t, [P]),
@@ -225,7 +229,7 @@ class Plan:
         arr = (UnitInfo * max(n, 1))()
         _check(lib().kda_plan_get_units(self.handle, arr, n), "kda_plan_get_units")
         return [dict(seq=u.seq, chunk0=u.chunk0, n_chunks=u.n_chunks, segment=u.segment,
-                     n_segments=u.n_segments) for u in arr[:n]]
+                     n_segments=u.n_segments, warm_chunks=u.warm_chunks) for u in arr[:n]]
 
     def cu_device(self):
         import torch
@@ -260,6 +264,20 @@ def plan_segments(cu_seqlens, H, seg_chunks, device=None):
     h = ctypes.c_void_p()
     _check(lib().kda_plan_prefill_segments(ctx.handle, arr, n, int(H), D, D, int(seg_chunks),
                                            ctypes.byref(h)), "kda_plan_prefill_segments")
+    return Plan(h, cu_seqlens, ctx.device)
+
+
+def plan_split(cu_seqlens, H, split_chunk, warm_chunks, device=None):
+    """Executable plan with forced warm-start splits: sequence i is split at
+    chunk split_chunk[i] (0: not split)."""
+    ctx = context(device)
+    arr, n = _cu_array(cu_seqlens)
+    if len(split_chunk) != n:
+        raise ValueError("split_chunk needs one entry per sequence (%d), got %d" % (n, len(split_chunk)))
+    sp = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in split_chunk])
+    h = ctypes.c_void_p()
+    _check(lib().kda_plan_prefill_split(ctx.handle, arr, n, int(H), D, D, sp, int(warm_chunks),
+                                        ctypes.byref(h)), "kda_plan_prefill_split")
     return Plan(h, cu_seqlens, ctx.device)
 
 

@@ -292,19 +292,45 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     const int w8 = __builtin_amdgcn_readfirstlane(wave & 7);
     int64_t beg, end;
     seq_bounds(a.c, u.seq, beg, end);
+    if (a.fixup) {
+        // fix-up launch over warm-start segments: the segment stands as
+        // computed when every tile of its warm-up transfer was exactly zero
+        const int32_t* fl = a.spec_flags + ((size_t)u.spec * H + h) * 8;
+        int live = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) live |= fl[j];
+        if (!live) {
+            if (!a.spec_final_direct && u.write_final && a.sT) {
+                const float* src = a.spec_states + ((size_t)u.spec * H + h) * (D * D);
+                const size_t off = ((size_t)u.seq * H + h) * (D * D);
+                for (int i = threadIdx.x; i < D * D; i += blockDim.x) {
+                    if (a.state_bf16) ((uint16_t*)a.sT)[off + i] = (uint16_t)pack_bf16(src[i], 0.f);
+                    else ((float*)a.sT)[off + i] = src[i];
+                }
+            }
+            return;
+        }
+    }
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
     const int nc = u.n_chunks;
-    const int n_int = (nc + 3) & ~1;  // barrier intervals i = -2 .. n_int - 3
+    // A warm-start segment runs `warm` chunks twice before its own: steps
+    // 0 .. W-1 form the transfer over chunks chunk0-W .. chunk0-1, steps
+    // W .. 2W-1 the state from zero over the same chunks, and step 2W + c
+    // is chunk chunk0 + c.
+    const int W = u.warm;
+    const int n_steps = nc + 2 * W;
+    const int n_int = (n_steps + 3) & ~1;  // barrier intervals i = -2 .. n_int - 3
     if (wave < 8) {
         // state wavefronts
         f32x4 S[8][1];
-        load_unit_state(a, u, h, S, w8, gg, m);
+        if (W > 0) identity_state(S, w8, gg, m);
+        else load_unit_state(a, u, h, S, w8, gg, m);
         lds_barrier();  // start-up: the first chunk is staged
         const int rem = (int)(end - tok0);
-        auto step = [&](int i) __attribute__((always_inline)) {
+        auto step = [&](int c, int i) __attribute__((always_inline)) {
             f32x4 oacc[1];
             chain_step<1, true, true>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, oacc);
-            store_output(a, h, tok0 + (int64_t)CH * i, chunk_rows(rem, i), oacc[0], w8, gg, m);
+            store_output(a, h, tok0 + (int64_t)CH * c, chunk_rows(rem, c), oacc[0], w8, gg, m);
         };
         // one loop per phase-2 role (0: none, 1: rows 4 w8.. of T', 2: A_qk),
         // so that each loop body is one block in which phase 2 of chunk i + 1
@@ -320,27 +346,52 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
             lds_barrier();  // interval -2: nothing to do yet
             p2(0);
             lds_barrier();  // interval -1
-            for (int i = 0; i < nc; ++i) {
+            if (W > 0) {
+                f32x4 unused[1];
+                for (int i = 0; i < W; ++i) {
+                    p2(i + 1);
+                    chain_step<1, false, false>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, unused);
+                    lds_barrier();
+                }
+                const bool live = tile_nonzero(S);
+                if (lane == 0) a.spec_flags[((size_t)u.spec * H + h) * 8 + w8] = live ? 1 : 0;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) S[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int i = W; i < 2 * W; ++i) {
+                    p2(i + 1);
+                    chain_step<1, true, false>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, unused);
+                    lds_barrier();
+                }
+            }
+            for (int i = 2 * W; i < n_steps; ++i) {
                 p2(i + 1);
-                step(i);
+                step(i - 2 * W, i);
                 lds_barrier();
             }
-            for (int i = nc; i < n_int - 2; ++i) lds_barrier();
+            for (int i = n_steps; i < n_int - 2; ++i) lds_barrier();
         };
         if (!P2_ON_STATE) run(std::integral_constant<int, 0>{});
         else if (w8 < N_WAVE_T) run(std::integral_constant<int, 1>{});
         else if (w8 == WAVE_QK) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 0>{});
-        store_unit_state(a, u, h, S, w8, gg, m);
+        if (u.out_slot >= 0) store_state(a.carries + ((size_t)u.out_slot * H + h) * (D * D), S, w8, gg, m);
+        if (u.spec >= 0 && !a.fixup && !a.spec_final_direct)
+            store_state(a.spec_states + ((size_t)u.spec * H + h) * (D * D), S, w8, gg, m);
+        else
+            store_unit_state(a, u, h, S, w8, gg, m);
     } else {
         // K1 wavefronts: chunk c is loaded into register set c & 1
         RowChunk r0, r1;
         const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, w8, lane);
-        const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0, h,
+        // rows from the first chunk the unit runs (its warm-up, if any)
+        const int64_t tok_k1 = tok0 - (int64_t)CH * W;
+        const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok_k1, h,
                                           h / a.c.group, w8);
-        // tokens of the sequence from the unit's first one (sequences are < 2^31 tokens)
-        const int rem = (int)(end - tok0);
-        auto load = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
+        // tokens of the sequence from that chunk on (sequences are < 2^31 tokens)
+        const int rem = (int)(end - tok_k1);
+        // step i -> chunk from tok_k1 (the warm-up chunks come twice)
+        auto load = [&](RowChunk& rc, int i) __attribute__((always_inline)) {
+            const int ci = i >= W ? i - W : i;
             k1_load_chunk<GVA>(rs, ci, chunk_rows(rem, ci), lo, rc);
         };
         auto stage = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {

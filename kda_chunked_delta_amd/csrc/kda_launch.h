@@ -24,6 +24,16 @@ struct UnitDesc {
     int32_t write_final; // 1: write final_state[seq] at the end
     int32_t segment;     // segment index within the sequence
     int32_t n_segments;  // segments of the sequence
+    // Warm-start segment (fused kernel only): the unit first runs the `warm`
+    // chunks before chunk0 twice, once as the transfer M (from the identity,
+    // V := 0) and once as the state from zero, and then continues from that
+    // state as if it were its carry. spec >= 0 names its slot of
+    // speculation flags and end state; out_slot >= 0 makes a unit write its
+    // end state to carries[out_slot] as well.
+    int32_t warm;
+    int32_t spec;
+    int32_t out_slot;
+    int32_t pad;
 };
 
 // CP pre_scan item: one segment whose (M, B) summary feeds the merge.
@@ -66,10 +76,23 @@ struct K2Args {
     int32_t n_units;
     const void* s0;      // may be null; fp32, or bf16 when state_bf16
     void* sT;            // may be null; fp32, or bf16 when state_bf16
-    const float* carries;
+    float* carries;      // [slots][H][128][128] fp32: read by in_slot, written by out_slot
     uint16_t* out;
     float scale;
     int32_t state_bf16;  // initial and final states are bf16
+    // Warm-start segments: per (spec slot, head), one flag per 16-column tile
+    // of the warm-up transfer (1 when that tile of M is not exactly zero)
+    // and the segment's end state.
+    int32_t* spec_flags;  // [spec slots][H][8]
+    float* spec_states;   // [spec slots][H][128][128] fp32
+    // Fix-up launch over warm-start segments: a unit whose warm-up transfer
+    // was exactly zero copies its end state to the final state and stops;
+    // any other reruns from its carry.
+    int32_t fixup;
+    // the warm-start segments write the final state themselves (it does not
+    // alias the initial state, which other units may still read); else they
+    // leave their end state in spec_states for the fix-up launch to publish
+    int32_t spec_final_direct;
 };
 
 struct PrescanArgs {

@@ -70,6 +70,11 @@ struct PlannerConsts {
     int min_seg_chunks;  // shortest segment the planner will form
     int prescan_per_cu;  // concurrent pre_scan workgroups per CU
     int rec_per_cu;      // concurrent K2-over-records workgroups per CU
+    // fused kernel interval per chunk against the fraction of busy CUs:
+    // alone_us with few busy, full_us with all busy, in between the shape
+    // measured on MI355X (the shader clock falls as more CUs work)
+    double alone_us, full_us;
+    int split_warm;      // warm-up chunks of a warm-start segment
 };
 
 PlannerConsts planner_consts() {
@@ -83,7 +88,50 @@ PlannerConsts planner_consts() {
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
     c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
     c.rec_per_cu = (int)env_double("KDA_CP_REC_PER_CU", 2.0);
+    c.alone_us = env_double("KDA_FUSED_CHUNK_US_ALONE", 1.31);
+    c.full_us = env_double("KDA_FUSED_CHUNK_US_FULL", 1.92);
+    c.split_warm = (int)env_double("KDA_SPLIT_WARM_CHUNKS", 12.0);
     return c;
+}
+
+// Interval of the fused kernel per chunk with `busy` of n_cus CUs working.
+double fused_interval_us(int busy, int n_cus, const PlannerConsts& pc) {
+    static const double xs[] = {0.0, 0.125, 0.25, 0.5, 0.75, 1.0};
+    static const double ys[] = {0.0, 0.016, 0.08, 0.26, 0.61, 1.0};
+    const double x = std::min(1.0, std::max(0.0, (double)busy / n_cus));
+    int i = 0;
+    while (i < 4 && x > xs[i + 1]) ++i;
+    const double phi = ys[i] + (ys[i + 1] - ys[i]) * (x - xs[i]) / (xs[i + 1] - xs[i]);
+    return pc.alone_us + (pc.full_us - pc.alone_us) * phi;
+}
+
+// Time of the fused kernel over work units of the given chunk counts,
+// started longest first on n_cus CUs (one workgroup per CU), every running
+// unit advancing one chunk per interval at the current occupancy.
+double simulate_fused_us(std::vector<int> work, int n_cus, const PlannerConsts& pc) {
+    std::sort(work.begin(), work.end(), std::greater<int>());
+    std::vector<double> heap;  // finish progress of running units (min-heap)
+    auto cmp = std::greater<double>();
+    size_t next = 0;
+    double progress = 0.0, t = 0.0;
+    while (next < work.size() && (int)heap.size() < n_cus) {
+        heap.push_back((double)work[next++]);
+        std::push_heap(heap.begin(), heap.end(), cmp);
+    }
+    while (!heap.empty()) {
+        const double f = heap.front();
+        t += (f - progress) * fused_interval_us((int)heap.size(), n_cus, pc);
+        progress = f;
+        while (!heap.empty() && heap.front() <= progress) {
+            std::pop_heap(heap.begin(), heap.end(), cmp);
+            heap.pop_back();
+        }
+        while (next < work.size() && (int)heap.size() < n_cus) {
+            heap.push_back(progress + work[next++]);
+            std::push_heap(heap.begin(), heap.end(), cmp);
+        }
+    }
+    return t;
 }
 
 }  // namespace
@@ -98,12 +146,14 @@ struct kda_plan {
     std::vector<UnitDesc> units;        // K2 units, launch order
     std::vector<PrescanDesc> prescan;   // CP pre_scan items
     std::vector<MergeDesc> merges;      // CP merge items
+    std::vector<UnitDesc> fixups;       // warm-start segments, as rerun from their carry
     // workspace layout (byte offsets into the arena)
     size_t off_rec = 0, off_b = 0, off_m = 0, off_mlive = 0, off_carry = 0;
+    size_t off_spec_states = 0, off_spec_flags = 0;
     // device copy of the tables
     int device = -1;
     void* dev_tables = nullptr;
-    size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_prescan = 0, dev_off_merges = 0;
+    size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_prescan = 0, dev_off_merges = 0, dev_off_fixups = 0;
 };
 
 namespace {
@@ -145,10 +195,66 @@ double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const Plan
     return t_k1 + t_pre + t_merge + t_k2 + 4 * pc.launch_us;
 }
 
-// seg_chunks > 0 forces that segment length on every longer sequence.
+// Fused work of each unit when sequence i is split at chunk split[i]
+// (0: not split): the first segment runs split[i] chunks, the warm-start
+// segment the rest plus twice the warm-up.
+std::vector<int> split_work(const std::vector<int>& nch, const std::vector<int>& split, int H, int warm) {
+    std::vector<int> w;
+    w.reserve(nch.size() * H * 2);
+    for (size_t i = 0; i < nch.size(); ++i) {
+        const int a = split[i];
+        for (int h = 0; h < H; ++h) {
+            if (a > 0) {
+                w.push_back(a);
+                w.push_back(nch[i] - a + 2 * warm);
+            } else {
+                w.push_back(nch[i]);
+            }
+        }
+    }
+    return w;
+}
+
+// Warm-start split search: the k longest sequences are split at the same
+// fraction f of their chunks; the cheapest (k, f) by the fused-kernel
+// simulation wins. Only for batches of at most a few rounds of units, where
+// the longest chains make the tail.
+double best_split(const std::vector<int>& nch, int H, int n_cus, const PlannerConsts& pc,
+                  std::vector<int>& split_out) {
+    const int n = (int)nch.size();
+    split_out.assign(n, 0);
+    const int W = pc.split_warm;
+    double best = 1e300;
+    if ((long long)n * H > 4LL * n_cus || W < 1) return best;
+    std::vector<int> order(n);
+    for (int i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return nch[x] > nch[y]; });
+    std::vector<int> split(n, 0);
+    for (int k = 1; k <= std::min(n, 8); ++k) {
+        for (int fi = 6; fi <= 12; ++fi) {
+            const double f = 0.05 * fi;
+            std::fill(split.begin(), split.end(), 0);
+            bool ok = true;
+            for (int j = 0; j < k; ++j) {
+                const int i = order[j];
+                const int a = (int)std::lround(nch[i] * f);
+                if (a < W || nch[i] - a < 1 || nch[i] < 4 * W) { ok = false; break; }
+                split[i] = a;
+            }
+            if (!ok) break;
+            const double t = simulate_fused_us(split_work(nch, split, H, W), n_cus, pc) + pc.launch_us;
+            if (t < best) { best = t; split_out = split; }
+        }
+    }
+    return best;
+}
+
+// seg_chunks > 0 forces that segment length on every longer sequence;
+// force_split (per sequence, 0 = none) forces warm-start splits with
+// force_warm warm-up chunks.
 kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int32_t H,
                       int32_t dk, int32_t dv, kda_cp_mode mode, int32_t seg_chunks,
-                      kda_plan** out) {
+                      kda_plan** out, const int32_t* force_split = nullptr, int32_t force_warm = 0) {
     if (!out) return fail(KDA_ERR_INVALID, "kda_plan_prefill: out is NULL");
     *out = nullptr;
     if (dk != 128 || dv != 128)
@@ -201,22 +307,51 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
         }
         if (mode == KDA_CP_AUTO && !(t_cp < 0.9 * t_serial)) seg = 0;
     }
+    // warm-start splits (fused serial path only)
+    const bool materialize_env = env_double("KDA_MATERIALIZE_K1", 0.0) > 0.5;
+    std::vector<int> split(n_seqs, 0);
+    int warm = pc.split_warm;
+    double t_split = 1e300, t_sim_serial = -1.0;
+    if (force_split) {
+        warm = force_warm;
+        for (int i = 0; i < n_seqs; ++i) split[i] = force_split[i];
+        t_split = simulate_fused_us(split_work(nch, split, H, warm), n_cus, pc) + pc.launch_us;
+    } else if (mode == KDA_CP_AUTO && seg == 0 && !materialize_env) {
+        t_sim_serial = simulate_fused_us(split_work(nch, split, H, 0), n_cus, pc);
+        std::vector<int> cand;
+        t_split = best_split(nch, H, n_cus, pc, cand);
+        if (t_split < 0.97 * t_sim_serial) split = cand;
+    }
+    int n_split = 0;
+    for (int i = 0; i < n_seqs; ++i) n_split += split[i] > 0;
 
     // units
     int n_cp_seqs = 0, n_prescan = 0, n_carry = 0;
     std::vector<int> order(n_seqs);
     for (int i = 0; i < n_seqs; ++i) order[i] = i;
+    int n_spec = 0;
     for (int i : order) {
+        if (split[i] > 0) {
+            // first segment from the initial state, writing its end state to a
+            // carry slot; warm-start segment from its warm-up; the fix-up
+            // table reruns the latter from that carry if its warm-up transfer
+            // did not vanish
+            const int a = split[i], carry = n_carry++, spec = n_spec++;
+            p->units.push_back(UnitDesc{i, 0, a, chunk_base[i], -1, 0, 0, 2, 0, -1, carry, 0});
+            p->units.push_back(UnitDesc{i, a, nch[i] - a, chunk_base[i] + a, -1, 1, 1, 2, warm, spec, -1, 0});
+            p->fixups.push_back(UnitDesc{i, a, nch[i] - a, chunk_base[i] + a, carry, 1, 1, 2, 0, spec, -1, 0});
+            continue;
+        }
         const int s = (seg > 0 && nch[i] > seg) ? (nch[i] + seg - 1) / seg : 1;
         if (s == 1) {
-            p->units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1});
+            p->units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1, 0, -1, -1, 0});
             continue;
         }
         MergeDesc md{i, s, n_carry, n_prescan};
         p->merges.push_back(md);
         for (int j = 0; j < s; ++j) {
             const int c0 = j * seg, n = std::min(seg, nch[i] - c0);
-            p->units.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, n_carry + j, j == s - 1, j, s});
+            p->units.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, n_carry + j, j == s - 1, j, s, 0, -1, -1, 0});
             if (j < s - 1)
                 p->prescan.push_back(PrescanDesc{i, c0, n, chunk_base[i] + c0, n_prescan + j, {0, 0, 0}});
         }
@@ -224,16 +359,17 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
         n_prescan += s - 1;
         n_carry += s;
     }
-    // longest chains first
-    std::stable_sort(p->units.begin(), p->units.end(),
-                     [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
+    // longest chains first (a warm-start segment runs its warm-up twice)
+    std::stable_sort(p->units.begin(), p->units.end(), [](const UnitDesc& a, const UnitDesc& b) {
+        return a.n_chunks + 2 * a.warm > b.n_chunks + 2 * b.warm;
+    });
     std::stable_sort(p->prescan.begin(), p->prescan.end(),
                      [](const PrescanDesc& a, const PrescanDesc& b) { return a.n_chunks > b.n_chunks; });
 
     // workspace layout
     // CP plans always materialise K1 (K1 once, then pre_scan and segment-K2
     // read its records); serial plans run the fused kernel unless asked not to.
-    const bool materialize = n_cp_seqs > 0 || env_double("KDA_MATERIALIZE_K1", 0.0) > 0.5;
+    const bool materialize = n_cp_seqs > 0 || (materialize_env && n_split == 0);
     size_t off = 0;
     p->off_rec = off;
     if (materialize) off = align_up(off + (size_t)total_chunks * H * kRecBytes, 256);
@@ -245,6 +381,10 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     off = align_up(off + (size_t)n_prescan * H * 8 * sizeof(int32_t), 256);
     p->off_carry = off;
     off = align_up(off + (size_t)n_carry * H * kStateBytes, 256);
+    p->off_spec_states = off;
+    off = align_up(off + (size_t)n_spec * H * kStateBytes, 256);
+    p->off_spec_flags = off;
+    off = align_up(off + (size_t)n_spec * H * 8 * sizeof(int32_t), 256);
 
     kda_plan_info& in = p->info;
     in.n_seqs = n_seqs;
@@ -265,6 +405,9 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     in.est_serial_us = t_serial;
     in.est_cp_us = t_cp < 1e299 ? t_cp : -1.0;
     in.k1_materialized = materialize ? 1 : 0;
+    in.n_split_seqs = n_split;
+    in.split_warm_chunks = n_split > 0 ? warm : 0;
+    in.est_split_us = t_split < 1e299 ? t_split : -1.0;
     *out = p;
     return KDA_OK;
 }
@@ -279,11 +422,14 @@ kda_status upload_plan(kda_plan* p, int device) {
     off = align_up(off + p->prescan.size() * sizeof(PrescanDesc), 256);
     p->dev_off_merges = off;
     off = align_up(off + p->merges.size() * sizeof(MergeDesc), 256);
+    p->dev_off_fixups = off;
+    off = align_up(off + p->fixups.size() * sizeof(UnitDesc), 256);
     std::vector<uint8_t> host(off, 0);
     if (!p->chunks.empty()) memcpy(&host[p->dev_off_chunks], p->chunks.data(), p->chunks.size() * sizeof(ChunkDesc));
     if (!p->units.empty()) memcpy(&host[p->dev_off_units], p->units.data(), p->units.size() * sizeof(UnitDesc));
     if (!p->prescan.empty()) memcpy(&host[p->dev_off_prescan], p->prescan.data(), p->prescan.size() * sizeof(PrescanDesc));
     if (!p->merges.empty()) memcpy(&host[p->dev_off_merges], p->merges.data(), p->merges.size() * sizeof(MergeDesc));
+    if (!p->fixups.empty()) memcpy(&host[p->dev_off_fixups], p->fixups.data(), p->fixups.size() * sizeof(UnitDesc));
     int prev = -1;
     hipError_t e = hipGetDevice(&prev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -436,6 +582,35 @@ kda_status kda_plan_prefill_segments(kda_ctx* ctx, const int32_t* cu_seqlens_hos
     return st;
 }
 
+kda_status kda_plan_prefill_split(kda_ctx* ctx, const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t H,
+                                  int32_t dk, int32_t dv, const int32_t* split_chunk, int32_t warm_chunks,
+                                  kda_plan** out) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_plan_prefill_split: ctx is NULL");
+    if (!out) return fail(KDA_ERR_INVALID, "kda_plan_prefill_split: out is NULL");
+    *out = nullptr;
+    if (!split_chunk || !cu_seqlens_host || n_seqs < 1)
+        return fail(KDA_ERR_INVALID, "kda_plan_prefill_split: split_chunk, cu_seqlens_host and n_seqs >= 1 required");
+    if (warm_chunks < 1) return fail(KDA_ERR_INVALID, "kda_plan_prefill_split: warm_chunks must be >= 1 (got %d)",
+                                     warm_chunks);
+    for (int i = 0; i < n_seqs; ++i) {
+        const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+        const int nch = L > 0 ? (L + kChunk - 1) / kChunk : 0;
+        const int a = split_chunk[i];
+        if (a != 0 && (a < warm_chunks || a >= nch))
+            return fail(KDA_ERR_INVALID, "kda_plan_prefill_split: sequence %d (%d chunks): split chunk %d must be 0 "
+                                         "or in [warm_chunks=%d, chunks)", i, nch, a, warm_chunks);
+    }
+    kda_status st = build_plan(ctx->n_cus, cu_seqlens_host, n_seqs, H, dk, dv, KDA_CP_OFF, 0, out, split_chunk,
+                               warm_chunks);
+    if (st != KDA_OK) return st;
+    st = upload_plan(*out, ctx->device);
+    if (st != KDA_OK) {
+        delete *out;
+        *out = nullptr;
+    }
+    return st;
+}
+
 void kda_plan_destroy(kda_plan* p) {
     if (!p) return;
     if (p->dev_tables) {
@@ -461,7 +636,7 @@ kda_status kda_plan_get_units(const kda_plan* p, kda_unit_info* units, int32_t m
     const int n = std::min<int>(max_units, (int)p->units.size());
     for (int i = 0; i < n; ++i) {
         const UnitDesc& u = p->units[i];
-        units[i] = kda_unit_info{u.seq, u.chunk0, u.n_chunks, u.segment, u.n_segments};
+        units[i] = kda_unit_info{u.seq, u.chunk0, u.n_chunks, u.segment, u.n_segments, u.warm};
     }
     return KDA_OK;
 }
@@ -682,11 +857,26 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
         if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
     }
     K2Args ka{c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(), s0, sT,
-              (const float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0};
+              (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0,
+              (int32_t*)(ws + p->off_spec_flags), (float*)(ws + p->off_spec_states), 0, 0};
+    // a final state that aliases the initial state is published by the fix-up
+    // launch, after every unit has read its initial state
+    ka.spec_final_direct = (sT && s0 && sT == s0) ? 0 : 1;
+    const bool split = p->info.n_split_seqs > 0;
     const char* k2name = mat ? (p->info.uses_cp ? "k2_segment" : "k2_recur")
-                             : (p->info.uses_cp ? "fused_segment" : "fused_serial");
+                             : (p->info.uses_cp ? "fused_segment" : (split ? "fused_split" : "fused_serial"));
     e = timed(k2name, [&] { return mat ? launch_k2_recur(ka, stream) : launch_fused(ka, stream); });
     if (e != hipSuccess) return hip_fail(e, "k2 launch");
+    if (split) {
+        // warm-start segments: keep (and publish the end state of) each one
+        // whose warm-up transfer vanished, rerun the others from their carry
+        K2Args kf = ka;
+        kf.units = (const UnitDesc*)(tabs + p->dev_off_fixups);
+        kf.n_units = (int32_t)p->fixups.size();
+        kf.fixup = 1;
+        e = timed("fused_fixup", [&] { return launch_fused(kf, stream); });
+        if (e != hipSuccess) return hip_fail(e, "fix-up launch");
+    }
     return KDA_OK;
 }
 

@@ -363,12 +363,84 @@ def test_steep_in_chunk_decay_matches_oracle(monkeypatch):
 
 
 # ---------------------------------------------------------------------------
+# warm-start splits (intracard CP inside the fused kernel)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("lengths,split,warm", [([300, 520], [10, 15], 8), ([1000, 40, 700], [30, 0, 8], 8),
+                                                ([250], [5], 4), ([161, 33], [10, 0], 10)])
+def test_split_plan_is_bitwise_serial(lengths, split, warm):
+    """Under the workloads' decay the warm-up transfer vanishes, so the
+    warm-start segment's state from zero is its carry: output and final state
+    equal the unsplit serial path bit for bit, and the oracle within 1e-2."""
+    say("case lengths", lengths, "split", split, "warm", warm)
+    d = draw(lengths, 4, seed=sum(lengths) + 3, state_std=0.1, device=DEV)
+    p = kda.plan_split(d["cu_seqlens_host"], 4, split, warm, device=DEV)
+    info = p.info()
+    assert info["n_split_seqs"] == sum(1 for x in split if x) and info["split_warm_chunks"] == warm
+    assert sorted(u["warm_chunks"] for u in p.units())[-1] == warm
+    o_ser, s_ser = run(d, mode=False)
+    o, s = run(d, plan=p)
+    assert torch.equal(o, o_ser), "split output differs from serial"
+    assert torch.equal(s, s_ser), "split final state differs from serial"
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+def test_split_plan_weak_decay_reruns_exactly():
+    """With weak decay the warm-up transfer does not vanish; the fix-up
+    launch reruns the warm-start segment from the first segment's end state,
+    so the result is still the serial path's, bit for bit."""
+    d = draw([900, 300], 3, seed=41, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * 0.05
+    p = kda.plan_split(d["cu_seqlens_host"], 3, [30, 9], 8, device=DEV)
+    o_ser, s_ser = run(d, mode=False)
+    o, s = run(d, plan=p)
+    assert torch.equal(o, o_ser) and torch.equal(s, s_ser)
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+@pytest.mark.parametrize("g_scale", [1.0, 0.05])
+def test_split_plan_state_variants(g_scale):
+    """In place (final state over the initial state), no initial state, no
+    final state: each equals the serial path's result."""
+    d = draw([600, 20], 3, seed=43, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * g_scale
+    cu = d["cu_seqlens_host"]
+    p = kda.plan_split(cu, 3, [20, 0], 8, device=DEV)
+    o_ser, s_ser = run(d, mode=False)
+    st = d["initial_state"].clone()
+    o, s = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                       cu_seqlens_host=cu, initial_state=st, final_state=st, plan=p)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ser) and torch.equal(st, s_ser), "in place"
+    o0, s0 = run(d, mode=False, s0=None)
+    o1, s1 = run(d, plan=p, s0=None)
+    assert torch.equal(o1, o0) and torch.equal(s1, s0), "no initial state"
+    o2, _ = run(d, plan=p, final=False)
+    assert torch.equal(o2, o_ser), "no final state"
+
+
+def test_split_plan_validation():
+    d = draw([100], 2, seed=1, device=DEV)
+    cu = d["cu_seqlens_host"]
+    for split, warm in (([3], 8), ([7], 8), ([0], 0)):
+        with pytest.raises(kda.KDAError):
+            kda.plan_split(cu, 2, split, warm, device=DEV)
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 def test_headline_varlen_h32_full_parity():
     say("case varlen8_h32 (auto plan, as benchmarked)")
     d = workload("varlen8_h32", device=DEV)
+    p = kda.plan(d["cu_seqlens_host"], 32, "auto", device=DEV)
+    say("  plan: %d warm-start splits" % p.info()["n_split_seqs"])
     o, s = run(d, mode="auto")
+    o_ser, s_ser = run(d, mode=False)
+    assert torch.equal(o, o_ser) and torch.equal(s, s_ser), "auto plan differs from serial"
     o_ref, s_ref = oracle(d)
     assert_close("out", o, o_ref)
     assert_close("final_state", s, s_ref)

@@ -116,6 +116,70 @@ def test_ragged_batch_splits_only_long_sequences(kda_lib):
     assert len(by_seq[0]) > 1
 
 
+def headline_lengths():
+    # the headline workload's lengths: 8 uniform in [512, 4096], CPU generator, seed 1002
+    import torch
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1002)
+    return torch.randint(512, 4097, (8,), generator=g).tolist()
+
+
+def test_auto_plan_splits_the_tail_of_one_round(kda_lib):
+    """Eight sequences x 32 heads fill 256 CUs once; the longest chains set
+    the time, so AUTO runs the longest sequences as a first segment plus a
+    warm-start segment."""
+    lengths = headline_lengths()
+    nch = [(L + 15) // 16 for L in lengths]
+    p = kda.plan_host(cu_of(lengths), H=32, n_cus=256, use_intracard_cp="auto")
+    info = p.info()
+    assert info["uses_cp"] == 0 and info["k1_materialized"] == 0
+    assert info["n_split_seqs"] >= 1 and info["split_warm_chunks"] >= 1
+    W = info["split_warm_chunks"]
+    by_seq = {}
+    for u in p.units():
+        by_seq.setdefault(u["seq"], []).append(u)
+    n_split = 0
+    for i, us in by_seq.items():
+        us.sort(key=lambda u: u["chunk0"])
+        assert sum(u["n_chunks"] for u in us) == nch[i]
+        if len(us) == 2:
+            n_split += 1
+            first, second = us
+            assert first["chunk0"] == 0 and first["warm_chunks"] == 0
+            assert second["chunk0"] == first["n_chunks"] >= W and second["warm_chunks"] == W
+        else:
+            assert len(us) == 1 and us[0]["warm_chunks"] == 0
+    assert n_split == info["n_split_seqs"]
+    # the split sequences are the longest ones
+    split_seqs = [i for i, us in by_seq.items() if len(us) == 2]
+    assert min(nch[i] for i in split_seqs) >= max(nch[i] for i in by_seq if i not in split_seqs)
+    # carry, end state and flags of each warm-start segment
+    assert info["workspace_bytes"] >= n_split * 32 * 2 * 128 * 128 * 4
+    # the warm-start segments run longest-first with their warm-up counted
+    work = [u["n_chunks"] + 2 * u["warm_chunks"] for u in p.units()]
+    assert work == sorted(work, reverse=True)
+
+
+def test_auto_plan_splits_nothing_else(kda_lib, monkeypatch):
+    # several rounds of units smooth the tail
+    assert kda.plan_host(cu_of([8192] * 16), H=64, n_cus=256, use_intracard_cp="auto").info()["n_split_seqs"] == 0
+    # off means off; CP plans segment instead
+    assert kda.plan_host(cu_of(headline_lengths()), H=32, n_cus=256).info()["n_split_seqs"] == 0
+    assert kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp="auto").info()["n_split_seqs"] == 0
+    # short sequences
+    assert kda.plan_host(cu_of([100, 64]), H=2, n_cus=256, use_intracard_cp="auto").info()["n_split_seqs"] == 0
+    # the fused kernel is the only one that runs warm-start segments
+    monkeypatch.setenv("KDA_MATERIALIZE_K1", "1")
+    assert kda.plan_host(cu_of(headline_lengths()), H=32, n_cus=256,
+                         use_intracard_cp="auto").info()["n_split_seqs"] == 0
+
+
+def test_split_warm_chunks_is_env_overridable(kda_lib, monkeypatch):
+    monkeypatch.setenv("KDA_SPLIT_WARM_CHUNKS", "12")
+    info = kda.plan_host(cu_of(headline_lengths()), H=32, n_cus=256, use_intracard_cp="auto").info()
+    assert info["n_split_seqs"] == 0 or info["split_warm_chunks"] == 12
+
+
 def test_planner_constants_are_env_overridable(kda_lib, monkeypatch):
     base = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=True).info()
     monkeypatch.setenv("KDA_CP_MIN_SEG_CHUNKS", "1024")
