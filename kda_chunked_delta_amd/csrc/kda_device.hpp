@@ -139,14 +139,31 @@ __device__ __forceinline__ float row_newbcast(float x) {
     return __builtin_amdgcn_update_dpp(0.0f, x, 0x150 + K, 0xF, 0xF, true);
 }
 
-// Byte offset of element (row m, column 4gg + j) of a 16-column tile in the
-// transposed 4-element fragment layout [lane (m >> 2) * 16 + 4gg + j][m & 3].
-__device__ __forceinline__ int tfrag_off(int gg, int m) { return ((m >> 2) * 16 + 4 * gg) * 8 + (m & 3) * 2; }
+// 4 x 4 transpose of 16-bit elements across the four lanes of a quad: lane j
+// holds elements x[0..3] as (x0 | x1 << 16, x2 | x3 << 16); afterwards it
+// holds element j of lanes 0..3, in lane order. First the 2 x 2 blocks of
+// dwords move between lanes j and j ^ 2, then each 2 x 2 block of halves is
+// transposed between lanes j and j ^ 1 (DPP quad permutes and a byte
+// permute).
+__device__ __forceinline__ u32x2 quad_transpose16(u32x2 x, int lane) {
+    const bool hi = (lane & 2) != 0;
+    const uint32_t send = hi ? x.x : x.y;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    const uint32_t y0 = hi ? recv : x.x;
+    const uint32_t y1 = hi ? x.y : recv;
+    const uint32_t p0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)y0, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)y1, 0xB1, 0xF, 0xF, false);
+    // even lane: own low half, then the partner's; odd lane: the partner's
+    // high half, then its own (v_perm_b32: bytes 0-3 from the second
+    // operand, 4-7 from the first)
+    const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
+    return u32x2{__builtin_amdgcn_perm(p0, y0, sel), __builtin_amdgcn_perm(p1, y1, sel)};
+}
 
 // Slot of lane l's 8-byte fragment in the Kt and V tiles: the low two bits
-// are rotated by l >> 4. The reads stay one contiguous 512-byte tile, and
-// the 16-bit scatter that K1 writes them with (for a fixed j, lanes
-// (gg, m) -> lane (m >> 2) * 16 + 4gg + j) then lands on distinct banks.
+// are rotated by l >> 4. The reads stay one contiguous 512-byte tile, and the
+// stores that K1 writes them with (lane (gg, 4a + j) -> fragment of lane
+// 16a + 4gg + j) cover the tile once, conflict-free.
 __device__ __forceinline__ int kv_slot(int l) { return (l & ~3) | (((l & 3) + (l >> 4)) & 3); }
 
 // ---------------------------------------------------------------------------
@@ -411,23 +428,15 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     *(u32x2*)(rec + REC_Q + fo) = pqt;
     *(u32x2*)(rec + REC_X + fo) = pxk;
     // Kt^T and V: element (token m, channel 16 wave + 4gg + j) -> tile wave,
-    // lane (m >> 2) * 16 + 4gg + j, slot m & 3
-    // lane (m >> 2) * 16 + 4gg + j sits in slot kv_slot of that lane:
-    // j rotated by m >> 2
-    const int a4 = m >> 2;
-    const int to = wave * 512 + tfrag_off(gg, m);
-    const int s0 = (a4 & 3) * 8, s1 = ((a4 + 1) & 3) * 8, s2 = ((a4 + 2) & 3) * 8, s3 = ((a4 + 3) & 3) * 8;
-    const u32x2 ktp = pkt;
-    uint8_t* kd = rec + REC_KT + to;
-    uint8_t* vd = rec + REC_V + to;
-    *(uint16_t*)(kd + s0) = (uint16_t)ktp.x;
-    *(uint16_t*)(kd + s1) = (uint16_t)(ktp.x >> 16);
-    *(uint16_t*)(kd + s2) = (uint16_t)ktp.y;
-    *(uint16_t*)(kd + s3) = (uint16_t)(ktp.y >> 16);
-    *(uint16_t*)(vd + s0) = (uint16_t)raw.v.x;
-    *(uint16_t*)(vd + s1) = (uint16_t)(raw.v.x >> 16);
-    *(uint16_t*)(vd + s2) = (uint16_t)raw.v.y;
-    *(uint16_t*)(vd + s3) = (uint16_t)(raw.v.y >> 16);
+    // lane (m >> 2) * 16 + 4gg + j, element m & 3. The four lanes of a quad
+    // (m = 4a .. 4a + 3) hold a 4 x 4 block of it (tokens x channels); after
+    // a 16-bit transpose inside the quad, lane (gg, 4a + j) holds channel
+    // 4gg + j for tokens 4a .. 4a + 3: the whole 8-byte fragment of lane
+    // 16a + 4gg + j, written with one store to that lane's slot.
+    const int dl = 16 * (m >> 2) + 4 * gg + (m & 3);
+    const int to = wave * 512 + kv_slot(dl) * 8;
+    *(u32x2*)(rec + REC_KT + to) = quad_transpose16(pkt, lane);
+    *(u32x2*)(rec + REC_V + to) = quad_transpose16(raw.v, lane);
     // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
     if (m == 15) *(f32x4*)(rec + REC_GC + (32 * gg + 4 * wave) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     if (wave == 0 && gg == 0) *(float*)(scr + K1_BETA + 4 * m) = raw.b;
