@@ -88,8 +88,8 @@ PlannerConsts planner_consts() {
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
     c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
     c.rec_per_cu = (int)env_double("KDA_CP_REC_PER_CU", 2.0);
-    c.alone_us = env_double("KDA_FUSED_CHUNK_US_ALONE", 1.31);
-    c.full_us = env_double("KDA_FUSED_CHUNK_US_FULL", 1.92);
+    c.alone_us = env_double("KDA_FUSED_CHUNK_US_ALONE", 1.21);
+    c.full_us = env_double("KDA_FUSED_CHUNK_US_FULL", 1.60);
     c.split_warm = (int)env_double("KDA_SPLIT_WARM_CHUNKS", 12.0);
     return c;
 }
@@ -97,7 +97,9 @@ PlannerConsts planner_consts() {
 // Interval of the fused kernel per chunk with `busy` of n_cus CUs working.
 double fused_interval_us(int busy, int n_cus, const PlannerConsts& pc) {
     static const double xs[] = {0.0, 0.125, 0.25, 0.5, 0.75, 1.0};
-    static const double ys[] = {0.0, 0.016, 0.08, 0.26, 0.61, 1.0};
+    // measured at steady clocks: 1.21, 1.23, 1.23, 1.25, 1.39 and 1.60 us
+    // per chunk with 8, 32, 64, 128, 192 and 256 of 256 CUs busy
+    static const double ys[] = {0.0, 0.046, 0.061, 0.096, 0.47, 1.0};
     const double x = std::min(1.0, std::max(0.0, (double)busy / n_cus));
     int i = 0;
     while (i < 4 && x > xs[i + 1]) ++i;

@@ -78,3 +78,23 @@ def test_bf16_options_on_the_cp_path():
     o_ref, s_ref = ref.recurrent_c(d["q"], d["k"], d["v"], d["g"], b16, d["cu_seqlens_host"], s0_16)
     assert_close("out", o1, o_ref)
     assert_close("final_state", s1, s_ref)
+
+
+@pytest.mark.parametrize("g_scale", [1.0, 0.05])
+def test_bf16_options_on_warm_start_splits(g_scale):
+    """Warm-start splits with bf16 beta and bf16 states, not aliased and in
+    place, under the workloads' decay (the segment stands) and weak decay
+    (the fix-up reruns it): bitwise the serial result."""
+    lengths, H = [700, 300], 4
+    say("case bf16 beta + states, split vs serial, g x", g_scale)
+    d = draw(lengths, H, seed=78, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * g_scale
+    b16, s0_16 = d["beta"].to(torch.bfloat16), d["initial_state"].to(torch.bfloat16)
+    o1, s1 = run(d, b16, s0_16)
+    sp = kda.plan_split(d["cu_seqlens_host"], H, [20, 12], 12, device=DEV)
+    o2, s2 = run(d, b16, s0_16, plan=sp)
+    assert s2.dtype == torch.bfloat16
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    st = s0_16.clone()
+    o3, s3 = run(d, b16, st, plan=sp, final=st)
+    assert s3.data_ptr() == st.data_ptr() and torch.equal(o3, o1) and torch.equal(st, s1)

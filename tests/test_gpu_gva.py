@@ -65,3 +65,25 @@ def test_gva_decode_matches_oracle():
     o_ref, s_ref = ref.decode_step(q, k, d["v"], d["g"], d["beta"], d["state"])
     assert_close("out", o, o_ref)
     assert_close("state", state, s_ref)
+
+
+@pytest.mark.parametrize("g_scale", [1.0, 0.05])
+def test_gva_warm_start_split_is_bitwise_equal_to_serial(g_scale):
+    """Grouped value heads on a warm-start split plan: the segment stands or
+    is rerun by the fix-up, and either way equals serial bit for bit."""
+    lengths, Hk, H = [600, 200], 2, 8
+    say("case GVA split", lengths, Hk, H, "g x", g_scale)
+    d = draw(lengths, H, seed=61, state_std=0.1, device=DEV, qk_heads=Hk)
+    d["g"] = d["g"] * g_scale
+    o1, s1 = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                         cu_seqlens_host=d["cu_seqlens_host"], initial_state=d["initial_state"],
+                         output_final_state=True)
+    p = kda.plan_split(d["cu_seqlens_host"], H, [18, 0], 12, device=DEV)
+    o2, s2 = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                         cu_seqlens_host=d["cu_seqlens_host"], initial_state=d["initial_state"],
+                         output_final_state=True, plan=p)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o_ref, s_ref = oracle_gva(d)
+    assert_close("out", o2, o_ref)
+    assert_close("final_state", s2, s_ref)

@@ -490,6 +490,39 @@ def test_graph_replay_picks_up_changed_beta():
     assert_close("out(replay)", o_buf, o_ref)
 
 
+@pytest.mark.parametrize("g_scale", [1.0, 0.05])
+def test_graph_replay_of_a_warm_start_split(g_scale):
+    """A split plan (main and fix-up launches) captured in a HIP graph: each
+    replay, with eager work between replays, equals the eager result, under
+    the workloads' decay (segments stand) and weak decay (fix-up reruns)."""
+    d = draw([600, 150], 4, seed=71, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * g_scale
+    cu_h = d["cu_seqlens_host"]
+    p = kda.plan_split(cu_h, 4, [20, 0], 12, device=DEV)
+    cu = p.cu_device()
+    o_buf = torch.empty_like(d["q"])
+    s_buf = torch.empty_like(d["initial_state"])
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):  # grow the side stream's arena outside capture
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=cu_h,
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=cu_h,
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    o_ser, s_ser = run(d, mode=False)
+    for trial in range(3):
+        o_buf.zero_()
+        s_buf.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_buf, o_ser) and torch.equal(s_buf, s_ser), "replay %d differs from serial" % trial
+        run(d, plan=p)  # eager work between replays
+
+
 def test_arena_reuse_across_shape_changes():
     big = draw([3000, 1000], 8, seed=1, state_std=0.1, device=DEV)
     small = draw([40], 2, seed=2, state_std=0.1, device=DEV)
