@@ -119,6 +119,9 @@ def cpu_baseline(d, max_seconds):
 
 
 def plan_kind(info):
+    if info.get("warm_cp", 0):
+        return "warm-start cp(segments of %d chunks, warm-up %d chunks)" % (info["warm_cp_seg_chunks"],
+                                                                            info["split_warm_chunks"])
     if info["uses_cp"]:
         return "cp"
     if info.get("n_split_seqs", 0) > 0:

@@ -90,6 +90,10 @@ typedef struct {
                                   otherwise leave the compute units idle at the end */
     int32_t split_warm_chunks; /* warm-up chunks of each warm-start segment */
     double  est_split_us;      /* planner's estimate of the split plan (-1: none) */
+    int32_t warm_cp;           /* 1: warm-start CP (see kda_plan_prefill_warm_cp) */
+    int32_t warm_cp_seg_chunks;/* its segment length in chunks */
+    int32_t n_warm_segments;   /* its speculation slots (warm-start and last segments) */
+    double  est_warm_cp_us;    /* planner's estimate of warm-start CP (-1: none) */
 } kda_plan_info;
 
 /* One K2 work unit of a plan (a whole sequence, or one segment of it). */
@@ -159,6 +163,23 @@ kda_status kda_plan_prefill_segments(kda_ctx *ctx, const int32_t *cu_seqlens_hos
 kda_status kda_plan_prefill_split(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
                                   int32_t H, int32_t dk, int32_t dv, const int32_t *split_chunk,
                                   int32_t warm_chunks, kda_plan **out);
+
+/* Warm-start CP: every sequence longer than seg_chunks chunks is cut into
+ * chunk-aligned segments of seg_chunks, and all segments run side by side in
+ * one fused launch, each after the first as a warm-start segment with
+ * warm_chunks warm-up chunks (see kda_plan_prefill_split). The segmented CP
+ * pipeline of kda_plan_prefill_segments with the same segment length is kept
+ * as the fallback. A flag reduction on the device arms it only if some
+ * warm-up transfer did not vanish; it then recomputes every output and
+ * final state. With the fallback unarmed, the result equals the serial
+ * path's bit for bit wherever the CP path's does; armed, it is the CP path's
+ * result. No host synchronisation is involved, so a captured graph replays
+ * either way. AUTO plans choose this for few-head long sequences when the
+ * planner predicts a win over the segmented path. 1 <= warm_chunks <=
+ * seg_chunks. Device tables are uploaded as in kda_plan_prefill. */
+kda_status kda_plan_prefill_warm_cp(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
+                                    int32_t H, int32_t dk, int32_t dv, int32_t seg_chunks,
+                                    int32_t warm_chunks, kda_plan **out);
 
 void kda_plan_destroy(kda_plan *plan);
 

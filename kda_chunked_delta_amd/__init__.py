@@ -52,7 +52,9 @@ class PlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("est_serial_us", ctypes.c_double),
                 ("est_cp_us", ctypes.c_double), ("k1_materialized", ctypes.c_int32),
                 ("n_split_seqs", ctypes.c_int32), ("split_warm_chunks", ctypes.c_int32),
-                ("est_split_us", ctypes.c_double)]
+                ("est_split_us", ctypes.c_double), ("warm_cp", ctypes.c_int32),
+                ("warm_cp_seg_chunks", ctypes.c_int32), ("n_warm_segments", ctypes.c_int32),
+                ("est_warm_cp_us", ctypes.c_double)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -92,6 +94,7 @@ def lib():
                 "kda_plan_prefill_host": (ctypes.c_int, [I32, P, I32, I32, I32, I32, ctypes.c_int, PP]),
                 "kda_plan_prefill_segments": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, PP]),
                 "kda_plan_prefill_split": (ctypes.c_int, [P, P, I32, I32, I32, I32, P, I32, PP]),
+                "kda_plan_prefill_warm_cp": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, I32, PP]),
                 "kda_plan_destroy": (None, [P]),
                 "kda_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(PlanInfo)]),
                 "kda_plan_workspace_bytes": (ctypes.c_size_t, [P]),
@@ -278,6 +281,16 @@ def plan_split(cu_seqlens, H, split_chunk, warm_chunks, device=None):
     h = ctypes.c_void_p()
     _check(lib().kda_plan_prefill_split(ctx.handle, arr, n, int(H), D, D, sp, int(warm_chunks),
                                         ctypes.byref(h)), "kda_plan_prefill_split")
+    return Plan(h, cu_seqlens, ctx.device)
+
+
+def plan_warm_cp(cu_seqlens, H, seg_chunks, warm_chunks, device=None):
+    """Executable warm-start CP plan with a forced segment length (chunks)."""
+    ctx = context(device)
+    arr, n = _cu_array(cu_seqlens)
+    h = ctypes.c_void_p()
+    _check(lib().kda_plan_prefill_warm_cp(ctx.handle, arr, n, int(H), D, D, int(seg_chunks), int(warm_chunks),
+                                          ctypes.byref(h)), "kda_plan_prefill_warm_cp")
     return Plan(h, cu_seqlens, ctx.device)
 
 

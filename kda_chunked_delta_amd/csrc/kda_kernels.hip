@@ -218,6 +218,7 @@ static_assert(STG_BYTES <= K1P_LDS, "staging overlays the record area");
 
 template <bool GVA>
 __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
+    if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
     __shared__ __align__(16) uint8_t lds[K1P_LDS];
     uint8_t* rec = lds;
     uint8_t* scr = lds + REC_BYTES;
@@ -294,11 +295,20 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     seq_bounds(a.c, u.seq, beg, end);
     if (a.fixup) {
         // fix-up launch over warm-start segments: the segment stands as
-        // computed when every tile of its warm-up transfer was exactly zero
-        const int32_t* fl = a.spec_flags + ((size_t)u.spec * H + h) * 8;
+        // computed when every tile of its warm-up transfer was exactly zero.
+        // With a gate (warm-start CP), the gate says whether any warm-up
+        // transfer of the plan survived; the segmented pipeline then
+        // recomputes everything, and this launch only publishes final states
+        // otherwise.
         int live = 0;
+        if (a.c.gate) {
+            live = *a.c.gate;
+        } else {
+            const int32_t* fl = a.spec_flags + ((size_t)u.spec * H + h) * 8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) live |= fl[j];
+            for (int j = 0; j < 8; ++j) live |= fl[j];
+        }
+        if (a.c.gate && live) return;
         if (!live) {
             if (!a.spec_final_direct && u.write_final && a.sT) {
                 const float* src = a.spec_states + ((size_t)u.spec * H + h) * (D * D);
@@ -325,6 +335,9 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         f32x4 S[8][1];
         if (W > 0) identity_state(S, w8, gg, m);
         else load_unit_state(a, u, h, S, w8, gg, m);
+        // a unit with a speculation slot but no warm-up has nothing to
+        // speculate on: its flags read "vanished"
+        if (W == 0 && u.spec >= 0 && !a.fixup && lane == 0) a.spec_flags[((size_t)u.spec * H + h) * 8 + w8] = 0;
         lds_barrier();  // start-up: the first chunk is staged
         const int rem = (int)(end - tok0);
         auto step = [&](int c, int i) __attribute__((always_inline)) {
@@ -375,10 +388,11 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         else if (w8 == WAVE_QK) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 0>{});
         if (u.out_slot >= 0) store_state(a.carries + ((size_t)u.out_slot * H + h) * (D * D), S, w8, gg, m);
-        if (u.spec >= 0 && !a.fixup && !a.spec_final_direct)
-            store_state(a.spec_states + ((size_t)u.spec * H + h) * (D * D), S, w8, gg, m);
-        else
+        if (u.spec >= 0 && !a.fixup && !a.spec_final_direct) {
+            if (u.write_final) store_state(a.spec_states + ((size_t)u.spec * H + h) * (D * D), S, w8, gg, m);
+        } else {
             store_unit_state(a, u, h, S, w8, gg, m);
+        }
     } else {
         // K1 wavefronts: chunk c is loaded into register set c & 1
         RowChunk r0, r1;
@@ -437,6 +451,7 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
 // columns 16w..16w+15.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
+    if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
     __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
@@ -466,6 +481,7 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
 // B follows K2's arithmetic exactly.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void kda_cp_prescan(PrescanArgs a) {
+    if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
     __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
@@ -518,6 +534,7 @@ struct MergeOperands {
 };
 
 __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
+    if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
     __shared__ float carry[D][16];
     const int H = a.c.H;
     const int vt = blockIdx.x & 7;
@@ -613,6 +630,23 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     if (attr1 != hipSuccess) return attr1;
     if (a.c.group > 1) hipLaunchKernelGGL(kda_fused<true>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
     else hipLaunchKernelGGL(kda_fused<false>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
+    return hipGetLastError();
+}
+
+// gate[0] = OR over flags (one workgroup of 256 threads).
+__global__ __launch_bounds__(256) void kda_flags_or(const int32_t* __restrict__ flags, int64_t n,
+                                                    int32_t* __restrict__ gate) {
+    __shared__ int32_t wave_any[4];
+    int32_t acc = 0;
+    for (int64_t i = threadIdx.x; i < n; i += 256) acc |= flags[i];
+    const bool any = __builtin_amdgcn_ballot_w64(acc != 0) != 0;
+    if ((threadIdx.x & 63) == 0) wave_any[threadIdx.x >> 6] = any ? 1 : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) gate[0] = wave_any[0] | wave_any[1] | wave_any[2] | wave_any[3];
+}
+
+hipError_t launch_flags_or(const int32_t* flags, int64_t n, int32_t* gate, hipStream_t s) {
+    hipLaunchKernelGGL(kda_flags_or, dim3(1), dim3(256), 0, s, flags, n, gate);
     return hipGetLastError();
 }
 

@@ -68,6 +68,10 @@ struct CommonArgs {
     int32_t n_seqs;
     int32_t total_chunks;
     uint8_t* rec;  // K1 records [H][total_chunks][REC_BYTES]
+    // When set, a kernel of the segmented pipeline does nothing unless
+    // *gate != 0 (the fallback of a warm-start CP plan: armed by the flag
+    // reduction when a warm-up transfer did not vanish).
+    const int32_t* gate;
 };
 
 struct K2Args {
@@ -127,6 +131,8 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s);
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
 hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);
+// gate[0] = 1 if any of flags[0..n) is nonzero, else 0 (one workgroup)
+hipError_t launch_flags_or(const int32_t* flags, int64_t n, int32_t* gate, hipStream_t s);
 
 constexpr int kChunk = 16;                      // tokens per chunk
 constexpr size_t kRecBytes = 18432;            // bytes of one K1 chunk record

@@ -149,13 +149,15 @@ struct kda_plan {
     std::vector<PrescanDesc> prescan;   // CP pre_scan items
     std::vector<MergeDesc> merges;      // CP merge items
     std::vector<UnitDesc> fixups;       // warm-start segments, as rerun from their carry
+    std::vector<UnitDesc> cp_units;     // warm-start CP: the segmented fallback's K2 units
     // workspace layout (byte offsets into the arena)
     size_t off_rec = 0, off_b = 0, off_m = 0, off_mlive = 0, off_carry = 0;
-    size_t off_spec_states = 0, off_spec_flags = 0;
+    size_t off_spec_states = 0, off_spec_flags = 0, off_gate = 0;
     // device copy of the tables
     int device = -1;
     void* dev_tables = nullptr;
     size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_prescan = 0, dev_off_merges = 0, dev_off_fixups = 0;
+    size_t dev_off_cp_units = 0;
 };
 
 namespace {
@@ -256,7 +258,8 @@ double best_split(const std::vector<int>& nch, int H, int n_cus, const PlannerCo
 // force_warm warm-up chunks.
 kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int32_t H,
                       int32_t dk, int32_t dv, kda_cp_mode mode, int32_t seg_chunks,
-                      kda_plan** out, const int32_t* force_split = nullptr, int32_t force_warm = 0) {
+                      kda_plan** out, const int32_t* force_split = nullptr, int32_t force_warm = 0,
+                      int32_t force_warm_cp_seg = 0) {
     if (!out) return fail(KDA_ERR_INVALID, "kda_plan_prefill: out is NULL");
     *out = nullptr;
     if (dk != 128 || dv != 128)
@@ -326,6 +329,34 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     }
     int n_split = 0;
     for (int i = 0; i < n_seqs; ++i) n_split += split[i] > 0;
+    // warm-start CP: every segment of the segmented plan runs in the fused
+    // kernel (segments after the first as warm-start segments), and the
+    // segmented pipeline is kept as a fallback, armed on the device only if
+    // a warm-up transfer survives
+    int wseg = 0;
+    double t_wcp = 1e300;
+    if (force_warm_cp_seg > 0) {
+        wseg = force_warm_cp_seg;
+        warm = force_warm;
+        seg = force_warm_cp_seg;
+    } else if (mode == KDA_CP_AUTO && seg > 0 && !materialize_env && pc.split_warm >= 1) {
+        std::vector<int> cands;
+        const int mx = *std::max_element(nch.begin(), nch.end());
+        for (int b = 16; b <= mx; b *= 2)
+            for (int s : {b, b + b / 2})
+                if (s >= 2 * pc.split_warm && s < mx) cands.push_back(s);
+        for (int s : cands) {
+            std::vector<int> work;
+            for (int i = 0; i < n_seqs; ++i)
+                for (int h = 0; h < H; ++h)
+                    for (int c0 = 0; c0 < std::max(nch[i], 1); c0 += s)
+                        work.push_back(std::min(s, nch[i] - c0) + (c0 > 0 ? 2 * pc.split_warm : 0));
+            const double t = simulate_fused_us(work, n_cus, pc) + 6 * pc.launch_us;
+            if (t < t_wcp) { t_wcp = t; wseg = s; }
+        }
+        if (!(t_wcp < 0.8 * t_cp)) wseg = 0;
+        else warm = pc.split_warm;
+    }
 
     // units
     int n_cp_seqs = 0, n_prescan = 0, n_carry = 0;
@@ -361,6 +392,29 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
         n_prescan += s - 1;
         n_carry += s;
     }
+    int n_wspec = 0;
+    if (wseg > 0) {
+        // the classic tables above are the fallback; the fused launch runs
+        // the warm-start segments
+        p->cp_units.swap(p->units);
+        for (int i = 0; i < n_seqs; ++i) {
+            const int ns = nch[i] > 0 ? (nch[i] + wseg - 1) / wseg : 1;
+            for (int j = 0; j < ns; ++j) {
+                const int c0 = j * wseg, n = std::min(wseg, nch[i] - c0);
+                const bool last = j == ns - 1;
+                const int spec = (j > 0 || last) ? n_wspec++ : -1;
+                // the last segment's end state is the final state; a warm-start
+                // one leaves it in spec_states when the final state aliases
+                // the initial state (published by the gated fix-up launch)
+                p->units.push_back(UnitDesc{i, c0, std::max(n, 0), chunk_base[i] + c0, -1, last ? 1 : 0, j, ns,
+                                            j > 0 ? warm : 0, spec, -1, 0});
+                if (last)
+                    p->fixups.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, -1, 1, j, ns, 0, spec, -1, 0});
+            }
+        }
+        std::stable_sort(p->cp_units.begin(), p->cp_units.end(),
+                         [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
+    }
     // longest chains first (a warm-start segment runs its warm-up twice)
     std::stable_sort(p->units.begin(), p->units.end(), [](const UnitDesc& a, const UnitDesc& b) {
         return a.n_chunks + 2 * a.warm > b.n_chunks + 2 * b.warm;
@@ -371,7 +425,7 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     // workspace layout
     // CP plans always materialise K1 (K1 once, then pre_scan and segment-K2
     // read its records); serial plans run the fused kernel unless asked not to.
-    const bool materialize = n_cp_seqs > 0 || (materialize_env && n_split == 0);
+    const bool materialize = n_cp_seqs > 0 || wseg > 0 || (materialize_env && n_split == 0);
     size_t off = 0;
     p->off_rec = off;
     if (materialize) off = align_up(off + (size_t)total_chunks * H * kRecBytes, 256);
@@ -383,10 +437,13 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     off = align_up(off + (size_t)n_prescan * H * 8 * sizeof(int32_t), 256);
     p->off_carry = off;
     off = align_up(off + (size_t)n_carry * H * kStateBytes, 256);
+    const int n_spec_slots = std::max(n_spec, n_wspec);
     p->off_spec_states = off;
-    off = align_up(off + (size_t)n_spec * H * kStateBytes, 256);
+    off = align_up(off + (size_t)n_spec_slots * H * kStateBytes, 256);
     p->off_spec_flags = off;
-    off = align_up(off + (size_t)n_spec * H * 8 * sizeof(int32_t), 256);
+    off = align_up(off + (size_t)n_spec_slots * H * 8 * sizeof(int32_t), 256);
+    p->off_gate = off;
+    if (wseg > 0) off = align_up(off + sizeof(int32_t), 256);
 
     kda_plan_info& in = p->info;
     in.n_seqs = n_seqs;
@@ -408,8 +465,17 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     in.est_cp_us = t_cp < 1e299 ? t_cp : -1.0;
     in.k1_materialized = materialize ? 1 : 0;
     in.n_split_seqs = n_split;
-    in.split_warm_chunks = n_split > 0 ? warm : 0;
+    in.split_warm_chunks = (n_split > 0 || wseg > 0) ? warm : 0;
     in.est_split_us = t_split < 1e299 ? t_split : -1.0;
+    in.warm_cp = wseg > 0 ? 1 : 0;
+    in.warm_cp_seg_chunks = wseg;
+    in.n_warm_segments = n_wspec;
+    in.est_warm_cp_us = t_wcp < 1e299 ? t_wcp : -1.0;
+    if (wseg > 0) {
+        in.n_units = (int32_t)p->units.size();
+        in.max_unit_chunks = 0;
+        for (const auto& u : p->units) in.max_unit_chunks = std::max(in.max_unit_chunks, u.n_chunks);
+    }
     *out = p;
     return KDA_OK;
 }
@@ -426,12 +492,16 @@ kda_status upload_plan(kda_plan* p, int device) {
     off = align_up(off + p->merges.size() * sizeof(MergeDesc), 256);
     p->dev_off_fixups = off;
     off = align_up(off + p->fixups.size() * sizeof(UnitDesc), 256);
+    p->dev_off_cp_units = off;
+    off = align_up(off + p->cp_units.size() * sizeof(UnitDesc), 256);
     std::vector<uint8_t> host(off, 0);
     if (!p->chunks.empty()) memcpy(&host[p->dev_off_chunks], p->chunks.data(), p->chunks.size() * sizeof(ChunkDesc));
     if (!p->units.empty()) memcpy(&host[p->dev_off_units], p->units.data(), p->units.size() * sizeof(UnitDesc));
     if (!p->prescan.empty()) memcpy(&host[p->dev_off_prescan], p->prescan.data(), p->prescan.size() * sizeof(PrescanDesc));
     if (!p->merges.empty()) memcpy(&host[p->dev_off_merges], p->merges.data(), p->merges.size() * sizeof(MergeDesc));
     if (!p->fixups.empty()) memcpy(&host[p->dev_off_fixups], p->fixups.data(), p->fixups.size() * sizeof(UnitDesc));
+    if (!p->cp_units.empty())
+        memcpy(&host[p->dev_off_cp_units], p->cp_units.data(), p->cp_units.size() * sizeof(UnitDesc));
     int prev = -1;
     hipError_t e = hipGetDevice(&prev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -604,6 +674,24 @@ kda_status kda_plan_prefill_split(kda_ctx* ctx, const int32_t* cu_seqlens_host, 
     }
     kda_status st = build_plan(ctx->n_cus, cu_seqlens_host, n_seqs, H, dk, dv, KDA_CP_OFF, 0, out, split_chunk,
                                warm_chunks);
+    if (st != KDA_OK) return st;
+    st = upload_plan(*out, ctx->device);
+    if (st != KDA_OK) {
+        delete *out;
+        *out = nullptr;
+    }
+    return st;
+}
+
+kda_status kda_plan_prefill_warm_cp(kda_ctx* ctx, const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t H,
+                                    int32_t dk, int32_t dv, int32_t seg_chunks, int32_t warm_chunks,
+                                    kda_plan** out) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_plan_prefill_warm_cp: ctx is NULL");
+    if (seg_chunks < 1 || warm_chunks < 1 || warm_chunks > seg_chunks)
+        return fail(KDA_ERR_INVALID, "kda_plan_prefill_warm_cp: need 1 <= warm_chunks <= seg_chunks (got %d, %d)",
+                    warm_chunks, seg_chunks);
+    kda_status st = build_plan(ctx->n_cus, cu_seqlens_host, n_seqs, H, dk, dv, KDA_CP_ON, seg_chunks, out, nullptr,
+                               warm_chunks, seg_chunks);
     if (st != KDA_OK) return st;
     st = upload_plan(*out, ctx->device);
     if (st != KDA_OK) {
@@ -838,6 +926,54 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
             return launch_beta_to_f32((const uint16_t*)beta, (float*)(ws + off_beta), (int64_t)n_beta, stream);
         });
         if (e != hipSuccess) return hip_fail(e, "beta_to_f32 launch");
+    }
+    if (p->info.warm_cp) {
+        // warm-start CP: all segments in one fused launch; the segmented
+        // pipeline runs only if the flag reduction arms its gate
+        const bool direct = !(sT && s0 && sT == s0);
+        int32_t* gate = (int32_t*)(ws + p->off_gate);
+        K2Args kw{c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(), s0, sT,
+                  (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0,
+                  (int32_t*)(ws + p->off_spec_flags), (float*)(ws + p->off_spec_states), 0, direct ? 1 : 0};
+        e = timed("fused_warm_cp", [&] { return launch_fused(kw, stream); });
+        if (e != hipSuccess) return hip_fail(e, "warm-start CP launch");
+        e = timed("flags_or", [&] {
+            return launch_flags_or(kw.spec_flags, (int64_t)p->info.n_warm_segments * p->info.H * 8, gate, stream);
+        });
+        if (e != hipSuccess) return hip_fail(e, "flags_or launch");
+        CommonArgs cg = c;
+        cg.gate = gate;
+        K1Args k1{cg, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
+        e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
+        if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+        PrescanArgs pa{cg, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
+                       (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
+        if (!p->prescan.empty()) {
+            e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
+            if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
+        }
+        MergeArgs ma{cg, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
+                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
+                     state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
+        if (!p->merges.empty()) {
+            e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
+            if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
+        }
+        K2Args kc{cg, (const UnitDesc*)(tabs + p->dev_off_cp_units), (int32_t)p->cp_units.size(), s0, sT,
+                  (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0, nullptr, nullptr, 0, 0};
+        e = timed("k2_segment", [&] { return launch_k2_recur(kc, stream); });
+        if (e != hipSuccess) return hip_fail(e, "k2_segment launch");
+        if (!direct && !p->fixups.empty()) {
+            // publish the final states the warm-start launch left in scratch
+            K2Args kf = kw;
+            kf.c = cg;
+            kf.units = (const UnitDesc*)(tabs + p->dev_off_fixups);
+            kf.n_units = (int32_t)p->fixups.size();
+            kf.fixup = 1;
+            e = timed("publish_final", [&] { return launch_fused(kf, stream); });
+            if (e != hipSuccess) return hip_fail(e, "publish launch");
+        }
+        return KDA_OK;
     }
     const bool mat = p->info.k1_materialized != 0;
     if (mat) {

@@ -98,3 +98,20 @@ def test_bf16_options_on_warm_start_splits(g_scale):
     st = s0_16.clone()
     o3, s3 = run(d, b16, st, plan=sp, final=st)
     assert s3.data_ptr() == st.data_ptr() and torch.equal(o3, o1) and torch.equal(st, s1)
+
+
+@pytest.mark.parametrize("g_scale", [1.0, 0.05])
+def test_bf16_options_on_warm_start_cp(g_scale):
+    """Warm-start CP with bf16 beta and bf16 states: the serial result under
+    the workloads' decay, the segmented CP result under weak decay."""
+    lengths, H = [1600, 90], 4
+    say("case bf16 beta + states, warm-start CP, g x", g_scale)
+    d = draw(lengths, H, seed=79, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * g_scale
+    b16, s0_16 = d["beta"].to(torch.bfloat16), d["initial_state"].to(torch.bfloat16)
+    cu = d["cu_seqlens_host"]
+    ref_plan = None if g_scale == 1.0 else kda.plan_segments(cu, H, 32, device=DEV)
+    o1, s1 = run(d, b16, s0_16, plan=ref_plan)
+    wp = kda.plan_warm_cp(cu, H, 32, 12, device=DEV)
+    o2, s2 = run(d, b16, s0_16, plan=wp)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)

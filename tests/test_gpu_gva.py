@@ -87,3 +87,15 @@ def test_gva_warm_start_split_is_bitwise_equal_to_serial(g_scale):
     o_ref, s_ref = oracle_gva(d)
     assert_close("out", o2, o_ref)
     assert_close("final_state", s2, s_ref)
+
+
+def test_gva_warm_start_cp_is_bitwise_equal_to_serial():
+    lengths, Hk, H = [1200, 50], 2, 6
+    d = draw(lengths, H, seed=62, state_std=0.1, device=DEV, qk_heads=Hk)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    kw = dict(cu_seqlens=d["cu_seqlens"], cu_seqlens_host=d["cu_seqlens_host"],
+              initial_state=d["initial_state"], output_final_state=True)
+    o1, s1 = kda.prefill(*args, **kw)
+    o2, s2 = kda.prefill(*args, plan=kda.plan_warm_cp(d["cu_seqlens_host"], H, 24, 12, device=DEV), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)

@@ -288,6 +288,8 @@ def test_cp_bitwise_on_long_sequence_and_oracle():
     d = workload("long65536_h8", device=DEV)
     p_auto = kda.plan(d["cu_seqlens_host"], 8, "auto", device=DEV)
     assert p_auto.info()["uses_cp"] == 1
+    say("  auto plan: warm-start CP %d (segments of %d chunks)" % (p_auto.info()["warm_cp"],
+                                                                 p_auto.info()["warm_cp_seg_chunks"]))
     o_ser, s_ser = run(d, mode=False)
     o_cp, s_cp = run(d, plan=p_auto)
     assert torch.equal(o_cp, o_ser), "CP output differs from serial"
@@ -295,6 +297,17 @@ def test_cp_bitwise_on_long_sequence_and_oracle():
     o_ref, s_ref = oracle(d)
     assert_close("out", o_cp, o_ref)
     assert_close("final_state", s_cp, s_ref)
+
+
+def test_long_sequence_segmented_cp_is_bitwise_serial():
+    """The segmented CP pipeline alone (forced) on the 65536-token workload:
+    bitwise the serial result."""
+    d = workload("long65536_h8", device=DEV)
+    p = kda.plan_segments(d["cu_seqlens_host"], 8, 64, device=DEV)
+    assert p.info()["warm_cp"] == 0
+    o_ser, s_ser = run(d, mode=False)
+    o_cp, s_cp = run(d, plan=p)
+    assert torch.equal(o_cp, o_ser) and torch.equal(s_cp, s_ser)
 
 
 def test_materialized_k1_paths_are_bitwise_equal_to_fused(monkeypatch):
@@ -422,12 +435,98 @@ def test_split_plan_state_variants(g_scale):
     assert torch.equal(o2, o_ser), "no final state"
 
 
+# ---------------------------------------------------------------------------
+# warm-start CP (all segments in the fused launch, segmented pipeline as fallback)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("aliased", [False, True])
+def test_warm_cp_is_bitwise_serial(aliased):
+    """Under the workloads' decay every warm-up transfer vanishes, the
+    fallback stays unarmed, and the result is the serial path's bit for
+    bit (in place too), and the oracle's within 1e-2."""
+    d = draw([3000, 900, 40, 0], 4, seed=51, state_std=0.1, device=DEV)
+    cu = d["cu_seqlens_host"]
+    p = kda.plan_warm_cp(cu, 4, 32, 12, device=DEV)
+    info = p.info()
+    assert info["warm_cp"] == 1 and info["warm_cp_seg_chunks"] == 32 and info["n_warm_segments"] >= 5
+    o_ser, s_ser = run(d, mode=False)
+    if aliased:
+        st = d["initial_state"].clone()
+        o, s = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                           cu_seqlens_host=cu, initial_state=st, final_state=st, plan=p)
+        torch.cuda.synchronize()
+    else:
+        o, s = run(d, plan=p)
+    assert torch.equal(o, o_ser), "warm-start CP output differs from serial"
+    assert torch.equal(s, s_ser), "warm-start CP final state differs from serial"
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+@pytest.mark.parametrize("aliased", [False, True])
+def test_warm_cp_weak_decay_is_the_cp_result(aliased):
+    """Weak decay: warm-up transfers survive, the fallback is armed, and the
+    result is that of the segmented CP plan with the same segments, bit for
+    bit, within 1e-2 of the oracle."""
+    d = draw([2500, 300], 3, seed=52, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * 0.05
+    cu = d["cu_seqlens_host"]
+    p = kda.plan_warm_cp(cu, 3, 32, 12, device=DEV)
+    o_cp, s_cp = run(d, plan=kda.plan_segments(cu, 3, 32, device=DEV))
+    if aliased:
+        st = d["initial_state"].clone()
+        o, s = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                           cu_seqlens_host=cu, initial_state=st, final_state=st, plan=p)
+        torch.cuda.synchronize()
+    else:
+        o, s = run(d, plan=p)
+    assert torch.equal(o, o_cp) and torch.equal(s, s_cp), "armed fallback differs from the CP plan"
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+
+
+@pytest.mark.parametrize("g_scale", [1.0, 0.05])
+def test_graph_replay_of_warm_cp(g_scale):
+    """Warm-start CP captured in a HIP graph: every replay, with eager work
+    between replays, equals the eager result (fallback unarmed or armed)."""
+    d = draw([1500, 100], 4, seed=53, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * g_scale
+    cu_h = d["cu_seqlens_host"]
+    p = kda.plan_warm_cp(cu_h, 4, 24, 12, device=DEV)
+    cu = p.cu_device()
+    o_buf = torch.empty_like(d["q"])
+    s_buf = torch.empty_like(d["initial_state"])
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=cu_h,
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=cu_h,
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    o_e, s_e = run(d, plan=p)
+    for trial in range(3):
+        o_buf.zero_()
+        s_buf.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_buf, o_e) and torch.equal(s_buf, s_e), "replay %d differs from eager" % trial
+        run(d, mode=False)  # eager work between replays
+
+
 def test_split_plan_validation():
     d = draw([100], 2, seed=1, device=DEV)
     cu = d["cu_seqlens_host"]
     for split, warm in (([3], 8), ([7], 8), ([0], 0)):
         with pytest.raises(kda.KDAError):
             kda.plan_split(cu, 2, split, warm, device=DEV)
+    for seg, warm in ((8, 0), (4, 8), (0, 1)):
+        with pytest.raises(kda.KDAError):
+            kda.plan_warm_cp(cu, 2, seg, warm, device=DEV)
 
 
 # ---------------------------------------------------------------------------

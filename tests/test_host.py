@@ -73,20 +73,32 @@ def test_materialized_plan_sizes_records(kda_lib, monkeypatch):
 
 
 def test_auto_plan_splits_few_head_long_sequence(kda_lib):
+    """One 65536-token sequence with 8 heads: AUTO picks warm-start CP (all
+    segments in the fused launch), keeping the segmented pipeline, with its
+    own segment table, as the fallback."""
     p = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp="auto")
     info = p.info()
     assert info["uses_cp"] == 1 and info["n_cp_seqs"] == 1
+    assert info["warm_cp"] == 1 and info["split_warm_chunks"] >= 1
+    S, W = info["warm_cp_seg_chunks"], info["split_warm_chunks"]
     units = p.units()
-    segs = sorted((u["chunk0"], u["n_chunks"]) for u in units)
-    # chunk-aligned, contiguous, covering all 4096 chunks
+    segs = sorted((u["chunk0"], u["n_chunks"], u["warm_chunks"]) for u in units)
+    # chunk-aligned, contiguous, covering all 4096 chunks; every segment but
+    # the first warms up, and none starts before its warm-up
     pos = 0
-    for c0, n in segs:
-        assert c0 == pos and n >= 1
+    for c0, n, w in segs:
+        assert c0 == pos and n >= 1 and n <= S
+        assert w == (W if c0 > 0 else 0) and c0 >= w
         pos += n
     assert pos == 4096
-    assert min(n for _, n in segs[:-1]) >= 64  # minimum segment length
-    assert info["n_prescan"] == len(segs) - 1
-    assert info["est_cp_us"] < info["est_serial_us"]
+    # speculation slots: every warm-start segment (the last one included)
+    assert info["n_warm_segments"] == len(segs) - 1
+    # the fallback's segmented tables: pre_scan over all but the last segment
+    assert info["n_prescan"] >= 1 and info["k1_materialized"] == 1
+    assert 0 < info["est_warm_cp_us"] < info["est_cp_us"] < info["est_serial_us"]
+    # forced CP stays the segmented pipeline alone
+    forced = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=True).info()
+    assert forced["uses_cp"] == 1 and forced["warm_cp"] == 0
 
 
 def test_auto_plan_declines_saturated_and_short(kda_lib):
