@@ -207,8 +207,9 @@ __device__ __forceinline__ void store_unit_state(const K2Args& a, const UnitDesc
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// K1 (materialised form): one workgroup of 8 wavefronts per (chunk, head);
-// grid = total_chunks * H, head fastest. The rows are loaded whole and
+// K1 (materialised form): one workgroup of 8 wavefronts per (chunk, head),
+// head fastest (a gated launch caps the grid and strides over the items).
+// The rows are loaded whole and
 // staged through LDS as in the fused kernel; the staging area overlays the
 // record and scratch, which are written only after every wavefront has read
 // its phase-1 fragments.
@@ -225,30 +226,37 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     float* lw = (float*)(lds + REC_BYTES + K1_BYTES);
     uint8_t* stg = lds;
     const int H = a.c.H;
-    const int h = blockIdx.x % H;
-    const int gc = blockIdx.x / H;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const ChunkDesc cd = a.chunks[gc];
-    int64_t beg, end;
-    seq_bounds(a.c, cd.seq, beg, end);
-    const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
     const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, wave, lane);
-    const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0, h, h / a.c.group, wave);
-    RowChunk rc;
-    k1_load_chunk<GVA>(rs, 0, rows_of(tok0, end), lo, rc);
-    k1_stage(rc, wave, lane, lo, stg);
-    lds_barrier();
-    RawChunk raw;
-    k1_read_staged(stg, lane, lo, raw);
-    lds_barrier();  // the staging area is free again
-    k1_phase1(raw, wave, lane, rec, scr);
-    lds_barrier();
-    k1_phase2(wave, lane, rec, scr, lw);
-    lds_barrier();
-    u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_BYTES);
-    const u32x4* src = (const u32x4*)rec;
-    for (int i = threadIdx.x; i < REC_VEC; i += 512) dst[i] = src[i];
+    // (chunk, head) items, head fastest; one per workgroup, or a stride over
+    // them when the grid is capped
+    const int64_t n_items = (int64_t)a.c.total_chunks * H;
+    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int h = (int)(item % H);
+        const int gc = (int)(item / H);
+        const ChunkDesc cd = a.chunks[gc];
+        int64_t beg, end;
+        seq_bounds(a.c, cd.seq, beg, end);
+        const int64_t tok0 = beg + (int64_t)CH * cd.chunk;
+        const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0, h, h / a.c.group,
+                                          wave);
+        RowChunk rc;
+        k1_load_chunk<GVA>(rs, 0, rows_of(tok0, end), lo, rc);
+        k1_stage(rc, wave, lane, lo, stg);
+        lds_barrier();
+        RawChunk raw;
+        k1_read_staged(stg, lane, lo, raw);
+        lds_barrier();  // the staging area is free again
+        k1_phase1(raw, wave, lane, rec, scr);
+        lds_barrier();
+        k1_phase2(wave, lane, rec, scr, lw);
+        lds_barrier();
+        u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_BYTES);
+        const u32x4* src = (const u32x4*)rec;
+        for (int i = threadIdx.x; i < REC_VEC; i += 512) dst[i] = src[i];
+        lds_barrier();  // the record is read before the next item stages over it
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -665,8 +673,11 @@ hipError_t launch_beta_to_f32(const uint16_t* src, float* dst, int64_t n, hipStr
 }
 
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s) {
-    const long long n = (long long)a.c.total_chunks * a.c.H;
+    long long n = (long long)a.c.total_chunks * a.c.H;
     if (n <= 0) return hipSuccess;
+    // a gated launch is usually empty: a capped grid that strides over the
+    // items costs little to dispatch when every workgroup returns at once
+    if (a.c.gate && n > 2048) n = 2048;
     if (a.c.group > 1) hipLaunchKernelGGL(kda_k1_prepare<true>, dim3((unsigned)n), dim3(512), 0, s, a);
     else hipLaunchKernelGGL(kda_k1_prepare<false>, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();
