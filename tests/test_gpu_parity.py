@@ -299,6 +299,26 @@ def test_cp_bitwise_on_long_sequence_and_oracle():
     assert_close("final_state", s_cp, s_ref)
 
 
+def test_padded_batch_cp_paths_are_bitwise_serial():
+    """Equal-length batches passed as [B, T, H, 128] (no cu_seqlens) run
+    through every CP form: the segmented pipeline forced, AUTO, and warm-start
+    CP forced; each equals the packed serial result bit for bit (the cuLA
+    pull request's reviewer notes list CP on padded B > 1 as a limitation)."""
+    B, T, H = 3, 2048, 2
+    d = draw([T] * B, H, seed=54, state_std=0.1, device=DEV)
+    o_ser, s_ser = run(d, mode=False)
+    as4 = lambda x: x.view(B, T, *x.shape[1:])
+    q, k, v, g, beta = (as4(d[n]) for n in ("q", "k", "v", "g", "beta"))
+    cu = [i * T for i in range(B + 1)]
+    for label, kw in (("cp on", dict(use_intracard_cp=True)), ("auto", dict(use_intracard_cp="auto")),
+                      ("warm-start cp", dict(plan=kda.plan_warm_cp(cu, H, 32, 12, device=DEV)))):
+        o, s = kda.prefill(q, k, v, g, beta, initial_state=d["initial_state"], output_final_state=True, **kw)
+        torch.cuda.synchronize()
+        assert o.shape == (B, T, H, 128), label
+        assert torch.equal(o.reshape(B * T, H, 128), o_ser) and torch.equal(s, s_ser), label
+    assert kda.plan(cu, H, True, device=DEV).info()["n_cp_seqs"] == B
+
+
 def test_long_sequence_segmented_cp_is_bitwise_serial():
     """The segmented CP pipeline alone (forced) on the 65536-token workload:
     bitwise the serial result."""
