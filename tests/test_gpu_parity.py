@@ -246,11 +246,20 @@ def test_head_permutation_is_bitwise():
     assert torch.equal(op, o.index_select(1, perm)) and torch.equal(sp, s.index_select(1, perm))
 
 
-def test_repeated_runs_are_bitwise_deterministic():
-    d = draw([300, 77], 4, seed=10, state_std=0.1, device=DEV)
-    o0, s0 = run(d)
+@pytest.mark.parametrize("form", ["serial", "split", "warm_cp", "cp"])
+def test_repeated_runs_are_bitwise_deterministic(form):
+    """Repeated runs are bitwise equal in every plan form (fixed reduction
+    orders everywhere; no atomics in any result)."""
+    d = draw([600, 77], 4, seed=10, state_std=0.1, device=DEV)
+    cu = d["cu_seqlens_host"]
+    plan = {"serial": None,
+            "split": lambda: kda.plan_split(cu, 4, [20, 0], 12, device=DEV),
+            "warm_cp": lambda: kda.plan_warm_cp(cu, 4, 16, 12, device=DEV),
+            "cp": lambda: kda.plan_segments(cu, 4, 8, device=DEV)}[form]
+    p = plan() if plan else None
+    o0, s0 = run(d, plan=p)
     for _ in range(20):
-        o, s = run(d)
+        o, s = run(d, plan=p)
         assert torch.equal(o, o0) and torch.equal(s, s0)
 
 
