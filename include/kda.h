@@ -123,7 +123,13 @@ const char *kda_version(void);
 /* Build the plan for one packed batch: chunk table, K2 work units ordered
  * longest chain first, and -- when `mode` asks for it, or AUTO predicts a win
  * for the device's compute-unit count -- chunk-aligned segments for intracard
- * CP. cu_seqlens_host: host int32 [n_seqs + 1]. dk and dv must be 128.
+ * CP. ON always gives the segmented pipeline (kda_plan_prefill_segments). AUTO
+ * may instead give warm-start CP (kda_plan_prefill_warm_cp) for few-head long
+ * sequences, or warm-start splits of the longest sequences of a batch that
+ * fills the compute units about once (kda_plan_prefill_split). Both speculate
+ * that the decay forgets a segment's carry within its warm-up, and stay exact
+ * when it does not, at a cost. OFF never segments.
+ * cu_seqlens_host: host int32 [n_seqs + 1]. dk and dv must be 128.
  * The plan keeps its tables in device memory of ctx's device (uploaded here,
  * synchronously; do not call while a stream of that device is being
  * captured). The caller frees it with kda_plan_destroy. */
@@ -158,7 +164,8 @@ kda_status kda_plan_prefill_segments(kda_ctx *ctx, const int32_t *cu_seqlens_hos
  * reruns the segment from the first segment's end state. Either way the
  * result equals the unsplit serial path's bit for bit wherever the CP
  * path's does. split_chunk[i] must be 0 or in [warm_chunks, chunks of
- * sequence i). AUTO plans (kda_plan_prefill) pick such splits themselves.
+ * sequence i), and warm_chunks >= 1; otherwise KDA_ERR_INVALID and no plan.
+ * AUTO plans (kda_plan_prefill) pick such splits themselves.
  * Device tables are uploaded as in kda_plan_prefill. */
 kda_status kda_plan_prefill_split(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
                                   int32_t H, int32_t dk, int32_t dv, const int32_t *split_chunk,
@@ -176,7 +183,9 @@ kda_status kda_plan_prefill_split(kda_ctx *ctx, const int32_t *cu_seqlens_host, 
  * result. No host synchronisation is involved, so a captured graph replays
  * either way. AUTO plans choose this for few-head long sequences when the
  * planner predicts a win over the segmented path. 1 <= warm_chunks <=
- * seg_chunks. Device tables are uploaded as in kda_plan_prefill. */
+ * seg_chunks, else KDA_ERR_INVALID. The plan's workspace includes the
+ * fallback's (the K1 records of every chunk). Device tables are uploaded as
+ * in kda_plan_prefill. */
 kda_status kda_plan_prefill_warm_cp(kda_ctx *ctx, const int32_t *cu_seqlens_host, int32_t n_seqs,
                                     int32_t H, int32_t dk, int32_t dv, int32_t seg_chunks,
                                     int32_t warm_chunks, kda_plan **out);
