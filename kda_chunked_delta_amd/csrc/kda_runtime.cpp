@@ -79,11 +79,15 @@ struct PlannerConsts {
 
 PlannerConsts planner_consts() {
     PlannerConsts c;
-    c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.7);
-    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 1.72);
-    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 2.93);
-    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.3);
-    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 2.63);
+    // fitted at steady clocks on the 65536-token, 8-head workload (K1 225 us
+    // over 128 chunk-heads per CU, pre_scan 138 us and segment-K2 139 us over
+    // 64-chunk segments, merge 56 us over 63 segments) and on the fused
+    // kernel's interval with few CUs busy
+    c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.21);
+    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 1.76);
+    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 2.16);
+    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.17);
+    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 0.90);
     c.launch_us = env_double("KDA_CP_LAUNCH_US", 5.0);
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
     c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
