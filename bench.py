@@ -118,6 +118,39 @@ def cpu_baseline(d, max_seconds):
                       % (nseq, len(cu) - 1, T, H, reps, dt)}
 
 
+def cold_steps(step, tokens, n):
+    """Per-step times with the caches cold: before each step a 512 MiB write
+    (twice the 256 MiB Infinity Cache) evicts the inputs; HIP events bracket
+    the step alone, after a synchronisation. The same one-step-at-a-time
+    timing without the flush is reported beside it, so the difference is the
+    caches' share, not the launch from an idle queue."""
+    import torch
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")
+
+    def one_by_one(cold):
+        times = []
+        for i in range(n):
+            if cold:
+                flush.fill_(float(i))
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        times.sort()
+        return times
+
+    warm = one_by_one(False)
+    cold = one_by_one(True)
+    med, wmed = cold[len(cold) // 2], warm[len(warm) // 2]
+    return {"steps": n, "flush_bytes": flush.numel() * 4, "ms_per_step_median": round(med, 5),
+            "ms_per_step_min": round(cold[0], 5), "ms_per_step_max": round(cold[-1], 5),
+            "value_median": round(tokens / (med * 1e-3), 1),
+            "warm_one_by_one_ms_median": round(wmed, 5)}
+
+
 def plan_kind(info):
     if info.get("warm_cp", 0):
         return "warm-start cp(segments of %d chunks, warm-up %d chunks)" % (info["warm_cp_seg_chunks"],
@@ -139,6 +172,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="varlen8_h32", choices=sorted(WORKLOAD_TEXT) + sorted(DECODE_TEXT))
     ap.add_argument("--cp", default="auto", choices=["auto", "on", "off"])
+    ap.add_argument("--cold-steps", type=int, default=50,
+                    help="after the timed steps, time this many more one by one with the caches "
+                         "flushed before each (reported as \"cold\"; 0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target duration of the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -243,6 +279,9 @@ def main():
         "mfma_roofline": {"bound": "mfma", "achieved": round(alg_flops / (path_ms * 1e-3) / 1e12, 2),
                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4)},
     }
+    if args.cold_steps > 0:
+        line["cold"] = cold_steps(step, Tt, args.cold_steps)
+        print("bench: cold %s" % line["cold"], file=sys.stderr, flush=True)
     if args.cpu_seconds > 0:
         print("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
