@@ -94,6 +94,10 @@ typedef struct {
     int32_t warm_cp_seg_chunks;/* its segment length in chunks */
     int32_t n_warm_segments;   /* its speculation slots (warm-start and last segments) */
     double  est_warm_cp_us;    /* planner's estimate of warm-start CP (-1: none) */
+    int32_t speculation_off;   /* 1 once an earlier call of this split or warm-start CP plan
+                                  found that speculation failed: later calls outside graph
+                                  capture run the plan's exact path (the batch unsplit, or
+                                  the segmented pipeline), which gives the same bits */
 } kda_plan_info;
 
 /* One K2 work unit of a plan (a whole sequence, or one segment of it). */

@@ -154,6 +154,7 @@ struct kda_plan {
     std::vector<MergeDesc> merges;      // CP merge items
     std::vector<UnitDesc> fixups;       // warm-start segments, as rerun from their carry
     std::vector<UnitDesc> cp_units;     // warm-start CP: the segmented fallback's K2 units
+    std::vector<UnitDesc> alt_units;    // split plans: the batch unsplit (the exact path)
     // workspace layout (byte offsets into the arena)
     size_t off_rec = 0, off_b = 0, off_m = 0, off_mlive = 0, off_carry = 0;
     size_t off_spec_states = 0, off_spec_flags = 0, off_gate = 0;
@@ -161,7 +162,21 @@ struct kda_plan {
     int device = -1;
     void* dev_tables = nullptr;
     size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_prescan = 0, dev_off_merges = 0, dev_off_fixups = 0;
-    size_t dev_off_cp_units = 0;
+    size_t dev_off_cp_units = 0, dev_off_alt_units = 0;
+    // Speculation feedback, outside graph capture: a speculative call (the
+    // first, then every 64th) copies its outcome (split plans: the speculation
+    // flags; warm-start CP: the gate) into pinned host memory and records an
+    // event; a later call
+    // that finds the copy complete and a failure in it turns speculation off
+    // for this plan, which then runs its exact path (unsplit serial, or the
+    // segmented pipeline ungated). Results are the same bits either way.
+    mutable std::mutex spec_mu;
+    mutable int32_t* spec_host = nullptr;
+    mutable size_t spec_words = 0;
+    mutable hipEvent_t spec_event = nullptr;
+    mutable bool spec_pending = false;
+    mutable bool spec_off = false;
+    mutable uint64_t spec_calls = 0;  // the outcome is copied on the first call and every 64th
 };
 
 namespace {
@@ -419,6 +434,12 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
         std::stable_sort(p->cp_units.begin(), p->cp_units.end(),
                          [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
     }
+    if (n_split > 0) {
+        for (int i = 0; i < n_seqs; ++i)
+            p->alt_units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1, 0, -1, -1, 0});
+        std::stable_sort(p->alt_units.begin(), p->alt_units.end(),
+                         [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
+    }
     // longest chains first (a warm-start segment runs its warm-up twice)
     std::stable_sort(p->units.begin(), p->units.end(), [](const UnitDesc& a, const UnitDesc& b) {
         return a.n_chunks + 2 * a.warm > b.n_chunks + 2 * b.warm;
@@ -498,6 +519,8 @@ kda_status upload_plan(kda_plan* p, int device) {
     off = align_up(off + p->fixups.size() * sizeof(UnitDesc), 256);
     p->dev_off_cp_units = off;
     off = align_up(off + p->cp_units.size() * sizeof(UnitDesc), 256);
+    p->dev_off_alt_units = off;
+    off = align_up(off + p->alt_units.size() * sizeof(UnitDesc), 256);
     std::vector<uint8_t> host(off, 0);
     if (!p->chunks.empty()) memcpy(&host[p->dev_off_chunks], p->chunks.data(), p->chunks.size() * sizeof(ChunkDesc));
     if (!p->units.empty()) memcpy(&host[p->dev_off_units], p->units.data(), p->units.size() * sizeof(UnitDesc));
@@ -506,6 +529,8 @@ kda_status upload_plan(kda_plan* p, int device) {
     if (!p->fixups.empty()) memcpy(&host[p->dev_off_fixups], p->fixups.data(), p->fixups.size() * sizeof(UnitDesc));
     if (!p->cp_units.empty())
         memcpy(&host[p->dev_off_cp_units], p->cp_units.data(), p->cp_units.size() * sizeof(UnitDesc));
+    if (!p->alt_units.empty())
+        memcpy(&host[p->dev_off_alt_units], p->alt_units.data(), p->alt_units.size() * sizeof(UnitDesc));
     int prev = -1;
     hipError_t e = hipGetDevice(&prev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -707,11 +732,16 @@ kda_status kda_plan_prefill_warm_cp(kda_ctx* ctx, const int32_t* cu_seqlens_host
 
 void kda_plan_destroy(kda_plan* p) {
     if (!p) return;
-    if (p->dev_tables) {
+    if (p->dev_tables || p->spec_event || p->spec_host) {
         int prev = -1;
         (void)hipGetDevice(&prev);
         (void)hipSetDevice(p->device);
-        (void)hipFree(p->dev_tables);
+        if (p->spec_event) {
+            (void)hipEventSynchronize(p->spec_event);  // the last copy into spec_host has landed
+            (void)hipEventDestroy(p->spec_event);
+        }
+        if (p->spec_host) (void)hipHostFree(p->spec_host);
+        if (p->dev_tables) (void)hipFree(p->dev_tables);
         if (prev >= 0) (void)hipSetDevice(prev);
     }
     delete p;
@@ -722,6 +752,8 @@ size_t kda_plan_workspace_bytes(const kda_plan* p) { return p ? p->info.workspac
 kda_status kda_plan_get_info(const kda_plan* p, kda_plan_info* info) {
     if (!p || !info) return fail(KDA_ERR_INVALID, "kda_plan_get_info: NULL argument");
     *info = p->info;
+    std::lock_guard<std::mutex> sl(p->spec_mu);
+    info->speculation_off = p->spec_off ? 1 : 0;
     return KDA_OK;
 }
 
@@ -931,6 +963,69 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
         });
         if (e != hipSuccess) return hip_fail(e, "beta_to_f32 launch");
     }
+    // speculation feedback from an earlier call of this plan (never under capture)
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    const bool speculative = p->info.warm_cp || p->info.n_split_seqs > 0;
+    bool spec_off = false;
+    if (speculative) {
+        std::lock_guard<std::mutex> sl(p->spec_mu);
+        if (p->spec_pending && !capturing && hipEventQuery(p->spec_event) == hipSuccess) {
+            p->spec_pending = false;
+            for (size_t i = 0; i < p->spec_words && !p->spec_off; ++i) p->spec_off = p->spec_host[i] != 0;
+        }
+        spec_off = p->spec_off;
+    }
+    // after a speculative call: copy its outcome back without waiting for it
+    // (on a plan's first call and every 64th, so the copy costs little)
+    auto report = [&](const int32_t* dev_words, size_t n_words) -> hipError_t {
+        if (capturing || n_words == 0) return hipSuccess;
+        std::lock_guard<std::mutex> sl(p->spec_mu);
+        if (p->spec_calls++ % 64 != 0 || p->spec_pending) return hipSuccess;
+        hipError_t err = hipSuccess;
+        if (!p->spec_host) {
+            err = hipHostMalloc((void**)&p->spec_host, n_words * sizeof(int32_t), hipHostMallocDefault);
+            if (err != hipSuccess) { p->spec_host = nullptr; return err; }
+            p->spec_words = n_words;
+            err = hipEventCreateWithFlags(&p->spec_event, hipEventDisableTiming);
+            if (err != hipSuccess) { p->spec_event = nullptr; return err; }
+        }
+        err = hipMemcpyAsync(p->spec_host, dev_words, p->spec_words * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+        if (err == hipSuccess) err = hipEventRecord(p->spec_event, stream);
+        if (err == hipSuccess) p->spec_pending = true;
+        return err;
+    };
+    if (p->info.warm_cp && spec_off) {
+        // the exact path of a warm-start CP plan: the segmented pipeline alone
+        K1Args k1{c, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
+        e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
+        if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+        PrescanArgs pa{c, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
+                       (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
+        if (!p->prescan.empty()) {
+            e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
+            if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
+        }
+        MergeArgs ma{c, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
+                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
+                     state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
+        if (!p->merges.empty()) {
+            e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
+            if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
+        }
+        K2Args kc{c, (const UnitDesc*)(tabs + p->dev_off_cp_units), (int32_t)p->cp_units.size(), s0, sT,
+                  (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0, nullptr, nullptr, 0, 0};
+        e = timed("k2_segment", [&] { return launch_k2_recur(kc, stream); });
+        if (e != hipSuccess) return hip_fail(e, "k2_segment launch");
+        return KDA_OK;
+    }
+    if (p->info.n_split_seqs > 0 && spec_off) {
+        // the exact path of a split plan: the batch unsplit
+        K2Args ks{c, (const UnitDesc*)(tabs + p->dev_off_alt_units), (int32_t)p->alt_units.size(), s0, sT,
+                  (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0, nullptr, nullptr, 0, 1};
+        e = timed("fused_serial", [&] { return launch_fused(ks, stream); });
+        if (e != hipSuccess) return hip_fail(e, "fused launch");
+        return KDA_OK;
+    }
     if (p->info.warm_cp) {
         // warm-start CP: all segments in one fused launch; the segmented
         // pipeline runs only if the flag reduction arms its gate
@@ -945,6 +1040,7 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
             return launch_flags_or(kw.spec_flags, (int64_t)p->info.n_warm_segments * p->info.H * 8, gate, stream);
         });
         if (e != hipSuccess) return hip_fail(e, "flags_or launch");
+        if ((e = report(gate, 1)) != hipSuccess) return hip_fail(e, "speculation feedback");
         CommonArgs cg = c;
         cg.gate = gate;
         K1Args k1{cg, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
@@ -1018,6 +1114,8 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
         kf.fixup = 1;
         e = timed("fused_fixup", [&] { return launch_fused(kf, stream); });
         if (e != hipSuccess) return hip_fail(e, "fix-up launch");
+        if ((e = report(ka.spec_flags, p->fixups.size() * (size_t)p->info.H * 8)) != hipSuccess)
+            return hip_fail(e, "speculation feedback");
     }
     return KDA_OK;
 }

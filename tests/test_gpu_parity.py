@@ -547,6 +547,55 @@ def test_graph_replay_of_warm_cp(g_scale):
         run(d, mode=False)  # eager work between replays
 
 
+def _launches(fn):
+    """Names of the library's launches during fn()."""
+    ctx = kda.context(DEV)
+    ctx.set_timing(True)
+    try:
+        r = fn()
+        torch.cuda.synchronize()
+        names = set(ctx.timing())
+    finally:
+        ctx.set_timing(False)
+    return r, names
+
+
+@pytest.mark.parametrize("kind", ["split", "warm_cp"])
+def test_speculation_turns_off_after_it_fails(kind):
+    """Weak decay: the first call speculates, fails and stays exact; once its
+    outcome has reached the host, the plan runs its exact path (the batch
+    unsplit, or the segmented pipeline), with the same bits."""
+    d = draw([1200, 300], 3, seed=81, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * 0.05
+    cu = d["cu_seqlens_host"]
+    if kind == "split":
+        p = kda.plan_split(cu, 3, [30, 0], 12, device=DEV)
+        ref_o, ref_s = run(d, mode=False)
+        spec_name, exact_name = "fused_split", "fused_serial"
+    else:
+        p = kda.plan_warm_cp(cu, 3, 24, 12, device=DEV)
+        ref_o, ref_s = run(d, plan=kda.plan_segments(cu, 3, 24, device=DEV))
+        spec_name, exact_name = "fused_warm_cp", "k2_segment"
+    (o1, s1), n1 = _launches(lambda: run(d, plan=p))
+    assert spec_name in n1 and p.info()["speculation_off"] == 0
+    (o2, s2), n2 = _launches(lambda: run(d, plan=p))
+    assert spec_name not in n2 and exact_name in n2, n2
+    assert p.info()["speculation_off"] == 1
+    for o, s in ((o1, s1), (o2, s2)):
+        assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
+
+
+def test_speculation_stays_on_while_it_holds():
+    d = draw([1200, 300], 3, seed=82, state_std=0.1, device=DEV)
+    cu = d["cu_seqlens_host"]
+    p = kda.plan_split(cu, 3, [30, 0], 12, device=DEV)
+    o_ser, s_ser = run(d, mode=False)
+    for _ in range(3):
+        (o, s), names = _launches(lambda: run(d, plan=p))
+        assert "fused_split" in names and torch.equal(o, o_ser) and torch.equal(s, s_ser)
+    assert p.info()["speculation_off"] == 0
+
+
 def test_split_plan_validation():
     d = draw([100], 2, seed=1, device=DEV)
     cu = d["cu_seqlens_host"]
