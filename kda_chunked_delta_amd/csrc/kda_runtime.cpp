@@ -994,30 +994,36 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
         if (err == hipSuccess) p->spec_pending = true;
         return err;
     };
-    if (p->info.warm_cp && spec_off) {
-        // the exact path of a warm-start CP plan: the segmented pipeline alone
-        K1Args k1{c, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
+    // The segmented pipeline: K1 records, pre_scan, carry merge, K2 over the
+    // records with the given units. cc.gate gates every launch when set (the
+    // fallback of warm-start CP).
+    auto segmented = [&](const CommonArgs& cc, const UnitDesc* k2_units, int32_t n_k2_units,
+                         const char* k2_name) -> kda_status {
+        K1Args k1{cc, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
         e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
         if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
-        PrescanArgs pa{c, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
-                       (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
         if (!p->prescan.empty()) {
+            PrescanArgs pa{cc, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
+                           (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
             e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
             if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
         }
-        MergeArgs ma{c, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
-                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
-                     state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
         if (!p->merges.empty()) {
+            MergeArgs ma{cc, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
+                         (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
+                         state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
             e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
             if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
         }
-        K2Args kc{c, (const UnitDesc*)(tabs + p->dev_off_cp_units), (int32_t)p->cp_units.size(), s0, sT,
-                  (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0, nullptr, nullptr, 0, 0};
-        e = timed("k2_segment", [&] { return launch_k2_recur(kc, stream); });
-        if (e != hipSuccess) return hip_fail(e, "k2_segment launch");
+        K2Args kc{cc, k2_units, n_k2_units, s0, sT, (float*)(ws + p->off_carry), (uint16_t*)out, scale,
+                  state16 ? 1 : 0, nullptr, nullptr, 0, 0};
+        e = timed(k2_name, [&] { return launch_k2_recur(kc, stream); });
+        if (e != hipSuccess) return hip_fail(e, "k2 launch");
         return KDA_OK;
-    }
+    };
+    const UnitDesc* cp_units = (const UnitDesc*)(tabs + p->dev_off_cp_units);
+    if (p->info.warm_cp && spec_off)  // the exact path of a warm-start CP plan: the pipeline alone
+        return segmented(c, cp_units, (int32_t)p->cp_units.size(), "k2_segment");
     if (p->info.n_split_seqs > 0 && spec_off) {
         // the exact path of a split plan: the batch unsplit
         K2Args ks{c, (const UnitDesc*)(tabs + p->dev_off_alt_units), (int32_t)p->alt_units.size(), s0, sT,
@@ -1043,26 +1049,8 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
         if ((e = report(gate, 1)) != hipSuccess) return hip_fail(e, "speculation feedback");
         CommonArgs cg = c;
         cg.gate = gate;
-        K1Args k1{cg, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
-        e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
-        if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
-        PrescanArgs pa{cg, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
-                       (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
-        if (!p->prescan.empty()) {
-            e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
-            if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
-        }
-        MergeArgs ma{cg, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
-                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
-                     state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
-        if (!p->merges.empty()) {
-            e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
-            if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
-        }
-        K2Args kc{cg, (const UnitDesc*)(tabs + p->dev_off_cp_units), (int32_t)p->cp_units.size(), s0, sT,
-                  (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0, nullptr, nullptr, 0, 0};
-        e = timed("k2_segment", [&] { return launch_k2_recur(kc, stream); });
-        if (e != hipSuccess) return hip_fail(e, "k2_segment launch");
+        const kda_status st2 = segmented(cg, cp_units, (int32_t)p->cp_units.size(), "k2_segment");
+        if (st2 != KDA_OK) return st2;
         if (!direct && !p->fixups.empty()) {
             // publish the final states the warm-start launch left in scratch
             K2Args kf = kw;
@@ -1076,24 +1064,9 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
         return KDA_OK;
     }
     const bool mat = p->info.k1_materialized != 0;
-    if (mat) {
-        K1Args k1{c, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
-        e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
-        if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
-    }
-    if (p->info.n_prescan > 0) {
-        PrescanArgs pa{c, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
-                       (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
-        e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
-        if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
-    }
-    if (p->info.n_cp_seqs > 0) {
-        MergeArgs ma{c, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
-                     (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
-                     state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
-        e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
-        if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
-    }
+    if (mat)  // segmented CP, or the two-kernel serial form (no pre_scan, no merge)
+        return segmented(c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(),
+                         p->info.uses_cp ? "k2_segment" : "k2_recur");
     K2Args ka{c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(), s0, sT,
               (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0,
               (int32_t*)(ws + p->off_spec_flags), (float*)(ws + p->off_spec_states), 0, 0};
@@ -1101,9 +1074,7 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     // launch, after every unit has read its initial state
     ka.spec_final_direct = (sT && s0 && sT == s0) ? 0 : 1;
     const bool split = p->info.n_split_seqs > 0;
-    const char* k2name = mat ? (p->info.uses_cp ? "k2_segment" : "k2_recur")
-                             : (p->info.uses_cp ? "fused_segment" : (split ? "fused_split" : "fused_serial"));
-    e = timed(k2name, [&] { return mat ? launch_k2_recur(ka, stream) : launch_fused(ka, stream); });
+    e = timed(split ? "fused_split" : "fused_serial", [&] { return launch_fused(ka, stream); });
     if (e != hipSuccess) return hip_fail(e, "k2 launch");
     if (split) {
         // warm-start segments: keep (and publish the end state of) each one
