@@ -72,6 +72,10 @@ constexpr int K1_BYTES = K1_BETA + 64;
 // stride puts the 16 lanes of each b128 phase on distinct banks)
 constexpr int K1_LSTRIDE = 20;
 constexpr int K1_LBYTES = 16 * K1_LSTRIDE * 4;
+// L^T shared by the fused kernel's T' wavefronts: K1_LBYTES of L^T, then
+// beta of the chunk's 16 rows
+constexpr int LB_BETA = K1_LBYTES;
+constexpr int LB_BYTES = K1_LBYTES + 64;
 
 // Phase-2 roles: wavefronts 0..3 (one per SIMD) each form four rows of T',
 // wavefront WAVE_QK forms A_qk.
@@ -451,7 +455,11 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
 // substitution over 15 dependent steps, each one DPP-broadcast
 // multiply-subtract.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, const uint8_t* scr, float* lw) {
+// L = strict-lower(diag(beta) A_kk) from the phase-1 Gram factors, stored
+// transposed (lt[c * K1_LSTRIDE + r] = L[r][c]), so that lane (gg, i) of a
+// reader finds column i of L in row i of lt. With lbeta, the chunk's beta
+// is copied beside it.
+__device__ __forceinline__ void k1_lkk(int lane, const uint8_t* scr, float* lt, float* lbeta) {
     const int gg = lane >> 4, m = lane & 15;
     // (k exp(G - G_ref)) (k exp(G_ref - G))^T: lane holds A_kk[r][m], r = 4gg + v,
     // which the row's beta then scales
@@ -464,13 +472,18 @@ __device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, cons
     f32x4 l;
 #pragma unroll
     for (int v = 0; v < 4; ++v) l[v] = (m < 4 * gg + v) ? br[v] * a[v] : 0.f;
-    // through LDS as L^T (lw[c * K1_LSTRIDE + r] = L[r][c]): lane (gg, i) then holds
-    // column i of L, lc[K] = L[K][i]
-    *(f32x4*)(lw + m * K1_LSTRIDE + 4 * gg) = l;
-    float lc[16];
+    *(f32x4*)(lt + m * K1_LSTRIDE + 4 * gg) = l;
+    if (lbeta && gg == 0) lbeta[m] = *(const float*)(scr + K1_BETA + 4 * m);
+}
+
+// Rows 4 s4 .. 4 s4 + 3 of T' = (I + L)^-1 diag(beta) from L^T (as k1_lkk
+// stores it) and beta, to the record.
+__device__ __forceinline__ void k1_tsolve(int lane, int s4, uint8_t* rec, const float* lt, const float* beta) {
+    const int gg = lane >> 4, m = lane & 15;
+    float lc[16];  // lc[K] = L[K][m]
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const f32x4 c = *(const f32x4*)(lw + m * K1_LSTRIDE + 4 * q);
+        const f32x4 c = *(const f32x4*)(lt + m * K1_LSTRIDE + 4 * q);
 #pragma unroll
         for (int v = 0; v < 4; ++v) lc[4 * q + v] = c[v];
     }
@@ -493,12 +506,18 @@ __device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, cons
     step(std::integral_constant<int, 1>{});
     // T'[r][i] = T[r][i] beta_i, split into bf16 hi + lo, to the A-fragment
     // layout T'[m'][4gg' + j] at lane (gg', m') = (i >> 2, r), j = i & 3
-    const float tb = t * *(const float*)(scr + K1_BETA + 4 * m);
+    const float tb = t * beta[m];
     const uint32_t th = pack_bf16(tb, tb);
     const uint32_t tl = pack_bf16(tb - bf16_lo(th), tb - bf16_lo(th));
     uint8_t* td = rec + REC_T + ((16 * (m >> 2) + 4 * s4 + gg) * 4 + (m & 3)) * 2;
     *(uint16_t*)(td + 0) = (uint16_t)th;
     *(uint16_t*)(td + 512) = (uint16_t)tl;
+}
+
+// Both halves on one wavefront, through its private lw (1 KiB).
+__device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, const uint8_t* scr, float* lw) {
+    k1_lkk(lane, scr, lw, nullptr);
+    k1_tsolve(lane, s4, rec, lw, (const float*)(scr + K1_BETA));
 }
 
 __device__ __forceinline__ void k1_phase2_qk(int lane, uint8_t* rec, const uint8_t* scr) {

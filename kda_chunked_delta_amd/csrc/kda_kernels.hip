@@ -265,32 +265,34 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 // ends with barrier i:
 //   - wavefronts 0..7 hold the state (wavefront w: value columns
 //     16w..16w+15, in MFMA accumulators for the whole unit), advance it over
-//     chunk i and store that chunk's output; with P2_ON_STATE they also run
-//     K1 phase 2 (T' on w < 4, A_qk on w = WAVE_QK) of chunk i+1;
-//   - wavefronts 8 + w run K1 phase 1 of chunk i+2 (key channels and value
-//     columns 16w..16w+15) from the staged rows, stage the rows of chunk i+3
+//     chunk i and store that chunk's output. Wavefronts 0..3 also form rows
+//     4w..4w+3 of T' of chunk i+1 from the shared L^T; wavefront WAVE_QK
+//     forms A_qk of chunk i+2 and L of chunk i+2, once, into the shared L^T;
+//   - wavefronts 8 + w run K1 phase 1 of chunk i+3 (key channels and value
+//     columns 16w..16w+15) from the staged rows, stage the rows of chunk i+4
 //     that they loaded two intervals earlier, and issue the row loads of
-//     chunk i+5 (rows 2w, 2w+1; into the register set just staged).
+//     chunk i+6 (rows 2w, 2w+1; into the register set just staged).
 // Each SIMD holds two state wavefronts and two K1 wavefronts. Records live in
-// a 3-deep LDS ring, K1 scratch and the staged rows in 2-deep ones. Both
-// roles run the same even number of intervals, nc + 2 rounded up, after one
-// start-up barrier: the trailing K1 work on chunks past the end reads zeros
-// (a buffer load of a chunk with no rows touches no memory) and fills slots
-// nobody reads, so the K1 loop body is unconditional and the compiler's wait
-// for a register set covers only that set's loads.
+// a 4-deep LDS ring; K1 scratch, the shared L^T and the staged rows in 2-deep
+// ones. Both roles run three start-up intervals and then the same even
+// number of intervals, after one start-up barrier: the trailing K1 work on
+// chunks past the end reads zeros (a buffer load of a chunk with no rows
+// touches no memory) and fills slots nobody reads, so the K1 loop body is
+// unconditional and the compiler's wait for a register set covers only that
+// set's loads.
 // ---------------------------------------------------------------------------
-constexpr bool P2_ON_STATE = true;
-constexpr int FUSED_LDS = 3 * REC_BYTES + 2 * K1_BYTES + N_WAVE_T * K1_LBYTES + 2 * STG_BYTES;
+constexpr int FUSED_LDS = 4 * REC_BYTES + 2 * K1_BYTES + 2 * LB_BYTES + 2 * STG_BYTES;
+static_assert(FUSED_LDS <= 160 * 1024, "fused kernel LDS");
 
 // GVA: q/k heads differ from the value heads (value head h reads q/k head
 // h / group); the plain instance keeps the q/k loads on v's offsets.
 template <bool GVA>
 __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* recs = smem;
-    uint8_t* scrs = smem + 3 * REC_BYTES;
-    float* lw = (float*)(scrs + 2 * K1_BYTES);
-    uint8_t* stgs = smem + 3 * REC_BYTES + 2 * K1_BYTES + N_WAVE_T * K1_LBYTES;
+    uint8_t* recs = smem;                      // 4 records
+    uint8_t* scrs = recs + 4 * REC_BYTES;      // 2 K1 scratch areas
+    uint8_t* lbs = scrs + 2 * K1_BYTES;        // 2 shared L^T + beta
+    uint8_t* stgs = lbs + 2 * LB_BYTES;        // 2 staged chunks
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const UnitDesc u = a.units[blockIdx.x / H];
@@ -337,7 +339,8 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     // is chunk chunk0 + c.
     const int W = u.warm;
     const int n_steps = nc + 2 * W;
-    const int n_int = (n_steps + 3) & ~1;  // barrier intervals i = -2 .. n_int - 3
+    // barrier intervals: -3, -2, -1, then 0 .. n_main - 1 (even)
+    const int n_main = (n_steps + 1) & ~1;
     if (wave < 8) {
         // state wavefronts
         f32x4 S[8][1];
@@ -350,28 +353,40 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         const int rem = (int)(end - tok0);
         auto step = [&](int c, int i) __attribute__((always_inline)) {
             f32x4 oacc[1];
-            chain_step<1, true, true>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, oacc);
+            chain_step<1, true, true>(recs + ring_off((i % 4) * REC_BYTES), S, w8, lane, oacc);
             store_output(a, h, tok0 + (int64_t)CH * c, chunk_rows(rem, c), oacc[0], w8, gg, m);
         };
-        // one loop per phase-2 role (0: none, 1: rows 4 w8.. of T', 2: A_qk),
-        // so that each loop body is one block in which phase 2 of chunk i + 1
-        // (independent of the chain) interleaves with the chain over chunk i
+        // one loop per phase-2 role (0: none, 1: rows 4 w8.. of T', 2: A_qk and
+        // L), so that each loop body is one block in which phase 2 of later
+        // chunks (independent of the chain) interleaves with the chain over chunk i
         auto run = [&](auto role) __attribute__((always_inline)) {
             constexpr int R = decltype(role)::value;
-            auto p2 = [&](int c) __attribute__((always_inline)) {
-                uint8_t* rec = recs + ring_off((c % 3) * REC_BYTES);
-                const uint8_t* scr = scrs + ring_off((c & 1) * K1_BYTES);
-                if constexpr (R == 1) k1_phase2_t(lane, w8, rec, scr, lw + w8 * (K1_LBYTES / 4));
-                if constexpr (R == 2) k1_phase2_qk(lane, rec, scr);
+            auto gram = [&](int c) __attribute__((always_inline)) {  // A_qk and L of chunk c
+                if constexpr (R == 2) {
+                    const uint8_t* scr = scrs + ring_off((c & 1) * K1_BYTES);
+                    float* lb = (float*)(lbs + ring_off((c & 1) * LB_BYTES));
+                    k1_phase2_qk(lane, recs + ring_off((c % 4) * REC_BYTES), scr);
+                    k1_lkk(lane, scr, lb, lb + LB_BETA / 4);
+                }
             };
-            lds_barrier();  // interval -2: nothing to do yet
-            p2(0);
+            auto solve = [&](int c) __attribute__((always_inline)) {  // rows of T' of chunk c
+                if constexpr (R == 1) {
+                    const float* lb = (const float*)(lbs + ring_off((c & 1) * LB_BYTES));
+                    k1_tsolve(lane, w8, recs + ring_off((c % 4) * REC_BYTES), lb, lb + LB_BETA / 4);
+                }
+            };
+            lds_barrier();  // interval -3: phase 1 of chunk 0
+            gram(0);
+            lds_barrier();  // interval -2
+            gram(1);
+            solve(0);
             lds_barrier();  // interval -1
             if (W > 0) {
                 f32x4 unused[1];
                 for (int i = 0; i < W; ++i) {
-                    p2(i + 1);
-                    chain_step<1, false, false>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, unused);
+                    gram(i + 2);
+                    solve(i + 1);
+                    chain_step<1, false, false>(recs + ring_off((i % 4) * REC_BYTES), S, w8, lane, unused);
                     lds_barrier();
                 }
                 const bool live = tile_nonzero(S);
@@ -379,20 +394,21 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) S[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
                 for (int i = W; i < 2 * W; ++i) {
-                    p2(i + 1);
-                    chain_step<1, true, false>(recs + ring_off((i % 3) * REC_BYTES), S, w8, lane, unused);
+                    gram(i + 2);
+                    solve(i + 1);
+                    chain_step<1, true, false>(recs + ring_off((i % 4) * REC_BYTES), S, w8, lane, unused);
                     lds_barrier();
                 }
             }
             for (int i = 2 * W; i < n_steps; ++i) {
-                p2(i + 1);
+                gram(i + 2);
+                solve(i + 1);
                 step(i - 2 * W, i);
                 lds_barrier();
             }
-            for (int i = n_steps; i < n_int - 2; ++i) lds_barrier();
+            for (int i = n_steps; i < n_main; ++i) lds_barrier();
         };
-        if (!P2_ON_STATE) run(std::integral_constant<int, 0>{});
-        else if (w8 < N_WAVE_T) run(std::integral_constant<int, 1>{});
+        if (w8 < N_WAVE_T) run(std::integral_constant<int, 1>{});
         else if (w8 == WAVE_QK) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 0>{});
         if (u.out_slot >= 0) store_state(a.carries + ((size_t)u.out_slot * H + h) * (D * D), S, w8, gg, m);
@@ -421,22 +437,19 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
             asm volatile("" : "+v"(rc.q), "+v"(rc.k), "+v"(rc.v), "+v"(rc.g), "+v"(rc.b));
             k1_stage(rc, w8, lane, lo, stgs + ring_off((ci & 1) * STG_BYTES));
         };
-        auto interval = [&](int i, RowChunk& rc, bool p2) __attribute__((always_inline)) {
+        auto interval = [&](int i, RowChunk& rc) __attribute__((always_inline)) {
             // Phase 1 reads LDS only after the barrier that ends the previous
             // interval, and the staging of rc waits for its loads there too:
             // the empty redefinitions keep the compiler from hoisting
             // either above that barrier.
             RawChunk raw;
-            k1_read_staged(stgs + ring_off(((i + 2) & 1) * STG_BYTES), lane, lo, raw);
+            k1_read_staged(stgs + ring_off(((i + 3) & 1) * STG_BYTES), lane, lo, raw);
             // ring slots as opaque uniform offsets, so every LDS access of a
             // phase is one per-lane base plus immediate offsets
-            k1_phase1(raw, w8, lane, recs + ring_off(((i + 2) % 3) * REC_BYTES),
-                      scrs + ring_off(((i + 2) & 1) * K1_BYTES));
-            stage(rc, i + 3);
-            load(rc, i + 5);
-            if (!P2_ON_STATE && p2)
-                k1_phase2(w8, lane, recs + ring_off(((i + 1) % 3) * REC_BYTES),
-                          scrs + ring_off(((i + 1) & 1) * K1_BYTES), lw);
+            k1_phase1(raw, w8, lane, recs + ring_off(((i + 3) % 4) * REC_BYTES),
+                      scrs + ring_off(((i + 3) & 1) * K1_BYTES));
+            stage(rc, i + 4);
+            load(rc, i + 6);
             lds_barrier();
         };
         load(r0, 0);
@@ -444,11 +457,12 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
         stage(r0, 0);
         load(r0, 2);
         lds_barrier();  // start-up: chunk 0 staged
-        interval(-2, r1, false);
-        interval(-1, r0, true);
-        for (int i = 0; i < n_int - 2; i += 2) {
-            interval(i, r1, true);
-            interval(i + 1, r0, true);
+        interval(-3, r1);
+        interval(-2, r0);
+        interval(-1, r1);
+        for (int i = 0; i < n_main; i += 2) {
+            interval(i, r0);
+            interval(i + 1, r1);
         }
     }
 }
