@@ -220,6 +220,13 @@ static_assert(STG_BYTES <= K1P_LDS, "staging overlays the record area");
 template <bool GVA>
 __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
     if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
+    if (a.gate_flags) {
+        int32_t acc = 0;
+        for (int64_t i = threadIdx.x; i < a.n_gate_flags; i += blockDim.x) acc |= a.gate_flags[i];
+        const int armed = __syncthreads_or(acc != 0);
+        if (blockIdx.x == 0 && threadIdx.x == 0) a.gate_out[0] = armed;
+        if (!armed) return;  // fallback not armed
+    }
     __shared__ __align__(16) uint8_t lds[K1P_LDS];
     uint8_t* rec = lds;
     uint8_t* scr = lds + REC_BYTES;
@@ -655,23 +662,6 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// gate[0] = OR over flags (one workgroup of 256 threads).
-__global__ __launch_bounds__(256) void kda_flags_or(const int32_t* __restrict__ flags, int64_t n,
-                                                    int32_t* __restrict__ gate) {
-    __shared__ int32_t wave_any[4];
-    int32_t acc = 0;
-    for (int64_t i = threadIdx.x; i < n; i += 256) acc |= flags[i];
-    const bool any = __builtin_amdgcn_ballot_w64(acc != 0) != 0;
-    if ((threadIdx.x & 63) == 0) wave_any[threadIdx.x >> 6] = any ? 1 : 0;
-    __syncthreads();
-    if (threadIdx.x == 0) gate[0] = wave_any[0] | wave_any[1] | wave_any[2] | wave_any[3];
-}
-
-hipError_t launch_flags_or(const int32_t* flags, int64_t n, int32_t* gate, hipStream_t s) {
-    hipLaunchKernelGGL(kda_flags_or, dim3(1), dim3(256), 0, s, flags, n, gate);
-    return hipGetLastError();
-}
-
 // bf16 beta -> fp32 beta (exact), for callers that keep beta in bf16.
 __global__ __launch_bounds__(256) void kda_beta_to_f32(const uint16_t* __restrict__ src, float* __restrict__ dst,
                                                        int64_t n) {
@@ -691,7 +681,7 @@ hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     // a gated launch is usually empty: a capped grid that strides over the
     // items costs little to dispatch when every workgroup returns at once
-    if (a.c.gate && n > 2048) n = 2048;
+    if ((a.c.gate || a.gate_flags) && n > 2048) n = 2048;
     if (a.c.group > 1) hipLaunchKernelGGL(kda_k1_prepare<true>, dim3((unsigned)n), dim3(512), 0, s, a);
     else hipLaunchKernelGGL(kda_k1_prepare<false>, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();

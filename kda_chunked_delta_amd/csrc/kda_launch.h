@@ -123,6 +123,12 @@ struct MergeArgs {
 struct K1Args {
     CommonArgs c;
     const ChunkDesc* chunks;
+    // Gate from flags (the first launch of warm-start CP's fallback): every
+    // workgroup ORs the n_gate_flags speculation flags and returns if none is
+    // set; workgroup 0 writes the result to gate_out for the later launches.
+    const int32_t* gate_flags;
+    int64_t n_gate_flags;
+    int32_t* gate_out;
 };
 
 hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s);
@@ -131,8 +137,7 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s);
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
 hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);
-// gate[0] = 1 if any of flags[0..n) is nonzero, else 0 (one workgroup)
-hipError_t launch_flags_or(const int32_t* flags, int64_t n, int32_t* gate, hipStream_t s);
+
 
 constexpr int kChunk = 16;                      // tokens per chunk
 constexpr size_t kRecBytes = 18432;            // bytes of one K1 chunk record

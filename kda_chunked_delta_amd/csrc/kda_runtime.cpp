@@ -997,11 +997,16 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     // The segmented pipeline: K1 records, pre_scan, carry merge, K2 over the
     // records with the given units. cc.gate gates every launch when set (the
     // fallback of warm-start CP).
+    // With gate_flags, the K1 launch first reduces those flags into the gate
+    // word cc.gate points to, and every launch is gated on it.
     auto segmented = [&](const CommonArgs& cc, const UnitDesc* k2_units, int32_t n_k2_units,
-                         const char* k2_name) -> kda_status {
-        K1Args k1{cc, (const ChunkDesc*)(tabs + p->dev_off_chunks)};
+                         const char* k2_name, const int32_t* gate_flags, int64_t n_gate_flags) -> kda_status {
+        K1Args k1{cc, (const ChunkDesc*)(tabs + p->dev_off_chunks), gate_flags, n_gate_flags,
+                  const_cast<int32_t*>(cc.gate)};
+        if (gate_flags) k1.c.gate = nullptr;  // the K1 launch computes the gate
         e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
         if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+        if (gate_flags && (e = report(cc.gate, 1)) != hipSuccess) return hip_fail(e, "speculation feedback");
         if (!p->prescan.empty()) {
             PrescanArgs pa{cc, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
                            (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
@@ -1023,7 +1028,7 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     };
     const UnitDesc* cp_units = (const UnitDesc*)(tabs + p->dev_off_cp_units);
     if (p->info.warm_cp && spec_off)  // the exact path of a warm-start CP plan: the pipeline alone
-        return segmented(c, cp_units, (int32_t)p->cp_units.size(), "k2_segment");
+        return segmented(c, cp_units, (int32_t)p->cp_units.size(), "k2_segment", nullptr, 0);
     if (p->info.n_split_seqs > 0 && spec_off) {
         // the exact path of a split plan: the batch unsplit
         K2Args ks{c, (const UnitDesc*)(tabs + p->dev_off_alt_units), (int32_t)p->alt_units.size(), s0, sT,
@@ -1042,14 +1047,10 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
                   (int32_t*)(ws + p->off_spec_flags), (float*)(ws + p->off_spec_states), 0, direct ? 1 : 0};
         e = timed("fused_warm_cp", [&] { return launch_fused(kw, stream); });
         if (e != hipSuccess) return hip_fail(e, "warm-start CP launch");
-        e = timed("flags_or", [&] {
-            return launch_flags_or(kw.spec_flags, (int64_t)p->info.n_warm_segments * p->info.H * 8, gate, stream);
-        });
-        if (e != hipSuccess) return hip_fail(e, "flags_or launch");
-        if ((e = report(gate, 1)) != hipSuccess) return hip_fail(e, "speculation feedback");
         CommonArgs cg = c;
         cg.gate = gate;
-        const kda_status st2 = segmented(cg, cp_units, (int32_t)p->cp_units.size(), "k2_segment");
+        const kda_status st2 = segmented(cg, cp_units, (int32_t)p->cp_units.size(), "k2_segment", kw.spec_flags,
+                                         (int64_t)p->info.n_warm_segments * p->info.H * 8);
         if (st2 != KDA_OK) return st2;
         if (!direct && !p->fixups.empty()) {
             // publish the final states the warm-start launch left in scratch
@@ -1066,7 +1067,7 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     const bool mat = p->info.k1_materialized != 0;
     if (mat)  // segmented CP, or the two-kernel serial form (no pre_scan, no merge)
         return segmented(c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(),
-                         p->info.uses_cp ? "k2_segment" : "k2_recur");
+                         p->info.uses_cp ? "k2_segment" : "k2_recur", nullptr, 0);
     K2Args ka{c, (const UnitDesc*)(tabs + p->dev_off_units), (int32_t)p->units.size(), s0, sT,
               (float*)(ws + p->off_carry), (uint16_t*)out, scale, state16 ? 1 : 0,
               (int32_t*)(ws + p->off_spec_flags), (float*)(ws + p->off_spec_states), 0, 0};
