@@ -56,10 +56,16 @@ DECODE_TEXT = {
 
 
 def source_digest(files=("kda_device.hpp", "kda_kernels.hip", "kda_launch.h")):
+    """Digest of the kernel sources with comments and blank lines removed, so
+    that it changes with the code and not with its commentary."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "kda_chunked_delta_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "kda_chunked_delta_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines()]
+        h.update("\n".join(l for l in lines if l.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -78,7 +78,7 @@ constexpr int LB_BETA = K1_LBYTES;
 constexpr int LB_BYTES = K1_LBYTES + 64;
 
 // Phase-2 roles: wavefronts 0..3 (one per SIMD) each form four rows of T',
-// wavefront WAVE_QK forms A_qk.
+// wavefront WAVE_QK forms A_qk (and, in the fused kernel, L for the others).
 constexpr int N_WAVE_T = 4;
 constexpr int WAVE_QK = 5;
 
@@ -447,13 +447,15 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
 }
 
 // ---------------------------------------------------------------------------
-// K1, phase 2 (after a barrier that publishes phase 1). Wavefront s < 4
-// forms L = strict-lower(diag(beta) A_kk) and rows 4s + gg of
-// T' = (I + L)^-1 diag(beta); wavefront WAVE_QK forms the masked A_qk. Both Grams run over all 128 channels on MFMA from the phase-1
-// fragments (each T' wavefront forms its own copy of L, in its private 1 KiB
-// lw, so phase 2 needs no barrier of its own). The inverse is a
-// substitution over 15 dependent steps, each one DPP-broadcast
-// multiply-subtract.
+// K1, phase 2 (after a barrier that publishes phase 1). L =
+// strict-lower(diag(beta) A_kk) and the masked A_qk are Grams over all 128
+// channels on MFMA from the phase-1 fragments; rows of T' = (I + L)^-1
+// diag(beta) follow by a substitution over 15 dependent steps, each one
+// DPP-broadcast multiply-subtract. In the materialised K1 kernel, wavefront
+// s < 4 forms its own copy of L in a private 1 KiB and rows 4s + gg of T'
+// (so phase 2 needs no barrier of its own), and wavefront WAVE_QK forms
+// A_qk. The fused kernel forms L once, a stage earlier (k1_lkk), and runs
+// only the substitution on the T' wavefronts (k1_tsolve).
 // ---------------------------------------------------------------------------
 // L = strict-lower(diag(beta) A_kk) from the phase-1 Gram factors, stored
 // transposed (lt[c * K1_LSTRIDE + r] = L[r][c]), so that lane (gg, i) of a
