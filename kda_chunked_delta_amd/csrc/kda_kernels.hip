@@ -294,7 +294,7 @@ static_assert(FUSED_LDS <= 160 * 1024, "fused kernel LDS");
 // GVA: q/k heads differ from the value heads (value head h reads q/k head
 // h / group); the plain instance keeps the q/k loads on v's offsets.
 template <bool GVA>
-__global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
+__device__ __forceinline__ void fused_body(const K2Args& a) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* recs = smem;                      // 4 records
     uint8_t* scrs = recs + 4 * REC_BYTES;      // 2 K1 scratch areas
@@ -474,6 +474,18 @@ __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
     }
 }
 
+template <bool GVA>
+__global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
+    fused_body<GVA>(a);
+}
+
+// The fix-up and publish launches (a.fixup): the same body under a symbol of
+// its own, so that kernel traces and statistics tell them from the main launch.
+template <bool GVA>
+__global__ __launch_bounds__(1024) void kda_fused_fixup(K2Args a) {
+    fused_body<GVA>(a);
+}
+
 // ---------------------------------------------------------------------------
 // K2 over materialised K1 records (two-kernel serial form and CP segment-K2):
 // one workgroup of 8 wavefronts per (unit, head), wavefront w on value
@@ -651,14 +663,24 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
 hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     const long long n = (long long)a.n_units * a.c.H;
     if (n <= 0) return hipSuccess;
-    static hipError_t attr0 = hipFuncSetAttribute((const void*)kda_fused<false>,
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
-    static hipError_t attr1 = hipFuncSetAttribute((const void*)kda_fused<true>,
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
-    if (attr0 != hipSuccess) return attr0;
-    if (attr1 != hipSuccess) return attr1;
-    if (a.c.group > 1) hipLaunchKernelGGL(kda_fused<true>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
-    else hipLaunchKernelGGL(kda_fused<false>, dim3((unsigned)n), dim3(1024), FUSED_LDS, s, a);
+    static const hipError_t attr = [] {
+        const void* fns[] = {(const void*)kda_fused<false>, (const void*)kda_fused<true>,
+                             (const void*)kda_fused_fixup<false>, (const void*)kda_fused_fixup<true>};
+        for (const void* f : fns) {
+            const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }();
+    if (attr != hipSuccess) return attr;
+    const dim3 grid((unsigned)n), block(1024);
+    if (a.fixup) {
+        if (a.c.group > 1) hipLaunchKernelGGL(kda_fused_fixup<true>, grid, block, FUSED_LDS, s, a);
+        else hipLaunchKernelGGL(kda_fused_fixup<false>, grid, block, FUSED_LDS, s, a);
+    } else {
+        if (a.c.group > 1) hipLaunchKernelGGL(kda_fused<true>, grid, block, FUSED_LDS, s, a);
+        else hipLaunchKernelGGL(kda_fused<false>, grid, block, FUSED_LDS, s, a);
+    }
     return hipGetLastError();
 }
 
