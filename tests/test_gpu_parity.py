@@ -464,6 +464,28 @@ def test_split_plan_state_variants(g_scale):
     assert torch.equal(o2, o_ser), "no final state"
 
 
+@pytest.mark.parametrize("g_scale", [1.0, 0.05])
+def test_split_plans_in_place_calls_in_a_row(g_scale):
+    """In place, each call's fix-up launch publishes (or reruns) the
+    warm-start segments after every unit has read its initial state. Five
+    calls in a row, alternating two split plans of different pairs on one
+    stream (so one arena), all equal the serial path bit for bit."""
+    d = draw([640, 400], 4, seed=53, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * g_scale
+    cu = d["cu_seqlens_host"]
+    p1 = kda.plan_split(cu, 4, [20, 12], 8, device=DEV)
+    p2 = kda.plan_split(cu, 4, [0, 13], 8, device=DEV)
+    o_ser, s_ser = run(d, mode=False)
+    for i in range(5):
+        for p in (p1, p2):
+            say("call", i, "split sequences", p.info()["n_split_seqs"], "g_scale", g_scale)
+            st = d["initial_state"].clone()
+            o, _ = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                               cu_seqlens_host=cu, initial_state=st, final_state=st, plan=p)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ser) and torch.equal(st, s_ser), f"call {i}"
+
+
 # ---------------------------------------------------------------------------
 # warm-start CP (all segments in the fused launch, segmented pipeline as fallback)
 # ---------------------------------------------------------------------------
