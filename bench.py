@@ -80,7 +80,9 @@ def traffic_from_profiles(kernel, digest, workload_name):
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = data.get(kernel)
+    # one entry per launch sequence, or per (launch sequence, workload) when
+    # it is measured on several workloads
+    ent = data.get(f"{kernel}@{workload_name}") or data.get(kernel)
     if not ent or ent.get("source_digest") != digest or ent.get("workload") != workload_name:
         return None
     return ent.get("bytes_per_launch")
