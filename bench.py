@@ -6,7 +6,13 @@ HBM. Prints one JSON line: tokens/s, the roofline of the path's kernels
 measured with HIP events on the launch stream, and the CPU oracle timed on the
 host cores as a reported baseline.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload varlen8_h32]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload varlen8_h32]
+
+After the warm-up steps, untimed steps run until the GPU has worked
+--settle-ms milliseconds at a stable step time (the clocks take tens of
+milliseconds of work to settle). The timed region is --steps steps back to
+back; a second pass of as many steps brackets every launch with HIP events
+for the per-kernel times of the roofline.
 
 With --workload decode_n256_h32 a step is instead one kda_decode call: one
 token for each of 256 sequences x 32 heads, the fp32 states advanced in place.
@@ -26,11 +32,15 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # Algorithmic work per token-head of the path (D = 128, chunk 16):
 #   bytes: q 256 + k 256 + v 256 (bf16) + g 512 (fp32) + beta 4 + o 256 (bf16)
-#   flops, per 16-token chunk: X S0, Qt S0 and Kt^T U (16x128x128 each),
-#          T'(V - X S0) and A_qk U (16x16x128 each), the Grams A_kk and A_qk
-#          (16x16x128 each): 2 * (3 * 262144 + 4 * 32768) / 16 per token
+#   flops of the chunked WY form, per 16-token chunk: the Grams A_kk and A_qk,
+#          W = T diag(beta)(K Gamma) and U~ = T diag(beta) V (16x16x128
+#          each), W S0, Qt S0 and Kt^T U (16x128x128 each) and A_qk U
+#          (16x16x128): 2 * (3 * 262144 + 5 * 32768) / 16 per token. The
+#          kernels regroup U = U~ - W S0 as T'(V - X S0), which needs one
+#          16x16x128 product fewer: 2 * (3 * 262144 + 4 * 32768) / 16.
 BYTES_PER_TOKEN_HEAD = 1540
-FLOPS_PER_TOKEN_HEAD = 114688
+FLOPS_PER_TOKEN_HEAD = 118784           # the method's count (the MFMA roofline's numerator)
+FLOPS_PER_TOKEN_HEAD_EXECUTED = 114688  # what the regrouped kernels issue
 STATE_BYTES = 128 * 128 * 4
 
 WORKLOAD_TEXT = {
@@ -170,14 +180,89 @@ def plan_kind(info):
     return "serial"
 
 
+def settle_clocks(step, stream, min_ms, max_ms):
+    """Untimed steps until the GPU has worked at least min_ms and the step
+    time has stopped falling (two batches in a row within 1%), or max_ms has
+    passed. The shader clock needs tens of milliseconds of work to reach its
+    steady level; without this a short run times the ramp."""
+    import torch
+    total, steps, prev, batch = 0.0, 0, None, 8
+    while True:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(batch):
+            step()
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b)
+        total += ms
+        steps += batch
+        per = ms / batch
+        stable = prev is not None and abs(per - prev) <= 0.01 * prev
+        prev = per
+        if (total >= min_ms and stable) or total >= max_ms:
+            return {"ms": round(total, 1), "steps": steps, "last_ms_per_step": round(per, 5)}
+        batch = max(4, min(4000, int(25.0 / max(per, 1e-3))))  # about 25 ms per batch
+
+
+def timed_steps(step, stream, n):
+    """n steps back to back with an event after each on the launch stream:
+    (total ms / n, median of the per-step intervals)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+    return evs[0].elapsed_time(evs[n]) / n, per[len(per) // 2]
+
+
+def host_cost(call_py, call_c, n=200):
+    """Host microseconds per prefill call, while the GPU works through the
+    queued calls: through the Python binding, and through the C ABI alone
+    (the same ctypes call with prepared arguments, less the cost of a ctypes
+    call into the library that does nothing)."""
+    import ctypes
+    import torch
+    import kda_chunked_delta_amd as kda
+
+    def per_call(f, reps):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            f()
+        dt = time.perf_counter() - t
+        torch.cuda.synchronize()
+        return dt / reps * 1e6
+
+    py = per_call(call_py, n)
+    raw = per_call(call_c, n)
+    noop = kda.lib().kda_version
+    t = time.perf_counter()
+    for _ in range(n):
+        noop()
+    ctypes_us = (time.perf_counter() - t) / n * 1e6
+    return {"python_us": round(py, 2), "c_abi_us": round(max(raw - ctypes_us, 0.0), 2),
+            "ctypes_call_us": round(ctypes_us, 2), "calls": n,
+            "note": "host time per kda_prefill call with the plan given, measured over back-to-back calls "
+                    "while the GPU works through them; c_abi_us is the ctypes call with prepared arguments "
+                    "less a no-op ctypes call"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # a step is well under a millisecond; the GPU's clocks take tens of
-    # milliseconds of work to settle, so the defaults warm up and time a few
-    # hundred steps (still well under a second of GPU time)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="after the warm-up steps, run untimed steps until the GPU has worked this many "
+                         "milliseconds and the step time is stable, so that the timed steps run at steady "
+                         "clocks whatever --warmup is (reported as clock_settle; 0: no settling)")
+    ap.add_argument("--host-calls", type=int, default=200,
+                    help="calls over which the host cost of one prefill call is measured (0: skip)")
     ap.add_argument("--workload", default="varlen8_h32", choices=sorted(WORKLOAD_TEXT) + sorted(DECODE_TEXT))
     ap.add_argument("--cp", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--cold-steps", type=int, default=50,
@@ -189,6 +274,9 @@ def main():
                     help="instead of the benchmark, run `steps` launches of a plain elementwise copy of "
                          "MIB MiB (fp32 negation: MIB MiB read, MIB MiB written); the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--g-scale", type=float, default=None,
+                    help="multiply g by this factor after drawing it (0.05: weak decay, the case in which "
+                         "the carried-in state is not forgotten within a segment)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: measures one GPU only; --gpus %d is not supported (the prefill shards by "
@@ -216,6 +304,8 @@ def main():
         bench_decode(args, dev)
         return
     d = workload(args.workload, device=dev)
+    if args.g_scale is not None:
+        d["g"].mul_(args.g_scale)
     H, cu = d["H"], d["cu_seqlens_host"]
     Tt, N = cu[-1], len(cu) - 1
     mode = {"auto": "auto", "on": True, "off": False}[args.cp]
@@ -231,25 +321,28 @@ def main():
 
     print("bench: workload %s Tt=%d H=%d plan=%s units=%d" % (args.workload, Tt, H,
           plan_kind(info), info["n_units"]), file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settle = settle_clocks(step, stream, args.settle_ms, max(3000.0, 4 * args.settle_ms)) if args.settle_ms > 0 \
+        else None
+    print("bench: clocks settled after %s" % settle, file=sys.stderr, flush=True)
 
+    # the timed region: `steps` steps back to back, one event after each on
+    # the launch stream
+    ms_step, ms_median = timed_steps(step, stream, args.steps)
+    # the roofline's kernel times: the same number of steps again, each launch
+    # bracketed by HIP events on the launch stream (those events add a gap
+    # before and after every launch, so this pass is not the headline)
     ctx = kda.context(dev)
     ctx.set_timing(True)
-    stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
+    ms_ev, ms_ev_median = timed_steps(step, stream, args.steps)
     per_kernel = ctx.timing()
     ctx.set_timing(False)
-    print("bench: %.3f ms/step; kernels %s" % (ms_step, {k: round(v[0] / v[1], 4) for k, v in per_kernel.items()}),
-          file=sys.stderr, flush=True)
+    print("bench: %.4f ms/step (median %.4f); with per-launch events %.4f ms/step, kernels %s" % (
+        ms_step, ms_median, ms_ev, {k: round(v[0] / v[1], 4) for k, v in per_kernel.items()}),
+        file=sys.stderr, flush=True)
 
     token_heads = Tt * H
     alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD + N * H * STATE_BYTES * (2 if s0 is not None else 1)
@@ -263,9 +356,30 @@ def main():
     traffic = traffic_from_profiles(names, digest, args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "frac_of_step": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "frac_of_median_step": round(alg_bytes / (ms_median * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "basis": "frac: algorithmic bytes over the summed HIP-event time of the step's kernels (the "
+                         "dominant one and the rest), from a pass of the same steps with every launch "
+                         "bracketed by events; frac_of_step: over the headline ms_per_step, launch gaps "
+                         "included",
                 "kernel": names, "dominant": dominant, "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
                 "alg_bytes_per_step": alg_bytes, "source_digest": digest}
     mfma_frac = alg_flops / (path_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+
+    def call_py():
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                    cu_seqlens_host=cu, initial_state=s0, final_state=s_out, out=o, plan=plan)
+
+    import ctypes
+    opts = kda.PrefillOpts(H, 0, 0)
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    c_args = (ctx.handle, plan.handle, ctypes.byref(opts), p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]),
+              p(d["beta"]), p(d["cu_seqlens"]), 1.0, p(s0), p(s_out), p(o), ctypes.c_void_p(stream.cuda_stream))
+    fn = kda.lib().kda_prefill_ex
+
+    def call_c():
+        if fn(*c_args) != 0:
+            raise RuntimeError("kda_prefill_ex: " + kda.lib().kda_last_error().decode())
 
     line = {
         "metric": METRIC,
@@ -275,6 +389,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(ms_median, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -283,10 +398,20 @@ def main():
         "config": {"workload": "%s: %s" % (args.workload, WORKLOAD_TEXT[args.workload]), "tokens": Tt,
                    "heads": H, "head_dim": 128, "sequences": N, "lengths": d["lengths"],
                    "plan": plan_kind(info), "cp_mode": args.cp},
+        "clock_settle": settle,
+        "kernel_timing_pass": {"ms_per_step": round(ms_ev, 5), "ms_per_step_median": round(ms_ev_median, 5),
+                               "steps": args.steps},
         "roofline": roofline,
         "mfma_roofline": {"bound": "mfma", "achieved": round(alg_flops / (path_ms * 1e-3) / 1e12, 2),
-                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4)},
+                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4),
+                          "flops_per_token_head": FLOPS_PER_TOKEN_HEAD,
+                          "flops_per_token_head_executed": FLOPS_PER_TOKEN_HEAD_EXECUTED},
     }
+    if args.g_scale is not None:
+        line["config"]["g_scale"] = args.g_scale
+    if args.host_calls > 0:
+        line["host_per_call"] = host_cost(call_py, call_c, args.host_calls)
+        print("bench: host per call %s" % line["host_per_call"], file=sys.stderr, flush=True)
     if args.cold_steps > 0:
         line["cold"] = cold_steps(step, Tt, args.cold_steps)
         print("bench: cold %s" % line["cold"], file=sys.stderr, flush=True)
@@ -333,19 +458,16 @@ def bench_decode(args, dev):
         kda.decode(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=o)
 
     print("bench: workload %s N=%d H=%d" % (args.workload, N, H), file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step()
+    torch.cuda.synchronize()
+    settle = settle_clocks(step, stream, args.settle_ms, max(3000.0, 4 * args.settle_ms)) if args.settle_ms > 0 \
+        else None
+    ms_step, ms_median = timed_steps(step, stream, args.steps)
     ctx = kda.context(dev)
-    torch.cuda.synchronize()
     ctx.set_timing(True)
-    stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
+    timed_steps(step, stream, args.steps)
     per_kernel = ctx.timing()
     ctx.set_timing(False)
     kern_ms = per_kernel["decode"][0] / per_kernel["decode"][1]
@@ -366,6 +488,7 @@ def bench_decode(args, dev):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(ms_median, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -373,6 +496,7 @@ def bench_decode(args, dev):
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (args.workload, DECODE_TEXT[args.workload]), "sequences": N,
                    "heads": H, "head_dim": 128},
+        "clock_settle": settle,
         "roofline": roofline,
     }
     if args.cpu_seconds > 0:

@@ -34,7 +34,17 @@
  *  - Asynchrony: kda_prefill only enqueues work on `stream` and never
  *    synchronises, except when it must grow the stream's workspace arena (a
  *    device synchronise, refused with KDA_ERR_CAPTURE while the stream is
- *    being captured into a graph).
+ *    being captured into a graph). A plan whose workspace is 0 bytes touches
+ *    no arena at all. "feat(cake_kda): share recurrent prefill kernels across
+ *    SM100 family" (FlashInfer pull request #4313, review threads) asks that
+ *    a captured call do no host preparation.
+ *  - Graph capture: a captured call bakes into the graph the plan's device
+ *    tables and the address of the stream's workspace arena. The plan must
+ *    outlive every graph captured with it. Arena memory that served a capture
+ *    is never freed before kda_destroy: growing or evicting such an arena
+ *    retires the old memory instead, so a graph replayed after an uncaptured
+ *    call with a larger plan on the same stream still finds its workspace
+ *    (with the contents the replay itself writes).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -111,14 +121,28 @@ typedef struct {
 } kda_unit_info;
 
 /* Create a context on HIP device `device`: caches the device properties
- * (compute-unit count) once. Returns KDA_ERR_HIP if the device is unusable. */
+ * (compute-unit count) once. The review thread of "feat(cake_kda): share
+ * recurrent prefill kernels across SM100 family" (FlashInfer pull request
+ * #4313) asks that device properties be cached rather than queried on every
+ * launch; the compute-unit count is also what the planner of "feat(kda/sm90):
+ * FlashKDA prefill port + intracard-CP prefill" (cuLA pull request #103,
+ * description) sizes its decision by. `out` receives the context, owned by
+ * the caller until kda_destroy. Returns KDA_ERR_INVALID for a NULL `out` or a
+ * device index out of range, KDA_ERR_HIP if the device is unusable. */
 kda_status kda_create(int device, kda_ctx **out);
 
-/* Wait for the device, free every workspace arena and the context. NULL is a
- * no-op. */
+/* Wait for the device, then free every workspace arena (including memory
+ * retired after serving a graph capture) and the context. The arena is the
+ * workspace reused across calls of the cuLA pull request's description; it
+ * lives as long as its context. NULL is a no-op. The caller must not destroy a
+ * context while another thread uses it. */
 void kda_destroy(kda_ctx *ctx);
 
-/* Message of the calling thread's most recent failure ("" if none). */
+/* Message of the calling thread's most recent failure ("" if none); the
+ * pointer stays valid until that thread's next failing call. A review thread
+ * of "feat(cake_kda): share recurrent prefill kernels across SM100 family"
+ * (FlashInfer pull request #4313) asks that an unsupported call be rejected
+ * by a check rather than crash; every check here fails with a message. */
 const char *kda_last_error(void);
 
 /* Library version string. */
@@ -199,7 +223,10 @@ void kda_plan_destroy(kda_plan *plan);
 /* Bytes of the per-stream workspace arena that kda_prefill needs for this
  * plan (0 for NULL), so that a caller can warm the arena up before graph
  * capture. kda_prefill_ex with a bf16 beta needs 4 * Tt * H bytes more,
- * after this much rounded up to 256. */
+ * after this much rounded up to 256. The workspace holds the scratch of the
+ * intracard CP pipeline (K1 records, the b_seg / m_seg summaries and the
+ * carries named in the cuLA pull request's review thread), which the arena
+ * reuses across calls (its description). */
 size_t kda_plan_workspace_bytes(const kda_plan *plan);
 
 /* Plan summary; returns KDA_ERR_INVALID for NULL arguments. */

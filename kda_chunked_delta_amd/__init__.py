@@ -210,9 +210,10 @@ class Plan:
 
     def __init__(self, handle, cu_host, device=None):
         self.handle = handle
-        self.cu_host = list(cu_host)
+        self.cu_host = [int(x) for x in cu_host]
         self.device = device
         self._cu_dev = None
+        self._shape = None
 
     def __del__(self):
         try:
@@ -226,6 +227,13 @@ class Plan:
         pi = PlanInfo()
         _check(lib().kda_plan_get_info(self.handle, ctypes.byref(pi)), "kda_plan_get_info")
         return pi.as_dict()
+
+    def shape(self):
+        """(H, total tokens, sequences) the plan was built for (cached)."""
+        if self._shape is None:
+            i = self.info()
+            self._shape = (i["H"], i["total_tokens"], i["n_seqs"])
+        return self._shape
 
     def units(self):
         n = self.info()["n_units"]
@@ -296,6 +304,9 @@ def plan_warm_cp(cu_seqlens, H, seg_chunks, warm_chunks, device=None):
 
 _plan_cache = collections.OrderedDict()
 _PLAN_CACHE_MAX = 64
+# Plans used by a call captured into a graph: the graph holds their device
+# tables, and may be replayed at any later time, so they are never released.
+_captured_plans = []
 
 
 def _cached_plan(cu_host, H, mode, device):
@@ -381,15 +392,29 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
             cu_seqlens_host = list(cu_seqlens)
         else:
             cu_seqlens_host = cu_seqlens.tolist()  # host copy for the planner (synchronises)
+    cu_seqlens_host = [int(x) for x in cu_seqlens_host]
+    N = len(cu_seqlens_host) - 1
+    # the library sizes every buffer from the plan, so the table must describe
+    # exactly the packed tokens the tensors hold
+    if (N < 1 or cu_seqlens_host[0] != 0 or cu_seqlens_host[-1] != Tt
+            or any(b < a for a, b in zip(cu_seqlens_host, cu_seqlens_host[1:]))):
+        raise ValueError("cu_seqlens must start at 0, never decrease and end at the %d packed tokens (got %d "
+                         "entries from %s to %s)" % (Tt, N + 1, cu_seqlens_host[0] if N >= 0 else None,
+                                                    cu_seqlens_host[-1] if N >= 0 else None))
     if plan is None:
         plan = _cached_plan(cu_seqlens_host, H, _cp_mode(use_intracard_cp), dev)
+    else:
+        if plan.device != dev:
+            raise ValueError("the plan is for device %s, the tensors are on device %d" % (plan.device, dev))
+        if plan.shape() != (H, Tt, N) or plan.cu_host != cu_seqlens_host:
+            raise ValueError("the plan was built for H=%d, %d tokens, %d sequences (cu_seqlens %s...); the call "
+                             "has H=%d, %d tokens, %d sequences" % (*plan.shape(), plan.cu_host[:4], H, Tt, N))
     if cu_seqlens is None or isinstance(cu_seqlens, (list, tuple)):
         cu_dev = plan.cu_device()
     else:
         cu_dev = cu_seqlens
-        if cu_dev.dtype != torch.int32 or not cu_dev.is_cuda:
-            raise ValueError("cu_seqlens must be an int32 CUDA tensor")
-    N = len(cu_seqlens_host) - 1
+        if cu_dev.dtype != torch.int32 or not cu_dev.is_cuda or cu_dev.numel() != N + 1:
+            raise ValueError("cu_seqlens must be an int32 CUDA tensor of %d entries" % (N + 1))
     if state_dtype is None:
         given = initial_state if initial_state is not None else final_state
         state_dtype = given.dtype if given is not None else torch.float32
@@ -406,6 +431,8 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
         final_state = torch.empty(N, H, D, D, dtype=state_dtype, device=q.device)
     ctx = context(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if torch.cuda.is_current_stream_capturing() and not any(p is plan for p in _captured_plans):
+        _captured_plans.append(plan)
     opts = PrefillOpts(Hk, int(beta16), int(state_dtype == torch.bfloat16))
     _check(lib().kda_prefill_ex(ctx.handle, plan.handle, ctypes.byref(opts), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                 _ptr(beta), _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state),

@@ -562,6 +562,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 struct Arena {
     void* ptr = nullptr;
     size_t bytes = 0;
+    // A call captured into a graph bakes this address into the graph, which
+    // may be replayed at any time after: such memory is never freed before
+    // kda_destroy (growing or evicting the arena retires it instead).
+    bool captured = false;
 };
 
 struct TimedLaunch {
@@ -575,6 +579,7 @@ struct kda_ctx {
     hipDeviceProp_t prop{};
     std::mutex mu;
     std::unordered_map<hipStream_t, Arena> arenas;
+    std::vector<void*> retired;  // arena memory that served a graph capture, freed in kda_destroy
     bool poison = false;
     bool timing = false;
     std::vector<TimedLaunch> events;  // pool, reused across calls
@@ -641,6 +646,7 @@ void kda_destroy(kda_ctx* c) {
     (void)hipDeviceSynchronize();
     for (auto& kv : c->arenas)
         if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    for (void* ptr : c->retired) (void)hipFree(ptr);
     for (auto& t : c->events) {
         (void)hipEventDestroy(t.beg);
         (void)hipEventDestroy(t.end);
@@ -875,9 +881,21 @@ kda_status kda_prefill(kda_ctx* ctx, const kda_plan* p, const void* q, const voi
     return kda_prefill_ex(ctx, p, nullptr, q, k, v, g, beta, cu_dev, scale, s0, sT, out, stream);
 }
 
-kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts* opts, const void* q,
-                          const void* k, const void* v, const float* g, const void* beta, const int32_t* cu_dev,
-                          float scale, const void* s0, void* sT, void* out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// A fixed workspace given instead of the stream's arena: the call then
+// allocates nothing, synchronises nothing and leaves no event behind.
+struct FixedWorkspace {
+    uint8_t* ptr;
+    size_t bytes;
+};
+
+kda_status prefill_impl(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts* opts, const void* q,
+                        const void* k, const void* v, const float* g, const void* beta, const int32_t* cu_dev,
+                        float scale, const void* s0, void* sT, void* out, hipStream_t stream,
+                        const FixedWorkspace* fixed) {
     if (!ctx) return fail(KDA_ERR_INVALID, "kda_prefill: ctx is NULL");
     kda_status st = kda_prefill_ex_validate(p, opts, q, k, v, g, beta, cu_dev, scale, s0, sT, out);
     if (st != KDA_OK) return st;
@@ -907,37 +925,56 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     const size_t off_beta = align_up(p->info.workspace_bytes, 256);
     const size_t n_beta = (size_t)p->info.total_tokens * p->info.H;
     const size_t need = beta16 ? off_beta + n_beta * 4 : p->info.workspace_bytes;
-    auto it = ctx->arenas.find(stream);
-    if (it == ctx->arenas.end() || it->second.bytes < need) {
-        if (cap != hipStreamCaptureStatusNone)
-            return fail(KDA_ERR_CAPTURE, "kda_prefill: the workspace arena of this stream must grow to %zu bytes, "
-                                         "which is not allowed while the stream is capturing; run once uncaptured first",
-                        need);
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-        if (it == ctx->arenas.end() && ctx->arenas.size() >= kMaxArenas) {
-            // evict one arena (the device is idle after the synchronise)
-            auto victim = ctx->arenas.begin();
-            if (victim->second.ptr) (void)hipFree(victim->second.ptr);
-            ctx->arenas.erase(victim);
-        }
-        Arena& a = ctx->arenas[stream];
-        if (a.ptr) (void)hipFree(a.ptr);
-        a.ptr = nullptr;
-        a.bytes = 0;
-        if (need > 0) {
+    // A plan that needs no workspace touches no arena (nor allocates, nor
+    // synchronises), also on a stream seen for the first time.
+    uint8_t* ws = nullptr;
+    if (fixed) {
+        if (need > fixed->bytes)
+            return fail(KDA_ERR_INVALID, "kda_prefill_noalloc: this plan needs %zu bytes of workspace, more than the "
+                                         "%zu bytes of static scratch (a serial plan needs none)", need, fixed->bytes);
+        ws = fixed->ptr;
+    } else if (need > 0) {
+        auto it = ctx->arenas.find(stream);
+        if (it == ctx->arenas.end() || it->second.bytes < need) {
+            if (cap != hipStreamCaptureStatusNone)
+                return fail(KDA_ERR_CAPTURE, "kda_prefill: the workspace arena of this stream must grow to %zu bytes, "
+                                             "which is not allowed while the stream is capturing; run once uncaptured "
+                                             "first", need);
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            // memory that a captured graph may still use is retired, not freed
+            auto release = [&](Arena& a) {
+                if (!a.ptr) return;
+                if (a.captured) ctx->retired.push_back(a.ptr);
+                else (void)hipFree(a.ptr);
+                a.ptr = nullptr;
+                a.bytes = 0;
+                a.captured = false;
+            };
+            if (it == ctx->arenas.end() && ctx->arenas.size() >= kMaxArenas) {
+                // evict one arena (the device is idle after the synchronise)
+                auto victim = ctx->arenas.begin();
+                release(victim->second);
+                ctx->arenas.erase(victim);
+            }
+            Arena& a = ctx->arenas[stream];
+            release(a);
             const size_t bytes = align_up(need + need / 8, 1 << 20);
             e = hipMalloc(&a.ptr, bytes);
-            if (e != hipSuccess) return hip_fail(e, "hipMalloc (workspace arena)");
+            if (e != hipSuccess) {
+                a.ptr = nullptr;
+                return hip_fail(e, "hipMalloc (workspace arena)");
+            }
             a.bytes = bytes;
             if (ctx->poison) {
                 e = hipMemset(a.ptr, 0xff, bytes);  // NaN in both bf16 and fp32
                 if (e != hipSuccess) return hip_fail(e, "hipMemset (poison)");
             }
+            it = ctx->arenas.find(stream);
         }
-        it = ctx->arenas.find(stream);
+        if (cap != hipStreamCaptureStatusNone) it->second.captured = true;
+        ws = (uint8_t*)it->second.ptr;
     }
-    uint8_t* ws = (uint8_t*)it->second.ptr;
 
     const uint8_t* tabs = (const uint8_t*)p->dev_tables;
     CommonArgs c{};
@@ -955,7 +992,11 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     c.total_chunks = p->info.total_chunks;
     c.rec = ws + p->off_rec;
 
-    auto timed = [&](const char* name, auto&& launch) { return timed_launch(ctx, stream, name, launch); };
+    // the fixed-workspace form records no timing events (creating one may allocate)
+    auto timed = [&](const char* name, auto&& launch) -> hipError_t {
+        if (fixed) return launch();
+        return timed_launch(ctx, stream, name, launch);
+    };
 
     if (beta16) {
         e = timed("beta_to_f32", [&] {
@@ -978,7 +1019,8 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
     // after a speculative call: copy its outcome back without waiting for it
     // (on a plan's first call and every 64th, so the copy costs little)
     auto report = [&](const int32_t* dev_words, size_t n_words) -> hipError_t {
-        if (capturing || n_words == 0) return hipSuccess;
+        // (the copy needs pinned host memory, allocated on first use)
+        if (capturing || fixed || n_words == 0) return hipSuccess;
         std::lock_guard<std::mutex> sl(p->spec_mu);
         if (p->spec_calls++ % 64 != 0 || p->spec_pending) return hipSuccess;
         hipError_t err = hipSuccess;
@@ -1090,6 +1132,16 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
             return hip_fail(e, "speculation feedback");
     }
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts* opts, const void* q,
+                          const void* k, const void* v, const float* g, const void* beta, const int32_t* cu_dev,
+                          float scale, const void* s0, void* sT, void* out, hipStream_t stream) {
+    return prefill_impl(ctx, p, opts, q, k, v, g, beta, cu_dev, scale, s0, sT, out, stream, nullptr);
 }
 
 kda_status kda_decode_slots_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,

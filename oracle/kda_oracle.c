@@ -4,12 +4,14 @@
  * benchmark may load it; the library path never does.
  *
  * What it computes: the per-token Kimi Delta Attention (KDA) recurrence in
- * fp64, the definition that the chunked two-kernel prefill of
+ * fp64. The chunked two-kernel prefill of
  *   "feat(kda/sm90): FlashKDA prefill port + intracard-CP prefill"
  *   (cuLA pull request #103; commit summary: K1 prepares decayed q/k, beta and
  *   the WY inverse, K2 runs the inter-chunk recurrence; CHUNK=16, D=128,
  *   forward only)
- * reaches in exact arithmetic. For one sequence and one head, with the state
+ * reaches it in exact arithmetic. That page names the method but prints no
+ * equation; the rule below is the published KDA definition (a gated delta
+ * rule with per-key-channel decay). For one sequence and one head, with the state
  * S (dk x dv, rows are key channels) and every token t in order:
  *
  *   S   <- Diag(exp(g_t)) S                      (per-key-channel decay)

@@ -66,7 +66,12 @@ def _cu(cu_seqlens, Tt):
 # The definition: per-token recurrence (numpy)
 # ---------------------------------------------------------------------------
 def recurrent(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0):
-    """Per-token KDA recurrence in fp64 (the definition, [P1] commit summary).
+    """Per-token KDA recurrence in fp64: the definition.
+
+    The pages name the method and its chunked two-kernel form ([P1] commit
+    summary) but print no equation for it; this is the published Kimi Delta
+    Attention rule (a gated delta rule with per-key-channel decay), in the
+    orientation that tests/golden/hand_two_tokens.txt pins by hand.
 
     For each sequence and head, token by token:
       S <- Diag(exp g_t) S;  e = v_t - S^T k_t;  S <- S + beta_t k_t e^T;

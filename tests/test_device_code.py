@@ -7,7 +7,11 @@ Regressions these guard against, both found in this library's own kernels:
     writes SCC must be followed by a fresh SCC write before any SCC read;
   * buffer descriptors that the compiler treats as divergent: each load then
     sits in a waterfall loop (a nested loop around a buffer load); the chunk
-    loops of the kernels must have none.
+    loops of the kernels must have none;
+  * an MFMA accumulator handed from one MFMA shape to another (a 16x16x16
+    product chained onto a 16x16x32 accumulator lost a contribution): every
+    MFMA's accumulator is last written by an MFMA of its own shape, or by
+    something other than an MFMA.
 """
 import os
 import re
@@ -73,3 +77,95 @@ def test_chunk_loops_have_no_waterfall_loads(device_asm):
             depth2 = "Depth=2" in line
         if depth2 and "buffer_load" in line:
             raise AssertionError("a buffer load inside a nested (waterfall) loop in %s" % fn)
+
+
+MFMA = re.compile(r"^\s*(v_mfma_\w+)\s+(.*)$")
+REG = re.compile(r"^([va])(?:\[(\d+):(\d+)\]|(\d+))$")
+
+
+def _reg_range(tok):
+    m = REG.match(tok.strip())
+    if not m:
+        return None
+    lo = int(m.group(2) if m.group(2) is not None else m.group(4))
+    hi = int(m.group(3) if m.group(3) is not None else m.group(4))
+    return m.group(1), lo, hi
+
+
+def mfma_shape_changes(lines):
+    """(line, mfma, accumulator, writer, writer line) for every MFMA whose
+    accumulator (C operand) an MFMA of another shape wrote last in the same
+    basic block, and the number of MFMAs with a register accumulator."""
+    found, checked = [], 0
+    for i, line in enumerate(lines):
+        m = MFMA.match(line)
+        if not m:
+            continue
+        ops = [o.strip() for o in m.group(2).split(",")]
+        if len(ops) < 4:
+            continue
+        c = _reg_range(ops[3].split()[0])
+        if c is None:
+            continue  # an inline constant accumulator (0)
+        checked += 1
+        for k in range(i - 1, -1, -1):
+            prev = lines[k].strip()
+            if prev.endswith(":"):
+                break  # start of the basic block
+            if not prev or prev.startswith(";") or prev.startswith("."):
+                continue
+            mnem = prev.split()[0]
+            if "store" in mnem or "write" in mnem or mnem.startswith("s_"):
+                continue
+            rest = prev[len(mnem):].strip()
+            dst = _reg_range(rest.split(",")[0]) if rest else None
+            if dst is None or dst[0] != c[0] or dst[2] < c[1] or dst[1] > c[2]:
+                continue
+            pm = MFMA.match(lines[k])
+            if pm and pm.group(1) != m.group(1):
+                found.append((i + 1, m.group(1), ops[3], pm.group(1), k + 1))
+            break
+    return found, checked
+
+
+def test_mfma_accumulators_keep_their_shape(device_asm):
+    """No MFMA takes as its accumulator (C operand) a register tile that an
+    MFMA of another shape wrote last. A 16x16x16 product chained onto a
+    16x16x32 accumulator was seen to lose the last 16x16x32 contribution in
+    two of the four output rows; each shape must start from a fresh
+    accumulator (or a VALU-written one) instead."""
+    total = 0
+    for src, lines in device_asm.items():
+        found, checked = mfma_shape_changes(lines)
+        assert not found, "%s: %s" % (src, found[:3])
+        total += checked
+    assert total > 0
+
+
+PLANTED = r"""
+#include <hip/hip_runtime.h>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ void planted(const bf16x8* a, const i16x4* b, f32x4* o) {
+    const int l = threadIdx.x;
+    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[l], a[l + 64], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(b[l], b[l + 64], acc, 0, 0, 0);
+    o[l] = acc;
+}
+"""
+
+
+def test_mfma_shape_check_catches_a_planted_chain(tmp_path):
+    """The check above flags a kernel (compiled only, never run) that hands a
+    16x16x32 accumulator to a 16x16x16 product."""
+    if not os.path.exists(kbuild.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    src = tmp_path / "planted.hip"
+    src.write_text(PLANTED)
+    dst = tmp_path / "planted.s"
+    flags = [f for f in kbuild.FLAGS if f not in ("-shared", "-fPIC") and not f.startswith("-I")]
+    subprocess.run([kbuild.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(dst), str(src)], check=True,
+                   stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    found, checked = mfma_shape_changes(dst.read_text().split("\n"))
+    assert checked == 1 and len(found) == 1 and "16x16x16" in found[0][1] and "16x16x32" in found[0][3]

@@ -29,6 +29,7 @@ def check_line(b, steps, warmup):
     assert KEYS <= set(b), KEYS - set(b)
     assert b["n_gpus"] == 1 and b["steps"] == steps and b["warmup"] == warmup
     assert b["value"] > 0 and b["ms_per_step"] > 0 and b["higher_is_better"] is True
+    assert b["ms_per_step_median"] > 0 and b["clock_settle"]["ms"] >= 50.0
     assert isinstance(b["config"], dict) and "workload" in b["config"]
     r = b["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
@@ -38,12 +39,18 @@ def check_line(b, steps, warmup):
 
 
 def test_bench_default_line():
-    b = run_bench("--steps", "3", "--warmup", "1", "--cpu-seconds", "1")
+    b = run_bench("--steps", "3", "--warmup", "1", "--cpu-seconds", "1", "--settle-ms", "50", "--cold-steps", "3")
     check_line(b, 3, 1)
     assert b["config"]["workload"].startswith("varlen8_h32") and b["dtype"] == "bf16"
+    r = b["roofline"]
+    assert 0 < r["frac_of_step"] < 1 and b["kernel_timing_pass"]["steps"] == 3
+    assert b["mfma_roofline"]["flops_per_token_head"] == 118784
+    h = b["host_per_call"]
+    assert h["python_us"] > 0 and h["c_abi_us"] >= 0
 
 
 def test_bench_decode_line():
-    b = run_bench("--workload", "decode_n256_h32", "--steps", "3", "--warmup", "1", "--cpu-seconds", "1")
+    b = run_bench("--workload", "decode_n256_h32", "--steps", "3", "--warmup", "1", "--cpu-seconds", "1",
+                  "--settle-ms", "50")
     check_line(b, 3, 1)
     assert b["config"]["workload"].startswith("decode_n256_h32")

@@ -736,13 +736,113 @@ def test_arena_reuse_across_shape_changes():
 
 
 def test_validation_errors_reach_python():
+    """Every check runs on the host before any launch."""
     d = workload("h12_2x32", device=DEV)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
     with pytest.raises(kda.KDAError) as e:
-        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
-                    cu_seqlens_host=d["cu_seqlens_host"], out=d["q"])
+        kda.prefill(*args, cu_seqlens=d["cu_seqlens"], cu_seqlens_host=d["cu_seqlens_host"], out=d["q"])
     assert e.value.status == 3
+    # a final state that partly overlaps the initial state
     st = d["initial_state"]
-    bad_final = torch.empty(st.numel() + 4096, device=DEV)[4096:].view(st.shape)
+    buf = torch.zeros(st.numel() + 4096, device=DEV)
+    init = buf[:st.numel()].view(st.shape)
+    init.copy_(st)
+    bad_final = buf[4096:].view(st.shape)
+    with pytest.raises(kda.KDAError) as e:
+        kda.prefill(*args, cu_seqlens=d["cu_seqlens"], cu_seqlens_host=d["cu_seqlens_host"],
+                    initial_state=init, final_state=bad_final)
+    assert e.value.status == 3 and "partially overlaps" in str(e.value)
     with pytest.raises(ValueError):
         kda.prefill(d["q"], d["k"], d["v"], d["g"].to(torch.bfloat16), d["beta"], cu_seqlens=d["cu_seqlens"])
-    del bad_final
+    # tables that do not describe the packed tokens exactly
+    Tt = d["q"].shape[0]
+    for cu in ([0, 32, Tt - 1], [0, 40, 32, Tt], [1, 32, Tt], [0, 32, Tt + 16], [0]):
+        with pytest.raises(ValueError, match="cu_seqlens"):
+            kda.prefill(*args, cu_seqlens=cu)
+    with pytest.raises(ValueError, match="int32 CUDA tensor"):
+        kda.prefill(*args, cu_seqlens=torch.tensor([0, Tt], dtype=torch.int32, device=DEV),
+                    cu_seqlens_host=d["cu_seqlens_host"])
+    # a plan built for other heads or other sequences
+    for cu_p, H_p in (([0, 32, 64], 8), ([0, 30, 64], 12), ([0, 64], 12)):
+        p_other = kda.plan(cu_p, H_p, device=DEV)
+        with pytest.raises(ValueError, match="plan"):
+            kda.prefill(*args, cu_seqlens=d["cu_seqlens"], cu_seqlens_host=d["cu_seqlens_host"], plan=p_other)
+
+
+@pytest.mark.parametrize("name", ["t64_h1", "h12_32_3", "h12_2x33"])
+def test_c_abi_kda_prefill_entry(name):
+    """kda_prefill itself (the entry without options), called through ctypes
+    with raw device pointers and the current stream, against the oracle and
+    bitwise against the binding's call."""
+    import ctypes
+    say("case", name)
+    d = workload(name, device=DEV)
+    cu_h, H = d["cu_seqlens_host"], d["H"]
+    N = len(cu_h) - 1
+    L = kda.lib()
+    ctx = kda.context(DEV)
+    p = kda.plan(cu_h, H, device=DEV)
+    o = torch.full_like(d["v"], float("nan"))
+    s = torch.full((N, H, 128, 128), float("nan"), device=DEV)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    st = L.kda_prefill(ctx.handle, p.handle, ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["g"]), ptr(d["beta"]),
+                       ptr(d["cu_seqlens"]), 1.0, ptr(d["initial_state"]), ptr(s), ptr(o),
+                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, L.kda_last_error().decode()
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle(d)
+    assert_close("out", o, o_ref)
+    assert_close("final_state", s, s_ref)
+    o_b, s_b = run(d, plan=p)
+    assert torch.equal(o, o_b) and torch.equal(s, s_b)
+
+
+def test_graph_replay_survives_arena_growth_and_plan_release():
+    """A graph captured with a split plan (which uses the stream's workspace
+    arena) is replayed after (a) an uncaptured call with a far larger plan on
+    the same stream has grown that arena and (b) the caller has dropped its
+    reference to the captured plan. Each replay equals the eager result."""
+    import gc
+    d = draw([600, 150], 4, seed=71, state_std=0.1, device=DEV)
+    cu_h = d["cu_seqlens_host"]
+    p = kda.plan_split(cu_h, 4, [20, 0], 12, device=DEV)
+    cu = p.cu_device()
+    o_buf = torch.empty_like(d["q"])
+    s_buf = torch.empty_like(d["initial_state"])
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=cu_h,
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, cu_seqlens_host=cu_h,
+                    initial_state=d["initial_state"], final_state=s_buf, out=o_buf, plan=p)
+    small_ws = p.info()["workspace_bytes"]
+    del p
+    gc.collect()
+    # a segmented plan on the same stream needs far more workspace: the arena grows
+    big = draw([3000, 1000], 8, seed=5, state_std=0.1, device=DEV)
+    p_big = kda.plan_segments(big["cu_seqlens_host"], 8, 64, device=DEV)
+    assert p_big.info()["workspace_bytes"] > 4 * small_ws + (1 << 20)
+    with torch.cuda.stream(stream):
+        o_big, s_big = kda.prefill(big["q"], big["k"], big["v"], big["g"], big["beta"],
+                                   cu_seqlens_host=big["cu_seqlens_host"], initial_state=big["initial_state"],
+                                   output_final_state=True, plan=p_big)
+    torch.cuda.current_stream().wait_stream(stream)
+    o_ser, s_ser = run(d, mode=False)
+    for trial in range(3):
+        o_buf.zero_()
+        s_buf.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_buf, o_ser) and torch.equal(s_buf, s_ser), "replay %d differs from serial" % trial
+        with torch.cuda.stream(stream):  # eager work on the capture stream between replays
+            kda.prefill(big["q"], big["k"], big["v"], big["g"], big["beta"],
+                        cu_seqlens_host=big["cu_seqlens_host"], initial_state=big["initial_state"],
+                        output_final_state=True, plan=p_big)
+        torch.cuda.synchronize()
+    o_ref, s_ref = oracle(big)
+    assert_close("out(big)", o_big, o_ref)
