@@ -359,6 +359,33 @@ kda_status kda_prefill_ex_validate(const kda_plan *plan, const kda_prefill_opts 
                                    const int32_t *cu_seqlens_dev, float scale, const void *initial_state,
                                    const void *final_state, const void *out);
 
+/* kda_prefill_ex for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc. The call
+ * allocates nothing and synchronises nothing: its workspace is a static
+ * device array of kda_noalloc_scratch_bytes() bytes (32 MiB) that each GPU
+ * the library runs on holds from the first kda_create on it until the
+ * process ends (its address is looked up once per device, in kda_create).
+ * Arguments, results and errors are those of kda_prefill_ex, and the
+ * results are bitwise those of kda_prefill_ex with the same plan. A plan
+ * whose workspace (kda_plan_workspace_bytes, plus 4 * Tt * H bytes after it,
+ * rounded up to 256, for a bf16 beta) exceeds the static array is refused
+ * with KDA_ERR_INVALID before any launch. Serial plans need no workspace;
+ * warm-start split plans need 128 KiB per (split sequence, head); the
+ * segmented and warm-start CP plans of long sequences usually exceed it. The
+ * speculation feedback of split and warm-start CP plans is not collected by
+ * this call (it needs pinned host memory), and no per-kernel timing is
+ * recorded. Every call on one GPU shares that GPU's array and leaves it
+ * holding its own intermediates; nothing in it needs clearing between calls,
+ * but calls that overlap in time on one GPU (on different streams, or from
+ * different threads without ordering) race on it. */
+kda_status kda_prefill_noalloc(kda_ctx *ctx, const kda_plan *plan, const kda_prefill_opts *opts, const void *q,
+                               const void *k, const void *v, const float *g, const void *beta,
+                               const int32_t *cu_seqlens_dev, float scale, const void *initial_state,
+                               void *final_state, void *out, hipStream_t stream);
+
+/* Bytes of the static scratch of kda_prefill_noalloc (32 MiB). */
+size_t kda_noalloc_scratch_bytes(void);
+
 /* K1 alone, for inspection and tests: write every chunk record of the plan
  * into `records` (device, total_chunks * H * KDA_RECORD_BYTES bytes, record
  * of (chunk c, head h) at index h * total_chunks + c; layout in

@@ -106,6 +106,9 @@ def lib():
                                                   P, P]),
                 "kda_prefill_ex_validate": (ctypes.c_int, [P, ctypes.POINTER(PrefillOpts), P, P, P, P, P, P, F32,
                                                            P, P, P]),
+                "kda_prefill_noalloc": (ctypes.c_int, [P, P, ctypes.POINTER(PrefillOpts), P, P, P, P, P, P, F32, P,
+                                                       P, P, P]),
+                "kda_noalloc_scratch_bytes": (ctypes.c_size_t, []),
                 "kda_decode": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P, P]),
                 "kda_decode_validate": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, P]),
                 "kda_decode_slots": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P, P, P, F32, P, I32, P, P, P]),
@@ -345,7 +348,7 @@ def _ptr(t):
 
 def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=False,
             use_intracard_cp=False, scale=1.0, final_state=None, out=None, plan=None,
-            cu_seqlens_host=None, state_dtype=None):
+            cu_seqlens_host=None, state_dtype=None, no_alloc=False):
     """KDA forward prefill.
 
     q, k, v: bf16 [Tt, H, 128] packed, or [B, T, H, 128] (B equal-length
@@ -358,6 +361,9 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
     initial_state: in-place update); with output_final_state=True and no
     final_state, a new one is allocated. States are fp32, or all bf16
     (state_dtype, default: the dtype of the given state, else fp32).
+    no_alloc=True runs kda_prefill_noalloc: the library then allocates
+    nothing and uses its static per-device scratch (pass out, and
+    final_state if wanted, so that this wrapper allocates nothing either).
     Returns (o, final_state or None).
     """
     import torch
@@ -434,9 +440,10 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_
     if torch.cuda.is_current_stream_capturing() and not any(p is plan for p in _captured_plans):
         _captured_plans.append(plan)
     opts = PrefillOpts(Hk, int(beta16), int(state_dtype == torch.bfloat16))
-    _check(lib().kda_prefill_ex(ctx.handle, plan.handle, ctypes.byref(opts), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                _ptr(beta), _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state),
-                                _ptr(out), ctypes.c_void_p(stream)), "kda_prefill")
+    entry = lib().kda_prefill_noalloc if no_alloc else lib().kda_prefill_ex
+    _check(entry(ctx.handle, plan.handle, ctypes.byref(opts), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                 _ptr(cu_dev), float(scale), _ptr(initial_state), _ptr(final_state), _ptr(out),
+                 ctypes.c_void_p(stream)), "kda_prefill_noalloc" if no_alloc else "kda_prefill")
     return out, final_state
 
 

@@ -658,6 +658,20 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Static scratch of the no-allocation prefill (kda_prefill_noalloc): the
+// workspace of a call that may not allocate, one copy per device, held until
+// the process ends. Host code must never pass the array's name to a kernel
+// (on the host it is only a stand-in): the runtime looks up each device's
+// address with hipGetSymbolAddress, once, and passes that.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t static_scratch_address(void** ptr) { return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch)); }
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_fused(const K2Args& a, hipStream_t s) {

@@ -138,6 +138,12 @@ hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
 hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);
 
+// The static scratch of the no-allocation prefill: its size, and its device
+// address on the current device (hipGetSymbolAddress, in the source file that
+// defines it).
+size_t static_scratch_bytes();
+hipError_t static_scratch_address(void** ptr);
+
 
 constexpr int kChunk = 16;                      // tokens per chunk
 constexpr size_t kRecBytes = 18432;            // bytes of one K1 chunk record

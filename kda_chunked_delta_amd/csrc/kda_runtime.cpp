@@ -48,6 +48,30 @@ kda_status hip_fail(hipError_t e, const char* what) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Per-device addresses of the static scratch of kda_prefill_noalloc, each
+// looked up once, with its device current.
+hipError_t device_scratch(int device, void** out) {
+    static std::mutex mu;
+    static std::unordered_map<int, void*> addr;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = addr.find(device);
+    if (it != addr.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return e;
+    if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = static_scratch_address(&ptr);
+    if (prev >= 0 && prev != device) (void)hipSetDevice(prev);
+    if (e != hipSuccess) return e;
+    addr[device] = ptr;
+    *out = ptr;
+    return hipSuccess;
+}
+
 double env_double(const char* name, double dflt) {
     const char* s = getenv(name);
     if (!s || !*s) return dflt;
@@ -580,6 +604,7 @@ struct kda_ctx {
     std::mutex mu;
     std::unordered_map<hipStream_t, Arena> arenas;
     std::vector<void*> retired;  // arena memory that served a graph capture, freed in kda_destroy
+    void* scratch = nullptr;     // this device's copy of the static scratch (kda_prefill_noalloc)
     bool poison = false;
     bool timing = false;
     std::vector<TimedLaunch> events;  // pool, reused across calls
@@ -632,6 +657,13 @@ kda_status kda_create(int device, kda_ctx** out) {
         return hip_fail(e, "hipGetDeviceProperties");
     }
     c->n_cus = c->prop.multiProcessorCount;
+    // the device address of the static scratch, looked up once per device
+    // with that device current
+    e = device_scratch(device, &c->scratch);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "hipGetSymbolAddress (static scratch)");
+    }
     const char* pz = getenv("KDA_DEBUG_POISON");
     c->poison = pz && *pz && strcmp(pz, "0") != 0;
     *out = c;
@@ -1143,6 +1175,19 @@ kda_status kda_prefill_ex(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opt
                           float scale, const void* s0, void* sT, void* out, hipStream_t stream) {
     return prefill_impl(ctx, p, opts, q, k, v, g, beta, cu_dev, scale, s0, sT, out, stream, nullptr);
 }
+
+kda_status kda_prefill_noalloc(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts* opts, const void* q,
+                               const void* k, const void* v, const float* g, const void* beta,
+                               const int32_t* cu_dev, float scale, const void* s0, void* sT, void* out,
+                               hipStream_t stream) {
+    if (!ctx) return fail(KDA_ERR_INVALID, "kda_prefill_noalloc: ctx is NULL");
+    if (!ctx->scratch)
+        return fail(KDA_ERR_HIP, "kda_prefill_noalloc: the static scratch of device %d has no address", ctx->device);
+    const FixedWorkspace fw{(uint8_t*)ctx->scratch, static_scratch_bytes()};
+    return prefill_impl(ctx, p, opts, q, k, v, g, beta, cu_dev, scale, s0, sT, out, stream, &fw);
+}
+
+size_t kda_noalloc_scratch_bytes(void) { return static_scratch_bytes(); }
 
 kda_status kda_decode_slots_validate(int32_t n_seqs, int32_t H, int32_t qk_heads, int32_t dk, int32_t dv,
                                      const void* q, const void* k, const void* v, const float* g,
