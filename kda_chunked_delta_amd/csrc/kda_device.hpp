@@ -68,6 +68,7 @@ constexpr int K1_KB = 4096;
 constexpr int K1_QA = 8192;
 constexpr int K1_BETA = 12288;
 constexpr int K1_BYTES = K1_BETA + 64;
+constexpr int K1_NB = K1_BETA;  // the Gram factors alone (beta kept elsewhere by the fused kernel)
 // per T' wavefront, private LDS: L^T as fp32 [16][K1_LSTRIDE] (a 20-float row
 // stride puts the 16 lanes of each b128 phase on distinct banks)
 constexpr int K1_LSTRIDE = 20;
@@ -210,6 +211,7 @@ constexpr int STG_V = 8192;    // v  [16][256 B]
 constexpr int STG_G = 12288;   // g  [16][512 B]
 constexpr int STG_B = 20480;   // beta [16] fp32
 constexpr int STG_BYTES = 20544;
+constexpr int STG_NB = STG_B;  // the staged rows alone (beta kept elsewhere by the fused kernel)
 
 // Staging byte offset of byte `byte` of row r of a 256-byte (bf16) row.
 __device__ __forceinline__ int stg_act_off(int r, int byte) {
@@ -326,24 +328,25 @@ __device__ __forceinline__ int chunk_rows(int rem, int ci) {
     return n;
 }
 
-// Write a loaded RowChunk to the staging area stg.
+// Write a loaded RowChunk to the staging area stg (rows) and stg_b (the 16
+// betas; stg + STG_B where the layout keeps them together).
 __device__ __forceinline__ void k1_stage(const RowChunk& rc, int wave, int lane, const RowLaneOffsets& lo,
-                                         uint8_t* stg) {
+                                         uint8_t* stg, float* stg_b) {
     *(u32x2*)(stg + STG_Q + lo.st_act) = rc.q;
     *(u32x2*)(stg + STG_K + lo.st_act) = rc.k;
     *(u32x2*)(stg + STG_V + lo.st_act) = rc.v;
     *(f32x4*)(stg + STG_G + lo.st_g) = rc.g;
-    if (wave == 0 && lane < 16) *(float*)(stg + STG_B + 4 * lane) = rc.b;
+    if (wave == 0 && lane < 16) stg_b[lane] = rc.b;
 }
 
 // Phase 1's fragments of wavefront w from a staged chunk.
-__device__ __forceinline__ void k1_read_staged(const uint8_t* stg, int lane, const RowLaneOffsets& lo,
-                                               RawChunk& raw) {
+__device__ __forceinline__ void k1_read_staged(const uint8_t* stg, const float* stg_b, int lane,
+                                               const RowLaneOffsets& lo, RawChunk& raw) {
     raw.q = *(const u32x2*)(stg + STG_Q + lo.rd_act);
     raw.k = *(const u32x2*)(stg + STG_K + lo.rd_act);
     raw.v = *(const u32x2*)(stg + STG_V + lo.rd_act);
     raw.g = *(const f32x4*)(stg + STG_G + lo.rd_g);
-    raw.b = *(const float*)(stg + STG_B + 4 * (lane & 15));
+    raw.b = stg_b[lane & 15];
 }
 
 // Largest |G| (log2 units) for which phase 1 factors the decays about the
@@ -351,8 +354,10 @@ __device__ __forceinline__ void k1_read_staged(const uint8_t* stg, int lane, con
 // the unmasked Gram terms exp(G_r - G_i) (i <= r) are at most 1.
 constexpr float G_FACTOR0_MAX = 100.0f;
 
+// scr_b: the chunk's 16 betas (scr + K1_BETA where the layout keeps them
+// together)
 __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lane, uint8_t* rec,
-                                          uint8_t* scr) {
+                                          uint8_t* scr, float* scr_b) {
     const int gg = lane >> 4, m = lane & 15;
     // in-chunk cumulative log2-decay per channel: inclusive scan over the tokens
     float G[4];
@@ -443,7 +448,7 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     *(u32x2*)(rec + REC_V + to) = quad_transpose16(raw.v, lane);
     // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
     if (m == 15) *(f32x4*)(rec + REC_GC + (32 * gg + 4 * wave) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
-    if (wave == 0 && gg == 0) *(float*)(scr + K1_BETA + 4 * m) = raw.b;
+    if (wave == 0 && gg == 0) scr_b[m] = raw.b;
 }
 
 // ---------------------------------------------------------------------------
@@ -461,7 +466,8 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
 // transposed (lt[c * K1_LSTRIDE + r] = L[r][c]), so that lane (gg, i) of a
 // reader finds column i of L in row i of lt. With lbeta, the chunk's beta
 // is copied beside it.
-__device__ __forceinline__ void k1_lkk(int lane, const uint8_t* scr, float* lt, float* lbeta) {
+__device__ __forceinline__ void k1_lkk(int lane, const uint8_t* scr, const float* scr_b, float* lt,
+                                       float* lbeta) {
     const int gg = lane >> 4, m = lane & 15;
     // (k exp(G - G_ref)) (k exp(G_ref - G))^T: lane holds A_kk[r][m], r = 4gg + v,
     // which the row's beta then scales
@@ -470,12 +476,12 @@ __device__ __forceinline__ void k1_lkk(int lane, const uint8_t* scr, float* lt, 
     for (int p = 0; p < 4; ++p)
         a = mfma_k32(*(const u32x4*)(scr + K1_KA + p * 1024 + lane * 16),
                      *(const u32x4*)(scr + K1_KB + p * 1024 + lane * 16), a);
-    const f32x4 br = *(const f32x4*)(scr + K1_BETA + 16 * gg);
+    const f32x4 br = *(const f32x4*)(scr_b + 4 * gg);
     f32x4 l;
 #pragma unroll
     for (int v = 0; v < 4; ++v) l[v] = (m < 4 * gg + v) ? br[v] * a[v] : 0.f;
     *(f32x4*)(lt + m * K1_LSTRIDE + 4 * gg) = l;
-    if (lbeta && gg == 0) lbeta[m] = *(const float*)(scr + K1_BETA + 4 * m);
+    if (lbeta && gg == 0) lbeta[m] = scr_b[m];
 }
 
 // Rows 4 s4 .. 4 s4 + 3 of T' = (I + L)^-1 diag(beta) from L^T (as k1_lkk
@@ -518,7 +524,7 @@ __device__ __forceinline__ void k1_tsolve(int lane, int s4, uint8_t* rec, const 
 
 // Both halves on one wavefront, through its private lw (1 KiB).
 __device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, const uint8_t* scr, float* lw) {
-    k1_lkk(lane, scr, lw, nullptr);
+    k1_lkk(lane, scr, (const float*)(scr + K1_BETA), lw, nullptr);
     k1_tsolve(lane, s4, rec, lw, (const float*)(scr + K1_BETA));
 }
 

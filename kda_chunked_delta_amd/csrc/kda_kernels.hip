@@ -250,12 +250,12 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
                                           wave);
         RowChunk rc;
         k1_load_chunk<GVA>(rs, 0, rows_of(tok0, end), lo, rc);
-        k1_stage(rc, wave, lane, lo, stg);
+        k1_stage(rc, wave, lane, lo, stg, (float*)(stg + STG_B));
         lds_barrier();
         RawChunk raw;
-        k1_read_staged(stg, lane, lo, raw);
+        k1_read_staged(stg, (const float*)(stg + STG_B), lane, lo, raw);
         lds_barrier();  // the staging area is free again
-        k1_phase1(raw, wave, lane, rec, scr);
+        k1_phase1(raw, wave, lane, rec, scr, (float*)(scr + K1_BETA));
         lds_barrier();
         k1_phase2(wave, lane, rec, scr, lw);
         lds_barrier();
@@ -281,14 +281,23 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 //     chunk i+6 (rows 2w, 2w+1; into the register set just staged).
 // Each SIMD holds two state wavefronts and two K1 wavefronts. Records live in
 // a 4-deep LDS ring; K1 scratch, the shared L^T and the staged rows in 2-deep
-// ones. Both roles run three start-up intervals and then the same even
+// ones. The staged rows and the K1 scratch (without their betas) fill the
+// first 64 KiB, so that every K1 access to them is a per-lane base plus an
+// immediate offset; the K1 loop is unrolled over the two slots of those
+// rings. Both roles run three start-up intervals and then the same even
 // number of intervals, after one start-up barrier: the trailing K1 work on
 // chunks past the end reads zeros (a buffer load of a chunk with no rows
 // touches no memory) and fills slots nobody reads, so the K1 loop body is
 // unconditional and the compiler's wait for a register set covers only that
 // set's loads.
 // ---------------------------------------------------------------------------
-constexpr int FUSED_LDS = 4 * REC_BYTES + 2 * K1_BYTES + 2 * LB_BYTES + 2 * STG_BYTES;
+constexpr int F_STG = 0;                              // 2 staged chunks (rows)
+constexpr int F_SCR = F_STG + 2 * STG_NB;             // 2 K1 scratch areas (Gram factors)
+constexpr int F_LB = F_SCR + 2 * K1_NB;               // 2 shared L^T + beta
+constexpr int F_BETA = F_LB + 2 * LB_BYTES;           // betas: 2 staged [16], 2 scratch [16]
+constexpr int F_REC = (F_BETA + 256 + 255) / 256 * 256;  // 4 records
+constexpr int FUSED_LDS = F_REC + 4 * REC_BYTES;
+static_assert(F_LB <= 65536, "the K1 rings fit the immediate-offset range of LDS instructions");
 static_assert(FUSED_LDS <= 160 * 1024, "fused kernel LDS");
 
 // GVA: q/k heads differ from the value heads (value head h reads q/k head
@@ -296,10 +305,12 @@ static_assert(FUSED_LDS <= 160 * 1024, "fused kernel LDS");
 template <bool GVA>
 __device__ __forceinline__ void fused_body(const K2Args& a) {
     extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* recs = smem;                      // 4 records
-    uint8_t* scrs = recs + 4 * REC_BYTES;      // 2 K1 scratch areas
-    uint8_t* lbs = scrs + 2 * K1_BYTES;        // 2 shared L^T + beta
-    uint8_t* stgs = lbs + 2 * LB_BYTES;        // 2 staged chunks
+    uint8_t* recs = smem + F_REC;              // 4 records
+    uint8_t* scrs = smem + F_SCR;              // 2 K1 scratch areas
+    uint8_t* lbs = smem + F_LB;                // 2 shared L^T + beta
+    uint8_t* stgs = smem + F_STG;              // 2 staged chunks
+    float* stg_betas = (float*)(smem + F_BETA);          // [2][16]
+    float* scr_betas = (float*)(smem + F_BETA + 128);    // [2][16]
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const UnitDesc u = a.units[blockIdx.x / H];
@@ -370,10 +381,11 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             constexpr int R = decltype(role)::value;
             auto gram = [&](int c) __attribute__((always_inline)) {  // A_qk and L of chunk c
                 if constexpr (R == 2) {
-                    const uint8_t* scr = scrs + ring_off((c & 1) * K1_BYTES);
+                    const uint8_t* scr = scrs + ring_off((c & 1) * K1_NB);
+                    const float* scr_b = (const float*)((const uint8_t*)scr_betas + ring_off((c & 1) * 64));
                     float* lb = (float*)(lbs + ring_off((c & 1) * LB_BYTES));
                     k1_phase2_qk(lane, recs + ring_off((c % 4) * REC_BYTES), scr);
-                    k1_lkk(lane, scr, lb, lb + LB_BETA / 4);
+                    k1_lkk(lane, scr, scr_b, lb, lb + LB_BETA / 4);
                 }
             };
             auto solve = [&](int c) __attribute__((always_inline)) {  // rows of T' of chunk c
@@ -439,37 +451,45 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             const int ci = i >= W ? i - W : i;
             k1_load_chunk<GVA>(rs, ci, chunk_rows(rem, ci), lo, rc);
         };
-        auto stage = [&](RowChunk& rc, int ci) __attribute__((always_inline)) {
+        // the staging and scratch slots are compile-time constants: chunk c
+        // uses slot c & 1 of both rings
+        auto stage = [&](RowChunk& rc, auto slot) __attribute__((always_inline)) {
+            constexpr int S = decltype(slot)::value;
             // the register set is read only from here on (see below)
             asm volatile("" : "+v"(rc.q), "+v"(rc.k), "+v"(rc.v), "+v"(rc.g), "+v"(rc.b));
-            k1_stage(rc, w8, lane, lo, stgs + ring_off((ci & 1) * STG_BYTES));
+            k1_stage(rc, w8, lane, lo, stgs + S * STG_NB, stg_betas + 16 * S);
         };
-        auto interval = [&](int i, RowChunk& rc) __attribute__((always_inline)) {
+        // interval i works on chunk i + 3 (staging and scratch slot R = (i + 3) & 1)
+        // and stages chunk i + 4 (slot 1 - R)
+        auto interval = [&](int i, RowChunk& rc, auto rslot) __attribute__((always_inline)) {
+            constexpr int R = decltype(rslot)::value;
             // Phase 1 reads LDS only after the barrier that ends the previous
             // interval, and the staging of rc waits for its loads there too:
             // the empty redefinitions keep the compiler from hoisting
             // either above that barrier.
             RawChunk raw;
-            k1_read_staged(stgs + ring_off(((i + 3) & 1) * STG_BYTES), lane, lo, raw);
-            // ring slots as opaque uniform offsets, so every LDS access of a
-            // phase is one per-lane base plus immediate offsets
-            k1_phase1(raw, w8, lane, recs + ring_off(((i + 3) % 4) * REC_BYTES),
-                      scrs + ring_off(((i + 3) & 1) * K1_BYTES));
-            stage(rc, i + 4);
+            k1_read_staged(stgs + R * STG_NB, stg_betas + 16 * R, lane, lo, raw);
+            // the record slot as an opaque uniform offset, so every record
+            // access of the phase is one per-lane base plus immediate offsets
+            k1_phase1(raw, w8, lane, recs + ring_off(((i + 3) % 4) * REC_BYTES), scrs + R * K1_NB,
+                      scr_betas + 16 * R);
+            stage(rc, std::integral_constant<int, 1 - R>{});
             load(rc, i + 6);
             lds_barrier();
         };
+        using Z = std::integral_constant<int, 0>;
+        using O = std::integral_constant<int, 1>;
         load(r0, 0);
         load(r1, 1);
-        stage(r0, 0);
+        stage(r0, Z{});
         load(r0, 2);
         lds_barrier();  // start-up: chunk 0 staged
-        interval(-3, r1);
-        interval(-2, r0);
-        interval(-1, r1);
+        interval(-3, r1, Z{});
+        interval(-2, r0, O{});
+        interval(-1, r1, Z{});
         for (int i = 0; i < n_main; i += 2) {
-            interval(i, r0);
-            interval(i + 1, r1);
+            interval(i, r0, O{});
+            interval(i + 1, r1, Z{});
         }
     }
 }
