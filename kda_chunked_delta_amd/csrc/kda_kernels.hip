@@ -186,6 +186,19 @@ template <int NT>
 __device__ __forceinline__ void load_unit_state(const K2Args& a, const UnitDesc& u, int h, f32x4 (&S)[8][NT],
                                                 int n0, int gg, int m) {
     const size_t off = ((size_t)u.seq * a.c.H + h) * (D * D);
+    if (u.b_slot >= 0) {
+        // a CP segment whose predecessor's transfer vanished starts from that
+        // segment's B summary (its carry, bit for bit)
+        const size_t so = (size_t)u.b_slot * a.c.H + h;
+        const int32_t* fl = a.m_live + so * 8;
+        int live = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) live |= fl[j];
+        if (!live) {
+            load_state(a.b_seg + so * (D * D), S, n0, gg, m);
+            return;
+        }
+    }
     if (u.in_slot >= 0)
         load_state(a.carries + ((size_t)u.in_slot * a.c.H + h) * (D * D), S, n0, gg, m);
     else if (a.s0 && a.state_bf16)
@@ -302,8 +315,23 @@ static_assert(FUSED_LDS <= 160 * 1024, "fused kernel LDS");
 
 // GVA: q/k heads differ from the value heads (value head h reads q/k head
 // h / group); the plain instance keeps the q/k loads on v's offsets.
-template <bool GVA>
+// BSUM: the K1 pass of the segmented CP pipeline. Every chunk record formed
+// in LDS is also written to the workspace (records [H][total_chunks]), and
+// the state wavefronts of a unit with out_slot >= 0 run the state update
+// from zero without output, whose end state (the segment's B summary) goes
+// to carries[out_slot] (the host points carries at the summaries).
+template <bool GVA, bool BSUM>
 __device__ __forceinline__ void fused_body(const K2Args& a) {
+    if constexpr (BSUM) {
+        if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
+        if (a.gate_flags) {
+            int32_t acc = 0;
+            for (int64_t i = threadIdx.x; i < a.n_gate_flags; i += blockDim.x) acc |= a.gate_flags[i];
+            const int armed = __syncthreads_or(acc != 0);
+            if (blockIdx.x == 0 && threadIdx.x == 0) a.gate_out[0] = armed;
+            if (!armed) return;  // fallback not armed
+        }
+    }
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* recs = smem + F_REC;              // 4 records
     uint8_t* scrs = smem + F_SCR;              // 2 K1 scratch areas
@@ -370,9 +398,21 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         lds_barrier();  // start-up: the first chunk is staged
         const int rem = (int)(end - tok0);
         auto step = [&](int c, int i) __attribute__((always_inline)) {
-            f32x4 oacc[1];
-            chain_step<1, true, true>(recs + ring_off((i % 4) * REC_BYTES), S, w8, lane, oacc);
-            store_output(a, h, tok0 + (int64_t)CH * c, chunk_rows(rem, c), oacc[0], w8, gg, m);
+            const uint8_t* rec = recs + ring_off((i % 4) * REC_BYTES);
+            if constexpr (BSUM) {
+                f32x4 unused[1];
+                if (u.out_slot >= 0) chain_step<1, true, false>(rec, S, w8, lane, unused);
+                // the record is complete in this interval (its T' was formed in
+                // the previous one) and its slot is overwritten after the next
+                // barrier: the state wavefronts copy it out now
+                u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0 + c) * REC_BYTES);
+                const u32x4* src = (const u32x4*)rec;
+                for (int v = (int)threadIdx.x; v < REC_VEC; v += 512) dst[v] = src[v];
+            } else {
+                f32x4 oacc[1];
+                chain_step<1, true, true>(rec, S, w8, lane, oacc);
+                store_output(a, h, tok0 + (int64_t)CH * c, chunk_rows(rem, c), oacc[0], w8, gg, m);
+            }
         };
         // one loop per phase-2 role (0: none, 1: rows 4 w8.. of T', 2: A_qk and
         // L), so that each loop body is one block in which phase 2 of later
@@ -496,14 +536,21 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
 
 template <bool GVA>
 __global__ __launch_bounds__(1024) void kda_fused(K2Args a) {
-    fused_body<GVA>(a);
+    fused_body<GVA, false>(a);
 }
 
 // The fix-up and publish launches (a.fixup): the same body under a symbol of
 // its own, so that kernel traces and statistics tell them from the main launch.
 template <bool GVA>
 __global__ __launch_bounds__(1024) void kda_fused_fixup(K2Args a) {
-    fused_body<GVA>(a);
+    fused_body<GVA, false>(a);
+}
+
+// K1 of the segmented CP pipeline with the B half of pre_scan: the records of
+// every chunk, written once, and each segment's B summary.
+template <bool GVA>
+__global__ __launch_bounds__(1024) void kda_k1_bsum(K2Args a) {
+    fused_body<GVA, true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -535,63 +582,119 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// CP pre_scan over materialised K1 records: one workgroup of 16 wavefronts
-// per (segment, head). Wavefronts 0..7 run the K2 state update from S = 0
-// over the segment (B, value columns 16w..), wavefronts 8..15 run it from
-// S = I with V := 0 (M, key columns 16(w-8)..). Both use K2's chain step, so
-// B follows K2's arithmetic exactly.
+// CP pre_scan, transfer half: one workgroup of 8 wavefronts per (segment,
+// head) runs K2's state update from S = I with V := 0 over the segment's
+// records (the transfer M; wavefront w holds key columns 16w..16w+15). The B
+// half (the update from S = 0) runs in the K1 launch, on the records it forms.
+// A tile of M that is exactly zero stays zero (its columns evolve
+// independently). Every 4 chunks the workgroup checks its tiles and stops
+// once all are zero: under decay the transfer underflows within a few chunks,
+// and the merge then takes B as the carry without reading M. Only the fields
+// the update reads (X, Kt, exp(G_C), T') are fetched.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void kda_cp_prescan(PrescanArgs a) {
+struct TransferFetch {
+    // 16-byte vectors of a record: X and Kt^T [256, 768), exp(G_C) and T'
+    // [1056, 1152)
+    static constexpr int NV = 608;
+    static constexpr int N = (NV + 511) / 512;
+    u32x4 r[N];
+    __device__ __forceinline__ static int index(int i) { return i < 512 ? 256 + i : 1056 + (i - 512); }
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ src) {
+        const u32x4* s = (const u32x4*)src;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int i = threadIdx.x + j * 512;
+            if (i < NV) r[j] = __builtin_nontemporal_load(s + index(i));
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t* dst) const {
+        u32x4* d = (u32x4*)dst;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int i = threadIdx.x + j * 512;
+            if (i < NV) d[index(i)] = r[j];
+        }
+    }
+};
+
+static_assert(REC_X / 16 == 256 && REC_KT / 16 == 512 && REC_V / 16 == 768 && REC_GC / 16 == 1056 &&
+                  REC_T / 16 == 1088 && REC_VEC == 1152,
+              "transfer fetch ranges follow the record layout");
+
+__global__ __launch_bounds__(512) void kda_cp_transfer(PrescanArgs a) {
     if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
     __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
+    __shared__ int32_t live_tiles[8];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const PrescanDesc it = a.items[blockIdx.x / H];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gg = lane >> 4, m = lane & 15;
-    const bool is_b = wave < 8;
-    const int n0 = wave & 7;
     f32x4 S[8][1];
-    if (is_b)
-        load_state(nullptr, S, n0, gg, m);
-    else
-        identity_state(S, n0, gg, m);
+    identity_state(S, wave, gg, m);
     f32x4 unused[1];
     const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
-    // An M tile (16 columns of the transfer matrix) that is exactly zero
-    // stays zero: its columns evolve independently, and the update of a zero
-    // column is zero. Under decay the transfer underflows within a few
-    // chunks, so an M wavefront checks its tile every 4 chunks and stops
-    // computing once it is zero (it still takes part in the record loads).
-    bool m_live = true;
-    record_loop<1024>(rb, it.n_chunks, recs, [&](int ci, const uint8_t* r) {
-        if (is_b) {
-            chain_step<1, true, false>(r, S, n0, lane, unused);
-        } else if (m_live) {
-            chain_step<1, false, false>(r, S, n0, lane, unused);
-            if ((ci & 3) == 3) m_live = tile_nonzero(S);
+    const int nc = it.n_chunks;
+    // whether any tile of the workgroup is nonzero (uniform; a barrier round)
+    auto any_live = [&]() __attribute__((always_inline)) {
+        const bool nz = tile_nonzero(S);
+        if (lane == 0) live_tiles[wave] = nz ? 1 : 0;
+        lds_barrier();
+        int any = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) any |= live_tiles[j];
+        return any != 0;
+    };
+    TransferFetch p0, p1;
+    if (nc > 0) p0.load(rb);
+    if (nc > 1) p1.load(rb + REC_BYTES);
+    if (nc > 0) p0.store(recs[0]);
+    lds_barrier();
+    bool live = true;
+    for (int ci = 0; ci < nc; ci += 2) {
+        if (ci + 2 < nc) p0.load(rb + (size_t)(ci + 2) * REC_BYTES);
+        chain_step<1, false, false>(recs[0], S, wave, lane, unused);
+        if (ci + 1 < nc) p1.store(recs[1]);
+        lds_barrier();
+        if (ci + 1 < nc) {
+            if (ci + 3 < nc) p1.load(rb + (size_t)(ci + 3) * REC_BYTES);
+            chain_step<1, false, false>(recs[1], S, wave, lane, unused);
+            if (ci + 2 < nc) p0.store(recs[0]);
+            lds_barrier();
         }
-    });
-    if (!is_b) m_live = tile_nonzero(S);
-    store_state((is_b ? a.b_seg : a.m_seg) + ((size_t)it.slot * H + h) * (D * D), S, n0, gg, m);
-    if (!is_b && lane == 0) a.m_live[((size_t)it.slot * H + h) * 8 + n0] = m_live ? 1 : 0;
+        if ((ci & 3) == 2 && ci + 2 < nc && !any_live()) {
+            live = false;
+            break;
+        }
+    }
+    if (live) live = any_live();
+    const size_t so = (size_t)it.slot * H + h;
+    const bool nz = live && tile_nonzero(S);  // (a wavefront-wide ballot)
+    if (lane == 0) a.m_live[so * 8 + wave] = nz ? 1 : 0;
+    // the merge reads a transfer only when some tile of it is live, and then
+    // reads all of it
+    if (live) store_state(a.m_seg + so * (D * D), S, wave, gg, m);
 }
 
 // ---------------------------------------------------------------------------
-// CP merge: one workgroup of 8 wavefronts per (segmented sequence, head,
-// 16-column value tile). carry_0 = S0 (or 0); carry_{s+1} = M_s carry_s + B_s,
-// in segment order, on fp32 MFMA. Wavefront t owns carry rows 16t..16t+15.
-// Every carry (including carry_0) is written to the carries scratch, so that
-// segment-K2 never reads initial_state while another segment writes
-// final_state in place. Only the carry is serial: the summaries (M_s, B_s)
-// of the next step are loaded while the current one computes, into the
-// other of two register sets, and each step splits its 32 MFMAs over two
-// accumulators.
+// CP merge: carry_0 = S0 (or 0); carry_{s+1} = M_s carry_s + B_s, in segment
+// order, on fp32 MFMA. Where M_s vanished (every tile exactly zero), carry_{s+1}
+// is B_s itself and depends on nothing before it, so the carries fall into
+// runs, each started by such a segment (or by segment 0) and continued over
+// the following live transfers. One workgroup of 8 wavefronts per (segment,
+// head, 16-column value tile); the workgroup of a segment that starts a run
+// computes the run, the others return at once. A segment whose predecessor's
+// transfer vanished takes its start state from B directly (segment-K2 reads
+// it), so only carry_0 and the carries after live transfers are written.
+// Carry_0 is always written, so that segment-K2 never reads initial_state
+// while another segment writes final_state in place. Wavefront t owns carry
+// rows 16t..16t+15; the summaries of the next step load while the current
+// one computes, and each step splits its 32 MFMAs over two accumulators.
 // ---------------------------------------------------------------------------
 struct MergeOperands {
-    f32x4 m[8];  // M_s[16 wave + m][32 gg + 4j .. + 3], j = 0..7
-    f32x4 b;     // B_s[16 wave + 4 gg + v][16 vt + m], v = 0..3
-    int zero;    // M_s is exactly zero (uniform)
+    f32x4 m[8];   // M_s[16 wave + m][32 gg + 4j .. + 3], j = 0..7
+    f32x4 b;      // B_s[16 wave + 4 gg + v][16 vt + m], v = 0..3
+    int32_t live; // some tile of M_s is nonzero (the same in every lane)
 };
 
 __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
@@ -600,81 +703,94 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
     const int H = a.c.H;
     const int vt = blockIdx.x & 7;
     const int h = (blockIdx.x >> 3) % H;
-    const MergeDesc it = a.items[(blockIdx.x >> 3) / H];
+    const MergeSeg sg = a.segs[(blockIdx.x >> 3) / H];
+    const MergeDesc it = a.items[sg.item];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gg = lane >> 4, m = lane & 15;
-
-    {
+    const int n_sum = it.n_segments - 1;  // summaries (segments 0 .. n-2)
+    auto flags = [&](int j) __attribute__((always_inline)) {
+        const int32_t* fl = a.m_live + ((size_t)(it.prescan0 + j) * H + h) * 8;
+        int32_t any = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) any |= fl[k];
+        return any;
+    };
+    const int s0 = sg.seg;
+    // a segment after a live transfer lies inside a run started earlier
+    if (s0 > 0 && __builtin_amdgcn_readfirstlane(flags(s0 - 1)) != 0) return;
+    if (s0 == 0) {
         const size_t s0_off = ((size_t)it.seq * H + h) * (D * D);
-        const float* s0 = (a.s0 && !a.state_bf16) ? (const float*)a.s0 + s0_off : nullptr;
-        const uint16_t* s0h = (a.s0 && a.state_bf16) ? (const uint16_t*)a.s0 + s0_off : nullptr;
+        const float* si = (a.s0 && !a.state_bf16) ? (const float*)a.s0 + s0_off : nullptr;
+        const uint16_t* sih = (a.s0 && a.state_bf16) ? (const uint16_t*)a.s0 + s0_off : nullptr;
         float* c0 = a.carries + ((size_t)it.carry0 * H + h) * (D * D);
         for (int i = tid; i < D * 16; i += 512) {
             const int row = i >> 4, col = i & 15;
-            const float val = s0 ? s0[row * D + 16 * vt + col] : (s0h ? bf16_lo(s0h[row * D + 16 * vt + col]) : 0.f);
+            const float val = si ? si[row * D + 16 * vt + col] : (sih ? bf16_lo(sih[row * D + 16 * vt + col]) : 0.f);
             carry[row][col] = val;
             c0[row * D + 16 * vt + col] = val;
         }
+    } else {
+        // the run starts from B_{s0-1}; a run of this segment alone has
+        // nothing to compute (segment-K2 reads B_{s0-1} itself)
+        if (s0 >= n_sum || __builtin_amdgcn_readfirstlane(flags(s0)) == 0) return;
+        const float* B = a.b_seg + ((size_t)(it.prescan0 + s0 - 1) * H + h) * (D * D);
+        for (int i = tid; i < D * 16; i += 512) {
+            const int row = i >> 4, col = i & 15;
+            carry[row][col] = B[row * D + 16 * vt + col];
+        }
     }
     __syncthreads();
-    const int n_steps = it.n_segments - 1;
-    if (n_steps <= 0) return;
-    // summaries of step s (clamped to the last one, so every load is valid
-    // and unconditional)
+    // summaries and flags of step s (transfer s0 + s; clamped to the last
+    // one, so every load is valid and unconditional): the run ends at the
+    // first step whose transfer vanished, or after the last summary
     auto load = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
-        const int ss = s < n_steps ? s : n_steps - 1;
-        const size_t sum_off = ((size_t)(it.prescan0 + ss) * H + h) * (D * D);
+        const int j = s0 + s;
+        const int jj = j < n_sum ? j : n_sum - 1;
+        x.live = j < n_sum ? flags(jj) : 0;
+        const size_t sum_off = ((size_t)(it.prescan0 + jj) * H + h) * (D * D);
         const float* M = a.m_seg + sum_off;
         const float* B = a.b_seg + sum_off;
-        // a transfer that underflowed to zero in every tile is not read: the
-        // carry is then B_s itself
-        const int32_t* live = a.m_live + ((size_t)(it.prescan0 + ss) * H + h) * 8;
-        int any = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) any |= live[j];
-        x.zero = __builtin_amdgcn_readfirstlane(any == 0 ? 1 : 0);
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) x.b[vv] = B[(16 * wave + 4 * gg + vv) * D + 16 * vt + m];
-        const __amdgpu_buffer_rsrc_t mr = chunk_rsrc(M, x.zero ? 0u : (uint32_t)(D * D * 4));
+        const __amdgpu_buffer_rsrc_t mr = chunk_rsrc(M, (uint32_t)(D * D * 4));
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            x.m[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                mr, (int)(((16 * wave + m) * D + 32 * gg + 4 * j) * 4), 0, 0));
+        for (int k = 0; k < 8; ++k)
+            x.m[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                mr, (int)(((16 * wave + m) * D + 32 * gg + 4 * k) * 4), 0, 0));
     };
+    // carry_{s0+s+1} = M carry + B; returns false at the end of the run
     auto step = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
         // the operands are read only from here on (keeps their wait here)
         asm volatile("" : "+v"(x.m[0]), "+v"(x.m[1]), "+v"(x.m[2]), "+v"(x.m[3]), "+v"(x.m[4]),
-                     "+v"(x.m[5]), "+v"(x.m[6]), "+v"(x.m[7]), "+v"(x.b));
-        f32x4 acc = x.b;
-        if (!x.zero) {
-            f32x4 acc0 = x.b, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+                     "+v"(x.m[5]), "+v"(x.m[6]), "+v"(x.m[7]), "+v"(x.b), "+v"(x.live));
+        if (__builtin_amdgcn_readfirstlane(x.live) == 0) return false;
+        f32x4 acc0 = x.b, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int qq = 0; qq < 32; qq += 2) {
-                acc0 = mfma_f32_k4(x.m[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc0);
-                acc1 = mfma_f32_k4(x.m[qq >> 2][(qq & 3) + 1], carry[32 * gg + qq + 1][m], acc1);
-            }
-            acc = acc0 + acc1;
+        for (int qq = 0; qq < 32; qq += 2) {
+            acc0 = mfma_f32_k4(x.m[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc0);
+            acc1 = mfma_f32_k4(x.m[qq >> 2][(qq & 3) + 1], carry[32 * gg + qq + 1][m], acc1);
         }
+        const f32x4 acc = acc0 + acc1;
         __syncthreads();
-        float* cn = a.carries + ((size_t)(it.carry0 + s + 1) * H + h) * (D * D);
+        float* cn = a.carries + ((size_t)(it.carry0 + s0 + s + 1) * H + h) * (D * D);
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) {
             carry[16 * wave + 4 * gg + vv][m] = acc[vv];
             cn[(16 * wave + 4 * gg + vv) * D + 16 * vt + m] = acc[vv];
         }
         __syncthreads();
+        return true;
     };
+    if (n_sum <= 0) return;
     MergeOperands xa, xb;
     load(0, xa);
     load(1, xb);
-    int s = 0;
-    for (; s + 1 < n_steps; s += 2) {
-        step(s, xa);
+    for (int s = 0;; s += 2) {
+        if (!step(s, xa)) break;
         load(s + 2, xa);
-        step(s + 1, xb);
+        if (!step(s + 1, xb)) break;
         load(s + 3, xb);
     }
-    if (s < n_steps) step(s, xa);
 }
 
 // ---------------------------------------------------------------------------
@@ -694,12 +810,14 @@ hipError_t static_scratch_address(void** ptr) { return hipGetSymbolAddress(ptr, 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_fused(const K2Args& a, hipStream_t s) {
+namespace {
+hipError_t launch_fused_any(const K2Args& a, hipStream_t s, bool bsum) {
     const long long n = (long long)a.n_units * a.c.H;
     if (n <= 0) return hipSuccess;
     static const hipError_t attr = [] {
         const void* fns[] = {(const void*)kda_fused<false>, (const void*)kda_fused<true>,
-                             (const void*)kda_fused_fixup<false>, (const void*)kda_fused_fixup<true>};
+                             (const void*)kda_fused_fixup<false>, (const void*)kda_fused_fixup<true>,
+                             (const void*)kda_k1_bsum<false>, (const void*)kda_k1_bsum<true>};
         for (const void* f : fns) {
             const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, FUSED_LDS);
             if (e != hipSuccess) return e;
@@ -708,7 +826,10 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     }();
     if (attr != hipSuccess) return attr;
     const dim3 grid((unsigned)n), block(1024);
-    if (a.fixup) {
+    if (bsum) {
+        if (a.c.group > 1) hipLaunchKernelGGL(kda_k1_bsum<true>, grid, block, FUSED_LDS, s, a);
+        else hipLaunchKernelGGL(kda_k1_bsum<false>, grid, block, FUSED_LDS, s, a);
+    } else if (a.fixup) {
         if (a.c.group > 1) hipLaunchKernelGGL(kda_fused_fixup<true>, grid, block, FUSED_LDS, s, a);
         else hipLaunchKernelGGL(kda_fused_fixup<false>, grid, block, FUSED_LDS, s, a);
     } else {
@@ -717,6 +838,11 @@ hipError_t launch_fused(const K2Args& a, hipStream_t s) {
     }
     return hipGetLastError();
 }
+}  // namespace
+
+hipError_t launch_fused(const K2Args& a, hipStream_t s) { return launch_fused_any(a, s, false); }
+
+hipError_t launch_k1_bsum(const K2Args& a, hipStream_t s) { return launch_fused_any(a, s, true); }
 
 // bf16 beta -> fp32 beta (exact), for callers that keep beta in bf16.
 __global__ __launch_bounds__(256) void kda_beta_to_f32(const uint16_t* __restrict__ src, float* __restrict__ dst,
@@ -750,15 +876,15 @@ hipError_t launch_k2_recur(const K2Args& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s) {
+hipError_t launch_cp_transfer(const PrescanArgs& a, hipStream_t s) {
     const long long n = (long long)a.n_items * a.c.H;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_cp_prescan, dim3((unsigned)n), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(kda_cp_transfer, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s) {
-    const long long n = (long long)a.n_items * a.c.H * 8;
+    const long long n = (long long)a.n_segs * a.c.H * 8;
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(kda_cp_merge, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();

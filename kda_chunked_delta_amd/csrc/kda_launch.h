@@ -33,7 +33,11 @@ struct UnitDesc {
     int32_t warm;
     int32_t spec;
     int32_t out_slot;
-    int32_t pad;
+    // CP segment-K2: the pre_scan summary slot of the previous segment (-1:
+    // none). When that segment's transfer vanished (all its tiles exactly
+    // zero), the unit starts from that segment's B summary, which is then its
+    // carry bit for bit, and the merge writes no carry for it.
+    int32_t b_slot;
 };
 
 // CP pre_scan item: one segment whose (M, B) summary feeds the merge.
@@ -52,6 +56,14 @@ struct MergeDesc {
     int32_t n_segments;
     int32_t carry0;    // carries slot of segment 0 (segments use carry0 + s)
     int32_t prescan0;  // summary slot of segment 0 (segments 0..n-2)
+};
+
+// One segment of a merge item: the merge runs one workgroup per (segment,
+// head, 16-column tile); only segments that start a run of live transfers
+// compute.
+struct MergeSeg {
+    int32_t item;  // index into the merge items
+    int32_t seg;   // segment index within the sequence
 };
 
 struct CommonArgs {
@@ -97,6 +109,17 @@ struct K2Args {
     // alias the initial state, which other units may still read); else they
     // leave their end state in spec_states for the fix-up launch to publish
     int32_t spec_final_direct;
+    // CP segment-K2 (units with b_slot >= 0): the pre_scan B summaries and
+    // the per-tile flags of the transfers
+    const float* b_seg;
+    const int32_t* m_live;
+    // K1 with the B summaries (the fused kernel's record-writing instance):
+    // with gate_flags, every workgroup first ORs those n_gate_flags flags,
+    // workgroup 0 writes the result to gate_out, and all return if none is
+    // set (the first launch of warm-start CP's fallback)
+    const int32_t* gate_flags;
+    int64_t n_gate_flags;
+    int32_t* gate_out;
 };
 
 struct PrescanArgs {
@@ -111,7 +134,8 @@ struct PrescanArgs {
 struct MergeArgs {
     CommonArgs c;
     const MergeDesc* items;
-    int32_t n_items;
+    const MergeSeg* segs;
+    int32_t n_segs;
     const void* s0;      // fp32, or bf16 when state_bf16
     const float* b_seg;
     const float* m_seg;
@@ -135,7 +159,8 @@ hipError_t launch_k1_prepare(const K1Args& a, hipStream_t s);
 hipError_t launch_beta_to_f32(const uint16_t* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_fused(const K2Args& a, hipStream_t s);
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
-hipError_t launch_cp_prescan(const PrescanArgs& a, hipStream_t s);
+hipError_t launch_k1_bsum(const K2Args& a, hipStream_t s);
+hipError_t launch_cp_transfer(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);
 
 // The static scratch of the no-allocation prefill: its size, and its device

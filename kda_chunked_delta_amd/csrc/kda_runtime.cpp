@@ -84,10 +84,13 @@ double env_double(const char* name, double dflt) {
 // from per-kernel timings of this library's kernels (environment-
 // overridable, as the pull request's planner constants are):
 //   fused      one chunk step of a fused serial workgroup (one per CU)
-//   k1         materialised K1 of one (chunk, head), per CU, at full load
-//   prescan    one chunk step of a pre_scan workgroup
+//   k1         K1 of one (chunk, head) with its record written and the B
+//              summary advanced, per CU, at full load
+//   prescan    one chunk step of a transfer (pre_scan) workgroup, when the
+//              transfer does not vanish (weak decay: the worst case)
 //   rec        one chunk step of a K2 workgroup over materialised records
-//   merge      one segment step of the carry merge
+//   merge      one segment step of the carry merge (weak decay: the worst
+//              case; under decay the transfers vanish and it costs little)
 //   launch     one kernel launch
 struct PlannerConsts {
     double fused_us, k1_us, prescan_us, rec_us, merge_us, launch_us;
@@ -103,15 +106,16 @@ struct PlannerConsts {
 
 PlannerConsts planner_consts() {
     PlannerConsts c;
-    // fitted at steady clocks on the 65536-token, 8-head workload (K1 225 us
-    // over 128 chunk-heads per CU, pre_scan 138 us and segment-K2 139 us over
-    // 64-chunk segments, merge 56 us over 63 segments) and on the fused
-    // kernel's interval with few CUs busy
+    // fitted at steady clocks on the 65536-token, 8-head workload with
+    // 64-chunk segments (K1 with B summaries 264 us over 128 chunk-heads per
+    // CU; under weak decay the transfer 99 us and the merge 197 us over 63
+    // segments; segment-K2 146 us) and on the fused kernel's interval with
+    // few CUs busy
     c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.21);
-    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 1.76);
-    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 2.16);
-    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.17);
-    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 0.90);
+    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 2.06);
+    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 1.55);
+    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.28);
+    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 3.1);
     c.launch_us = env_double("KDA_CP_LAUNCH_US", 5.0);
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
     c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
@@ -179,6 +183,8 @@ struct kda_plan {
     std::vector<UnitDesc> fixups;       // warm-start segments, as rerun from their carry
     std::vector<UnitDesc> cp_units;     // warm-start CP: the segmented fallback's K2 units
     std::vector<UnitDesc> alt_units;    // split plans: the batch unsplit (the exact path)
+    std::vector<UnitDesc> k1_units;     // segmented pipeline: K1 with the B summaries, one per K2 unit
+    std::vector<MergeSeg> merge_segs;   // segmented pipeline: one merge workgroup row per segment
     // workspace layout (byte offsets into the arena)
     size_t off_rec = 0, off_b = 0, off_m = 0, off_mlive = 0, off_carry = 0;
     size_t off_spec_states = 0, off_spec_flags = 0, off_gate = 0;
@@ -186,7 +192,7 @@ struct kda_plan {
     int device = -1;
     void* dev_tables = nullptr;
     size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_prescan = 0, dev_off_merges = 0, dev_off_fixups = 0;
-    size_t dev_off_cp_units = 0, dev_off_alt_units = 0;
+    size_t dev_off_cp_units = 0, dev_off_alt_units = 0, dev_off_k1_units = 0, dev_off_merge_segs = 0;
     // Speculation feedback, outside graph capture: a speculative call (the
     // first, then every 64th) copies its outcome (split plans: the speculation
     // flags; warm-start CP: the gate) into pinned host memory and records an
@@ -216,8 +222,9 @@ double est_serial(const std::vector<int>& nch, int H, int n_cus, const PlannerCo
 }
 
 // Segmented estimate for segment length `seg` (chunks): K1 materialised for
-// every chunk, pre_scan over every segment but the last of each split
-// sequence, a serial merge over segments, then K2 over all units.
+// every chunk (with the B summaries), the transfer half of pre_scan over
+// every segment but the last of each split sequence, a serial merge over
+// segments, then K2 over all units.
 double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const PlannerConsts& pc) {
     long long tot = 0, pre_work = 0;
     int longest_unit = 0, max_segs = 0;
@@ -413,21 +420,29 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
             // table reruns the latter from that carry if its warm-up transfer
             // did not vanish
             const int a = split[i], carry = n_carry++, spec = n_spec++;
-            p->units.push_back(UnitDesc{i, 0, a, chunk_base[i], -1, 0, 0, 2, 0, -1, carry, 0});
-            p->units.push_back(UnitDesc{i, a, nch[i] - a, chunk_base[i] + a, -1, 1, 1, 2, warm, spec, -1, 0});
-            p->fixups.push_back(UnitDesc{i, a, nch[i] - a, chunk_base[i] + a, carry, 1, 1, 2, 0, spec, -1, 0});
+            p->units.push_back(UnitDesc{i, 0, a, chunk_base[i], -1, 0, 0, 2, 0, -1, carry, -1});
+            p->units.push_back(UnitDesc{i, a, nch[i] - a, chunk_base[i] + a, -1, 1, 1, 2, warm, spec, -1, -1});
+            p->fixups.push_back(UnitDesc{i, a, nch[i] - a, chunk_base[i] + a, carry, 1, 1, 2, 0, spec, -1, -1});
             continue;
         }
         const int s = (seg > 0 && nch[i] > seg) ? (nch[i] + seg - 1) / seg : 1;
         if (s == 1) {
-            p->units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1, 0, -1, -1, 0});
+            p->units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1, 0, -1, -1, -1});
+            p->k1_units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 0, 0, 1, 0, -1, -1, -1});
             continue;
         }
         MergeDesc md{i, s, n_carry, n_prescan};
+        for (int j = 0; j < s; ++j) p->merge_segs.push_back(MergeSeg{(int32_t)p->merges.size(), j});
         p->merges.push_back(md);
         for (int j = 0; j < s; ++j) {
             const int c0 = j * seg, n = std::min(seg, nch[i] - c0);
-            p->units.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, n_carry + j, j == s - 1, j, s, 0, -1, -1, 0});
+            // segment j starts from carry j, or from B_{j-1} itself when the
+            // transfer of segment j - 1 vanished
+            p->units.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, n_carry + j, j == s - 1, j, s, 0, -1, -1,
+                                        j > 0 ? n_prescan + j - 1 : -1});
+            // K1 of its chunks, and (but for the last segment) its B summary
+            p->k1_units.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, -1, 0, j, s, 0, -1,
+                                           j < s - 1 ? n_prescan + j : -1, -1});
             if (j < s - 1)
                 p->prescan.push_back(PrescanDesc{i, c0, n, chunk_base[i] + c0, n_prescan + j, {0, 0, 0}});
         }
@@ -450,9 +465,9 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
                 // one leaves it in spec_states when the final state aliases
                 // the initial state (published by the gated fix-up launch)
                 p->units.push_back(UnitDesc{i, c0, std::max(n, 0), chunk_base[i] + c0, -1, last ? 1 : 0, j, ns,
-                                            j > 0 ? warm : 0, spec, -1, 0});
+                                            j > 0 ? warm : 0, spec, -1, -1});
                 if (last)
-                    p->fixups.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, -1, 1, j, ns, 0, spec, -1, 0});
+                    p->fixups.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, -1, 1, j, ns, 0, spec, -1, -1});
             }
         }
         std::stable_sort(p->cp_units.begin(), p->cp_units.end(),
@@ -460,7 +475,7 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     }
     if (n_split > 0) {
         for (int i = 0; i < n_seqs; ++i)
-            p->alt_units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1, 0, -1, -1, 0});
+            p->alt_units.push_back(UnitDesc{i, 0, nch[i], chunk_base[i], -1, 1, 0, 1, 0, -1, -1, -1});
         std::stable_sort(p->alt_units.begin(), p->alt_units.end(),
                          [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
     }
@@ -470,6 +485,8 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     });
     std::stable_sort(p->prescan.begin(), p->prescan.end(),
                      [](const PrescanDesc& a, const PrescanDesc& b) { return a.n_chunks > b.n_chunks; });
+    std::stable_sort(p->k1_units.begin(), p->k1_units.end(),
+                     [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
 
     // workspace layout
     // CP plans always materialise K1 (K1 once, then pre_scan and segment-K2
@@ -545,6 +562,10 @@ kda_status upload_plan(kda_plan* p, int device) {
     off = align_up(off + p->cp_units.size() * sizeof(UnitDesc), 256);
     p->dev_off_alt_units = off;
     off = align_up(off + p->alt_units.size() * sizeof(UnitDesc), 256);
+    p->dev_off_k1_units = off;
+    off = align_up(off + p->k1_units.size() * sizeof(UnitDesc), 256);
+    p->dev_off_merge_segs = off;
+    off = align_up(off + p->merge_segs.size() * sizeof(MergeSeg), 256);
     std::vector<uint8_t> host(off, 0);
     if (!p->chunks.empty()) memcpy(&host[p->dev_off_chunks], p->chunks.data(), p->chunks.size() * sizeof(ChunkDesc));
     if (!p->units.empty()) memcpy(&host[p->dev_off_units], p->units.data(), p->units.size() * sizeof(UnitDesc));
@@ -555,6 +576,10 @@ kda_status upload_plan(kda_plan* p, int device) {
         memcpy(&host[p->dev_off_cp_units], p->cp_units.data(), p->cp_units.size() * sizeof(UnitDesc));
     if (!p->alt_units.empty())
         memcpy(&host[p->dev_off_alt_units], p->alt_units.data(), p->alt_units.size() * sizeof(UnitDesc));
+    if (!p->k1_units.empty())
+        memcpy(&host[p->dev_off_k1_units], p->k1_units.data(), p->k1_units.size() * sizeof(UnitDesc));
+    if (!p->merge_segs.empty())
+        memcpy(&host[p->dev_off_merge_segs], p->merge_segs.data(), p->merge_segs.size() * sizeof(MergeSeg));
     int prev = -1;
     hipError_t e = hipGetDevice(&prev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -1068,34 +1093,55 @@ kda_status prefill_impl(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts*
         if (err == hipSuccess) p->spec_pending = true;
         return err;
     };
-    // The segmented pipeline: K1 records, pre_scan, carry merge, K2 over the
-    // records with the given units. cc.gate gates every launch when set (the
-    // fallback of warm-start CP).
-    // With gate_flags, the K1 launch first reduces those flags into the gate
-    // word cc.gate points to, and every launch is gated on it.
+    // The segmented pipeline. CP plans: K1 writes the records of every chunk
+    // and each segment's B summary (the update from zero) in one launch, the
+    // transfer half of pre_scan runs over the records, the merge forms the
+    // carries, and K2 runs every unit over the records. A serial plan with
+    // materialised K1 runs K1 alone and then K2. cc.gate gates every launch
+    // when set (the fallback of warm-start CP); with gate_flags, the first
+    // launch reduces those flags into the gate word cc.gate points to.
     auto segmented = [&](const CommonArgs& cc, const UnitDesc* k2_units, int32_t n_k2_units,
                          const char* k2_name, const int32_t* gate_flags, int64_t n_gate_flags) -> kda_status {
-        K1Args k1{cc, (const ChunkDesc*)(tabs + p->dev_off_chunks), gate_flags, n_gate_flags,
-                  const_cast<int32_t*>(cc.gate)};
-        if (gate_flags) k1.c.gate = nullptr;  // the K1 launch computes the gate
-        e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
-        if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+        const bool cp = !p->merges.empty();
+        float* b_seg = (float*)(ws + p->off_b);
+        int32_t* m_live = (int32_t*)(ws + p->off_mlive);
+        if (cp) {
+            K2Args kb{};
+            kb.c = cc;
+            if (gate_flags) kb.c.gate = nullptr;  // this launch computes the gate
+            kb.units = (const UnitDesc*)(tabs + p->dev_off_k1_units);
+            kb.n_units = (int32_t)p->k1_units.size();
+            kb.carries = b_seg;  // the B summaries go to their pre_scan slots
+            kb.scale = scale;
+            kb.spec_final_direct = 1;
+            kb.gate_flags = gate_flags;
+            kb.n_gate_flags = n_gate_flags;
+            kb.gate_out = const_cast<int32_t*>(cc.gate);
+            e = timed("k1_bsum", [&] { return launch_k1_bsum(kb, stream); });
+            if (e != hipSuccess) return hip_fail(e, "k1_bsum launch");
+        } else {
+            K1Args k1{cc, (const ChunkDesc*)(tabs + p->dev_off_chunks), gate_flags, n_gate_flags,
+                      const_cast<int32_t*>(cc.gate)};
+            if (gate_flags) k1.c.gate = nullptr;  // the K1 launch computes the gate
+            e = timed("k1_prepare", [&] { return launch_k1_prepare(k1, stream); });
+            if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
+        }
         if (gate_flags && (e = report(cc.gate, 1)) != hipSuccess) return hip_fail(e, "speculation feedback");
         if (!p->prescan.empty()) {
             PrescanArgs pa{cc, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
-                           (float*)(ws + p->off_b), (float*)(ws + p->off_m), (int32_t*)(ws + p->off_mlive)};
-            e = timed("cp_prescan", [&] { return launch_cp_prescan(pa, stream); });
-            if (e != hipSuccess) return hip_fail(e, "cp_prescan launch");
+                           b_seg, (float*)(ws + p->off_m), m_live};
+            e = timed("cp_transfer", [&] { return launch_cp_transfer(pa, stream); });
+            if (e != hipSuccess) return hip_fail(e, "cp_transfer launch");
         }
-        if (!p->merges.empty()) {
-            MergeArgs ma{cc, (const MergeDesc*)(tabs + p->dev_off_merges), (int32_t)p->merges.size(), s0,
-                         (const float*)(ws + p->off_b), (const float*)(ws + p->off_m), (float*)(ws + p->off_carry),
-                         state16 ? 1 : 0, (const int32_t*)(ws + p->off_mlive)};
+        if (cp) {
+            MergeArgs ma{cc, (const MergeDesc*)(tabs + p->dev_off_merges),
+                         (const MergeSeg*)(tabs + p->dev_off_merge_segs), (int32_t)p->merge_segs.size(), s0, b_seg,
+                         (const float*)(ws + p->off_m), (float*)(ws + p->off_carry), state16 ? 1 : 0, m_live};
             e = timed("cp_merge", [&] { return launch_cp_merge(ma, stream); });
             if (e != hipSuccess) return hip_fail(e, "cp_merge launch");
         }
         K2Args kc{cc, k2_units, n_k2_units, s0, sT, (float*)(ws + p->off_carry), (uint16_t*)out, scale,
-                  state16 ? 1 : 0, nullptr, nullptr, 0, 0};
+                  state16 ? 1 : 0, nullptr, nullptr, 0, 0, b_seg, m_live};
         e = timed(k2_name, [&] { return launch_k2_recur(kc, stream); });
         if (e != hipSuccess) return hip_fail(e, "k2 launch");
         return KDA_OK;
