@@ -353,7 +353,8 @@ def main():
     names = "+".join(per_kernel.keys())
     achieved = alg_bytes / (path_ms * 1e-3) / 1e9
     digest = source_digest()
-    traffic = traffic_from_profiles(names, digest, args.workload)
+    wl_key = args.workload if args.g_scale is None else "%s@g%g" % (args.workload, args.g_scale)
+    traffic = traffic_from_profiles(names, digest, wl_key)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "frac_of_step": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
