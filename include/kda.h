@@ -398,7 +398,7 @@ size_t kda_noalloc_scratch_bytes(void);
  *   [0, 4096)      Qt = q * exp(G): [p 4][lane 64][j 8] = Qt[i][dkperm(p, g, j)]
  *   [4096, 8192)   X = k * exp(G): same layout as Qt
  *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][slot 64][j 4]; slot s(l) holds
- *                  lane l's Kt[4g + j][16t + i], s(l) = (l & ~3) | (((l & 3) + (l >> 4)) & 3)
+ *                  lane l's Kt[4g + j][16t + i], s(l) = (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2)
  *   [12288, 16384) V (the chunk's values): [n 8][slot 64][j 4]; slot s(l) holds
  *                  lane l's V[4g + j][16n + i]
  *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]

@@ -165,11 +165,15 @@ __device__ __forceinline__ u32x2 quad_transpose16(u32x2 x, int lane) {
     return u32x2{__builtin_amdgcn_perm(p0, y0, sel), __builtin_amdgcn_perm(p1, y1, sel)};
 }
 
-// Slot of lane l's 8-byte fragment in the Kt and V tiles: the low two bits
-// are rotated by l >> 4. The reads stay one contiguous 512-byte tile, and the
+// Slot of lane l's 8-byte fragment in the Kt and V tiles: lane l = 16g + 4a +
+// j sits in slot 16g + 4((a + g) & 3) + j. The reads stay one contiguous
+// 512-byte tile (each half-wavefront's 32 reads on distinct banks), and the
 // stores that K1 writes them with (lane (gg, 4a + j) -> fragment of lane
-// 16a + 4gg + j) cover the tile once, conflict-free.
-__device__ __forceinline__ int kv_slot(int l) { return (l & ~3) | (((l & 3) + (l >> 4)) & 3); }
+// 16a + 4gg + j) put each group of 16 lanes on 16 distinct 8-byte slots of a
+// 128-byte bank row, so neither side has a bank conflict. (Measured: the
+// earlier rotation of the low two bits by l >> 4 made those stores 4-way
+// conflicted, 16 instead of 4 LDS cycles each.)
+__device__ __forceinline__ int kv_slot(int l) { return (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2); }
 
 // ---------------------------------------------------------------------------
 // K1, phase 1 (8 wavefronts). Wavefront w owns key channels and value

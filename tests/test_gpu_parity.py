@@ -136,8 +136,8 @@ def decode_records(rec):
             for j in range(8):
                 x[i, 32 * p + 16 * (j // 4) + 4 * g + j % 4] = a[p, :, j]
         out[name] = x
-    # Kt and V: lane l's fragment sits in slot (l & ~3) | (((l & 3) + (l >> 4)) & 3)
-    slot = (lanes & ~3) | (((lanes & 3) + (lanes >> 4)) & 3)
+    # Kt and V: lane l's fragment sits in slot (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2)
+    slot = (lanes & 0x33) | ((((lanes >> 2) + (lanes >> 4)) & 3) << 2)
     for name, off in (("Kt", 8192), ("V", 12288)):
         a = bf(r[off:off + 4096].view(np.uint16).reshape(8, 64, 4))[:, slot, :]
         x = np.zeros((16, 128), np.float32)
