@@ -289,29 +289,32 @@ __device__ __forceinline__ RowStreams row_streams(const uint16_t* q, const uint1
 
 // Loads of chunk ci of the streams with nrows (0..16) valid rows. Each range
 // covers nrows whole token rows, so the lanes of rows past them, and every
-// lane when nrows = 0, read zeros and touch no memory. GVA = false: q/k heads
-// are the value heads, and q/k share v's offsets and ranges.
+// lane when nrows = 0, read zeros and touch no memory. nrows_qv (0 or nrows)
+// is the rows of q and v alone: 0 where the chunk's use needs neither (a
+// warm-up pass), which then reads zeros for them. GVA = false: q/k heads are
+// the value heads, and q/k share v's offsets and ranges.
 template <bool GVA>
-__device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int nrows, const RowLaneOffsets& lo,
-                                              RowChunk& rc) {
+__device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,
+                                              const RowLaneOffsets& lo, RowChunk& rc) {
     const uint32_t n_act = (uint32_t)nrows * rs.st_act;
     const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
     const uint8_t* qb = rs.q + c_act;
     const uint8_t* kb = rs.k + c_act;
-    uint32_t n_qk = n_act, o_qk = lo.act;
+    uint32_t n_qk = n_act, o_qk = lo.act, n_q = (uint32_t)nrows_q * rs.st_act;
     if constexpr (GVA) {
         const size_t c_qk = (size_t)ci * (CH * (size_t)rs.st_qk);
         qb = rs.q + c_qk;
         kb = rs.k + c_qk;
         n_qk = (uint32_t)nrows * rs.st_qk;
+        n_q = (uint32_t)nrows_q * rs.st_qk;
         o_qk = lo.qk;
     }
-    rc.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(qb, n_qk), (int)o_qk, 0,
+    rc.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(qb, n_q), (int)o_qk, 0,
                                                                           BUF_POLICY));
     rc.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(kb, n_qk), (int)o_qk, 0,
                                                                           BUF_POLICY));
-    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(rs.v + c_act, n_act),
-                                                                          (int)lo.act, 0, BUF_POLICY));
+    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc(rs.v + c_act, (uint32_t)nrows_v * rs.st_act), (int)lo.act, 0, BUF_POLICY));
     // g rows are twice as long as v rows, beta rows 1/64 of them
     rc.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
         chunk_rsrc(rs.g + 2 * c_act, (uint32_t)nrows * rs.st_g), (int)lo.g, 0, BUF_POLICY));

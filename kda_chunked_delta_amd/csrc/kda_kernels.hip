@@ -262,7 +262,8 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
         const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok0, h, h / a.c.group,
                                           wave);
         RowChunk rc;
-        k1_load_chunk<GVA>(rs, 0, rows_of(tok0, end), lo, rc);
+        const int nr = rows_of(tok0, end);
+        k1_load_chunk<GVA>(rs, 0, nr, nr, nr, lo, rc);
         k1_stage(rc, wave, lane, lo, stg, (float*)(stg + STG_B));
         lds_barrier();
         RawChunk raw;
@@ -486,10 +487,15 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                                           h / a.c.group, w8);
         // tokens of the sequence from that chunk on (sequences are < 2^31 tokens)
         const int rem = (int)(end - tok_k1);
-        // step i -> chunk from tok_k1 (the warm-up chunks come twice)
+        // step i -> chunk from tok_k1 (the warm-up chunks come twice). The
+        // first warm-up pass (the transfer, V := 0, no output) reads neither
+        // q nor v, the second (the state from zero, no output) no q: their
+        // rows read as zeros, and no record field that pass uses depends on
+        // them.
         auto load = [&](RowChunk& rc, int i) __attribute__((always_inline)) {
             const int ci = i >= W ? i - W : i;
-            k1_load_chunk<GVA>(rs, ci, chunk_rows(rem, ci), lo, rc);
+            const int nr = chunk_rows(rem, ci);
+            k1_load_chunk<GVA>(rs, ci, nr, i >= 2 * W ? nr : 0, i >= W ? nr : 0, lo, rc);
         };
         // the staging and scratch slots are compile-time constants: chunk c
         // uses slot c & 1 of both rings
