@@ -341,7 +341,11 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
     float* stg_betas = (float*)(smem + F_BETA);          // [2][16]
     float* scr_betas = (float*)(smem + F_BETA + 128);    // [2][16]
     const int H = a.c.H;
-    const int h = blockIdx.x % H;
+    // workgroups go round-robin to the 8 XCDs by index: within a unit, index
+    // w lands on XCD w % 8, which takes heads (w % 8) * H/8 + w / 8 (when H is
+    // a multiple of 8), so each XCD reads H/8 adjacent heads of every row
+    int h = blockIdx.x % H;
+    if ((H & 7) == 0) h = (h & 7) * (H >> 3) + (h >> 3);
     const UnitDesc u = a.units[blockIdx.x / H];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int gg = lane >> 4, m = lane & 15;
