@@ -360,6 +360,16 @@ __device__ __forceinline__ void k1_read_staged(const uint8_t* stg, const float* 
 // chunk start: exp(G) and exp(-G) are then normal fp32 and bf16 values, and
 // the unmasked Gram terms exp(G_r - G_i) (i <= r) are at most 1.
 constexpr float G_FACTOR0_MAX = 100.0f;
+// Largest |G - G_7| (log2 units) the row-7 factors exp(G - G_7), exp(G_7 - G)
+// take as normal fp32 values.
+constexpr float G_SPAN_MAX = 126.0f;
+// Floor on one token's log2-decay for the rare chunk whose in-chunk decay
+// exceeds even the row-7 range (a token decaying beyond about e^-87, or g =
+// -inf): with it, no token's decay exceeds 2^-15.5 (about e^-10.7), and 8
+// tokens span at most 124. The flooring changes a carried-in state's
+// contribution by at most that factor, against the exact decay of such a
+// token, which is smaller still.
+constexpr float G_TOKEN_FLOOR = 15.5f;
 
 // scr_b: the chunk's 16 betas (scr + K1_BETA where the layout keeps them
 // together)
@@ -410,6 +420,24 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
         pka = pxk;
         pqa = pqt;
     } else {
+        // The row-7 factors need |G - G_7| within G_SPAN_MAX; a chunk beyond
+        // that (the check also catches NaN, from g = -inf) is scanned again
+        // with each token's log-decay floored at -G_TOKEN_FLOOR. The choice is
+        // again uniform per wavefront and chunk, and a function of g alone.
+        bool wide = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wide |= !(fabsf(G[j] - row_newbcast<7>(G[j])) <= G_SPAN_MAX);
+        if (__builtin_amdgcn_ballot_w64(wide) != 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x = fmaxf(raw.g[j] * LOG2E, -G_TOKEN_FLOOR);
+                x += row_shr<1>(x);
+                x += row_shr<2>(x);
+                x += row_shr<4>(x);
+                x += row_shr<8>(x);
+                G[j] = x;
+            }
+        }
         // E = exp(G - G_7), F = exp(G_7 - G)
         float E[4], F[4];
 #pragma unroll

@@ -404,6 +404,42 @@ def test_steep_in_chunk_decay_matches_oracle(monkeypatch):
     assert_close("final(cp)", s2, s_ref)
 
 
+def test_extreme_in_chunk_decay_stays_finite(monkeypatch):
+    """Decays beyond what either factoring of the Grams holds in fp32: tokens
+    with g = -100 (e^-100) at rows 3 and 5 of two chunks on some channels, a
+    token with g = -200 on every channel of one head, and tokens with g = -inf
+    (a reset of those channels) at rows 7, 13 and 9. Such chunks are taken
+    with each token's log-decay floored at about e^-10.7, which changes the
+    carried-in state's contribution by at most that factor. Outputs and final
+    states stay finite and match the oracle; fused serial, materialised K1 and
+    forced CP agree."""
+    d = draw([200, 77], 6, seed=123, state_std=0.1, device=DEV)
+    cu = d["cu_seqlens_host"]
+    g = d["g"].clone()
+    g[3, :, :40] = -100.0
+    g[21, :, 64:] = -100.0
+    g[40, 2, :] = -200.0
+    g[55, :, 64:] = float("-inf")
+    g[77, :, 16:48] = float("-inf")
+    g[cu[1] + 9, :, :] = float("-inf")
+    d["g"] = g
+    o_ref, s_ref = oracle(d)
+    assert np.isfinite(o_ref).all() and np.isfinite(s_ref).all()
+    o, s = run(d)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+    assert_close("out(fused)", o, o_ref)
+    assert_close("final(fused)", s, s_ref)
+    monkeypatch.setenv("KDA_MATERIALIZE_K1", "1")
+    p_ser = kda.plan(cu, 6, False, device=DEV)
+    monkeypatch.delenv("KDA_MATERIALIZE_K1")
+    o1, s1 = run(d, plan=p_ser)
+    assert torch.equal(o1, o) and torch.equal(s1, s), "materialised K1 differs from fused"
+    p_cp = kda.plan_segments(cu, 6, 3, device=DEV)
+    o2, s2 = run(d, plan=p_cp)
+    assert_close("out(cp)", o2, o_ref)
+    assert_close("final(cp)", s2, s_ref)
+
+
 # ---------------------------------------------------------------------------
 # warm-start splits (intracard CP inside the fused kernel)
 # ---------------------------------------------------------------------------
