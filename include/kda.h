@@ -390,7 +390,7 @@ size_t kda_noalloc_scratch_bytes(void);
  * into `records` (device, total_chunks * H * KDA_RECORD_BYTES bytes, record
  * of (chunk c, head h) at index h * total_chunks + c; layout in
  * KDA_RECORD_* below). Arguments as in kda_prefill. */
-#define KDA_RECORD_BYTES 18432
+#define KDA_RECORD_BYTES 14336
 /* Record layout: the order in which a 64-wide wavefront reads its MFMA
  * fragments (bf16 unless noted). Lane l has g = l / 16, i = l % 16;
  * dkperm(p, g, j) = 32p + 16(j / 4) + 4g + j % 4. r = token row 0..15 of the
@@ -399,14 +399,13 @@ size_t kda_noalloc_scratch_bytes(void);
  *   [4096, 8192)   X = k * exp(G): same layout as Qt
  *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][slot 64][j 4]; slot s(l) holds
  *                  lane l's Kt[4g + j][16t + i], s(l) = (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2)
- *   [12288, 16384) V (the chunk's values): [n 8][slot 64][j 4]; slot s(l) holds
- *                  lane l's V[4g + j][16n + i]
- *   [16384, 16896) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]
- *   [16896, 17408) exp(G_C): fp32 [128], channel 16t + 4g + j at position 32g + 4t + j
- *   [17408, 18432) T' = (I + L)^-1 diag(beta), L = strict-lower(diag(beta) A_kk),
+ *   [12288, 12800) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]
+ *   [12800, 13312) exp(G_C): fp32 [128], channel 16t + 4g + j at position 32g + 4t + j
+ *   [13312, 14336) T' = (I + L)^-1 diag(beta), L = strict-lower(diag(beta) A_kk),
  *                  as a bf16 pair hi + lo: [2][lane 64][j 4] = T'[i][4g + j]
  * K2 forms U = T' (V - X S) (= U~ - W S in WY terms), then O = Qt S + A_qk U
- * and S <- Diag(exp G_C) S + Kt^T U.
+ * and S <- Diag(exp G_C) S + Kt^T U. A record holds no copy of V: K2 reads
+ * the chunk's value rows from v itself.
  */
 kda_status kda_debug_k1_records(kda_ctx *ctx, const kda_plan *plan, const void *q, const void *k,
                                 const void *v, const float *g, const float *beta,

@@ -339,7 +339,7 @@ def k1_records(q, k, v, g, beta, plan):
     return rec
 
 
-RECORD_BYTES = 18432
+RECORD_BYTES = 14336
 
 
 def _ptr(t):

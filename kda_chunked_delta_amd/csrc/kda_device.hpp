@@ -46,7 +46,10 @@ constexpr int CH = 16;   // chunk length
 //            32gg + 4t + v: lane (gg, m) of a state wavefront reads the pair
 //            at 2 * lane, which holds channels 16(m >> 1) + 4gg + 2(m & 1) + 0..1
 //   REC_T  : T' fragments, hi then lo [2][lane 64][4 bf16]: T'[m][4gg + j]
-// The same bytes are used in LDS and, when K1 is materialised, in HBM.
+// When K1 is materialised, HBM holds each record without V (REC_HBM_BYTES:
+// the fields before REC_V at their offsets, those after it 4096 bytes
+// earlier): V is a copy of the input, and its reader takes the rows from
+// there instead, into the REC_V area of its LDS record (vrow_off).
 // ---------------------------------------------------------------------------
 constexpr int REC_Q = 0;
 constexpr int REC_X = 4096;
@@ -57,6 +60,17 @@ constexpr int REC_GC = 16896;
 constexpr int REC_T = 17408;
 constexpr int REC_BYTES = 18432;
 constexpr int REC_VEC = REC_BYTES / 16;  // 1152 16-byte vectors
+constexpr int REC_HBM_BYTES = REC_BYTES - 4096;
+constexpr int REC_HBM_VEC = REC_HBM_BYTES / 16;  // 896
+// LDS vector of a record's HBM vector i
+__device__ __forceinline__ int rec_lds_vec(int i) { return i < REC_V / 16 ? i : i + 256; }
+// V rows staged from the input (K2 over materialised records): token row r
+// at r * 256 bytes, its 16-byte granule q at granule q ^ ((r >> 1) & 6), so
+// that the four token quads a wavefront's 16-bit reads touch fall into
+// distinct banks. Byte of element (r, column c):
+__device__ __forceinline__ int vrow_off(int r, int c) {
+    return r * 256 + ((((c >> 3) ^ ((r >> 1) & 6))) << 4) + (c & 7) * 2;
+}
 
 // K1 scratch of one chunk (LDS only), from phase 1 to phase 2:
 //   K1_KA, K1_KB, K1_QA: the Gram factors k exp(G - G_ref), k exp(G_ref - G),
@@ -590,9 +604,11 @@ __device__ __forceinline__ void k1_phase2(int wave, int lane, uint8_t* rec, cons
 // WITH_V = false runs the same update with V := 0 (the segment transfer of
 // the CP pre_scan). WITH_OUT also forms O^T = S0^T Qt^T + U^T A_qk^T, whose
 // accumulator oacc[n][v] is o[token m][16(n0 + n) + 4gg + v].
-// The arithmetic of a tile is identical in every instantiation.
+// V_ROWS reads V from rows staged at REC_V (vrow_off) instead of the
+// fragment layout. The arithmetic of a tile is identical in every
+// instantiation.
 // ---------------------------------------------------------------------------
-template <int NT, bool WITH_V, bool WITH_OUT>
+template <int NT, bool WITH_V, bool WITH_OUT, bool V_ROWS = false>
 __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT], int n0, int lane,
                                            f32x4 (&oacc)[NT]) {
     const int gg = lane >> 4;
@@ -624,7 +640,14 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         f32x4 r;
-        if constexpr (WITH_V) {
+        if constexpr (WITH_V && V_ROWS) {
+            // the same bf16 values from the staged rows
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = *(const uint16_t*)(rec + REC_V + vrow_off(4 * gg + j, 16 * (n0 + n) + (lane & 15)));
+                r[j] = __uint_as_float(e << 16) - P[n][j];
+            }
+        } else if constexpr (WITH_V) {
             const u32x2 vw = *(const u32x2*)(rec + REC_V + (n0 + n) * 512 + kv_slot(lane) * 8);
             r[0] = bf16_lo(vw.x) - P[n][0];
             r[1] = bf16_hi(vw.x) - P[n][1];

@@ -8,7 +8,7 @@
 
 namespace kda {
 
-static_assert(REC_BYTES == kRecBytes, "record size differs between host and device");
+static_assert(REC_HBM_BYTES == kRecBytes, "record size differs between host and device");
 
 namespace {
 
@@ -32,47 +32,69 @@ __device__ __forceinline__ int rows_of(int64_t tok, int64_t end) {
     return n <= 0 ? 0 : (n >= CH ? CH : (int)n);
 }
 
-// Record prefetch through registers: NT threads each hold N 16-byte vectors.
-template <int NT>
-struct RecordPrefetch {
-    static constexpr int N = (REC_VEC + NT - 1) / NT;
+// The input rows of V for K2 over materialised records (the HBM records
+// carry no V): the unit's first token row of head h, the bytes per token
+// row, and the tokens of the sequence from that row on.
+struct VRows {
+    const uint8_t* base;
+    uint32_t stride;
+    int rem;
+};
+
+// K2's record prefetch through registers: the 896 vectors of an HBM record,
+// two per thread, and the chunk's 16 value rows, one 16-byte granule per
+// thread of wavefronts 0..3 (row tid >> 4, granule tid & 15). Wavefronts
+// 4..7 issue the same load over an empty range (no memory access), so that
+// every load is unconditional; rows past the sequence read as zeros.
+struct K2Prefetch {
+    static constexpr int N = (REC_HBM_VEC + 511) / 512;
     u32x4 r[N];
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ src) {
+    u32x4 vr;
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ src, const VRows& v, int ci) {
         const u32x4* s = (const u32x4*)src;
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            const int i = threadIdx.x + j * NT;
-            if (i < REC_VEC) r[j] = __builtin_nontemporal_load(s + i);
+            const int i = threadIdx.x + j * 512;
+            if (i < REC_HBM_VEC) r[j] = __builtin_nontemporal_load(s + i);
         }
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t bytes = wave < 4 ? (uint32_t)chunk_rows(v.rem, ci) * v.stride : 0u;
+        const int off = (int)((threadIdx.x >> 4) & 15) * (int)v.stride + (int)(threadIdx.x & 15) * 16;
+        vr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            chunk_rsrc(v.base + (size_t)ci * CH * v.stride, bytes), off, 0, BUF_POLICY));
     }
     __device__ __forceinline__ void store(uint8_t* dst) const {
         u32x4* d = (u32x4*)dst;
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            const int i = threadIdx.x + j * NT;
-            if (i < REC_VEC) d[i] = r[j];
+            const int i = threadIdx.x + j * 512;
+            if (i < REC_HBM_VEC) d[rec_lds_vec(i)] = r[j];
+        }
+        if (threadIdx.x < 256) {
+            const int row = threadIdx.x >> 4;
+            *(u32x4*)(dst + REC_V + vrow_off(row, (threadIdx.x & 15) * 8)) = vr;
         }
     }
 };
 
-// Stream nc materialised records (starting at rb) through a double-buffered
-// LDS stage; records are fetched two chunks ahead. step(ci, rec) runs once
-// per chunk with the record in LDS, by every thread.
-template <int NT, class Step>
-__device__ __forceinline__ void record_loop(const uint8_t* __restrict__ rb, int nc,
+// Stream nc materialised records (starting at rb) and the chunks' value rows
+// through a double-buffered LDS stage; both are fetched two chunks ahead.
+// step(ci, rec) runs once per chunk with the record in LDS, by every thread.
+template <class Step>
+__device__ __forceinline__ void record_loop(const uint8_t* __restrict__ rb, const VRows& v, int nc,
                                             uint8_t (*recs)[REC_BYTES], Step&& step) {
-    RecordPrefetch<NT> p0, p1;
-    if (nc > 0) p0.load(rb);
-    if (nc > 1) p1.load(rb + REC_BYTES);
+    K2Prefetch p0, p1;
+    if (nc > 0) p0.load(rb, v, 0);
+    if (nc > 1) p1.load(rb + REC_HBM_BYTES, v, 1);
     if (nc > 0) p0.store(recs[0]);
     lds_barrier();
     for (int ci = 0; ci < nc; ci += 2) {
-        if (ci + 2 < nc) p0.load(rb + (size_t)(ci + 2) * REC_BYTES);
+        if (ci + 2 < nc) p0.load(rb + (size_t)(ci + 2) * REC_HBM_BYTES, v, ci + 2);
         step(ci, recs[0]);
         if (ci + 1 < nc) p1.store(recs[1]);
         lds_barrier();
         if (ci + 1 < nc) {
-            if (ci + 3 < nc) p1.load(rb + (size_t)(ci + 3) * REC_BYTES);
+            if (ci + 3 < nc) p1.load(rb + (size_t)(ci + 3) * REC_HBM_BYTES, v, ci + 3);
             step(ci + 1, recs[1]);
             if (ci + 2 < nc) p0.store(recs[0]);
             lds_barrier();
@@ -273,9 +295,9 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
         lds_barrier();
         k1_phase2(wave, lane, rec, scr, lw);
         lds_barrier();
-        u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_BYTES);
+        u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_HBM_BYTES);
         const u32x4* src = (const u32x4*)rec;
-        for (int i = threadIdx.x; i < REC_VEC; i += 512) dst[i] = src[i];
+        for (int i = threadIdx.x; i < REC_HBM_VEC; i += 512) dst[i] = src[rec_lds_vec(i)];
         lds_barrier();  // the record is read before the next item stages over it
     }
 }
@@ -410,9 +432,9 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                 // the record is complete in this interval (its T' was formed in
                 // the previous one) and its slot is overwritten after the next
                 // barrier: the state wavefronts copy it out now
-                u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0 + c) * REC_BYTES);
+                u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0 + c) * REC_HBM_BYTES);
                 const u32x4* src = (const u32x4*)rec;
-                for (int v = (int)threadIdx.x; v < REC_VEC; v += 512) dst[v] = src[v];
+                for (int v = (int)threadIdx.x; v < REC_HBM_VEC; v += 512) dst[v] = src[rec_lds_vec(v)];
             } else {
                 f32x4 oacc[1];
                 chain_step<1, true, true>(rec, S, w8, lane, oacc);
@@ -581,11 +603,12 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
     f32x4 S[8][1];
     load_unit_state(a, u, h, S, wave, gg, m);
-    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0) * REC_BYTES;
+    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0) * REC_HBM_BYTES;
     const int rem = (int)(end - tok0);
-    record_loop<512>(rb, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
+    const VRows vrows{(const uint8_t*)a.c.v + ((size_t)tok0 * H + h) * (D * 2), (uint32_t)H * (D * 2), rem};
+    record_loop(rb, vrows, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
         f32x4 oacc[1];
-        chain_step<1, true, true>(r, S, wave, lane, oacc);
+        chain_step<1, true, true, true>(r, S, wave, lane, oacc);
         store_output(a, h, tok0 + (int64_t)CH * ci, chunk_rows(rem, ci), oacc[0], wave, gg, m);
     });
     store_unit_state(a, u, h, S, wave, gg, m);
@@ -603,12 +626,12 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
 // the update reads (X, Kt, exp(G_C), T') are fetched.
 // ---------------------------------------------------------------------------
 struct TransferFetch {
-    // 16-byte vectors of a record: X and Kt^T [256, 768), exp(G_C) and T'
-    // [1056, 1152)
+    // 16-byte vectors of an HBM record: X and Kt^T [256, 768), exp(G_C) and
+    // T' [800, 896) (LDS [1056, 1152))
     static constexpr int NV = 608;
     static constexpr int N = (NV + 511) / 512;
     u32x4 r[N];
-    __device__ __forceinline__ static int index(int i) { return i < 512 ? 256 + i : 1056 + (i - 512); }
+    __device__ __forceinline__ static int index(int i) { return i < 512 ? 256 + i : 800 + (i - 512); }
     __device__ __forceinline__ void load(const uint8_t* __restrict__ src) {
         const u32x4* s = (const u32x4*)src;
 #pragma unroll
@@ -622,13 +645,13 @@ struct TransferFetch {
 #pragma unroll
         for (int j = 0; j < N; ++j) {
             const int i = threadIdx.x + j * 512;
-            if (i < NV) d[index(i)] = r[j];
+            if (i < NV) d[rec_lds_vec(index(i))] = r[j];
         }
     }
 };
 
 static_assert(REC_X / 16 == 256 && REC_KT / 16 == 512 && REC_V / 16 == 768 && REC_GC / 16 == 1056 &&
-                  REC_T / 16 == 1088 && REC_VEC == 1152,
+                  REC_T / 16 == 1088 && REC_VEC == 1152 && REC_HBM_VEC == 896,
               "transfer fetch ranges follow the record layout");
 
 __global__ __launch_bounds__(512) void kda_cp_transfer(PrescanArgs a) {
@@ -643,7 +666,7 @@ __global__ __launch_bounds__(512) void kda_cp_transfer(PrescanArgs a) {
     f32x4 S[8][1];
     identity_state(S, wave, gg, m);
     f32x4 unused[1];
-    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_BYTES;
+    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_HBM_BYTES;
     const int nc = it.n_chunks;
     // whether any tile of the workgroup is nonzero (uniform; a barrier round)
     auto any_live = [&]() __attribute__((always_inline)) {
@@ -657,17 +680,17 @@ __global__ __launch_bounds__(512) void kda_cp_transfer(PrescanArgs a) {
     };
     TransferFetch p0, p1;
     if (nc > 0) p0.load(rb);
-    if (nc > 1) p1.load(rb + REC_BYTES);
+    if (nc > 1) p1.load(rb + REC_HBM_BYTES);
     if (nc > 0) p0.store(recs[0]);
     lds_barrier();
     bool live = true;
     for (int ci = 0; ci < nc; ci += 2) {
-        if (ci + 2 < nc) p0.load(rb + (size_t)(ci + 2) * REC_BYTES);
+        if (ci + 2 < nc) p0.load(rb + (size_t)(ci + 2) * REC_HBM_BYTES);
         chain_step<1, false, false>(recs[0], S, wave, lane, unused);
         if (ci + 1 < nc) p1.store(recs[1]);
         lds_barrier();
         if (ci + 1 < nc) {
-            if (ci + 3 < nc) p1.load(rb + (size_t)(ci + 3) * REC_BYTES);
+            if (ci + 3 < nc) p1.load(rb + (size_t)(ci + 3) * REC_HBM_BYTES);
             chain_step<1, false, false>(recs[1], S, wave, lane, unused);
             if (ci + 2 < nc) p0.store(recs[0]);
             lds_barrier();

@@ -171,7 +171,7 @@ hipError_t static_scratch_address(void** ptr);
 
 
 constexpr int kChunk = 16;                      // tokens per chunk
-constexpr size_t kRecBytes = 18432;            // bytes of one K1 chunk record
+constexpr size_t kRecBytes = 14336;            // bytes of one K1 chunk record in HBM (no V)
 constexpr size_t kStateBytes = 128 * 128 * 4;  // one (sequence, head) state
 
 }  // namespace kda
