@@ -73,10 +73,15 @@ __device__ __forceinline__ int vrow_off(int r, int c) {
 }
 
 // K1 scratch of one chunk (LDS only), from phase 1 to phase 2:
-//   K1_KA, K1_KB, K1_QA: the Gram factors k exp(G - G_ref), k exp(G_ref - G),
-//                        q exp(G - G_ref) as fragments in the REC_Q layout,
-//                        with G_ref = 0 (the chunk start) or G_7 (see k1_phase1)
-//   K1_BETA            : beta of the chunk's 16 rows, fp32
+//   K1_KA, K1_QA: the Gram row factors k exp(G - G_ref), q exp(G - G_ref) as
+//                 fragments in the REC_Q layout, with G_ref = 0 (the chunk
+//                 start) or G_7 (see k1_phase1)
+//   K1_KB       : the column factor k exp(G_ref - G), each 16x16x32 fragment
+//                 split into halves: K-step p holds at p * 1024 + 8 l the
+//                 first half of lane l's fragment (from wavefront 2p) and at
+//                 p * 1024 + 512 + 8 l the second (from wavefront 2p + 1), so
+//                 that each wavefront writes 512 contiguous bytes
+//   K1_BETA     : beta of the chunk's 16 rows, fp32
 constexpr int K1_KA = 0;
 constexpr int K1_KB = 4096;
 constexpr int K1_QA = 8192;
@@ -478,11 +483,12 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
         pxk = pack4(xk);
         pkt = pack4(kt);
     }
-    // fragments in the REC_Q layout: half (wave & 1) of K-step (wave >> 1)
+    // fragments in the REC_Q layout: half (wave & 1) of K-step (wave >> 1);
+    // K1_KB in its split-half layout
     const int fo = (wave >> 1) * 1024 + lane * 16 + (wave & 1) * 8;
     *(u32x2*)(scr + K1_KA + fo) = pka;
-    *(u32x2*)(scr + K1_KB + fo) = pkb;
     *(u32x2*)(scr + K1_QA + fo) = pqa;
+    *(u32x2*)(scr + K1_KB + (wave >> 1) * 1024 + (wave & 1) * 512 + lane * 8) = pkb;
     *(u32x2*)(rec + REC_Q + fo) = pqt;
     *(u32x2*)(rec + REC_X + fo) = pxk;
     // Kt^T and V: element (token m, channel 16 wave + 4gg + j) -> tile wave,
@@ -511,26 +517,38 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
 // A_qk. The fused kernel forms L once, a stage earlier (k1_lkk), and runs
 // only the substitution on the T' wavefronts (k1_tsolve).
 // ---------------------------------------------------------------------------
-// L = strict-lower(diag(beta) A_kk) from the phase-1 Gram factors, stored
-// transposed (lt[c * K1_LSTRIDE + r] = L[r][c]), so that lane (gg, i) of a
-// reader finds column i of L in row i of lt. With lbeta, the chunk's beta
-// is copied beside it.
-__device__ __forceinline__ void k1_lkk(int lane, const uint8_t* scr, const float* scr_b, float* lt,
-                                       float* lbeta) {
+// The Gram operands of K-step p for lane `lane`: the column factor from its
+// split-half layout, and a row factor (K1_KA or K1_QA).
+__device__ __forceinline__ u32x4 gram_kb(const uint8_t* scr, int p, int lane) {
+    const u32x2 lo = *(const u32x2*)(scr + K1_KB + p * 1024 + lane * 8);
+    const u32x2 hi = *(const u32x2*)(scr + K1_KB + p * 1024 + 512 + lane * 8);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+__device__ __forceinline__ u32x4 gram_row(const uint8_t* scr, int off, int p, int lane) {
+    return *(const u32x4*)(scr + off + p * 1024 + lane * 16);
+}
+
+// L = strict-lower(diag(beta) A_kk) from A_kk (lane: A_kk[4gg + v][m]),
+// stored transposed (lt[c * K1_LSTRIDE + r] = L[r][c]), so that lane (gg, i)
+// of a reader finds column i of L in row i of lt. With lbeta, the chunk's
+// beta is copied beside it.
+__device__ __forceinline__ void k1_store_l(int lane, const f32x4& a, const float* scr_b, float* lt, float* lbeta) {
     const int gg = lane >> 4, m = lane & 15;
-    // (k exp(G - G_ref)) (k exp(G_ref - G))^T: lane holds A_kk[r][m], r = 4gg + v,
-    // which the row's beta then scales
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-        a = mfma_k32(*(const u32x4*)(scr + K1_KA + p * 1024 + lane * 16),
-                     *(const u32x4*)(scr + K1_KB + p * 1024 + lane * 16), a);
     const f32x4 br = *(const f32x4*)(scr_b + 4 * gg);
     f32x4 l;
 #pragma unroll
     for (int v = 0; v < 4; ++v) l[v] = (m < 4 * gg + v) ? br[v] * a[v] : 0.f;
     *(f32x4*)(lt + m * K1_LSTRIDE + 4 * gg) = l;
     if (lbeta && gg == 0) lbeta[m] = scr_b[m];
+}
+
+// L from the phase-1 Gram factors (see k1_store_l): A_kk = KA KB^T over the
+// 128 channels, lane holding A_kk[4gg + v][m].
+__device__ __forceinline__ void k1_lkk(int lane, const uint8_t* scr, const float* scr_b, float* lt, float* lbeta) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) a = mfma_k32(gram_row(scr, K1_KA, p, lane), gram_kb(scr, p, lane), a);
+    k1_store_l(lane, a, scr_b, lt, lbeta);
 }
 
 // Rows 4 s4 .. 4 s4 + 3 of T' = (I + L)^-1 diag(beta) from L^T (as k1_lkk
@@ -577,17 +595,38 @@ __device__ __forceinline__ void k1_phase2_t(int lane, int s4, uint8_t* rec, cons
     k1_tsolve(lane, s4, rec, lw, (const float*)(scr + K1_BETA));
 }
 
-__device__ __forceinline__ void k1_phase2_qk(int lane, uint8_t* rec, const uint8_t* scr) {
+// A_qk^T = (k exp(G_ref - G)) (q exp(G - G_ref))^T, masked (i <= r), to the
+// record: lane holds A_qk[m][4gg + v]. kb: the column-factor fragments.
+__device__ __forceinline__ void k1_aqk(int lane, uint8_t* rec, const uint8_t* scr, const u32x4 (&kb)[4]) {
     const int gg = lane >> 4, m = lane & 15;
-    // A_qk^T = (k exp(G_ref - G)) (q exp(G - G_ref))^T: lane holds A_qk[m][4gg + v]
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-        a = mfma_k32(*(const u32x4*)(scr + K1_KB + p * 1024 + lane * 16),
-                     *(const u32x4*)(scr + K1_QA + p * 1024 + lane * 16), a);
+    for (int p = 0; p < 4; ++p) a = mfma_k32(kb[p], gram_row(scr, K1_QA, p, lane), a);
 #pragma unroll
     for (int v = 0; v < 4; ++v) a[v] = (4 * gg + v <= m) ? a[v] : 0.f;
     *(u32x2*)(rec + REC_AQK + lane * 8) = pack4(a);
+}
+
+__device__ __forceinline__ void k1_phase2_qk(int lane, uint8_t* rec, const uint8_t* scr) {
+    u32x4 kb[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) kb[p] = gram_kb(scr, p, lane);
+    k1_aqk(lane, rec, scr, kb);
+}
+
+// Both Grams of a chunk on one wavefront (the fused kernel's WAVE_QK): A_qk
+// to the record and L to the shared lt (with beta at lbeta), reading the
+// column factor once.
+__device__ __forceinline__ void k1_grams(int lane, uint8_t* rec, const uint8_t* scr, const float* scr_b, float* lt,
+                                         float* lbeta) {
+    u32x4 kb[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) kb[p] = gram_kb(scr, p, lane);
+    k1_aqk(lane, rec, scr, kb);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) a = mfma_k32(gram_row(scr, K1_KA, p, lane), kb[p], a);
+    k1_store_l(lane, a, scr_b, lt, lbeta);
 }
 
 // Phase 2 by role; other wavefronts have nothing to do in it. lw is the

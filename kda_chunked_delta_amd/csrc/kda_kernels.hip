@@ -451,8 +451,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                     const uint8_t* scr = scrs + ring_off((c & 1) * K1_NB);
                     const float* scr_b = (const float*)((const uint8_t*)scr_betas + ring_off((c & 1) * 64));
                     float* lb = (float*)(lbs + ring_off((c & 1) * LB_BYTES));
-                    k1_phase2_qk(lane, recs + ring_off((c % 4) * REC_BYTES), scr);
-                    k1_lkk(lane, scr, scr_b, lb, lb + LB_BETA / 4);
+                    k1_grams(lane, recs + ring_off((c % 4) * REC_BYTES), scr, scr_b, lb, lb + LB_BETA / 4);
                 }
             };
             auto solve = [&](int c) __attribute__((always_inline)) {  // rows of T' of chunk c
