@@ -720,18 +720,26 @@ __global__ __launch_bounds__(512) void kda_cp_transfer(PrescanArgs a) {
 // it), so only carry_0 and the carries after live transfers are written.
 // Carry_0 is always written, so that segment-K2 never reads initial_state
 // while another segment writes final_state in place. Wavefront t owns carry
-// rows 16t..16t+15; the summaries of the next step load while the current
-// one computes, and each step splits its 32 MFMAs over two accumulators.
+// rows 16t..16t+15, and each step splits its 32 MFMAs over two accumulators.
+// The run's length is found before its first step, so the steps test no
+// flag, and the summaries of each step load while the step before it runs. In the
+// product M carry, lane group gg of MFMA step q takes key index
+// merge_k(gg, q): the lane's 32 entries of its M row come in two runs of 16,
+// and with the carry's LDS rows padded to MERGE_CST floats the 64 lanes of
+// each carry read fall on distinct banks. The carry is double-buffered in
+// LDS, so a step needs one barrier.
 // ---------------------------------------------------------------------------
+constexpr int MERGE_CST = 17;
+__device__ __forceinline__ int merge_k(int gg, int q) { return (q < 16 ? 0 : 48) + 16 * gg + q; }
 struct MergeOperands {
-    f32x4 m[8];   // M_s[16 wave + m][32 gg + 4j .. + 3], j = 0..7
-    f32x4 b;      // B_s[16 wave + 4 gg + v][16 vt + m], v = 0..3
-    int32_t live; // some tile of M_s is nonzero (the same in every lane)
+    f32x4 m[8];  // M_s[16 wave + m][merge_k(gg, 4j) .. + 3], j = 0..7
+    f32x4 b;     // B_s[16 wave + 4 gg + v][16 vt + m], v = 0..3
 };
 
-__global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
+__global__ __launch_bounds__(512, 4) void kda_cp_merge(MergeArgs a) {
     if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
-    __shared__ float carry[D][16];
+    __shared__ float carry[2][D][MERGE_CST];
+    __shared__ int32_t run_end;
     const int H = a.c.H;
     const int vt = blockIdx.x & 7;
     const int h = (blockIdx.x >> 3) % H;
@@ -750,6 +758,18 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
     const int s0 = sg.seg;
     // a segment after a live transfer lies inside a run started earlier
     if (s0 > 0 && __builtin_amdgcn_readfirstlane(flags(s0 - 1)) != 0) return;
+    // a run of this segment alone has nothing to compute (segment-K2 reads
+    // B_{s0-1} itself)
+    const bool live0 = s0 < n_sum && __builtin_amdgcn_readfirstlane(flags(s0)) != 0;
+    if (s0 > 0 && !live0) return;
+    // the run: transfers s0 .. run_end - 1 are live (the first vanished one,
+    // or the last summary, ends it), so its length is known before the
+    // first step and the steps need no flag of their own
+    if (tid == 0) run_end = live0 ? n_sum : s0;
+    __syncthreads();
+    if (live0)
+        for (int j = s0 + 1 + tid; j < n_sum; j += 512)
+            if (flags(j) == 0) atomicMin(&run_end, j);
     if (s0 == 0) {
         const size_t s0_off = ((size_t)it.seq * H + h) * (D * D);
         const float* si = (a.s0 && !a.state_bf16) ? (const float*)a.s0 + s0_off : nullptr;
@@ -758,27 +778,23 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
         for (int i = tid; i < D * 16; i += 512) {
             const int row = i >> 4, col = i & 15;
             const float val = si ? si[row * D + 16 * vt + col] : (sih ? bf16_lo(sih[row * D + 16 * vt + col]) : 0.f);
-            carry[row][col] = val;
+            carry[0][row][col] = val;
             c0[row * D + 16 * vt + col] = val;
         }
     } else {
-        // the run starts from B_{s0-1}; a run of this segment alone has
-        // nothing to compute (segment-K2 reads B_{s0-1} itself)
-        if (s0 >= n_sum || __builtin_amdgcn_readfirstlane(flags(s0)) == 0) return;
+        // the run starts from B_{s0-1}
         const float* B = a.b_seg + ((size_t)(it.prescan0 + s0 - 1) * H + h) * (D * D);
         for (int i = tid; i < D * 16; i += 512) {
             const int row = i >> 4, col = i & 15;
-            carry[row][col] = B[row * D + 16 * vt + col];
+            carry[0][row][col] = B[row * D + 16 * vt + col];
         }
     }
     __syncthreads();
-    // summaries and flags of step s (transfer s0 + s; clamped to the last
-    // one, so every load is valid and unconditional): the run ends at the
-    // first step whose transfer vanished, or after the last summary
+    const int n_run = __builtin_amdgcn_readfirstlane(run_end - s0);
+    // summaries of step s (transfer s0 + s; clamped to the run's last, so
+    // every load is valid and unconditional)
     auto load = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
-        const int j = s0 + s;
-        const int jj = j < n_sum ? j : n_sum - 1;
-        x.live = j < n_sum ? flags(jj) : 0;
+        const int jj = s0 + (s < n_run ? s : n_run - 1);
         const size_t sum_off = ((size_t)(it.prescan0 + jj) * H + h) * (D * D);
         const float* M = a.m_seg + sum_off;
         const float* B = a.b_seg + sum_off;
@@ -788,39 +804,54 @@ __global__ __launch_bounds__(512) void kda_cp_merge(MergeArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             x.m[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                mr, (int)(((16 * wave + m) * D + 32 * gg + 4 * k) * 4), 0, 0));
+                mr, (int)(((16 * wave + m) * D + merge_k(gg, 4 * k)) * 4), 0, 0));
     };
-    // carry_{s0+s+1} = M carry + B; returns false at the end of the run
+    // carry_{s0+s+1} = M carry + B
     auto step = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
         // the operands are read only from here on (keeps their wait here)
         asm volatile("" : "+v"(x.m[0]), "+v"(x.m[1]), "+v"(x.m[2]), "+v"(x.m[3]), "+v"(x.m[4]),
-                     "+v"(x.m[5]), "+v"(x.m[6]), "+v"(x.m[7]), "+v"(x.b), "+v"(x.live));
-        if (__builtin_amdgcn_readfirstlane(x.live) == 0) return false;
+                     "+v"(x.m[5]), "+v"(x.m[6]), "+v"(x.m[7]), "+v"(x.b));
+        // the carry operands of the products, 16 at a time, each half read
+        // before its first product: one wait per half, not one per product
+        const float(*cur)[MERGE_CST] = carry[s & 1];
         f32x4 acc0 = x.b, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qq = 0; qq < 32; qq += 2) {
-            acc0 = mfma_f32_k4(x.m[qq >> 2][qq & 3], carry[32 * gg + qq][m], acc0);
-            acc1 = mfma_f32_k4(x.m[qq >> 2][(qq & 3) + 1], carry[32 * gg + qq + 1][m], acc1);
+        for (int hh = 0; hh < 32; hh += 16) {
+            float cb[16];
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) cb[qq] = cur[merge_k(gg, hh + qq)][m];
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) asm volatile("" : "+v"(cb[qq]));
+#pragma unroll
+            for (int qq = 0; qq < 16; qq += 2) {
+                acc0 = mfma_f32_k4(x.m[(hh + qq) >> 2][qq & 3], cb[qq], acc0);
+                acc1 = mfma_f32_k4(x.m[(hh + qq) >> 2][(qq & 3) + 1], cb[qq + 1], acc1);
+            }
         }
         const f32x4 acc = acc0 + acc1;
-        __syncthreads();
+        float(*nxt)[MERGE_CST] = carry[(s + 1) & 1];
         float* cn = a.carries + ((size_t)(it.carry0 + s0 + s + 1) * H + h) * (D * D);
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) {
-            carry[16 * wave + 4 * gg + vv][m] = acc[vv];
+            nxt[16 * wave + 4 * gg + vv][m] = acc[vv];
             cn[(16 * wave + 4 * gg + vv) * D + 16 * vt + m] = acc[vv];
         }
-        __syncthreads();
-        return true;
+        // orders the LDS carry only (no wait for the global stores or the
+        // summaries in flight)
+        lds_barrier();
     };
-    if (n_sum <= 0) return;
+    if (n_run <= 0) return;
+    // two operand sets in flight: a step's summaries load a step ahead of
+    // the step before it (deeper rings measured slower: the compiler then
+    // waits for every load at the loop head)
     MergeOperands xa, xb;
     load(0, xa);
     load(1, xb);
-    for (int s = 0;; s += 2) {
-        if (!step(s, xa)) break;
+    for (int s = 0; s < n_run; s += 2) {
+        step(s, xa);
         load(s + 2, xa);
-        if (!step(s + 1, xb)) break;
+        if (s + 1 >= n_run) break;
+        step(s + 1, xb);
         load(s + 3, xb);
     }
 }
