@@ -367,6 +367,37 @@ def test_cp_weak_decay_within_tolerance():
     assert_close("out(serial)", o_ser, o_ref)
 
 
+def test_cp_merge_runs_starting_mid_sequence():
+    """Decay that alternates by region: strong (g x 4) where a segment's
+    transfer vanishes, weak (g x 0.05) where it survives. The merge then has
+    runs of live transfers that start after segment 0 (from the B of a
+    segment whose transfer vanished) and end at a vanished transfer or at
+    the last summary, with odd and even lengths. CP matches the oracle and
+    the serial path within 1e-2; in place as well."""
+    seg = 8  # chunks per segment
+    regions = [(5, 4.0), (10, 0.05), (5, 4.0), (7, 0.05), (2, 4.0), (11, 0.05)]  # (segments, g scale)
+    n_seg = sum(r[0] for r in regions)
+    T = n_seg * seg * 16
+    say("case: %d segments of %d chunks, regions %s" % (n_seg, seg, regions))
+    d = draw([T], 2, seed=91, state_std=0.1, device=DEV)
+    scale = torch.cat([torch.full((n * seg * 16,), f, dtype=torch.float32) for n, f in regions]).to(DEV)
+    d["g"] = d["g"] * scale[:, None, None]
+    cu = d["cu_seqlens_host"]
+    p = kda.plan_segments(cu, 2, seg, device=DEV)
+    assert p.info()["uses_cp"] == 1
+    o_cp, s_cp = run(d, plan=p)
+    o_ser, s_ser = run(d)
+    o_ref, s_ref = oracle(d)
+    assert_close("out(cp)", o_cp, o_ref)
+    assert_close("final(cp)", s_cp, s_ref)
+    assert_close("out(cp vs serial)", o_cp, o_ser.double().cpu().numpy())
+    st = d["initial_state"].clone()
+    o_in, _ = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                          cu_seqlens_host=cu, initial_state=st, final_state=st, plan=p)
+    torch.cuda.synchronize()
+    assert torch.equal(o_in, o_cp) and torch.equal(st, s_cp), "in-place CP differs from out-of-place CP"
+
+
 def test_steep_in_chunk_decay_matches_oracle(monkeypatch):
     """Decay steps of e^-40 at rows 0 and 8 of every chunk, on the key
     channels of two of the eight K1 wavefronts of the second sequence: the
