@@ -141,26 +141,30 @@ double fused_interval_us(int busy, int n_cus, const PlannerConsts& pc) {
 
 // Time of the fused kernel over work units of the given chunk counts,
 // started longest first on n_cus CUs (one workgroup per CU), every running
-// unit advancing one chunk per interval at the current occupancy.
-double simulate_fused_us(std::vector<int> work, int n_cus, const PlannerConsts& pc) {
+// unit advancing one chunk per interval at the current occupancy. With
+// copies > 1, `work` is one of `copies` identical groups of units (the heads
+// of a batch) and the group runs on n_cus / copies CUs: the same timeline as
+// all groups together, since identical units start and finish together.
+double simulate_fused_us(std::vector<int> work, int n_cus, const PlannerConsts& pc, int copies = 1) {
     std::sort(work.begin(), work.end(), std::greater<int>());
+    const int slots = n_cus / copies;
     std::vector<double> heap;  // finish progress of running units (min-heap)
     auto cmp = std::greater<double>();
     size_t next = 0;
     double progress = 0.0, t = 0.0;
-    while (next < work.size() && (int)heap.size() < n_cus) {
+    while (next < work.size() && (int)heap.size() < slots) {
         heap.push_back((double)work[next++]);
         std::push_heap(heap.begin(), heap.end(), cmp);
     }
     while (!heap.empty()) {
         const double f = heap.front();
-        t += (f - progress) * fused_interval_us((int)heap.size(), n_cus, pc);
+        t += (f - progress) * fused_interval_us((int)heap.size() * copies, n_cus, pc);
         progress = f;
         while (!heap.empty() && heap.front() <= progress) {
             std::pop_heap(heap.begin(), heap.end(), cmp);
             heap.pop_back();
         }
-        while (next < work.size() && (int)heap.size() < n_cus) {
+        while (next < work.size() && (int)heap.size() < slots) {
             heap.push_back(progress + work[next++]);
             std::push_heap(heap.begin(), heap.end(), cmp);
         }
@@ -269,20 +273,30 @@ std::vector<int> split_work(const std::vector<int>& nch, const std::vector<int>&
     return w;
 }
 
-// Warm-start split search: the k longest sequences are split at the same
-// fraction f of their chunks; the cheapest (k, f) by the fused-kernel
-// simulation wins. Only for batches of at most a few rounds of units, where
-// the longest chains make the tail.
+// Warm-start split search. First a grid: the k longest sequences split at
+// the same fraction f of their chunks. Then, from the best few grid points,
+// a coordinate descent that moves each split sequence's split point over a
+// set of fractions, one sequence at a time, while the simulated time falls
+// (a split's two pieces can then pair with different units in the
+// schedule). Only for batches of at most a few rounds of units, where the
+// longest chains make the tail. When H divides the CU count the simulation
+// runs one head's units on its share of the CUs.
 double best_split(const std::vector<int>& nch, int H, int n_cus, const PlannerConsts& pc,
                   std::vector<int>& split_out) {
     const int n = (int)nch.size();
     split_out.assign(n, 0);
     const int W = pc.split_warm;
-    double best = 1e300;
-    if ((long long)n * H > 4LL * n_cus || W < 1) return best;
+    if ((long long)n * H > 4LL * n_cus || W < 1) return 1e300;
+    const bool grouped = H <= n_cus && n_cus % H == 0;
+    auto cost = [&](const std::vector<int>& sp) {
+        return grouped ? simulate_fused_us(split_work(nch, sp, 1, W), n_cus, pc, H)
+                       : simulate_fused_us(split_work(nch, sp, H, W), n_cus, pc);
+    };
+    auto valid = [&](int i, int a) { return a >= W && nch[i] - a >= 1 && nch[i] >= 4 * W; };
     std::vector<int> order(n);
     for (int i = 0; i < n; ++i) order[i] = i;
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return nch[x] > nch[y]; });
+    std::vector<std::pair<double, std::vector<int>>> grid;
     std::vector<int> split(n, 0);
     for (int k = 1; k <= std::min(n, 8); ++k) {
         for (int fi = 6; fi <= 12; ++fi) {
@@ -292,15 +306,51 @@ double best_split(const std::vector<int>& nch, int H, int n_cus, const PlannerCo
             for (int j = 0; j < k; ++j) {
                 const int i = order[j];
                 const int a = (int)std::lround(nch[i] * f);
-                if (a < W || nch[i] - a < 1 || nch[i] < 4 * W) { ok = false; break; }
+                if (!valid(i, a)) { ok = false; break; }
                 split[i] = a;
             }
             if (!ok) break;
-            const double t = simulate_fused_us(split_work(nch, split, H, W), n_cus, pc) + pc.launch_us;
-            if (t < best) { best = t; split_out = split; }
+            grid.emplace_back(cost(split), split);
         }
     }
-    return best;
+    if (grid.empty()) return 1e300;
+    std::stable_sort(grid.begin(), grid.end(),
+                     [](const std::pair<double, std::vector<int>>& x, const std::pair<double, std::vector<int>>& y) {
+                         return x.first < y.first;
+                     });
+    double best = grid[0].first;
+    split_out = grid[0].second;
+    static const double fracs[] = {0.25, 0.35, 0.45, 0.55, 0.65, 0.75};
+    const size_t seeds = std::min<size_t>(grid.size(), 8);
+    for (size_t g = 0; g < seeds; ++g) {
+        std::vector<int> cur = grid[g].second;
+        double ct = grid[g].first;
+        for (int sweep = 0; sweep < 3; ++sweep) {
+            bool improved = false;
+            for (int i = 0; i < n; ++i) {
+                if (cur[i] == 0) continue;
+                for (double f : fracs) {
+                    const int a = (int)std::lround(nch[i] * f);
+                    if (a == cur[i] || !valid(i, a)) continue;
+                    const int keep = cur[i];
+                    cur[i] = a;
+                    const double t = cost(cur);
+                    if (t < ct - 1e-9) {
+                        ct = t;
+                        improved = true;
+                    } else {
+                        cur[i] = keep;
+                    }
+                }
+            }
+            if (!improved) break;
+        }
+        if (ct < best) {
+            best = ct;
+            split_out = cur;
+        }
+    }
+    return best + pc.launch_us;
 }
 
 // seg_chunks > 0 forces that segment length on every longer sequence;

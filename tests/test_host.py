@@ -172,6 +172,73 @@ def test_auto_plan_splits_the_tail_of_one_round(kda_lib):
     assert work == sorted(work, reverse=True)
 
 
+def _fused_model_us(work, n_cus):
+    """The planner's fused-kernel schedule model: units start longest first,
+    one per CU, and every running unit advances one chunk per interval, the
+    interval rising with the fraction of busy CUs (1.21 us alone, 1.60 us with
+    all busy, piecewise linear through the measured shape)."""
+    import heapq
+    xs = [0.0, 0.125, 0.25, 0.5, 0.75, 1.0]
+    ys = [0.0, 0.046, 0.061, 0.096, 0.47, 1.0]
+
+    def interval(busy):
+        x = min(1.0, max(0.0, busy / n_cus))
+        i = 0
+        while i < 4 and x > xs[i + 1]:
+            i += 1
+        return 1.21 + 0.39 * (ys[i] + (ys[i + 1] - ys[i]) * (x - xs[i]) / (xs[i + 1] - xs[i]))
+
+    work = sorted(work, reverse=True)
+    heap, nxt, prog, t = [], 0, 0.0, 0.0
+    while nxt < len(work) and len(heap) < n_cus:
+        heapq.heappush(heap, float(work[nxt]))
+        nxt += 1
+    while heap:
+        f = heap[0]
+        t += (f - prog) * interval(len(heap))
+        prog = f
+        while heap and heap[0] <= prog:
+            heapq.heappop(heap)
+        while nxt < len(work) and len(heap) < n_cus:
+            heapq.heappush(heap, prog + work[nxt])
+            nxt += 1
+    return t
+
+
+def test_split_search_is_at_least_the_uniform_grid(kda_lib):
+    """The split search starts from the grid of uniform fractions (the k
+    longest sequences split at the same fraction f) and only moves split
+    points while the modelled time falls: its estimate is the model's time
+    of the plan's own units, and no grid point models faster."""
+    lengths = headline_lengths()
+    nch = [(L + 15) // 16 for L in lengths]
+    H, n_cus = 32, 256
+    p = kda.plan_host(cu_of(lengths), H=H, n_cus=n_cus, use_intracard_cp="auto")
+    info = p.info()
+    W = info["split_warm_chunks"]
+    work = [u["n_chunks"] + 2 * u["warm_chunks"] for u in p.units()] * H
+    t_plan = _fused_model_us(work, n_cus)
+    assert abs(info["est_split_us"] - (t_plan + 5.0)) < 1e-3
+    order = sorted(range(len(nch)), key=lambda i: -nch[i])
+    best_grid = 1e300
+    for k in range(1, len(nch) + 1):
+        for fi in range(6, 13):
+            f = 0.05 * fi
+            units = list(nch)
+            ok = True
+            for i in order[:k]:
+                a = int(round(nch[i] * f + 1e-9))
+                if a < W or nch[i] - a < 1 or nch[i] < 4 * W:
+                    ok = False
+                    break
+                units[i] = a
+                units.append(nch[i] - a + 2 * W)
+            if not ok:
+                break
+            best_grid = min(best_grid, _fused_model_us(units * H, n_cus))
+    assert t_plan <= best_grid + 1e-6
+
+
 def test_auto_plan_splits_nothing_else(kda_lib, monkeypatch):
     # several rounds of units smooth the tail
     assert kda.plan_host(cu_of([8192] * 16), H=64, n_cus=256, use_intracard_cp="auto").info()["n_split_seqs"] == 0
