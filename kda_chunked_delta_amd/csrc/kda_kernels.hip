@@ -42,7 +42,7 @@ struct VRows {
 };
 
 // K2's record prefetch through registers: the 896 vectors of an HBM record,
-// two per thread, and the chunk's 16 value rows, one 16-byte granule per
+// up to two per thread, and the chunk's 16 value rows, one 16-byte granule per
 // thread of wavefronts 0..3 (row tid >> 4, granule tid & 15). Wavefronts
 // 4..7 issue the same load over an empty range (no memory access), so that
 // every load is unconditional; rows past the sequence read as zeros.
@@ -722,8 +722,8 @@ __global__ __launch_bounds__(512) void kda_cp_transfer(PrescanArgs a) {
 // while another segment writes final_state in place. Wavefront t owns carry
 // rows 16t..16t+15, and each step splits its 32 MFMAs over two accumulators.
 // The run's length is found before its first step, so the steps test no
-// flag, and the summaries of each step load while the step before it runs. In the
-// product M carry, lane group gg of MFMA step q takes key index
+// flag, and the summaries of each step load while the step before it runs.
+// In the product M carry, lane group gg of MFMA step q takes key index
 // merge_k(gg, q): the lane's 32 entries of its M row come in two runs of 16,
 // and with the carry's LDS rows padded to MERGE_CST floats the 64 lanes of
 // each carry read fall on distinct banks. The carry is double-buffered in
