@@ -322,18 +322,24 @@ double best_split(const std::vector<int>& nch, int H, int n_cus, const PlannerCo
     split_out = grid[0].second;
     static const double fracs[] = {0.25, 0.35, 0.45, 0.55, 0.65, 0.75};
     const size_t seeds = std::min<size_t>(grid.size(), 8);
-    for (size_t g = 0; g < seeds; ++g) {
+    // grid and descent together simulate at most 64K units, so planning a
+    // batch of many sequences stays cheap (the grid alone reaches that at
+    // the largest shapes considered, n * H = 4 CUs' worth)
+    const long long units_per_sim = (long long)(n + 8) * (grouped ? 1 : H);
+    long long budget = 64 * 1024 - (long long)grid.size() * units_per_sim;
+    for (size_t g = 0; g < seeds && budget > 0; ++g) {
         std::vector<int> cur = grid[g].second;
         double ct = grid[g].first;
-        for (int sweep = 0; sweep < 3; ++sweep) {
+        for (int sweep = 0; sweep < 3 && budget > 0; ++sweep) {
             bool improved = false;
-            for (int i = 0; i < n; ++i) {
+            for (int i = 0; i < n && budget > 0; ++i) {
                 if (cur[i] == 0) continue;
                 for (double f : fracs) {
                     const int a = (int)std::lround(nch[i] * f);
                     if (a == cur[i] || !valid(i, a)) continue;
                     const int keep = cur[i];
                     cur[i] = a;
+                    budget -= units_per_sim;
                     const double t = cost(cur);
                     if (t < ct - 1e-9) {
                         ct = t;
