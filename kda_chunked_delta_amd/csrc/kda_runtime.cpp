@@ -94,9 +94,11 @@ double env_double(const char* name, double dflt) {
 //   launch     one kernel launch
 struct PlannerConsts {
     double fused_us, k1_us, prescan_us, rec_us, merge_us, launch_us;
+    double k1_alone_us;   // K1 with few CUs busy (k1_us: all busy)
+    double prescan_one_us, prescan_half_us;  // transfer with 1 and 1/2 workgroups per CU (prescan_us: 2)
+    double rec_alone_us;  // K2 over records, one workgroup's chunk step (rec_us: per CU, HBM-bound)
     int min_seg_chunks;  // shortest segment the planner will form
     int prescan_per_cu;  // concurrent pre_scan workgroups per CU
-    int rec_per_cu;      // concurrent K2-over-records workgroups per CU
     // fused kernel interval per chunk against the fraction of busy CUs:
     // alone_us with few busy, full_us with all busy, in between the shape
     // measured on MI355X (the shader clock falls as more CUs work)
@@ -106,20 +108,23 @@ struct PlannerConsts {
 
 PlannerConsts planner_consts() {
     PlannerConsts c;
-    // fitted at steady clocks on the 65536-token, 8-head workload with
-    // 64-chunk segments (K1 with B summaries 264 us over 128 chunk-heads per
-    // CU; under weak decay the transfer 99 us and the merge 197 us over 63
-    // segments; segment-K2 146 us) and on the fused kernel's interval with
-    // few CUs busy
+    // fitted at steady clocks on the 65536-token, 8-head workload with 64-,
+    // 128- and 256-chunk segments (512, 256 and 128 workgroups): K1 with B
+    // summaries 237, 230 and 299 us; under weak decay the transfer 99, 157
+    // and 194 us and the merge 2.3 us per segment step; segment-K2 148, 149
+    // and 228 us. And on the fused kernel's interval with few CUs busy.
     c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.21);
-    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 2.06);
-    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 1.55);
-    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 2.28);
-    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 3.1);
+    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 1.80);
+    c.k1_alone_us = env_double("KDA_CP_K1_CHUNK_US_ALONE", 1.10);
+    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 1.54);
+    c.prescan_one_us = env_double("KDA_CP_PRESCAN_CHUNK_US_ONE", 1.23);
+    c.prescan_half_us = env_double("KDA_CP_PRESCAN_CHUNK_US_HALF", 0.78);
+    c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 1.16);
+    c.rec_alone_us = env_double("KDA_CP_REC_CHUNK_US_ALONE", 0.89);
+    c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 2.3);
     c.launch_us = env_double("KDA_CP_LAUNCH_US", 5.0);
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
     c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
-    c.rec_per_cu = (int)env_double("KDA_CP_REC_PER_CU", 2.0);
     c.alone_us = env_double("KDA_FUSED_CHUNK_US_ALONE", 1.21);
     c.full_us = env_double("KDA_FUSED_CHUNK_US_FULL", 1.60);
     c.split_warm = (int)env_double("KDA_SPLIT_WARM_CHUNKS", 12.0);
@@ -228,15 +233,18 @@ double est_serial(const std::vector<int>& nch, int H, int n_cus, const PlannerCo
 // Segmented estimate for segment length `seg` (chunks): K1 materialised for
 // every chunk (with the B summaries), the transfer half of pre_scan over
 // every segment but the last of each split sequence, a serial merge over
-// segments, then K2 over all units.
+// segments, then K2 over all units. The transfer and the merge are priced
+// at weak decay, where no transfer vanishes (the worst case).
 double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const PlannerConsts& pc) {
-    long long tot = 0, pre_work = 0;
+    long long tot = 0, n_pre = 0;
     int longest_unit = 0, max_segs = 0;
+    std::vector<int> k1_work;  // K1 units of one head
     for (int n : nch) {
         tot += n;
         const int s = (n > seg) ? (n + seg - 1) / seg : 1;
+        for (int j = 0; j < s; ++j) k1_work.push_back(std::min(seg, n - j * seg));
         if (s > 1) {
-            pre_work += (long long)(s - 1) * seg;
+            n_pre += s - 1;
             max_segs = std::max(max_segs, s);
             longest_unit = std::max(longest_unit, seg);
         } else {
@@ -244,12 +252,30 @@ double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const Plan
         }
     }
     if (max_segs == 0) return 1e300;
-    const double t_k1 = pc.k1_us * std::ceil((double)tot * H / n_cus);
-    const double t_pre = pc.prescan_us *
-                         std::max((double)seg, std::ceil((double)pre_work * H / ((double)n_cus * pc.prescan_per_cu)));
+    // K1 runs the fused kernel's body (with the record writes) one workgroup
+    // per CU: its schedule in the fused kernel's model, at K1's own interval
+    PlannerConsts k1c = pc;
+    k1c.alone_us = pc.k1_alone_us;
+    k1c.full_us = pc.k1_us;
+    const bool grouped = H <= n_cus && n_cus % H == 0;
+    if (!grouped) {
+        const std::vector<int> one = k1_work;
+        for (int h = 1; h < H; ++h) k1_work.insert(k1_work.end(), one.begin(), one.end());
+    }
+    const double t_k1 = simulate_fused_us(k1_work, n_cus, k1c, grouped ? H : 1);
+    // the transfer: each workgroup one segment; its chunk step slows as more
+    // share a CU (piecewise linear through 1/2, 1 and 2 per CU), in rounds
+    // of prescan_per_cu per CU
+    const double per_cu = (double)n_pre * H / n_cus;
+    const double cap = std::max(1, pc.prescan_per_cu);
+    const double c = std::min(per_cu, cap);
+    const double step = c <= 0.5 ? pc.prescan_half_us
+                        : c <= 1.0 ? pc.prescan_half_us + (pc.prescan_one_us - pc.prescan_half_us) * (c - 0.5) / 0.5
+                                   : pc.prescan_one_us + (pc.prescan_us - pc.prescan_one_us) * std::min(1.0, c - 1.0);
+    const double t_pre = std::ceil(per_cu / cap) * seg * step;
     const double t_merge = pc.merge_us * (max_segs - 1);
-    const double t_k2 = pc.rec_us *
-                        std::max((double)longest_unit, std::ceil((double)tot * H / ((double)n_cus * pc.rec_per_cu)));
+    // K2: the longest unit's chain, or the HBM stream over the CUs
+    const double t_k2 = std::max(pc.rec_alone_us * longest_unit, pc.rec_us * std::ceil((double)tot * H / n_cus));
     return t_k1 + t_pre + t_merge + t_k2 + 4 * pc.launch_us;
 }
 
