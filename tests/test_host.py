@@ -259,6 +259,22 @@ def test_split_warm_chunks_is_env_overridable(kda_lib, monkeypatch):
     assert info["n_split_seqs"] == 0 or info["split_warm_chunks"] == 12
 
 
+def test_forced_cp_segment_length_follows_the_measured_sweep(kda_lib, monkeypatch):
+    """One 65536-token sequence with 8 heads on 256 CUs: the segmented model
+    picks 128-chunk segments (one workgroup per CU), which measured fastest
+    of 32, 48, 64, 128 and 256 chunks under both strong and weak decay. K2
+    streams the records at the same rate with one or two workgroups per CU,
+    so it is priced by the longer of one unit's chain and the HBM stream;
+    with a slower chain step (its constant overridden) the chain term wins
+    and the model prefers 64-chunk segments."""
+    info = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=True).info()
+    assert info["uses_cp"] == 1 and info["warm_cp"] == 0
+    assert info["max_unit_chunks"] == 128 and info["n_units"] == 32
+    monkeypatch.setenv("KDA_CP_REC_CHUNK_US_ALONE", "3.0")
+    slow_chain = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=True).info()
+    assert slow_chain["max_unit_chunks"] == 64 and slow_chain["est_cp_us"] > info["est_cp_us"]
+
+
 def test_planner_constants_are_env_overridable(kda_lib, monkeypatch):
     base = kda.plan_host([0, 65536], H=8, n_cus=256, use_intracard_cp=True).info()
     monkeypatch.setenv("KDA_CP_MIN_SEG_CHUNKS", "1024")
