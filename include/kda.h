@@ -108,6 +108,10 @@ typedef struct {
                                   found that speculation failed: later calls outside graph
                                   capture run the plan's exact path (the batch unsplit, or
                                   the segmented pipeline), which gives the same bits */
+    int32_t split_warm_work;   /* the warm-up's cost in chunk intervals as the planner
+                                  counts it (a warm-start segment of n chunks costs
+                                  n + split_warm_work): its W chunks each form two
+                                  states, the transfer and the state from zero */
 } kda_plan_info;
 
 /* One K2 work unit of a plan (a whole sequence, or one segment of it). */

@@ -54,7 +54,8 @@ class PlanInfo(ctypes.Structure):
                 ("n_split_seqs", ctypes.c_int32), ("split_warm_chunks", ctypes.c_int32),
                 ("est_split_us", ctypes.c_double), ("warm_cp", ctypes.c_int32),
                 ("warm_cp_seg_chunks", ctypes.c_int32), ("n_warm_segments", ctypes.c_int32),
-                ("est_warm_cp_us", ctypes.c_double), ("speculation_off", ctypes.c_int32)]
+                ("est_warm_cp_us", ctypes.c_double), ("speculation_off", ctypes.c_int32),
+                ("split_warm_work", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

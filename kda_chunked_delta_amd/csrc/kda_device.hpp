@@ -741,4 +741,59 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
     decay(std::integral_constant<int, 6>{}); decay(std::integral_constant<int, 7>{});
 }
 
+// The warm-up step of a warm-start segment: the transfer M (V := 0) and the
+// state from zero Z (with V from the fragment layout) over the same record,
+// each tile's arithmetic exactly that of chain_step<1, false, false> and
+// chain_step<1, true, false>. The record's operands are read once for both,
+// and each bf16 operand of a state is packed just before its one use (no
+// output is formed), so the two states fit the registers beside the step.
+__device__ __forceinline__ void chain_step_warm(const uint8_t* rec, f32x4 (&M)[8][1], f32x4 (&Z)[8][1], int n0,
+                                                int lane) {
+    f32x4 pm = {0.f, 0.f, 0.f, 0.f}, pz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const u32x4 xf = *(const u32x4*)(rec + REC_X + p * 1024 + lane * 16);
+        u32x4 sm, sz;
+        sm.x = pack_bf16(M[2 * p][0][0], M[2 * p][0][1]);
+        sm.y = pack_bf16(M[2 * p][0][2], M[2 * p][0][3]);
+        sm.z = pack_bf16(M[2 * p + 1][0][0], M[2 * p + 1][0][1]);
+        sm.w = pack_bf16(M[2 * p + 1][0][2], M[2 * p + 1][0][3]);
+        sz.x = pack_bf16(Z[2 * p][0][0], Z[2 * p][0][1]);
+        sz.y = pack_bf16(Z[2 * p][0][2], Z[2 * p][0][3]);
+        sz.z = pack_bf16(Z[2 * p + 1][0][0], Z[2 * p + 1][0][1]);
+        sz.w = pack_bf16(Z[2 * p + 1][0][2], Z[2 * p + 1][0][3]);
+        pm = mfma_k32(xf, sm, pm);
+        pz = mfma_k32(xf, sz, pz);
+    }
+    const u32x2 th = *(const u32x2*)(rec + REC_T + lane * 8);
+    const u32x2 tl = *(const u32x2*)(rec + REC_T + 512 + lane * 8);
+    const u32x2 vw = *(const u32x2*)(rec + REC_V + n0 * 512 + kv_slot(lane) * 8);
+    f32x4 rz;
+    rz[0] = bf16_lo(vw.x) - pz[0];
+    rz[1] = bf16_hi(vw.x) - pz[1];
+    rz[2] = bf16_lo(vw.y) - pz[2];
+    rz[3] = bf16_hi(vw.y) - pz[3];
+    const u32x2 rbm = pack4(-pm), rbz = pack4(rz);
+    f32x4 um = mfma_k16(th, rbm, f32x4{0.f, 0.f, 0.f, 0.f});
+    f32x4 uz = mfma_k16(th, rbz, f32x4{0.f, 0.f, 0.f, 0.f});
+    um = mfma_k16(tl, rbm, um);
+    uz = mfma_k16(tl, rbz, uz);
+    const u32x2 ubm = pack4(um), ubz = pack4(uz);
+    const f32x2 gcp = *(const f32x2*)(rec + REC_GC + lane * 8);
+    auto decay = [&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        const f32x4 gcv = {row_newbcast<2 * t>(gcp[0]), row_newbcast<2 * t>(gcp[1]),
+                           row_newbcast<2 * t + 1>(gcp[0]), row_newbcast<2 * t + 1>(gcp[1])};
+        const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + kv_slot(lane) * 8);
+        M[t][0] = gcv * M[t][0];
+        M[t][0] = mfma_k16(kt, ubm, M[t][0]);
+        Z[t][0] = gcv * Z[t][0];
+        Z[t][0] = mfma_k16(kt, ubz, Z[t][0]);
+    };
+    decay(std::integral_constant<int, 0>{}); decay(std::integral_constant<int, 1>{});
+    decay(std::integral_constant<int, 2>{}); decay(std::integral_constant<int, 3>{});
+    decay(std::integral_constant<int, 4>{}); decay(std::integral_constant<int, 5>{});
+    decay(std::integral_constant<int, 6>{}); decay(std::integral_constant<int, 7>{});
+}
+
 }  // namespace kda

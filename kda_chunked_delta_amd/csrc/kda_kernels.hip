@@ -406,12 +406,12 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
     }
     const int64_t tok0 = beg + (int64_t)CH * u.chunk0;
     const int nc = u.n_chunks;
-    // A warm-start segment runs `warm` chunks twice before its own: steps
-    // 0 .. W-1 form the transfer over chunks chunk0-W .. chunk0-1, steps
-    // W .. 2W-1 the state from zero over the same chunks, and step 2W + c
-    // is chunk chunk0 + c.
+    // A warm-start segment runs `warm` chunks before its own: steps 0 .. W-1
+    // are chunks chunk0-W .. chunk0-1, over which the state wavefronts form
+    // the transfer and the state from zero side by side, and step W + c is
+    // chunk chunk0 + c.
     const int W = u.warm;
-    const int n_steps = nc + 2 * W;
+    const int n_steps = nc + W;
     // barrier intervals: -3, -2, -1, then 0 .. n_main - 1 (even)
     const int n_main = (n_steps + 1) & ~1;
     if (wave < 8) {
@@ -467,28 +467,30 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             solve(0);
             lds_barrier();  // interval -1
             if (W > 0) {
-                f32x4 unused[1];
+                // the transfer M (S, from the identity, V := 0) and the state
+                // from zero (Z) over the same warm-up records, each with the
+                // arithmetic of its own chain (pre_scan's M and B chains)
+                f32x4 Z[8][1];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) Z[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
                 for (int i = 0; i < W; ++i) {
                     gram(i + 2);
                     solve(i + 1);
-                    chain_step<1, false, false>(recs + ring_off((i % 4) * REC_BYTES), S, w8, lane, unused);
+                    // the role's work first: interleaved with the two states'
+                    // step it does not fit the registers
+                    __builtin_amdgcn_sched_barrier(0);
+                    chain_step_warm(recs + ring_off((i % 4) * REC_BYTES), S, Z, w8, lane);
                     lds_barrier();
                 }
                 const bool live = tile_nonzero(S);
                 if (lane == 0) a.spec_flags[((size_t)u.spec * H + h) * 8 + w8] = live ? 1 : 0;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) S[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int i = W; i < 2 * W; ++i) {
-                    gram(i + 2);
-                    solve(i + 1);
-                    chain_step<1, true, false>(recs + ring_off((i % 4) * REC_BYTES), S, w8, lane, unused);
-                    lds_barrier();
-                }
+                for (int t = 0; t < 8; ++t) S[t][0] = Z[t][0];
             }
-            for (int i = 2 * W; i < n_steps; ++i) {
+            for (int i = W; i < n_steps; ++i) {
                 gram(i + 2);
                 solve(i + 1);
-                step(i - 2 * W, i);
+                step(i - W, i);
                 lds_barrier();
             }
             for (int i = n_steps; i < n_main; ++i) lds_barrier();
@@ -512,15 +514,12 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                                           h / a.c.group, w8);
         // tokens of the sequence from that chunk on (sequences are < 2^31 tokens)
         const int rem = (int)(end - tok_k1);
-        // step i -> chunk from tok_k1 (the warm-up chunks come twice). The
-        // first warm-up pass (the transfer, V := 0, no output) reads neither
-        // q nor v, the second (the state from zero, no output) no q: their
-        // rows read as zeros, and no record field that pass uses depends on
-        // them.
+        // step i -> chunk i from tok_k1. The warm-up chunks form no output
+        // and read no q: its rows read as zeros, and no record field that
+        // the warm-up uses depends on them.
         auto load = [&](RowChunk& rc, int i) __attribute__((always_inline)) {
-            const int ci = i >= W ? i - W : i;
-            const int nr = chunk_rows(rem, ci);
-            k1_load_chunk<GVA>(rs, ci, nr, i >= 2 * W ? nr : 0, i >= W ? nr : 0, lo, rc);
+            const int nr = chunk_rows(rem, i);
+            k1_load_chunk<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, rc);
         };
         // the staging and scratch slots are compile-time constants: chunk c
         // uses slot c & 1 of both rings

@@ -104,6 +104,9 @@ struct PlannerConsts {
     // measured on MI355X (the shader clock falls as more CUs work)
     double alone_us, full_us;
     int split_warm;      // warm-up chunks of a warm-start segment
+    // a warm-up chunk's interval against a main chunk's: both states (the
+    // transfer and the state from zero) advance in it
+    double warm_cost;
 };
 
 PlannerConsts planner_consts() {
@@ -128,8 +131,14 @@ PlannerConsts planner_consts() {
     c.alone_us = env_double("KDA_FUSED_CHUNK_US_ALONE", 1.21);
     c.full_us = env_double("KDA_FUSED_CHUNK_US_FULL", 1.60);
     c.split_warm = (int)env_double("KDA_SPLIT_WARM_CHUNKS", 12.0);
+    // measured: 12 warm-up chunks add 25 us to a 128-chunk warm-start
+    // segment whose chunks take 1.33 us each
+    c.warm_cost = env_double("KDA_SPLIT_WARM_COST", 1.6);
     return c;
 }
+
+// The warm-up of W chunks in chunk intervals.
+int warm_work(int W, const PlannerConsts& pc) { return W > 0 ? (int)std::lround(pc.warm_cost * W) : 0; }
 
 // Interval of the fused kernel per chunk with `busy` of n_cus CUs working.
 double fused_interval_us(int busy, int n_cus, const PlannerConsts& pc) {
@@ -281,7 +290,7 @@ double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const Plan
 
 // Fused work of each unit when sequence i is split at chunk split[i]
 // (0: not split): the first segment runs split[i] chunks, the warm-start
-// segment the rest plus twice the warm-up.
+// segment the rest plus the warm-up's work.
 std::vector<int> split_work(const std::vector<int>& nch, const std::vector<int>& split, int H, int warm) {
     std::vector<int> w;
     w.reserve(nch.size() * H * 2);
@@ -290,7 +299,7 @@ std::vector<int> split_work(const std::vector<int>& nch, const std::vector<int>&
         for (int h = 0; h < H; ++h) {
             if (a > 0) {
                 w.push_back(a);
-                w.push_back(nch[i] - a + 2 * warm);
+                w.push_back(nch[i] - a + warm);
             } else {
                 w.push_back(nch[i]);
             }
@@ -315,8 +324,8 @@ double best_split(const std::vector<int>& nch, int H, int n_cus, const PlannerCo
     if ((long long)n * H > 4LL * n_cus || W < 1) return 1e300;
     const bool grouped = H <= n_cus && n_cus % H == 0;
     auto cost = [&](const std::vector<int>& sp) {
-        return grouped ? simulate_fused_us(split_work(nch, sp, 1, W), n_cus, pc, H)
-                       : simulate_fused_us(split_work(nch, sp, H, W), n_cus, pc);
+        return grouped ? simulate_fused_us(split_work(nch, sp, 1, warm_work(W, pc)), n_cus, pc, H)
+                       : simulate_fused_us(split_work(nch, sp, H, warm_work(W, pc)), n_cus, pc);
     };
     auto valid = [&](int i, int a) { return a >= W && nch[i] - a >= 1 && nch[i] >= 4 * W; };
     std::vector<int> order(n);
@@ -452,7 +461,7 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     if (force_split) {
         warm = force_warm;
         for (int i = 0; i < n_seqs; ++i) split[i] = force_split[i];
-        t_split = simulate_fused_us(split_work(nch, split, H, warm), n_cus, pc) + pc.launch_us;
+        t_split = simulate_fused_us(split_work(nch, split, H, warm_work(warm, pc)), n_cus, pc) + pc.launch_us;
     } else if (mode == KDA_CP_AUTO && seg == 0 && !materialize_env) {
         t_sim_serial = simulate_fused_us(split_work(nch, split, H, 0), n_cus, pc);
         std::vector<int> cand;
@@ -482,7 +491,7 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
             for (int i = 0; i < n_seqs; ++i)
                 for (int h = 0; h < H; ++h)
                     for (int c0 = 0; c0 < std::max(nch[i], 1); c0 += s)
-                        work.push_back(std::min(s, nch[i] - c0) + (c0 > 0 ? 2 * pc.split_warm : 0));
+                        work.push_back(std::min(s, nch[i] - c0) + (c0 > 0 ? warm_work(pc.split_warm, pc) : 0));
             const double t = simulate_fused_us(work, n_cus, pc) + 6 * pc.launch_us;
             if (t < t_wcp) { t_wcp = t; wseg = s; }
         }
@@ -561,9 +570,9 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
         std::stable_sort(p->alt_units.begin(), p->alt_units.end(),
                          [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
     }
-    // longest chains first (a warm-start segment runs its warm-up twice)
-    std::stable_sort(p->units.begin(), p->units.end(), [](const UnitDesc& a, const UnitDesc& b) {
-        return a.n_chunks + 2 * a.warm > b.n_chunks + 2 * b.warm;
+    // longest chains first (a warm-start segment's warm-up counted at its cost)
+    std::stable_sort(p->units.begin(), p->units.end(), [&](const UnitDesc& a, const UnitDesc& b) {
+        return a.n_chunks + warm_work(a.warm, pc) > b.n_chunks + warm_work(b.warm, pc);
     });
     std::stable_sort(p->prescan.begin(), p->prescan.end(),
                      [](const PrescanDesc& a, const PrescanDesc& b) { return a.n_chunks > b.n_chunks; });
@@ -619,6 +628,7 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     in.warm_cp_seg_chunks = wseg;
     in.n_warm_segments = n_wspec;
     in.est_warm_cp_us = t_wcp < 1e299 ? t_wcp : -1.0;
+    in.split_warm_work = in.split_warm_chunks > 0 ? warm_work(in.split_warm_chunks, pc) : 0;
     if (wseg > 0) {
         in.n_units = (int32_t)p->units.size();
         in.max_unit_chunks = 0;

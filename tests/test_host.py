@@ -146,7 +146,9 @@ def test_auto_plan_splits_the_tail_of_one_round(kda_lib):
     info = p.info()
     assert info["uses_cp"] == 0 and info["k1_materialized"] == 0
     assert info["n_split_seqs"] >= 1 and info["split_warm_chunks"] >= 1
-    W = info["split_warm_chunks"]
+    W, WW = info["split_warm_chunks"], info["split_warm_work"]
+    # the warm-up counted at its cost: W chunks, each advancing two states
+    assert W < WW < 2 * W
     by_seq = {}
     for u in p.units():
         by_seq.setdefault(u["seq"], []).append(u)
@@ -168,7 +170,7 @@ def test_auto_plan_splits_the_tail_of_one_round(kda_lib):
     # carry, end state and flags of each warm-start segment
     assert info["workspace_bytes"] >= n_split * 32 * 2 * 128 * 128 * 4
     # the warm-start segments run longest-first with their warm-up counted
-    work = [u["n_chunks"] + 2 * u["warm_chunks"] for u in p.units()]
+    work = [u["n_chunks"] + (WW if u["warm_chunks"] else 0) for u in p.units()]
     assert work == sorted(work, reverse=True)
 
 
@@ -215,8 +217,8 @@ def test_split_search_is_at_least_the_uniform_grid(kda_lib):
     H, n_cus = 32, 256
     p = kda.plan_host(cu_of(lengths), H=H, n_cus=n_cus, use_intracard_cp="auto")
     info = p.info()
-    W = info["split_warm_chunks"]
-    work = [u["n_chunks"] + 2 * u["warm_chunks"] for u in p.units()] * H
+    W, WW = info["split_warm_chunks"], info["split_warm_work"]
+    work = [u["n_chunks"] + (WW if u["warm_chunks"] else 0) for u in p.units()] * H
     t_plan = _fused_model_us(work, n_cus)
     assert abs(info["est_split_us"] - (t_plan + 5.0)) < 1e-3
     order = sorted(range(len(nch)), key=lambda i: -nch[i])
@@ -232,7 +234,7 @@ def test_split_search_is_at_least_the_uniform_grid(kda_lib):
                     ok = False
                     break
                 units[i] = a
-                units.append(nch[i] - a + 2 * W)
+                units.append(nch[i] - a + WW)
             if not ok:
                 break
             best_grid = min(best_grid, _fused_model_us(units * H, n_cus))
