@@ -104,8 +104,8 @@ struct PlannerConsts {
     // measured on MI355X (the shader clock falls as more CUs work)
     double alone_us, full_us;
     int split_warm;      // warm-up chunks of a warm-start segment
-    // a warm-up chunk's interval against a main chunk's: both states (the
-    // transfer and the state from zero) advance in it
+    // a warm-up chunk's cost in the schedule model, in main-chunk intervals
+    // (both states, the transfer and the state from zero, advance in it)
     double warm_cost;
 };
 
@@ -131,8 +131,10 @@ PlannerConsts planner_consts() {
     c.alone_us = env_double("KDA_FUSED_CHUNK_US_ALONE", 1.21);
     c.full_us = env_double("KDA_FUSED_CHUNK_US_FULL", 1.60);
     c.split_warm = (int)env_double("KDA_SPLIT_WARM_CHUNKS", 12.0);
-    // measured: 12 warm-up chunks add 25 us to a 128-chunk warm-start
-    // segment whose chunks take 1.33 us each
+    // fitted on the plans it yields: with 1.0, 1.2 and 1.6 the searched
+    // split plan of the 8-sequence, 32-head batch ran 0.2597, 0.2601 and
+    // 0.2545 ms (a warm-up interval itself takes about as long as a main
+    // one; the factor also stands for what the schedule model leaves out)
     c.warm_cost = env_double("KDA_SPLIT_WARM_COST", 1.6);
     return c;
 }
