@@ -190,8 +190,9 @@ kda_status kda_plan_prefill_segments(kda_ctx *ctx, const int32_t *cu_seqlens_hos
  * intracard-CP prefill" (cuLA pull request #103, description) without its
  * separate pre_scan and merge passes. The first segment runs from the initial
  * state. The second, a warm-start segment, first runs the warm_chunks chunks
- * before its start twice: as the transfer M from the identity with V := 0,
- * and as the state B from zero. Where every tile of M is exactly zero, B is
+ * before its start, advancing two states over them: the transfer M from the
+ * identity with V := 0, and the state B from zero. Where every tile of M is
+ * exactly zero, B is
  * its carry, exactly as the CP merge takes it; otherwise a fix-up launch
  * reruns the segment from the first segment's end state. Either way the
  * result equals the unsplit serial path's bit for bit wherever the CP

@@ -308,9 +308,9 @@ __device__ __forceinline__ RowStreams row_streams(const uint16_t* q, const uint1
 
 // Loads of chunk ci of the streams with nrows (0..16) valid rows. Each range
 // covers nrows whole token rows, so the lanes of rows past them, and every
-// lane when nrows = 0, read zeros and touch no memory. nrows_qv (0 or nrows)
-// is the rows of q and v alone: 0 where the chunk's use needs neither (a
-// warm-up pass), which then reads zeros for them. GVA = false: q/k heads are
+// lane when nrows = 0, read zeros and touch no memory. nrows_q and nrows_v
+// (0 or nrows) are the rows of q and of v alone: 0 where the chunk's use
+// needs no q (a warm-up chunk), which then reads zeros for it. GVA = false: q/k heads are
 // the value heads, and q/k share v's offsets and ranges.
 template <bool GVA>
 __device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,

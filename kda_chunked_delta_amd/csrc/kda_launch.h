@@ -25,8 +25,8 @@ struct UnitDesc {
     int32_t segment;     // segment index within the sequence
     int32_t n_segments;  // segments of the sequence
     // Warm-start segment (fused kernel only): the unit first runs the `warm`
-    // chunks before chunk0 twice, once as the transfer M (from the identity,
-    // V := 0) and once as the state from zero, and then continues from that
+    // chunks before chunk0, advancing over them both the transfer M (from the
+    // identity, V := 0) and the state from zero, and then continues from that
     // state as if it were its carry. spec >= 0 names its slot of
     // speculation flags and end state; out_slot >= 0 makes a unit write its
     // end state to carries[out_slot] as well.
