@@ -512,8 +512,11 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         const int64_t tok_k1 = tok0 - (int64_t)CH * W;
         const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok_k1, h,
                                           h / a.c.group, w8);
-        // tokens of the sequence from that chunk on (sequences are < 2^31 tokens)
-        const int rem = (int)(end - tok_k1);
+        // tokens of the unit from that chunk on (sequences are < 2^31 tokens):
+        // its rows end with its last chunk, so the loads issued ahead for the
+        // chunks after it (the loop's tail) read zeros and touch no memory
+        const int64_t unit_end = tok0 + (int64_t)CH * nc < end ? tok0 + (int64_t)CH * nc : end;
+        const int rem = (int)(unit_end - tok_k1);
         // step i -> chunk i from tok_k1. The warm-up chunks form no output
         // and read no q: its rows read as zeros, and no record field that
         // the warm-up uses depends on them.
