@@ -221,9 +221,13 @@ constexpr int BUF_POLICY = 0;
 // Row-coalesced K1 input path (both K1 kernels). A per-lane load of phase 1's
 // layout touches 16 rows with 32-64 bytes each and four wavefronts fetch
 // every line; measured, that runs at about a third of the rate of whole-row
-// loads. So wavefront w loads whole rows 2w and 2w + 1 of q, k, v and g
-// into registers (RowChunk), writes them to an LDS staging area, and after
-// the next barrier each wavefront reads its phase-1 fragments from there.
+// loads. So the wavefronts load whole rows into registers (RowChunk):
+// wavefront w rows 2w and 2w + 1 of v and g, and 16 bytes per lane of rows
+// 4w .. 4w + 3 of q (w < 4) or of k (w >= 4), so that a chunk takes 25 load
+// instructions rather than 33 (at full occupancy the loads' issue waits on
+// the memory system, and fewer, wider ones wait less). They write the rows
+// to an LDS staging area, and after the next barrier each wavefront reads
+// its phase-1 fragments from there.
 // Staging of one chunk: rows in order; the 16-byte granules of row r are
 // XOR-swizzled with r & 15, so both the row writes and phase 1's column
 // reads (16 rows, one granule each) spread over all banks.
@@ -247,15 +251,17 @@ __device__ __forceinline__ int stg_g_off(int r, int byte) {
 }
 
 struct RowChunk {
-    u32x2 q, k, v;  // 8 bytes of row 2w + (lane >> 5) at byte 8 (lane & 31)
+    u32x4 qk;       // wavefronts 0-3: 16 bytes of q row 4w + (lane >> 4) at byte 16 (lane & 15); 4-7: of k
+    u32x2 v;        // 8 bytes of row 2w + (lane >> 5) at byte 8 (lane & 31)
     f32x4 g;        // 16 bytes of that row of g at byte 16 (lane & 31)
     float b;        // beta of row lane & 15 (wavefront 0 only)
 };
 
 // Per-lane constants of the row path of wavefront w.
 struct RowLaneOffsets {
-    uint32_t qk, act, g, beta;  // global byte offsets from the chunk's first row (qk: of q and k)
+    uint32_t qk, act, g, beta;  // global byte offsets from the chunk's first row (qk: of q or k)
     int st_act, st_g;       // staging offsets of the row writes
+    int st_qk;              // staging offset of the q or k write (its tensor's area included)
     int rd_act, rd_g;       // staging offsets of phase 1's reads
 };
 
@@ -263,7 +269,9 @@ struct RowLaneOffsets {
 __device__ __forceinline__ RowLaneOffsets row_lane_offsets(int H, int Hk, int wave, int lane) {
     const int r = 2 * wave + (lane >> 5), gg = lane >> 4, m = lane & 15;
     RowLaneOffsets o;
-    o.qk = (uint32_t)r * (uint32_t)Hk * (D * 2) + (lane & 31) * 8;
+    const int r4 = 4 * (wave & 3) + (lane >> 4);
+    o.qk = (uint32_t)r4 * (uint32_t)Hk * (D * 2) + (lane & 15) * 16;
+    o.st_qk = (wave < 4 ? STG_Q : STG_K) + stg_act_off(r4, (lane & 15) * 16);
     o.act = (uint32_t)r * (uint32_t)H * (D * 2) + (lane & 31) * 8;
     o.g = (uint32_t)r * (uint32_t)H * (D * 4) + (lane & 31) * 16;
     o.beta = (uint32_t)m * (uint32_t)H * 4;
@@ -314,24 +322,21 @@ __device__ __forceinline__ RowStreams row_streams(const uint16_t* q, const uint1
 // the value heads, and q/k share v's offsets and ranges.
 template <bool GVA>
 __device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,
-                                              const RowLaneOffsets& lo, RowChunk& rc) {
+                                              const RowLaneOffsets& lo, RowChunk& rc, int wave) {
     const uint32_t n_act = (uint32_t)nrows * rs.st_act;
     const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
-    const uint8_t* qb = rs.q + c_act;
-    const uint8_t* kb = rs.k + c_act;
-    uint32_t n_qk = n_act, o_qk = lo.act, n_q = (uint32_t)nrows_q * rs.st_act;
+    size_t c_qk = c_act;
+    uint32_t st_qk = rs.st_act;
     if constexpr (GVA) {
-        const size_t c_qk = (size_t)ci * (CH * (size_t)rs.st_qk);
-        qb = rs.q + c_qk;
-        kb = rs.k + c_qk;
-        n_qk = (uint32_t)nrows * rs.st_qk;
-        n_q = (uint32_t)nrows_q * rs.st_qk;
-        o_qk = lo.qk;
+        c_qk = (size_t)ci * (CH * (size_t)rs.st_qk);
+        st_qk = rs.st_qk;
     }
-    rc.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(qb, n_q), (int)o_qk, 0,
-                                                                          BUF_POLICY));
-    rc.k = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(chunk_rsrc(kb, n_qk), (int)o_qk, 0,
-                                                                          BUF_POLICY));
+    // wavefronts 0-3 load q, 4-7 k (uniform per wavefront)
+    const bool is_q = wave < 4;
+    const uint8_t* qkb = (is_q ? rs.q : rs.k) + c_qk;
+    const uint32_t n_qk = (uint32_t)(is_q ? nrows_q : nrows) * st_qk;
+    rc.qk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(chunk_rsrc(qkb, n_qk), (int)lo.qk, 0,
+                                                                           BUF_POLICY));
     rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
         chunk_rsrc(rs.v + c_act, (uint32_t)nrows_v * rs.st_act), (int)lo.act, 0, BUF_POLICY));
     // g rows are twice as long as v rows, beta rows 1/64 of them
@@ -358,8 +363,7 @@ __device__ __forceinline__ int chunk_rows(int rem, int ci) {
 // betas; stg + STG_B where the layout keeps them together).
 __device__ __forceinline__ void k1_stage(const RowChunk& rc, int wave, int lane, const RowLaneOffsets& lo,
                                          uint8_t* stg, float* stg_b) {
-    *(u32x2*)(stg + STG_Q + lo.st_act) = rc.q;
-    *(u32x2*)(stg + STG_K + lo.st_act) = rc.k;
+    *(u32x4*)(stg + lo.st_qk) = rc.qk;
     *(u32x2*)(stg + STG_V + lo.st_act) = rc.v;
     *(f32x4*)(stg + STG_G + lo.st_g) = rc.g;
     if (wave == 0 && lane < 16) stg_b[lane] = rc.b;

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
                                           wave);
         RowChunk rc;
         const int nr = rows_of(tok0, end);
-        k1_load_chunk<GVA>(rs, 0, nr, nr, nr, lo, rc);
+        k1_load_chunk<GVA>(rs, 0, nr, nr, nr, lo, rc, wave);
         k1_stage(rc, wave, lane, lo, stg, (float*)(stg + STG_B));
         lds_barrier();
         RawChunk raw;
@@ -522,14 +522,14 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         // the warm-up uses depends on them.
         auto load = [&](RowChunk& rc, int i) __attribute__((always_inline)) {
             const int nr = chunk_rows(rem, i);
-            k1_load_chunk<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, rc);
+            k1_load_chunk<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, rc, w8);
         };
         // the staging and scratch slots are compile-time constants: chunk c
         // uses slot c & 1 of both rings
         auto stage = [&](RowChunk& rc, auto slot) __attribute__((always_inline)) {
             constexpr int S = decltype(slot)::value;
             // the register set is read only from here on (see below)
-            asm volatile("" : "+v"(rc.q), "+v"(rc.k), "+v"(rc.v), "+v"(rc.g), "+v"(rc.b));
+            asm volatile("" : "+v"(rc.qk), "+v"(rc.v), "+v"(rc.g), "+v"(rc.b));
             k1_stage(rc, w8, lane, lo, stgs + S * STG_NB, stg_betas + 16 * S);
         };
         // interval i works on chunk i + 3 (staging and scratch slot R = (i + 3) & 1)
