@@ -379,6 +379,75 @@ __device__ __forceinline__ void k1_read_staged(const uint8_t* stg, const float* 
     raw.b = stg_b[lane & 15];
 }
 
+// The fused kernel's row path: q, k and v as above, staged through registers
+// into slots of FSTG_NB bytes; g goes from memory straight into a ring of
+// LDS slots of GRING_BYTES (one per chunk, the staged layout of STG_G) by
+// direct-to-LDS buffer loads, so the K1 wavefronts neither hold nor stage
+// it. Lane l of wavefront w loads the 16-byte granule that the staged
+// layout puts at slot l & 31 of row 2w + (l >> 5): a direct-to-LDS load
+// writes lane l's 16 bytes at the wavefront's LDS base + 16 l (lanes
+// past the descriptor's range write zeros).
+constexpr int FSTG_NB = STG_G;      // q, k, v [16][256 B] each
+constexpr int GRING_BYTES = 8192;   // g [16][512 B]
+
+struct RowChunkF {
+    u32x4 qk;  // as RowChunk
+    u32x2 v;
+    float b;
+};
+
+// Global byte offset (from the chunk's first g row) of lane `lane`'s
+// direct-to-LDS g granule in wavefront w.
+__device__ __forceinline__ uint32_t g_dma_off(int H, int wave, int lane) {
+    const int r = 2 * wave + (lane >> 5), sl = lane & 31;
+    const int c = (sl & 16) | ((sl ^ r) & 15);
+    return (uint32_t)r * (uint32_t)H * (D * 4) + c * 16;
+}
+
+template <bool GVA>
+__device__ __forceinline__ void k1_load_chunk_f(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,
+                                                const RowLaneOffsets& lo, uint32_t g_off, RowChunkF& rc, int wave,
+                                                uint8_t* gslot) {
+    const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
+    // g first: the compiler's wait for this batch's register loads then
+    // covers it too (loads complete in order)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        chunk_rsrc(rs.g + 2 * c_act, (uint32_t)nrows * rs.st_g),
+        (__attribute__((address_space(3))) void*)(gslot + 2 * wave * (D * 4)), 16, (int)g_off, 0, 0, BUF_POLICY);
+    __builtin_amdgcn_sched_barrier(0);
+    size_t c_qk = c_act;
+    uint32_t st_qk = rs.st_act;
+    if constexpr (GVA) {
+        c_qk = (size_t)ci * (CH * (size_t)rs.st_qk);
+        st_qk = rs.st_qk;
+    }
+    const bool is_q = wave < 4;
+    const uint8_t* qkb = (is_q ? rs.q : rs.k) + c_qk;
+    const uint32_t n_qk = (uint32_t)(is_q ? nrows_q : nrows) * st_qk;
+    rc.qk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(chunk_rsrc(qkb, n_qk), (int)lo.qk, 0,
+                                                                           BUF_POLICY));
+    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        chunk_rsrc(rs.v + c_act, (uint32_t)nrows_v * rs.st_act), (int)lo.act, 0, BUF_POLICY));
+    rc.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        chunk_rsrc(rs.b + (c_act >> 6), (uint32_t)nrows * rs.st_b), (int)lo.beta, 0, BUF_POLICY));
+}
+
+__device__ __forceinline__ void k1_stage_f(const RowChunkF& rc, int wave, int lane, const RowLaneOffsets& lo,
+                                           uint8_t* stg, float* stg_b) {
+    *(u32x4*)(stg + lo.st_qk) = rc.qk;
+    *(u32x2*)(stg + STG_V + lo.st_act) = rc.v;
+    if (wave == 0 && lane < 16) stg_b[lane] = rc.b;
+}
+
+__device__ __forceinline__ void k1_read_staged_f(const uint8_t* stg, const float* stg_b, const uint8_t* gslot,
+                                                 int lane, const RowLaneOffsets& lo, RawChunk& raw) {
+    raw.q = *(const u32x2*)(stg + STG_Q + lo.rd_act);
+    raw.k = *(const u32x2*)(stg + STG_K + lo.rd_act);
+    raw.v = *(const u32x2*)(stg + STG_V + lo.rd_act);
+    raw.g = *(const f32x4*)(gslot + lo.rd_g);
+    raw.b = stg_b[lane & 15];
+}
+
 // Largest |G| (log2 units) for which phase 1 factors the decays about the
 // chunk start: exp(G) and exp(-G) are then normal fp32 and bf16 values, and
 // the unmasked Gram terms exp(G_r - G_i) (i <= r) are at most 1.

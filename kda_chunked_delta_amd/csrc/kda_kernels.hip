@@ -312,26 +312,32 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 //     4w..4w+3 of T' of chunk i+1 from the shared L^T; wavefront WAVE_QK
 //     forms A_qk of chunk i+2 and L of chunk i+2, once, into the shared L^T;
 //   - wavefronts 8 + w run K1 phase 1 of chunk i+3 (key channels and value
-//     columns 16w..16w+15) from the staged rows, stage the rows of chunk i+4
-//     that they loaded two intervals earlier, and issue the row loads of
-//     chunk i+6 (rows 2w, 2w+1; into the register set just staged).
-// Each SIMD holds two state wavefronts and two K1 wavefronts. Records live in
-// a 4-deep LDS ring; K1 scratch, the shared L^T and the staged rows in 2-deep
-// ones. The staged rows and the K1 scratch (without their betas) fill the
-// first 64 KiB, so that every K1 access to them is a per-lane base plus an
-// immediate offset; the K1 loop is unrolled over the two slots of those
-// rings. Both roles run three start-up intervals and then the same even
+//     columns 16w..16w+15) from the staged rows, stage the q, k and v rows of
+//     chunk i+4 that they loaded two intervals earlier, and issue the row
+//     loads of chunk i+6 (into the register set just staged; its g rows go
+//     straight to their LDS slot).
+// Each SIMD holds two state wavefronts and two K1 wavefronts. Records and the
+// staged g rows live in 4-deep LDS rings (a g slot is written by the loads
+// issued three intervals before it is read, and read once); K1 scratch, the
+// shared L^T and the staged q, k, v rows in 2-deep ones. The staged q, k, v
+// rows and the K1 scratch (without their betas) lie in the first 64 KiB, so
+// that every K1 access to them is a per-lane base plus an immediate offset;
+// the K1 loop is unrolled over the two slots of those rings. A g slot is
+// complete once the compiler's wait for the register loads issued after it
+// in the same batch returns (loads complete in order), which comes before
+// the barrier that precedes its read. Both roles run three start-up intervals and then the same even
 // number of intervals, after one start-up barrier: the trailing K1 work on
 // chunks past the end reads zeros (a buffer load of a chunk with no rows
 // touches no memory) and fills slots nobody reads, so the K1 loop body is
 // unconditional and the compiler's wait for a register set covers only that
 // set's loads.
 // ---------------------------------------------------------------------------
-constexpr int F_STG = 0;                              // 2 staged chunks (rows)
-constexpr int F_SCR = F_STG + 2 * STG_NB;             // 2 K1 scratch areas (Gram factors)
+constexpr int F_STG = 0;                              // 2 staged chunks (q, k, v rows)
+constexpr int F_SCR = F_STG + 2 * FSTG_NB;            // 2 K1 scratch areas (Gram factors)
 constexpr int F_LB = F_SCR + 2 * K1_NB;               // 2 shared L^T + beta
 constexpr int F_BETA = F_LB + 2 * LB_BYTES;           // betas: 2 staged [16], 2 scratch [16]
-constexpr int F_REC = (F_BETA + 256 + 255) / 256 * 256;  // 4 records
+constexpr int F_GR = (F_BETA + 256 + 255) / 256 * 256;  // 4 staged g chunks (direct-to-LDS)
+constexpr int F_REC = F_GR + 4 * GRING_BYTES;         // 4 records
 constexpr int FUSED_LDS = F_REC + 4 * REC_BYTES;
 static_assert(F_LB <= 65536, "the K1 rings fit the immediate-offset range of LDS instructions");
 static_assert(FUSED_LDS <= 160 * 1024, "fused kernel LDS");
@@ -360,6 +366,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
     uint8_t* scrs = smem + F_SCR;              // 2 K1 scratch areas
     uint8_t* lbs = smem + F_LB;                // 2 shared L^T + beta
     uint8_t* stgs = smem + F_STG;              // 2 staged chunks
+    uint8_t* grs = smem + F_GR;                // 4 staged g chunks
     float* stg_betas = (float*)(smem + F_BETA);          // [2][16]
     float* scr_betas = (float*)(smem + F_BETA + 128);    // [2][16]
     const int H = a.c.H;
@@ -506,8 +513,9 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         }
     } else {
         // K1 wavefronts: chunk c is loaded into register set c & 1
-        RowChunk r0, r1;
+        RowChunkF r0, r1;
         const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, w8, lane);
+        const uint32_t g_off = g_dma_off(H, w8, lane);
         // rows from the first chunk the unit runs (its warm-up, if any)
         const int64_t tok_k1 = tok0 - (int64_t)CH * W;
         const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok_k1, h,
@@ -520,28 +528,28 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         // step i -> chunk i from tok_k1. The warm-up chunks form no output
         // and read no q: its rows read as zeros, and no record field that
         // the warm-up uses depends on them.
-        auto load = [&](RowChunk& rc, int i) __attribute__((always_inline)) {
+        auto load = [&](RowChunkF& rc, int i) __attribute__((always_inline)) {
             const int nr = chunk_rows(rem, i);
-            k1_load_chunk<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, rc, w8);
+            k1_load_chunk_f<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, g_off, rc, w8, grs + (i & 3) * GRING_BYTES);
         };
         // the staging and scratch slots are compile-time constants: chunk c
         // uses slot c & 1 of both rings
-        auto stage = [&](RowChunk& rc, auto slot) __attribute__((always_inline)) {
+        auto stage = [&](RowChunkF& rc, auto slot) __attribute__((always_inline)) {
             constexpr int S = decltype(slot)::value;
             // the register set is read only from here on (see below)
-            asm volatile("" : "+v"(rc.qk), "+v"(rc.v), "+v"(rc.g), "+v"(rc.b));
-            k1_stage(rc, w8, lane, lo, stgs + S * STG_NB, stg_betas + 16 * S);
+            asm volatile("" : "+v"(rc.qk), "+v"(rc.v), "+v"(rc.b));
+            k1_stage_f(rc, w8, lane, lo, stgs + S * FSTG_NB, stg_betas + 16 * S);
         };
         // interval i works on chunk i + 3 (staging and scratch slot R = (i + 3) & 1)
         // and stages chunk i + 4 (slot 1 - R)
-        auto interval = [&](int i, RowChunk& rc, auto rslot) __attribute__((always_inline)) {
+        auto interval = [&](int i, RowChunkF& rc, auto rslot) __attribute__((always_inline)) {
             constexpr int R = decltype(rslot)::value;
             // Phase 1 reads LDS only after the barrier that ends the previous
             // interval, and the staging of rc waits for its loads there too:
             // the empty redefinitions keep the compiler from hoisting
             // either above that barrier.
             RawChunk raw;
-            k1_read_staged(stgs + R * STG_NB, stg_betas + 16 * R, lane, lo, raw);
+            k1_read_staged_f(stgs + R * FSTG_NB, stg_betas + 16 * R, grs + ((i + 3) & 3) * GRING_BYTES, lane, lo, raw);
             // the record slot as an opaque uniform offset, so every record
             // access of the phase is one per-lane base plus immediate offsets
             k1_phase1(raw, w8, lane, recs + ring_off(((i + 3) % 4) * REC_BYTES), scrs + R * K1_NB,
