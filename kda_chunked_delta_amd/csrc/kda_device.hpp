@@ -404,17 +404,23 @@ __device__ __forceinline__ uint32_t g_dma_off(int H, int wave, int lane) {
     return (uint32_t)r * (uint32_t)H * (D * 4) + c * 16;
 }
 
-template <bool GVA>
-__device__ __forceinline__ void k1_load_chunk_f(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,
-                                                const RowLaneOffsets& lo, uint32_t g_off, RowChunkF& rc, int wave,
-                                                uint8_t* gslot) {
+// The g rows of chunk ci into their LDS slot. Issued before the chunk's
+// register loads (k1_load_rows_f), so that the compiler's wait for those
+// also covers it (loads complete in order).
+__device__ __forceinline__ void k1_load_g_dma(const RowStreams& rs, int ci, int nrows, uint32_t g_off, int wave,
+                                              uint8_t* gslot) {
     const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
-    // g first: the compiler's wait for this batch's register loads then
-    // covers it too (loads complete in order)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         chunk_rsrc(rs.g + 2 * c_act, (uint32_t)nrows * rs.st_g),
         (__attribute__((address_space(3))) void*)(gslot + 2 * wave * (D * 4)), 16, (int)g_off, 0, 0, BUF_POLICY);
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// The q or k, v and beta rows of chunk ci into a register set.
+template <bool GVA>
+__device__ __forceinline__ void k1_load_rows_f(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,
+                                               const RowLaneOffsets& lo, RowChunkF& rc, int wave) {
+    const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
     size_t c_qk = c_act;
     uint32_t st_qk = rs.st_act;
     if constexpr (GVA) {

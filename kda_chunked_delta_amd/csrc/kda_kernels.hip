@@ -311,11 +311,12 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 //     chunk i and store that chunk's output. Wavefronts 0..3 also form rows
 //     4w..4w+3 of T' of chunk i+1 from the shared L^T; wavefront WAVE_QK
 //     forms A_qk of chunk i+2 and L of chunk i+2, once, into the shared L^T;
-//   - wavefronts 8 + w run K1 phase 1 of chunk i+3 (key channels and value
-//     columns 16w..16w+15) from the staged rows, stage the q, k and v rows of
-//     chunk i+4 that they loaded two intervals earlier, and issue the row
-//     loads of chunk i+6 (into the register set just staged; its g rows go
-//     straight to their LDS slot).
+//   - wavefronts 8 + w issue the direct-to-LDS load of the g rows of chunk
+//     i+6, run K1 phase 1 of chunk i+3 (key channels and value columns
+//     16w..16w+15) from the staged rows, stage the q, k and v rows of chunk
+//     i+4 that they loaded two intervals earlier, and issue the register
+//     loads of those rows of chunk i+6 (into the register set just staged).
+//     Issuing the g load first spreads the loads over the interval.
 // Each SIMD holds two state wavefronts and two K1 wavefronts. Records and the
 // staged g rows live in 4-deep LDS rings (a g slot is written by the loads
 // issued three intervals before it is read, and read once); K1 scratch, the
@@ -323,10 +324,10 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 // rows and the K1 scratch (without their betas) lie in the first 64 KiB, so
 // that every K1 access to them is a per-lane base plus an immediate offset;
 // the K1 loop is unrolled over the two slots of those rings. A g slot is
-// complete once the compiler's wait for the register loads issued after it
-// in the same batch returns (loads complete in order), which comes before
-// the barrier that precedes its read. Both roles run three start-up intervals and then the same even
-// number of intervals, after one start-up barrier: the trailing K1 work on
+// complete once the compiler's wait for the same chunk's register loads,
+// issued after it, returns (loads complete in order), which comes before
+// the barrier that precedes its read. Both roles run three start-up
+// intervals and then the same even number of intervals, after one start-up barrier: the trailing K1 work on
 // chunks past the end reads zeros (a buffer load of a chunk with no rows
 // touches no memory) and fills slots nobody reads, so the K1 loop body is
 // unconditional and the compiler's wait for a register set covers only that
@@ -528,9 +529,16 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         // step i -> chunk i from tok_k1. The warm-up chunks form no output
         // and read no q: its rows read as zeros, and no record field that
         // the warm-up uses depends on them.
-        auto load = [&](RowChunkF& rc, int i) __attribute__((always_inline)) {
+        auto load_g = [&](int i) __attribute__((always_inline)) {
+            k1_load_g_dma(rs, i, chunk_rows(rem, i), g_off, w8, grs + (i & 3) * GRING_BYTES);
+        };
+        auto load_rows = [&](RowChunkF& rc, int i) __attribute__((always_inline)) {
             const int nr = chunk_rows(rem, i);
-            k1_load_chunk_f<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, g_off, rc, w8, grs + (i & 3) * GRING_BYTES);
+            k1_load_rows_f<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, rc, w8);
+        };
+        auto load = [&](RowChunkF& rc, int i) __attribute__((always_inline)) {
+            load_g(i);
+            load_rows(rc, i);
         };
         // the staging and scratch slots are compile-time constants: chunk c
         // uses slot c & 1 of both rings
@@ -548,6 +556,9 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             // interval, and the staging of rc waits for its loads there too:
             // the empty redefinitions keep the compiler from hoisting
             // either above that barrier.
+            // the g rows of chunk i + 6 first: their slot was last read in
+            // the previous interval
+            load_g(i + 6);
             RawChunk raw;
             k1_read_staged_f(stgs + R * FSTG_NB, stg_betas + 16 * R, grs + ((i + 3) & 3) * GRING_BYTES, lane, lo, raw);
             // the record slot as an opaque uniform offset, so every record
@@ -555,7 +566,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             k1_phase1(raw, w8, lane, recs + ring_off(((i + 3) % 4) * REC_BYTES), scrs + R * K1_NB,
                       scr_betas + 16 * R);
             stage(rc, std::integral_constant<int, 1 - R>{});
-            load(rc, i + 6);
+            load_rows(rc, i + 6);
             lds_barrier();
         };
         using Z = std::integral_constant<int, 0>;
