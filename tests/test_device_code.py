@@ -1,6 +1,6 @@
 """Checks of the compiled gfx950 device code (no GPU needed; needs hipcc).
 
-Regressions these guard against, both found in this library's own kernels:
+Regressions these guard against, found in this library's own kernels:
   * an inline-asm block that writes SCC while the compiler keeps SCC live
     across it: a 64-bit address add split around the block (s_add_u32 before,
     s_addc_u32 after) loses its carry and the load faults; every block that
@@ -12,6 +12,9 @@ Regressions these guard against, both found in this library's own kernels:
     product chained onto a 16x16x32 accumulator lost a contribution): every
     MFMA's accumulator is last written by an MFMA of its own shape, or by
     something other than an MFMA.
+It also checks two properties the fused kernel's speed or correctness
+rests on: the order of its direct-to-LDS g loads against the register
+loads whose wait covers them, and no spill reloads inside its output loops.
 """
 import os
 import re
@@ -169,3 +172,72 @@ def test_mfma_shape_check_catches_a_planted_chain(tmp_path):
                    stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
     found, checked = mfma_shape_changes(dst.read_text().split("\n"))
     assert checked == 1 and len(found) == 1 and "16x16x16" in found[0][1] and "16x16x32" in found[0][3]
+
+
+def _function_body(lines, name_prefix):
+    """Lines of the first function whose symbol starts with name_prefix."""
+    start = next(i for i, l in enumerate(lines) if re.match(re.escape(name_prefix) + r"\w*:", l))
+    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    return lines[start:end + 1]
+
+
+def test_direct_to_lds_g_loads_precede_their_register_loads(device_asm):
+    """The fused kernel's K1 wavefronts load each chunk's g rows straight into
+    LDS and rely on the compiler's wait for the same chunk's register loads,
+    issued later, to cover them (loads complete in order). In the start-up
+    batches each chunk's g load opens its batch; in the chunk loop it is
+    issued at the start of an interval and the register loads at its end,
+    and no register load may have moved above it within the interval."""
+    body = _function_body(device_asm["kda_kernels.hip"], "_ZN3kda9kda_fusedILb0EEEvNS_6K2ArgsE")
+    blocks, cur = [], []
+    for line in body:
+        if re.match(r"^\.LBB\d+_\d+:", line) or re.match(r"^\s*s_(cbranch_\w+|branch)\b", line):
+            blocks.append(cur)
+            cur = []
+        elif "s_barrier" in line:
+            cur.append("barrier")
+        elif "buffer_load" in line:
+            cur.append("lds" if re.search(r"\blds\b", line) else "reg")
+    blocks.append(cur)
+    # barrier-delimited pieces (within a basic block): one interval's loads
+    pieces = []
+    for b in blocks:
+        piece = []
+        for e in b + ["barrier"]:
+            if e == "barrier":
+                if piece:
+                    pieces.append(piece)
+                piece = []
+            else:
+                piece.append(e)
+    with_dma = [p for p in pieces if "lds" in p]
+    assert sum(p.count("lds") for p in with_dma) >= 4, "direct-to-LDS loads not found"
+    # the start-up piece issues whole batches, each opening with its g load
+    start = with_dma[0]
+    assert start[0] == "lds" and all(start[i + 1] == "reg" for i, e in enumerate(start[:-1]) if e == "lds"), start
+    # in the chunk loop each interval issues the g load before any register load
+    for p in with_dma[1:]:
+        assert "reg" not in p[:p.index("lds")], p
+
+
+def test_fused_chunk_loops_reload_no_spills(device_asm):
+    """Spill reloads (scratch loads) inside the fused kernel's chunk loops
+    that store output cost a memory round trip per chunk (one such reload in
+    a Gram wavefront's loop made the 16 x 8192, 64-head batch 3% slower)."""
+    body = _function_body(device_asm["kda_kernels.hip"], "_ZN3kda9kda_fusedILb0EEEvNS_6K2ArgsE")
+    heads = {}
+    for i, line in enumerate(body):
+        m = re.match(r"^(\.LBB\d+_\d+):.*Loop Header", line)
+        if m:
+            heads[m.group(1)] = i
+    checked = 0
+    for label, h in heads.items():
+        ends = [i for i, l in enumerate(body) if re.search(r"s_(cbranch_\w+|branch)\s+" + re.escape(label) + r"\s*$", l)]
+        if not ends or max(ends) < h:
+            continue
+        loop = body[h:max(ends) + 1]
+        if not any("buffer_store" in l or "global_store" in l for l in loop):
+            continue
+        checked += 1
+        assert not any("scratch_load" in l for l in loop), "spill reload in an output loop at line %d" % h
+    assert checked >= 3
