@@ -224,10 +224,10 @@ constexpr int BUF_POLICY = 0;
 // loads. So the wavefronts load whole rows into registers (RowChunk):
 // wavefront w rows 2w and 2w + 1 of v and g, and 16 bytes per lane of rows
 // 4w .. 4w + 3 of q (w < 4) or of k (w >= 4), so that a chunk takes 25 load
-// instructions rather than 33 (at full occupancy the loads' issue waits on
-// the memory system, and fewer, wider ones wait less). They write the rows
-// to an LDS staging area, and after the next barrier each wavefront reads
-// its phase-1 fragments from there.
+// instructions rather than 33 (measured 1-1.5% faster than two rows per
+// wavefront of each). They write the rows to an LDS staging area, and
+// after the next barrier each wavefront reads its phase-1 fragments from
+// there. (The fused kernel loads g straight into LDS instead.)
 // Staging of one chunk: rows in order; the 16-byte granules of row r are
 // XOR-swizzled with r & 15, so both the row writes and phase 1's column
 // reads (16 rows, one granule each) spread over all banks.
