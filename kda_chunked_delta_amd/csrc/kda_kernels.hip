@@ -339,17 +339,20 @@ constexpr int F_LB = F_SCR + 2 * K1_NB;               // 2 shared L^T + beta
 constexpr int F_BETA = F_LB + 2 * LB_BYTES;           // betas: 2 staged [16], 2 scratch [16]
 constexpr int F_GR = (F_BETA + 256 + 255) / 256 * 256;  // 4 staged g chunks (direct-to-LDS)
 constexpr int F_REC = F_GR + 4 * GRING_BYTES;         // 4 records
-constexpr int FUSED_LDS = F_REC + 4 * REC_BYTES;
+constexpr int F_MFL = F_REC + 4 * REC_BYTES;          // K1 pass: flags of the 8 transfer tiles
+constexpr int FUSED_LDS = F_MFL + 32;
 static_assert(F_LB <= 65536, "the K1 rings fit the immediate-offset range of LDS instructions");
 static_assert(FUSED_LDS <= 160 * 1024, "fused kernel LDS");
 
 // GVA: q/k heads differ from the value heads (value head h reads q/k head
 // h / group); the plain instance keeps the q/k loads on v's offsets.
-// BSUM: the K1 pass of the segmented CP pipeline. Every chunk record formed
-// in LDS is also written to the workspace (records [H][total_chunks]), and
-// the state wavefronts of a unit with out_slot >= 0 run the state update
-// from zero without output, whose end state (the segment's B summary) goes
-// to carries[out_slot] (the host points carries at the summaries).
+// BSUM: the K1 pass of the segmented CP pipeline, with pre_scan. Every chunk
+// record formed in LDS is also written to the workspace (records
+// [H][total_chunks]), and the state wavefronts of a unit with out_slot >= 0
+// run, without output, the state update from zero, whose end state (the
+// segment's B summary) goes to carries[out_slot] (the host points carries at
+// the summaries), and beside it the update from the identity with V := 0
+// (the transfer M, to m_out[out_slot]) until it vanishes.
 template <bool GVA, bool BSUM>
 __device__ __forceinline__ void fused_body(const K2Args& a) {
     if constexpr (BSUM) {
@@ -418,7 +421,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
     // are chunks chunk0-W .. chunk0-1, over which the state wavefronts form
     // the transfer and the state from zero side by side, and step W + c is
     // chunk chunk0 + c.
-    const int W = u.warm;
+    const int W = BSUM ? 0 : u.warm;  // the K1 pass of the pipeline has no warm-start units
     const int n_steps = nc + W;
     // barrier intervals: -3, -2, -1, then 0 .. n_main - 1 (even)
     const int n_main = (n_steps + 1) & ~1;
@@ -432,17 +435,31 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         if (W == 0 && u.spec >= 0 && !a.fixup && lane == 0) a.spec_flags[((size_t)u.spec * H + h) * 8 + w8] = 0;
         lds_barrier();  // start-up: the first chunk is staged
         const int rem = (int)(end - tok0);
-        auto step = [&](int c, int i) __attribute__((always_inline)) {
+        // K1 pass: whether this wavefront's tile of the transfer lives, and
+        // every tile's flag (written when its wavefront leaves the transfer)
+        bool m_nz = true;
+        volatile int32_t* m_flags = (volatile int32_t*)(smem + F_MFL);
+        // the record of chunk c is complete in its interval (its T' was
+        // formed in the previous one) and its slot is overwritten after the
+        // next barrier: the state wavefronts other than WAVE_QK (whose phase-2
+        // role is the heaviest) copy it out then, two 16-byte vectors per
+        // thread
+        static_assert(REC_HBM_VEC == 2 * 7 * 64 && WAVE_QK < 8, "seven wavefronts copy a record out");
+        auto copy_out = [&](int c, const uint8_t* rec) __attribute__((always_inline)) {
+            u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0 + c) * REC_HBM_BYTES);
+            const u32x4* src = (const u32x4*)rec;
+            const int v0 = (w8 < WAVE_QK ? w8 : w8 - 1) * 64 + lane, v1 = v0 + 7 * 64;
+            const u32x4 x0 = src[rec_lds_vec(v0)];
+            const u32x4 x1 = src[rec_lds_vec(v1)];
+            dst[v0] = x0;
+            dst[v1] = x1;
+        };
+        auto step = [&](int c, int i, auto role) __attribute__((always_inline)) {
             const uint8_t* rec = recs + ring_off((i % 4) * REC_BYTES);
             if constexpr (BSUM) {
                 f32x4 unused[1];
                 if (u.out_slot >= 0) chain_step<1, true, false>(rec, S, w8, lane, unused);
-                // the record is complete in this interval (its T' was formed in
-                // the previous one) and its slot is overwritten after the next
-                // barrier: the state wavefronts copy it out now
-                u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0 + c) * REC_HBM_BYTES);
-                const u32x4* src = (const u32x4*)rec;
-                for (int v = (int)threadIdx.x; v < REC_HBM_VEC; v += 512) dst[v] = src[rec_lds_vec(v)];
+                if constexpr (decltype(role)::value != 2) copy_out(c, rec);
             } else {
                 f32x4 oacc[1];
                 chain_step<1, true, true>(rec, S, w8, lane, oacc);
@@ -495,10 +512,45 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) S[t][0] = Z[t][0];
             }
-            for (int i = W; i < n_steps; ++i) {
+            int i0 = W;
+            if constexpr (BSUM) {
+                if (u.out_slot >= 0 && a.m_out) {
+                    // the segment's transfer M (from the identity, V := 0)
+                    // beside its B summary, over the same records, each with
+                    // the arithmetic of its own chain. A tile of M that is
+                    // exactly zero stays zero (its columns evolve on their
+                    // own), so every 4 chunks a wavefront whose tile vanished
+                    // leaves M and continues with B alone.
+                    f32x4 M[8][1];
+                    identity_state(M, w8, gg, m);
+                    bool live = true;
+                    while (live && i0 < n_steps) {
+                        gram(i0 + 2);
+                        solve(i0 + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        const uint8_t* rec = recs + ring_off((i0 % 4) * REC_BYTES);
+                        chain_step_warm(rec, M, S, w8, lane);
+                        if constexpr (R != 2) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            copy_out(i0 - W, rec);
+                        }
+                        lds_barrier();
+                        ++i0;
+                        if ((i0 & 3) == 0) live = tile_nonzero(M);
+                    }
+                    const bool nz = tile_nonzero(M);
+                    if (lane == 0) {
+                        a.m_live_out[((size_t)u.out_slot * H + h) * 8 + w8] = nz ? 1 : 0;
+                        m_flags[w8] = nz ? 1 : 0;
+                    }
+                    m_nz = nz;
+                    if (nz) store_state(a.m_out + ((size_t)u.out_slot * H + h) * (D * D), M, w8, gg, m);
+                }
+            }
+            for (int i = i0; i < n_steps; ++i) {
                 gram(i + 2);
                 solve(i + 1);
-                step(i - W, i);
+                step(i - W, i, role);
                 lds_barrier();
             }
             for (int i = n_steps; i < n_main; ++i) lds_barrier();
@@ -506,6 +558,23 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         if (w8 < N_WAVE_T) run(std::integral_constant<int, 1>{});
         else if (w8 == WAVE_QK) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 0>{});
+        if constexpr (BSUM) {
+            if (u.out_slot >= 0 && a.m_out) {
+                // the merge reads every tile of M once any flag is set: a tile
+                // that vanished is stored as zeros when another one lives
+                lds_barrier();  // the last, after every tile's flag
+                int any = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) any |= m_flags[j];
+                if (!m_nz && any) {
+                    float* mo = a.m_out + ((size_t)u.out_slot * H + h) * (D * D);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+#pragma unroll
+                        for (int vv = 0; vv < 4; ++vv) mo[(16 * t + 4 * gg + vv) * D + 16 * w8 + m] = 0.f;
+                }
+            }
+        }
         if (u.out_slot >= 0) store_state(a.carries + ((size_t)u.out_slot * H + h) * (D * D), S, w8, gg, m);
         if (u.spec >= 0 && !a.fixup && !a.spec_final_direct) {
             if (u.write_final) store_state(a.spec_states + ((size_t)u.spec * H + h) * (D * D), S, w8, gg, m);
@@ -583,6 +652,9 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             interval(i, r0, O{});
             interval(i + 1, r1, Z{});
         }
+        if constexpr (BSUM) {
+            if (u.out_slot >= 0 && a.m_out) lds_barrier();  // the transfer flags' barrier
+        }
     }
 }
 
@@ -598,8 +670,8 @@ __global__ __launch_bounds__(1024) void kda_fused_fixup(K2Args a) {
     fused_body<GVA, false>(a);
 }
 
-// K1 of the segmented CP pipeline with the B half of pre_scan: the records of
-// every chunk, written once, and each segment's B summary.
+// K1 of the segmented CP pipeline with pre_scan: the records of every chunk,
+// written once, and each segment's B and M summaries.
 template <bool GVA>
 __global__ __launch_bounds__(1024) void kda_k1_bsum(K2Args a) {
     fused_body<GVA, true>(a);
@@ -632,101 +704,6 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
         store_output(a, h, tok0 + (int64_t)CH * ci, chunk_rows(rem, ci), oacc[0], wave, gg, m);
     });
     store_unit_state(a, u, h, S, wave, gg, m);
-}
-
-// ---------------------------------------------------------------------------
-// CP pre_scan, transfer half: one workgroup of 8 wavefronts per (segment,
-// head) runs K2's state update from S = I with V := 0 over the segment's
-// records (the transfer M; wavefront w holds key columns 16w..16w+15). The B
-// half (the update from S = 0) runs in the K1 launch, on the records it forms.
-// A tile of M that is exactly zero stays zero (its columns evolve
-// independently). Every 4 chunks the workgroup checks its tiles and stops
-// once all are zero: under decay the transfer underflows within a few chunks,
-// and the merge then takes B as the carry without reading M. Only the fields
-// the update reads (X, Kt, exp(G_C), T') are fetched.
-// ---------------------------------------------------------------------------
-struct TransferFetch {
-    // 16-byte vectors of an HBM record: X and Kt^T [256, 768), exp(G_C) and
-    // T' [800, 896) (LDS [1056, 1152))
-    static constexpr int NV = 608;
-    static constexpr int N = (NV + 511) / 512;
-    u32x4 r[N];
-    __device__ __forceinline__ static int index(int i) { return i < 512 ? 256 + i : 800 + (i - 512); }
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ src) {
-        const u32x4* s = (const u32x4*)src;
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            const int i = threadIdx.x + j * 512;
-            if (i < NV) r[j] = __builtin_nontemporal_load(s + index(i));
-        }
-    }
-    __device__ __forceinline__ void store(uint8_t* dst) const {
-        u32x4* d = (u32x4*)dst;
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            const int i = threadIdx.x + j * 512;
-            if (i < NV) d[rec_lds_vec(index(i))] = r[j];
-        }
-    }
-};
-
-static_assert(REC_X / 16 == 256 && REC_KT / 16 == 512 && REC_V / 16 == 768 && REC_GC / 16 == 1056 &&
-                  REC_T / 16 == 1088 && REC_VEC == 1152 && REC_HBM_VEC == 896,
-              "transfer fetch ranges follow the record layout");
-
-__global__ __launch_bounds__(512) void kda_cp_transfer(PrescanArgs a) {
-    if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
-    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
-    __shared__ int32_t live_tiles[8];
-    const int H = a.c.H;
-    const int h = blockIdx.x % H;
-    const PrescanDesc it = a.items[blockIdx.x / H];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int gg = lane >> 4, m = lane & 15;
-    f32x4 S[8][1];
-    identity_state(S, wave, gg, m);
-    f32x4 unused[1];
-    const uint8_t* rb = a.c.rec + ((size_t)h * a.c.total_chunks + it.rec_chunk0) * REC_HBM_BYTES;
-    const int nc = it.n_chunks;
-    // whether any tile of the workgroup is nonzero (uniform; a barrier round)
-    auto any_live = [&]() __attribute__((always_inline)) {
-        const bool nz = tile_nonzero(S);
-        if (lane == 0) live_tiles[wave] = nz ? 1 : 0;
-        lds_barrier();
-        int any = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) any |= live_tiles[j];
-        return any != 0;
-    };
-    TransferFetch p0, p1;
-    if (nc > 0) p0.load(rb);
-    if (nc > 1) p1.load(rb + REC_HBM_BYTES);
-    if (nc > 0) p0.store(recs[0]);
-    lds_barrier();
-    bool live = true;
-    for (int ci = 0; ci < nc; ci += 2) {
-        if (ci + 2 < nc) p0.load(rb + (size_t)(ci + 2) * REC_HBM_BYTES);
-        chain_step<1, false, false>(recs[0], S, wave, lane, unused);
-        if (ci + 1 < nc) p1.store(recs[1]);
-        lds_barrier();
-        if (ci + 1 < nc) {
-            if (ci + 3 < nc) p1.load(rb + (size_t)(ci + 3) * REC_HBM_BYTES);
-            chain_step<1, false, false>(recs[1], S, wave, lane, unused);
-            if (ci + 2 < nc) p0.store(recs[0]);
-            lds_barrier();
-        }
-        if ((ci & 3) == 2 && ci + 2 < nc && !any_live()) {
-            live = false;
-            break;
-        }
-    }
-    if (live) live = any_live();
-    const size_t so = (size_t)it.slot * H + h;
-    const bool nz = live && tile_nonzero(S);  // (a wavefront-wide ballot)
-    if (lane == 0) a.m_live[so * 8 + wave] = nz ? 1 : 0;
-    // the merge reads a transfer only when some tile of it is live, and then
-    // reads all of it
-    if (live) store_state(a.m_seg + so * (D * D), S, wave, gg, m);
 }
 
 // ---------------------------------------------------------------------------
@@ -957,13 +934,6 @@ hipError_t launch_k2_recur(const K2Args& a, hipStream_t s) {
     const long long n = (long long)a.n_units * a.c.H;
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(kda_k2_recur, dim3((unsigned)n), dim3(512), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_cp_transfer(const PrescanArgs& a, hipStream_t s) {
-    const long long n = (long long)a.n_items * a.c.H;
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_cp_transfer, dim3((unsigned)n), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -40,16 +40,6 @@ struct UnitDesc {
     int32_t b_slot;
 };
 
-// CP pre_scan item: one segment whose (M, B) summary feeds the merge.
-struct PrescanDesc {
-    int32_t seq;
-    int32_t chunk0;
-    int32_t n_chunks;
-    int32_t rec_chunk0;
-    int32_t slot;  // summary slot in b_seg / m_seg
-    int32_t pad[3];
-};
-
 // CP merge item: one segmented sequence.
 struct MergeDesc {
     int32_t seq;
@@ -120,15 +110,12 @@ struct K2Args {
     const int32_t* gate_flags;
     int64_t n_gate_flags;
     int32_t* gate_out;
-};
-
-struct PrescanArgs {
-    CommonArgs c;
-    const PrescanDesc* items;
-    int32_t n_items;
-    float* b_seg;  // [slots][H][128][128]
-    float* m_seg;
-    int32_t* m_live;  // [slots][H][8]: 0 when that 16-column tile of M is exactly zero
+    // K1 with the B summaries also forms each summarised segment's transfer M
+    // (the update from S = I with V := 0) into m_out[out_slot], one flag per
+    // 16-column tile into m_live_out (0: that tile is exactly zero). M is
+    // stored only when some tile lives, a vanished tile then as zeros.
+    float* m_out;
+    int32_t* m_live_out;
 };
 
 struct MergeArgs {
@@ -141,7 +128,7 @@ struct MergeArgs {
     const float* m_seg;
     float* carries;  // [slots][H][128][128]
     int32_t state_bf16;
-    const int32_t* m_live;  // as PrescanArgs::m_live
+    const int32_t* m_live;  // [slots][H][8]: 0 when that 16-column tile of M is exactly zero
 };
 
 struct K1Args {
@@ -160,7 +147,6 @@ hipError_t launch_beta_to_f32(const uint16_t* src, float* dst, int64_t n, hipStr
 hipError_t launch_fused(const K2Args& a, hipStream_t s);
 hipError_t launch_k2_recur(const K2Args& a, hipStream_t s);
 hipError_t launch_k1_bsum(const K2Args& a, hipStream_t s);
-hipError_t launch_cp_transfer(const PrescanArgs& a, hipStream_t s);
 hipError_t launch_cp_merge(const MergeArgs& a, hipStream_t s);
 
 // The static scratch of the no-allocation prefill: its size, and its device

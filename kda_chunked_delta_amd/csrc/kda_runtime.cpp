@@ -84,21 +84,20 @@ double env_double(const char* name, double dflt) {
 // from per-kernel timings of this library's kernels (environment-
 // overridable, as the pull request's planner constants are):
 //   fused      one chunk step of a fused serial workgroup (one per CU)
-//   k1         K1 of one (chunk, head) with its record written and the B
-//              summary advanced, per CU, at full load
-//   prescan    one chunk step of a transfer (pre_scan) workgroup, when the
-//              transfer does not vanish (weak decay: the worst case)
+//   k1         K1 of one (chunk, head) with its record written and both
+//              pre_scan summaries advanced (B, and the transfer M while any
+//              tile of it lives), per CU, at full load; priced at weak
+//              decay, where the transfer lives through the whole segment
+//              (the worst case)
 //   rec        one chunk step of a K2 workgroup over materialised records
 //   merge      one segment step of the carry merge (weak decay: the worst
 //              case; under decay the transfers vanish and it costs little)
 //   launch     one kernel launch
 struct PlannerConsts {
-    double fused_us, k1_us, prescan_us, rec_us, merge_us, launch_us;
+    double fused_us, k1_us, rec_us, merge_us, launch_us;
     double k1_alone_us;   // K1 with few CUs busy (k1_us: all busy)
-    double prescan_one_us, prescan_half_us;  // transfer with 1 and 1/2 workgroups per CU (prescan_us: 2)
     double rec_alone_us;  // K2 over records, one workgroup's chunk step (rec_us: per CU, HBM-bound)
     int min_seg_chunks;  // shortest segment the planner will form
-    int prescan_per_cu;  // concurrent pre_scan workgroups per CU
     // fused kernel interval per chunk against the fraction of busy CUs:
     // alone_us with few busy, full_us with all busy, in between the shape
     // measured on MI355X (the shader clock falls as more CUs work)
@@ -111,23 +110,20 @@ struct PlannerConsts {
 
 PlannerConsts planner_consts() {
     PlannerConsts c;
-    // fitted at steady clocks on the 65536-token, 8-head workload with 64-,
-    // 128- and 256-chunk segments (512, 256 and 128 workgroups): K1 with B
-    // summaries 237, 230 and 299 us; under weak decay the transfer 99, 157
-    // and 194 us and the merge 2.3 us per segment step; segment-K2 148, 149
-    // and 228 us. And on the fused kernel's interval with few CUs busy.
+    // fitted at steady clocks on the 65536-token, 8-head workload with
+    // segments of 64, 96, 128, 160, 192 and 256 chunks (512 .. 128
+    // workgroups) under weak decay (g x 0.05): K1 with both summaries 250,
+    // 331, 237, 276, 317 and 369 us, the merge 2.3 us per segment step while
+    // the transfers live, segment-K2 150, 185, 154, 170, 184 and 229 us. And
+    // on the fused kernel's interval with few CUs busy.
     c.fused_us = env_double("KDA_CP_FUSED_CHUNK_US", 1.21);
-    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 1.80);
-    c.k1_alone_us = env_double("KDA_CP_K1_CHUNK_US_ALONE", 1.10);
-    c.prescan_us = env_double("KDA_CP_PRESCAN_CHUNK_US", 1.54);
-    c.prescan_one_us = env_double("KDA_CP_PRESCAN_CHUNK_US_ONE", 1.23);
-    c.prescan_half_us = env_double("KDA_CP_PRESCAN_CHUNK_US_HALF", 0.78);
+    c.k1_us = env_double("KDA_CP_K1_CHUNK_US", 1.85);
+    c.k1_alone_us = env_double("KDA_CP_K1_CHUNK_US_ALONE", 1.44);
     c.rec_us = env_double("KDA_CP_REC_CHUNK_US", 1.16);
     c.rec_alone_us = env_double("KDA_CP_REC_CHUNK_US_ALONE", 0.89);
     c.merge_us = env_double("KDA_CP_MERGE_SEG_US", 2.3);
     c.launch_us = env_double("KDA_CP_LAUNCH_US", 5.0);
     c.min_seg_chunks = (int)env_double("KDA_CP_MIN_SEG_CHUNKS", 64.0);
-    c.prescan_per_cu = (int)env_double("KDA_CP_PRESCAN_PER_CU", 2.0);
     c.alone_us = env_double("KDA_FUSED_CHUNK_US_ALONE", 1.21);
     c.full_us = env_double("KDA_FUSED_CHUNK_US_FULL", 1.60);
     c.split_warm = (int)env_double("KDA_SPLIT_WARM_CHUNKS", 12.0);
@@ -198,7 +194,6 @@ struct kda_plan {
     std::vector<int32_t> cu;            // host copy of cu_seqlens
     std::vector<ChunkDesc> chunks;      // K1 items (global chunk order)
     std::vector<UnitDesc> units;        // K2 units, launch order
-    std::vector<PrescanDesc> prescan;   // CP pre_scan items
     std::vector<MergeDesc> merges;      // CP merge items
     std::vector<UnitDesc> fixups;       // warm-start segments, as rerun from their carry
     std::vector<UnitDesc> cp_units;     // warm-start CP: the segmented fallback's K2 units
@@ -211,7 +206,7 @@ struct kda_plan {
     // device copy of the tables
     int device = -1;
     void* dev_tables = nullptr;
-    size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_prescan = 0, dev_off_merges = 0, dev_off_fixups = 0;
+    size_t dev_off_chunks = 0, dev_off_units = 0, dev_off_merges = 0, dev_off_fixups = 0;
     size_t dev_off_cp_units = 0, dev_off_alt_units = 0, dev_off_k1_units = 0, dev_off_merge_segs = 0;
     // Speculation feedback, outside graph capture: a speculative call (the
     // first, then every 64th) copies its outcome (split plans: the speculation
@@ -242,12 +237,12 @@ double est_serial(const std::vector<int>& nch, int H, int n_cus, const PlannerCo
 }
 
 // Segmented estimate for segment length `seg` (chunks): K1 materialised for
-// every chunk (with the B summaries), the transfer half of pre_scan over
-// every segment but the last of each split sequence, a serial merge over
-// segments, then K2 over all units. The transfer and the merge are priced
-// at weak decay, where no transfer vanishes (the worst case).
+// every chunk, with both pre_scan summaries of every segment but the last of
+// each split sequence, a serial merge over segments, then K2 over all units.
+// K1 and the merge are priced at weak decay, where no transfer vanishes (the
+// worst case).
 double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const PlannerConsts& pc) {
-    long long tot = 0, n_pre = 0;
+    long long tot = 0;
     int longest_unit = 0, max_segs = 0;
     std::vector<int> k1_work;  // K1 units of one head
     for (int n : nch) {
@@ -255,7 +250,6 @@ double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const Plan
         const int s = (n > seg) ? (n + seg - 1) / seg : 1;
         for (int j = 0; j < s; ++j) k1_work.push_back(std::min(seg, n - j * seg));
         if (s > 1) {
-            n_pre += s - 1;
             max_segs = std::max(max_segs, s);
             longest_unit = std::max(longest_unit, seg);
         } else {
@@ -274,20 +268,10 @@ double est_cp(const std::vector<int>& nch, int H, int n_cus, int seg, const Plan
         for (int h = 1; h < H; ++h) k1_work.insert(k1_work.end(), one.begin(), one.end());
     }
     const double t_k1 = simulate_fused_us(k1_work, n_cus, k1c, grouped ? H : 1);
-    // the transfer: each workgroup one segment; its chunk step slows as more
-    // share a CU (piecewise linear through 1/2, 1 and 2 per CU), in rounds
-    // of prescan_per_cu per CU
-    const double per_cu = (double)n_pre * H / n_cus;
-    const double cap = std::max(1, pc.prescan_per_cu);
-    const double c = std::min(per_cu, cap);
-    const double step = c <= 0.5 ? pc.prescan_half_us
-                        : c <= 1.0 ? pc.prescan_half_us + (pc.prescan_one_us - pc.prescan_half_us) * (c - 0.5) / 0.5
-                                   : pc.prescan_one_us + (pc.prescan_us - pc.prescan_one_us) * std::min(1.0, c - 1.0);
-    const double t_pre = std::ceil(per_cu / cap) * seg * step;
     const double t_merge = pc.merge_us * (max_segs - 1);
     // K2: the longest unit's chain, or the HBM stream over the CUs
     const double t_k2 = std::max(pc.rec_alone_us * longest_unit, pc.rec_us * std::ceil((double)tot * H / n_cus));
-    return t_k1 + t_pre + t_merge + t_k2 + 4 * pc.launch_us;
+    return t_k1 + t_merge + t_k2 + 3 * pc.launch_us;
 }
 
 // Fused work of each unit when sequence i is split at chunk split[i]
@@ -536,8 +520,6 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
             // K1 of its chunks, and (but for the last segment) its B summary
             p->k1_units.push_back(UnitDesc{i, c0, n, chunk_base[i] + c0, -1, 0, j, s, 0, -1,
                                            j < s - 1 ? n_prescan + j : -1, -1});
-            if (j < s - 1)
-                p->prescan.push_back(PrescanDesc{i, c0, n, chunk_base[i] + c0, n_prescan + j, {0, 0, 0}});
         }
         n_cp_seqs++;
         n_prescan += s - 1;
@@ -576,8 +558,6 @@ kda_status build_plan(int32_t n_cus, const int32_t* cu_host, int32_t n_seqs, int
     std::stable_sort(p->units.begin(), p->units.end(), [&](const UnitDesc& a, const UnitDesc& b) {
         return a.n_chunks + warm_work(a.warm, pc) > b.n_chunks + warm_work(b.warm, pc);
     });
-    std::stable_sort(p->prescan.begin(), p->prescan.end(),
-                     [](const PrescanDesc& a, const PrescanDesc& b) { return a.n_chunks > b.n_chunks; });
     std::stable_sort(p->k1_units.begin(), p->k1_units.end(),
                      [](const UnitDesc& a, const UnitDesc& b) { return a.n_chunks > b.n_chunks; });
 
@@ -646,8 +626,6 @@ kda_status upload_plan(kda_plan* p, int device) {
     off = align_up(off + p->chunks.size() * sizeof(ChunkDesc), 256);
     p->dev_off_units = off;
     off = align_up(off + p->units.size() * sizeof(UnitDesc), 256);
-    p->dev_off_prescan = off;
-    off = align_up(off + p->prescan.size() * sizeof(PrescanDesc), 256);
     p->dev_off_merges = off;
     off = align_up(off + p->merges.size() * sizeof(MergeDesc), 256);
     p->dev_off_fixups = off;
@@ -663,7 +641,6 @@ kda_status upload_plan(kda_plan* p, int device) {
     std::vector<uint8_t> host(off, 0);
     if (!p->chunks.empty()) memcpy(&host[p->dev_off_chunks], p->chunks.data(), p->chunks.size() * sizeof(ChunkDesc));
     if (!p->units.empty()) memcpy(&host[p->dev_off_units], p->units.data(), p->units.size() * sizeof(UnitDesc));
-    if (!p->prescan.empty()) memcpy(&host[p->dev_off_prescan], p->prescan.data(), p->prescan.size() * sizeof(PrescanDesc));
     if (!p->merges.empty()) memcpy(&host[p->dev_off_merges], p->merges.data(), p->merges.size() * sizeof(MergeDesc));
     if (!p->fixups.empty()) memcpy(&host[p->dev_off_fixups], p->fixups.data(), p->fixups.size() * sizeof(UnitDesc));
     if (!p->cp_units.empty())
@@ -1188,9 +1165,9 @@ kda_status prefill_impl(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts*
         return err;
     };
     // The segmented pipeline. CP plans: K1 writes the records of every chunk
-    // and each segment's B summary (the update from zero) in one launch, the
-    // transfer half of pre_scan runs over the records, the merge forms the
-    // carries, and K2 runs every unit over the records. A serial plan with
+    // and each segment's pre_scan summaries (B, the update from zero, and the
+    // transfer M, the update from the identity with V := 0) in one launch,
+    // the merge forms the carries, and K2 runs every unit over the records. A serial plan with
     // materialised K1 runs K1 alone and then K2. cc.gate gates every launch
     // when set (the fallback of warm-start CP); with gate_flags, the first
     // launch reduces those flags into the gate word cc.gate points to.
@@ -1206,6 +1183,8 @@ kda_status prefill_impl(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts*
             kb.units = (const UnitDesc*)(tabs + p->dev_off_k1_units);
             kb.n_units = (int32_t)p->k1_units.size();
             kb.carries = b_seg;  // the B summaries go to their pre_scan slots
+            kb.m_out = (float*)(ws + p->off_m);  // and the transfers to theirs
+            kb.m_live_out = m_live;
             kb.scale = scale;
             kb.spec_final_direct = 1;
             kb.gate_flags = gate_flags;
@@ -1221,12 +1200,6 @@ kda_status prefill_impl(kda_ctx* ctx, const kda_plan* p, const kda_prefill_opts*
             if (e != hipSuccess) return hip_fail(e, "k1_prepare launch");
         }
         if (gate_flags && (e = report(cc.gate, 1)) != hipSuccess) return hip_fail(e, "speculation feedback");
-        if (!p->prescan.empty()) {
-            PrescanArgs pa{cc, (const PrescanDesc*)(tabs + p->dev_off_prescan), (int32_t)p->prescan.size(),
-                           b_seg, (float*)(ws + p->off_m), m_live};
-            e = timed("cp_transfer", [&] { return launch_cp_transfer(pa, stream); });
-            if (e != hipSuccess) return hip_fail(e, "cp_transfer launch");
-        }
         if (cp) {
             MergeArgs ma{cc, (const MergeDesc*)(tabs + p->dev_off_merges),
                          (const MergeSeg*)(tabs + p->dev_off_merge_segs), (int32_t)p->merge_segs.size(), s0, b_seg,

@@ -398,6 +398,38 @@ def test_cp_merge_runs_starting_mid_sequence():
     assert torch.equal(o_in, o_cp) and torch.equal(st, s_cp), "in-place CP differs from out-of-place CP"
 
 
+def test_cp_transfer_with_vanished_and_live_tiles():
+    """A transfer whose 16-column tiles differ: keys are zero on channels
+    0..15 (no delta-rule mixing into or out of them) and those channels
+    decay strongly (g x 4), the rest weakly (g x 0.05). Tile 0 of every
+    segment's transfer then underflows to exactly zero while the other seven
+    live, so the merge reads a transfer with a tile that vanished. The same
+    plan first runs a weak-decay batch that leaves every tile of the
+    workspace's transfers nonzero, so a vanished tile that were not written
+    as zeros would corrupt the carries. CP matches the oracle within 1e-2."""
+    seg, n_seg = 8, 6
+    T = seg * n_seg * 16
+    d = draw([T], 2, seed=17, state_std=0.1, device=DEV)
+    cu = d["cu_seqlens_host"]
+    p = kda.plan_segments(cu, 2, seg, device=DEV)
+    assert p.info()["uses_cp"] == 1
+    weak = dict(d)
+    weak["g"] = d["g"] * 0.05
+    run(weak, plan=p)  # every transfer tile live
+    mixed = dict(d)
+    k = d["k"].clone()
+    k[:, :, :16] = 0
+    mixed["k"] = k
+    chan = torch.full((128,), 0.05, dtype=torch.float32, device=DEV)
+    chan[:16] = 4.0
+    mixed["g"] = d["g"] * chan
+    say("case: %d segments of %d chunks, keys zero and decay x4 on channels 0..15" % (n_seg, seg))
+    o_cp, s_cp = run(mixed, plan=p)
+    o_ref, s_ref = oracle(mixed)
+    assert_close("out(cp)", o_cp, o_ref)
+    assert_close("final(cp)", s_cp, s_ref)
+
+
 def test_steep_in_chunk_decay_matches_oracle(monkeypatch):
     """Decay steps of e^-40 at rows 0 and 8 of every chunk, on the key
     channels of two of the eight K1 wavefronts of the second sequence: the
