@@ -37,10 +37,12 @@ constexpr int CH = 16;   // chunk length
 // feeds the next MFMA as an operand without any shuffle.
 //   REC_Q  : Qt fragments [p 4][lane 64][8 bf16]: Qt[m][dkperm(p, gg, j)]
 //   REC_X  : X fragments, same layout as REC_Q
-//   REC_KT : Kt^T fragments [t 8][slot 64][4 bf16]: lane l's fragment
-//            Kt[4gg + j][16t + m] in slot kv_slot(l)
-//   REC_V  : V in accumulator layout [n 8][slot 64][4 bf16]: lane l's
-//            V[4gg + j][16n + m] in slot kv_slot(l)
+//   REC_KT : Kt in 4-channel row segments [t 8][slot 64][4 bf16]: slot
+//            kv_store_slot(a, 4b + c) holds Kt[4a + b][16t + 4c + j]; lane l
+//            reads slot kv_load_slot(l) with a transposing load and gets its
+//            Kt^T fragment Kt[4gg + j][16t + m]
+//   REC_V  : V in the same layout [n 8][slot 64][4 bf16]; the transposing
+//            load gives lane l its V[4gg + j][16n + m]
 //   REC_AQK: A_qk fragment [lane 64][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
 //   REC_GC : exp(G_C) [128] fp32, channel c = 16t + 4gg + v at position
 //            32gg + 4t + v: lane (gg, m) of a state wavefront reads the pair
@@ -163,36 +165,30 @@ __device__ __forceinline__ float row_newbcast(float x) {
     return __builtin_amdgcn_update_dpp(0.0f, x, 0x150 + K, 0xF, 0xF, true);
 }
 
-// 4 x 4 transpose of 16-bit elements across the four lanes of a quad: lane j
-// holds elements x[0..3] as (x0 | x1 << 16, x2 | x3 << 16); afterwards it
-// holds element j of lanes 0..3, in lane order. First the 2 x 2 blocks of
-// dwords move between lanes j and j ^ 2, then each 2 x 2 block of halves is
-// transposed between lanes j and j ^ 1 (DPP quad permutes and a byte
-// permute).
-__device__ __forceinline__ u32x2 quad_transpose16(u32x2 x, int lane) {
-    const bool hi = (lane & 2) != 0;
-    const uint32_t send = hi ? x.x : x.y;
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-    const uint32_t y0 = hi ? recv : x.x;
-    const uint32_t y1 = hi ? x.y : recv;
-    const uint32_t p0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)y0, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-    const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)y1, 0xB1, 0xF, 0xF, false);
-    // even lane: own low half, then the partner's; odd lane: the partner's
-    // high half, then its own (v_perm_b32: bytes 0-3 from the second
-    // operand, 4-7 from the first)
-    const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
-    return u32x2{__builtin_amdgcn_perm(p0, y0, sel), __builtin_amdgcn_perm(p1, y1, sel)};
+// Kt and V tiles: K1 lane (gg, m) holds token m, channels 4gg .. 4gg + 3 of
+// a tile, an 8-byte row segment, and stores it untransposed in slot
+// kv_store_slot(gg, m). gfx950's transposing LDS load (ds_read_b64_tr_b16)
+// works on groups of 16 lanes: lane 4r + c of a group loads row segment
+// (r, c) of a 4 x 16 block of 16-bit elements, and lane i then receives
+// column i of the block (its element i & 3 from the segments of lanes
+// 4r + (i >> 2), r = 0..3; checked on the GPU with an in-bounds probe). A
+// state lane l = 16gg + 4r + c therefore loads the segment of token 4gg + r
+// and channels 4c .. 4c + 3, and receives tokens 4gg .. 4gg + 3 of channel
+// m: its 16x16x16 MFMA fragment. Slots rotate the segment index by gg, so
+// the loads of a 16-lane group stay in one 128-byte row (no bank conflict)
+// and each group of 16 stores (fixed gg, m = 0..15) covers 16 distinct
+// 8-byte positions of a 128-byte bank row (none either).
+__device__ __forceinline__ int kv_store_slot(int gg, int m) {
+    return 16 * (m >> 2) + 4 * (m & 3) + ((gg + (m >> 2)) & 3);
 }
+__device__ __forceinline__ int kv_load_slot(int l) { return (l & 0x3C) | (((l & 3) + (l >> 4)) & 3); }
 
-// Slot of lane l's 8-byte fragment in the Kt and V tiles: lane l = 16g + 4a +
-// j sits in slot 16g + 4((a + g) & 3) + j. The reads stay one contiguous
-// 512-byte tile (each half-wavefront's 32 reads on distinct banks), and the
-// stores that K1 writes them with (lane (gg, 4a + j) -> fragment of lane
-// 16a + 4gg + j) put each group of 16 lanes on 16 distinct 8-byte slots of a
-// 128-byte bank row, so neither side has a bank conflict. (Measured: the
-// earlier rotation of the low two bits by l >> 4 made those stores 4-way
-// conflicted, 16 instead of 4 LDS cycles each.)
-__device__ __forceinline__ int kv_slot(int l) { return (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2); }
+// The transposing 8-byte LDS load (p: an LDS address).
+__device__ __forceinline__ u32x2 lds_load_tr16(const uint8_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
 
 // ---------------------------------------------------------------------------
 // K1, phase 1 (8 wavefronts). Wavefront w owns key channels and value
@@ -570,16 +566,11 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     *(u32x2*)(scr + K1_KB + (wave >> 1) * 1024 + (wave & 1) * 512 + lane * 8) = pkb;
     *(u32x2*)(rec + REC_Q + fo) = pqt;
     *(u32x2*)(rec + REC_X + fo) = pxk;
-    // Kt^T and V: element (token m, channel 16 wave + 4gg + j) -> tile wave,
-    // lane (m >> 2) * 16 + 4gg + j, element m & 3. The four lanes of a quad
-    // (m = 4a .. 4a + 3) hold a 4 x 4 block of it (tokens x channels); after
-    // a 16-bit transpose inside the quad, lane (gg, 4a + j) holds channel
-    // 4gg + j for tokens 4a .. 4a + 3: the whole 8-byte fragment of lane
-    // 16a + 4gg + j, written with one store to that lane's slot.
-    const int dl = 16 * (m >> 2) + 4 * gg + (m & 3);
-    const int to = wave * 512 + kv_slot(dl) * 8;
-    *(u32x2*)(rec + REC_KT + to) = quad_transpose16(pkt, lane);
-    *(u32x2*)(rec + REC_V + to) = quad_transpose16(raw.v, lane);
+    // Kt and V of tile `wave`: the lane's row segment, untransposed (the
+    // state wavefronts transpose it as they load it)
+    const int to = wave * 512 + kv_store_slot(gg, m) * 8;
+    *(u32x2*)(rec + REC_KT + to) = pkt;
+    *(u32x2*)(rec + REC_V + to) = raw.v;
     // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
     if (m == 15) *(f32x4*)(rec + REC_GC + (32 * gg + 4 * wave) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     if (wave == 0 && gg == 0) scr_b[m] = raw.b;
@@ -766,7 +757,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
                 r[j] = __uint_as_float(e << 16) - P[n][j];
             }
         } else if constexpr (WITH_V) {
-            const u32x2 vw = *(const u32x2*)(rec + REC_V + (n0 + n) * 512 + kv_slot(lane) * 8);
+            const u32x2 vw = lds_load_tr16(rec + REC_V + (n0 + n) * 512 + kv_load_slot(lane) * 8);
             r[0] = bf16_lo(vw.x) - P[n][0];
             r[1] = bf16_hi(vw.x) - P[n][1];
             r[2] = bf16_lo(vw.y) - P[n][2];
@@ -807,7 +798,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
         constexpr int t = decltype(tc)::value;
         const f32x4 gcv = {row_newbcast<2 * t>(gcp[0]), row_newbcast<2 * t>(gcp[1]),
                            row_newbcast<2 * t + 1>(gcp[0]), row_newbcast<2 * t + 1>(gcp[1])};
-        const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + kv_slot(lane) * 8);
+        const u32x2 kt = lds_load_tr16(rec + REC_KT + t * 512 + kv_load_slot(lane) * 8);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             S[t][n] = gcv * S[t][n];
@@ -846,7 +837,7 @@ __device__ __forceinline__ void chain_step_warm(const uint8_t* rec, f32x4 (&M)[8
     }
     const u32x2 th = *(const u32x2*)(rec + REC_T + lane * 8);
     const u32x2 tl = *(const u32x2*)(rec + REC_T + 512 + lane * 8);
-    const u32x2 vw = *(const u32x2*)(rec + REC_V + n0 * 512 + kv_slot(lane) * 8);
+    const u32x2 vw = lds_load_tr16(rec + REC_V + n0 * 512 + kv_load_slot(lane) * 8);
     f32x4 rz;
     rz[0] = bf16_lo(vw.x) - pz[0];
     rz[1] = bf16_hi(vw.x) - pz[1];
@@ -863,7 +854,7 @@ __device__ __forceinline__ void chain_step_warm(const uint8_t* rec, f32x4 (&M)[8
         constexpr int t = decltype(tc)::value;
         const f32x4 gcv = {row_newbcast<2 * t>(gcp[0]), row_newbcast<2 * t>(gcp[1]),
                            row_newbcast<2 * t + 1>(gcp[0]), row_newbcast<2 * t + 1>(gcp[1])};
-        const u32x2 kt = *(const u32x2*)(rec + REC_KT + t * 512 + kv_slot(lane) * 8);
+        const u32x2 kt = lds_load_tr16(rec + REC_KT + t * 512 + kv_load_slot(lane) * 8);
         M[t][0] = gcv * M[t][0];
         M[t][0] = mfma_k16(kt, ubm, M[t][0]);
         Z[t][0] = gcv * Z[t][0];
