@@ -41,37 +41,42 @@ constexpr int CH = 16;   // chunk length
 //            kv_store_slot(a, 4b + c) holds Kt[4a + b][16t + 4c + j]; lane l
 //            reads slot kv_load_slot(l) with a transposing load and gets its
 //            Kt^T fragment Kt[4gg + j][16t + m]
-//   REC_V  : V in the same layout [n 8][slot 64][4 bf16]; the transposing
-//            load gives lane l its V[4gg + j][16n + m]
 //   REC_AQK: A_qk fragment [lane 64][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
 //   REC_GC : exp(G_C) [128] fp32, channel c = 16t + 4gg + v at position
 //            32gg + 4t + v: lane (gg, m) of a state wavefront reads the pair
 //            at 2 * lane, which holds channels 16(m >> 1) + 4gg + 2(m & 1) + 0..1
 //   REC_T  : T' fragments, hi then lo [2][lane 64][4 bf16]: T'[m][4gg + j]
-// When K1 is materialised, HBM holds each record without V (REC_HBM_BYTES:
-// the fields before REC_V at their offsets, those after it 4096 bytes
-// earlier): V is a copy of the input, and its reader takes the rows from
-// there instead, into the REC_V area of its LDS record (vrow_off).
+// A record holds no V: the chunk's value rows are a copy of the input, and
+// they reach LDS as a V block of their own (VBLK_*), straight from memory.
+// HBM holds the same bytes when K1 is materialised.
 // ---------------------------------------------------------------------------
 constexpr int REC_Q = 0;
 constexpr int REC_X = 4096;
 constexpr int REC_KT = 8192;
-constexpr int REC_V = 12288;
-constexpr int REC_AQK = 16384;
-constexpr int REC_GC = 16896;
-constexpr int REC_T = 17408;
-constexpr int REC_BYTES = 18432;
-constexpr int REC_VEC = REC_BYTES / 16;  // 1152 16-byte vectors
-constexpr int REC_HBM_BYTES = REC_BYTES - 4096;
-constexpr int REC_HBM_VEC = REC_HBM_BYTES / 16;  // 896
-// LDS vector of a record's HBM vector i
-__device__ __forceinline__ int rec_lds_vec(int i) { return i < REC_V / 16 ? i : i + 256; }
-// V rows staged from the input (K2 over materialised records): token row r
-// at r * 256 bytes, its 16-byte granule q at granule q ^ ((r >> 1) & 6), so
-// that the four token quads a wavefront's 16-bit reads touch fall into
-// distinct banks. Byte of element (r, column c):
-__device__ __forceinline__ int vrow_off(int r, int c) {
-    return r * 256 + ((((c >> 3) ^ ((r >> 1) & 6))) << 4) + (c & 7) * 2;
+constexpr int REC_AQK = 12288;
+constexpr int REC_GC = 12800;
+constexpr int REC_T = 13312;
+constexpr int REC_BYTES = 14336;
+constexpr int REC_HBM_BYTES = REC_BYTES;
+constexpr int REC_HBM_VEC = REC_HBM_BYTES / 16;  // 896 16-byte vectors
+
+// V block of one chunk (LDS only): its 16 value rows (256 bytes each) in four
+// 1 KiB blocks of four rows. Granule gi (16 bytes, columns 8gi .. 8gi + 7)
+// of row 4b + r sits at granule position 16r + (gi ^ (2r + 8(b & 1))) of
+// block b. A state lane l = 16gg + 4r + c loads, with the transposing load,
+// the 8-byte segment of row 4gg + r and columns 16n + 4c .. + 3 of value
+// tile n, and so receives its 16x16x16 B fragment V[4gg + j][16n + m]. Per
+// half-wavefront the 16 granules a tile's load touches sit at distinct
+// positions modulo 16 (no bank conflict); the writers store whole 1 KiB
+// blocks.
+constexpr int VBLK_BYTES = 4096;
+__device__ __forceinline__ int vblk_off(int row, int gi) {
+    const int b = row >> 2, r = row & 3;
+    return 1024 * b + 16 * (16 * r + (gi ^ (2 * r + 8 * (b & 1))));
+}
+__device__ __forceinline__ int vblk_load_off(int lane, int n) {
+    const int c = lane & 3;
+    return vblk_off(4 * (lane >> 4) + ((lane >> 2) & 3), 2 * n + (c >> 1)) + 8 * (c & 1);
 }
 
 // K1 scratch of one chunk (LDS only), from phase 1 to phase 2:
@@ -197,7 +202,7 @@ __device__ __forceinline__ u32x2 lds_load_tr16(const uint8_t* p) {
 // beta = 0), which leaves them inert.
 // ---------------------------------------------------------------------------
 struct RawChunk {
-    u32x2 q, k, v;
+    u32x2 q, k;
     f32x4 g;
     float b;
 };
@@ -218,22 +223,21 @@ constexpr int BUF_POLICY = 0;
 // layout touches 16 rows with 32-64 bytes each and four wavefronts fetch
 // every line; measured, that runs at about a third of the rate of whole-row
 // loads. So the wavefronts load whole rows into registers (RowChunk):
-// wavefront w rows 2w and 2w + 1 of v and g, and 16 bytes per lane of rows
-// 4w .. 4w + 3 of q (w < 4) or of k (w >= 4), so that a chunk takes 25 load
-// instructions rather than 33 (measured 1-1.5% faster than two rows per
-// wavefront of each). They write the rows to an LDS staging area, and
-// after the next barrier each wavefront reads its phase-1 fragments from
-// there. (The fused kernel loads g straight into LDS instead.)
+// wavefront w rows 2w and 2w + 1 of g, and 16 bytes per lane of rows
+// 4w .. 4w + 3 of q (w < 4) or of k (w >= 4) (measured 1-1.5% faster than
+// two rows per wavefront of each). They write the rows to an LDS staging
+// area, and after the next barrier each wavefront reads its phase-1
+// fragments from there. (The fused kernel loads g straight into LDS
+// instead.) K1 does not read v: the value rows are not part of a record.
 // Staging of one chunk: rows in order; the 16-byte granules of row r are
 // XOR-swizzled with r & 15, so both the row writes and phase 1's column
 // reads (16 rows, one granule each) spread over all banks.
 // ---------------------------------------------------------------------------
 constexpr int STG_Q = 0;       // q  [16][256 B]
 constexpr int STG_K = 4096;    // k  [16][256 B]
-constexpr int STG_V = 8192;    // v  [16][256 B]
-constexpr int STG_G = 12288;   // g  [16][512 B]
-constexpr int STG_B = 20480;   // beta [16] fp32
-constexpr int STG_BYTES = 20544;
+constexpr int STG_G = 8192;    // g  [16][512 B]
+constexpr int STG_B = 16384;   // beta [16] fp32
+constexpr int STG_BYTES = 16448;
 constexpr int STG_NB = STG_B;  // the staged rows alone (beta kept elsewhere by the fused kernel)
 
 // Staging byte offset of byte `byte` of row r of a 256-byte (bf16) row.
@@ -248,17 +252,16 @@ __device__ __forceinline__ int stg_g_off(int r, int byte) {
 
 struct RowChunk {
     u32x4 qk;       // wavefronts 0-3: 16 bytes of q row 4w + (lane >> 4) at byte 16 (lane & 15); 4-7: of k
-    u32x2 v;        // 8 bytes of row 2w + (lane >> 5) at byte 8 (lane & 31)
-    f32x4 g;        // 16 bytes of that row of g at byte 16 (lane & 31)
+    f32x4 g;        // 16 bytes of row 2w + (lane >> 5) of g at byte 16 (lane & 31)
     float b;        // beta of row lane & 15 (wavefront 0 only)
 };
 
 // Per-lane constants of the row path of wavefront w.
 struct RowLaneOffsets {
-    uint32_t qk, act, g, beta;  // global byte offsets from the chunk's first row (qk: of q or k)
-    int st_act, st_g;       // staging offsets of the row writes
-    int st_qk;              // staging offset of the q or k write (its tensor's area included)
-    int rd_act, rd_g;       // staging offsets of phase 1's reads
+    uint32_t qk, g, beta;  // global byte offsets from the chunk's first row (qk: of q or k)
+    int st_g;              // staging offset of the g row write
+    int st_qk;             // staging offset of the q or k write (its tensor's area included)
+    int rd_act, rd_g;      // staging offsets of phase 1's reads (q and k; g)
 };
 
 // H value heads (v, g, beta rows), Hk q/k heads (q, k rows)
@@ -268,10 +271,8 @@ __device__ __forceinline__ RowLaneOffsets row_lane_offsets(int H, int Hk, int wa
     const int r4 = 4 * (wave & 3) + (lane >> 4);
     o.qk = (uint32_t)r4 * (uint32_t)Hk * (D * 2) + (lane & 15) * 16;
     o.st_qk = (wave < 4 ? STG_Q : STG_K) + stg_act_off(r4, (lane & 15) * 16);
-    o.act = (uint32_t)r * (uint32_t)H * (D * 2) + (lane & 31) * 8;
     o.g = (uint32_t)r * (uint32_t)H * (D * 4) + (lane & 31) * 16;
     o.beta = (uint32_t)m * (uint32_t)H * 4;
-    o.st_act = stg_act_off(r, (lane & 31) * 8);
     o.st_g = stg_g_off(r, (lane & 31) * 16);
     o.rd_act = stg_act_off(m, 32 * wave + 8 * gg);
     o.rd_g = stg_g_off(m, 64 * wave + 16 * gg);
@@ -312,14 +313,13 @@ __device__ __forceinline__ RowStreams row_streams(const uint16_t* q, const uint1
 
 // Loads of chunk ci of the streams with nrows (0..16) valid rows. Each range
 // covers nrows whole token rows, so the lanes of rows past them, and every
-// lane when nrows = 0, read zeros and touch no memory. nrows_q and nrows_v
-// (0 or nrows) are the rows of q and of v alone: 0 where the chunk's use
-// needs no q (a warm-up chunk), which then reads zeros for it. GVA = false: q/k heads are
-// the value heads, and q/k share v's offsets and ranges.
+// lane when nrows = 0, read zeros and touch no memory. nrows_q (0 or nrows)
+// is the rows of q alone: 0 where the chunk's use needs no q (a warm-up
+// chunk), which then reads zeros for it. GVA = false: q/k heads are the
+// value heads, and q/k share v's offsets and ranges.
 template <bool GVA>
-__device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,
+__device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int nrows, int nrows_q,
                                               const RowLaneOffsets& lo, RowChunk& rc, int wave) {
-    const uint32_t n_act = (uint32_t)nrows * rs.st_act;
     const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
     size_t c_qk = c_act;
     uint32_t st_qk = rs.st_act;
@@ -333,8 +333,6 @@ __device__ __forceinline__ void k1_load_chunk(const RowStreams& rs, int ci, int 
     const uint32_t n_qk = (uint32_t)(is_q ? nrows_q : nrows) * st_qk;
     rc.qk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(chunk_rsrc(qkb, n_qk), (int)lo.qk, 0,
                                                                            BUF_POLICY));
-    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc(rs.v + c_act, (uint32_t)nrows_v * rs.st_act), (int)lo.act, 0, BUF_POLICY));
     // g rows are twice as long as v rows, beta rows 1/64 of them
     rc.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
         chunk_rsrc(rs.g + 2 * c_act, (uint32_t)nrows * rs.st_g), (int)lo.g, 0, BUF_POLICY));
@@ -360,7 +358,6 @@ __device__ __forceinline__ int chunk_rows(int rem, int ci) {
 __device__ __forceinline__ void k1_stage(const RowChunk& rc, int wave, int lane, const RowLaneOffsets& lo,
                                          uint8_t* stg, float* stg_b) {
     *(u32x4*)(stg + lo.st_qk) = rc.qk;
-    *(u32x2*)(stg + STG_V + lo.st_act) = rc.v;
     *(f32x4*)(stg + STG_G + lo.st_g) = rc.g;
     if (wave == 0 && lane < 16) stg_b[lane] = rc.b;
 }
@@ -370,27 +367,46 @@ __device__ __forceinline__ void k1_read_staged(const uint8_t* stg, const float* 
                                                const RowLaneOffsets& lo, RawChunk& raw) {
     raw.q = *(const u32x2*)(stg + STG_Q + lo.rd_act);
     raw.k = *(const u32x2*)(stg + STG_K + lo.rd_act);
-    raw.v = *(const u32x2*)(stg + STG_V + lo.rd_act);
     raw.g = *(const f32x4*)(stg + STG_G + lo.rd_g);
     raw.b = stg_b[lane & 15];
 }
 
-// The fused kernel's row path: q, k and v as above, staged through registers
+// The fused kernel's row path: q and k as above, staged through registers
 // into slots of FSTG_NB bytes; g goes from memory straight into a ring of
 // LDS slots of GRING_BYTES (one per chunk, the staged layout of STG_G) by
 // direct-to-LDS buffer loads, so the K1 wavefronts neither hold nor stage
 // it. Lane l of wavefront w loads the 16-byte granule that the staged
 // layout puts at slot l & 31 of row 2w + (l >> 5): a direct-to-LDS load
 // writes lane l's 16 bytes at the wavefront's LDS base + 16 l (lanes
-// past the descriptor's range write zeros).
-constexpr int FSTG_NB = STG_G;      // q, k, v [16][256 B] each
+// past the descriptor's range write zeros). The value rows go the same way
+// into V blocks (VBLK_*) that the state wavefronts read: lane l of a K1
+// wavefront with w & 3 = b loads granule (l & 15) ^ (2r + 8(b & 1)) of row
+// 4b + r, r = l >> 4, into block b.
+constexpr int FSTG_NB = STG_G;      // q, k [16][256 B] each
 constexpr int GRING_BYTES = 8192;   // g [16][512 B]
 
 struct RowChunkF {
     u32x4 qk;  // as RowChunk
-    u32x2 v;
     float b;
 };
+
+// Global byte offset (from the chunk's first v row) of lane `lane`'s
+// direct-to-LDS v granule in a K1 wavefront that loads block b.
+__device__ __forceinline__ uint32_t v_dma_off(int H, int b, int lane) {
+    const int r = lane >> 4;
+    const int gi = (lane & 15) ^ (2 * r + 8 * (b & 1));
+    return (uint32_t)(4 * b + r) * (uint32_t)H * (D * 2) + gi * 16;
+}
+
+// Block b of the V block of chunk ci into vblk, by one direct-to-LDS load.
+__device__ __forceinline__ void k1_load_v_dma(const RowStreams& rs, int ci, int nrows, uint32_t v_off, int b,
+                                              uint8_t* vblk) {
+    const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(chunk_rsrc(rs.v + c_act, (uint32_t)nrows * rs.st_act),
+                                             (__attribute__((address_space(3))) void*)(vblk + 1024 * b), 16,
+                                             (int)v_off, 0, 0, BUF_POLICY);
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // Global byte offset (from the chunk's first g row) of lane `lane`'s
 // direct-to-LDS g granule in wavefront w.
@@ -412,9 +428,9 @@ __device__ __forceinline__ void k1_load_g_dma(const RowStreams& rs, int ci, int 
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The q or k, v and beta rows of chunk ci into a register set.
+// The q or k and beta rows of chunk ci into a register set.
 template <bool GVA>
-__device__ __forceinline__ void k1_load_rows_f(const RowStreams& rs, int ci, int nrows, int nrows_q, int nrows_v,
+__device__ __forceinline__ void k1_load_rows_f(const RowStreams& rs, int ci, int nrows, int nrows_q,
                                                const RowLaneOffsets& lo, RowChunkF& rc, int wave) {
     const size_t c_act = (size_t)ci * (CH * (size_t)rs.st_act);
     size_t c_qk = c_act;
@@ -428,8 +444,6 @@ __device__ __forceinline__ void k1_load_rows_f(const RowStreams& rs, int ci, int
     const uint32_t n_qk = (uint32_t)(is_q ? nrows_q : nrows) * st_qk;
     rc.qk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(chunk_rsrc(qkb, n_qk), (int)lo.qk, 0,
                                                                            BUF_POLICY));
-    rc.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-        chunk_rsrc(rs.v + c_act, (uint32_t)nrows_v * rs.st_act), (int)lo.act, 0, BUF_POLICY));
     rc.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
         chunk_rsrc(rs.b + (c_act >> 6), (uint32_t)nrows * rs.st_b), (int)lo.beta, 0, BUF_POLICY));
 }
@@ -437,7 +451,6 @@ __device__ __forceinline__ void k1_load_rows_f(const RowStreams& rs, int ci, int
 __device__ __forceinline__ void k1_stage_f(const RowChunkF& rc, int wave, int lane, const RowLaneOffsets& lo,
                                            uint8_t* stg, float* stg_b) {
     *(u32x4*)(stg + lo.st_qk) = rc.qk;
-    *(u32x2*)(stg + STG_V + lo.st_act) = rc.v;
     if (wave == 0 && lane < 16) stg_b[lane] = rc.b;
 }
 
@@ -445,7 +458,6 @@ __device__ __forceinline__ void k1_read_staged_f(const uint8_t* stg, const float
                                                  int lane, const RowLaneOffsets& lo, RawChunk& raw) {
     raw.q = *(const u32x2*)(stg + STG_Q + lo.rd_act);
     raw.k = *(const u32x2*)(stg + STG_K + lo.rd_act);
-    raw.v = *(const u32x2*)(stg + STG_V + lo.rd_act);
     raw.g = *(const f32x4*)(gslot + lo.rd_g);
     raw.b = stg_b[lane & 15];
 }
@@ -566,11 +578,9 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     *(u32x2*)(scr + K1_KB + (wave >> 1) * 1024 + (wave & 1) * 512 + lane * 8) = pkb;
     *(u32x2*)(rec + REC_Q + fo) = pqt;
     *(u32x2*)(rec + REC_X + fo) = pxk;
-    // Kt and V of tile `wave`: the lane's row segment, untransposed (the
-    // state wavefronts transpose it as they load it)
-    const int to = wave * 512 + kv_store_slot(gg, m) * 8;
-    *(u32x2*)(rec + REC_KT + to) = pkt;
-    *(u32x2*)(rec + REC_V + to) = raw.v;
+    // Kt of tile `wave`: the lane's row segment, untransposed (the state
+    // wavefronts transpose it as they load it)
+    *(u32x2*)(rec + REC_KT + wave * 512 + kv_store_slot(gg, m) * 8) = pkt;
     // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
     if (m == 15) *(f32x4*)(rec + REC_GC + (32 * gg + 4 * wave) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     if (wave == 0 && gg == 0) scr_b[m] = raw.b;
@@ -708,18 +718,17 @@ __device__ __forceinline__ void k1_phase2(int wave, int lane, uint8_t* rec, cons
 
 // ---------------------------------------------------------------------------
 // K2 chain step: one wavefront advances NT value-column tiles n0..n0+NT-1 of
-// the state (16 columns each) over one chunk record held in LDS.
+// the state (16 columns each) over one chunk record held in LDS, with the
+// chunk's V block vb (VBLK_* layout; unused without V).
 // State tile S[t][n] holds S[16t + 4gg + v][16(n0 + n) + m], v = 0..3.
 // WITH_V = false runs the same update with V := 0 (the segment transfer of
 // the CP pre_scan). WITH_OUT also forms O^T = S0^T Qt^T + U^T A_qk^T, whose
 // accumulator oacc[n][v] is o[token m][16(n0 + n) + 4gg + v].
-// V_ROWS reads V from rows staged at REC_V (vrow_off) instead of the
-// fragment layout. The arithmetic of a tile is identical in every
-// instantiation.
+// The arithmetic of a tile is identical in every instantiation.
 // ---------------------------------------------------------------------------
-template <int NT, bool WITH_V, bool WITH_OUT, bool V_ROWS = false>
-__device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT], int n0, int lane,
-                                           f32x4 (&oacc)[NT]) {
+template <int NT, bool WITH_V, bool WITH_OUT>
+__device__ __forceinline__ void chain_step(const uint8_t* rec, const uint8_t* vb, f32x4 (&S)[8][NT], int n0,
+                                           int lane, f32x4 (&oacc)[NT]) {
     const int gg = lane >> 4;
     // bf16 copy of the chunk-start state, as K=32 operands
     u32x4 Sb[4][NT];
@@ -749,15 +758,8 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         f32x4 r;
-        if constexpr (WITH_V && V_ROWS) {
-            // the same bf16 values from the staged rows
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t e = *(const uint16_t*)(rec + REC_V + vrow_off(4 * gg + j, 16 * (n0 + n) + (lane & 15)));
-                r[j] = __uint_as_float(e << 16) - P[n][j];
-            }
-        } else if constexpr (WITH_V) {
-            const u32x2 vw = lds_load_tr16(rec + REC_V + (n0 + n) * 512 + kv_load_slot(lane) * 8);
+        if constexpr (WITH_V) {
+            const u32x2 vw = lds_load_tr16(vb + vblk_load_off(lane, n0 + n));
             r[0] = bf16_lo(vw.x) - P[n][0];
             r[1] = bf16_hi(vw.x) - P[n][1];
             r[2] = bf16_lo(vw.y) - P[n][2];
@@ -812,13 +814,13 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, f32x4 (&S)[8][NT]
 }
 
 // The warm-up step of a warm-start segment: the transfer M (V := 0) and the
-// state from zero Z (with V from the fragment layout) over the same record,
+// state from zero Z (with V from the V block vb) over the same record,
 // each tile's arithmetic exactly that of chain_step<1, false, false> and
 // chain_step<1, true, false>. The record's operands are read once for both,
 // and each bf16 operand of a state is packed just before its one use (no
 // output is formed), so the two states fit the registers beside the step.
-__device__ __forceinline__ void chain_step_warm(const uint8_t* rec, f32x4 (&M)[8][1], f32x4 (&Z)[8][1], int n0,
-                                                int lane) {
+__device__ __forceinline__ void chain_step_warm(const uint8_t* rec, const uint8_t* vb, f32x4 (&M)[8][1],
+                                                f32x4 (&Z)[8][1], int n0, int lane) {
     f32x4 pm = {0.f, 0.f, 0.f, 0.f}, pz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -837,7 +839,7 @@ __device__ __forceinline__ void chain_step_warm(const uint8_t* rec, f32x4 (&M)[8
     }
     const u32x2 th = *(const u32x2*)(rec + REC_T + lane * 8);
     const u32x2 tl = *(const u32x2*)(rec + REC_T + 512 + lane * 8);
-    const u32x2 vw = lds_load_tr16(rec + REC_V + n0 * 512 + kv_load_slot(lane) * 8);
+    const u32x2 vw = lds_load_tr16(vb + vblk_load_off(lane, n0));
     f32x4 rz;
     rz[0] = bf16_lo(vw.x) - pz[0];
     rz[1] = bf16_hi(vw.x) - pz[1];

@@ -45,7 +45,9 @@ struct VRows {
 // up to two per thread, and the chunk's 16 value rows, one 16-byte granule per
 // thread of wavefronts 0..3 (row tid >> 4, granule tid & 15). Wavefronts
 // 4..7 issue the same load over an empty range (no memory access), so that
-// every load is unconditional; rows past the sequence read as zeros.
+// every load is unconditional; rows past the sequence read as zeros. In LDS
+// a stage holds the record and, after it, the chunk's V block.
+constexpr int K2_STAGE_BYTES = REC_BYTES + VBLK_BYTES;
 struct K2Prefetch {
     static constexpr int N = (REC_HBM_VEC + 511) / 512;
     u32x4 r[N];
@@ -68,21 +70,19 @@ struct K2Prefetch {
 #pragma unroll
         for (int j = 0; j < N; ++j) {
             const int i = threadIdx.x + j * 512;
-            if (i < REC_HBM_VEC) d[rec_lds_vec(i)] = r[j];
+            if (i < REC_HBM_VEC) d[i] = r[j];
         }
-        if (threadIdx.x < 256) {
-            const int row = threadIdx.x >> 4;
-            *(u32x4*)(dst + REC_V + vrow_off(row, (threadIdx.x & 15) * 8)) = vr;
-        }
+        if (threadIdx.x < 256) *(u32x4*)(dst + REC_BYTES + vblk_off(threadIdx.x >> 4, threadIdx.x & 15)) = vr;
     }
 };
 
 // Stream nc materialised records (starting at rb) and the chunks' value rows
 // through a double-buffered LDS stage; both are fetched two chunks ahead.
-// step(ci, rec) runs once per chunk with the record in LDS, by every thread.
+// step(ci, rec) runs once per chunk with the record (and its V block) in
+// LDS, by every thread.
 template <class Step>
 __device__ __forceinline__ void record_loop(const uint8_t* __restrict__ rb, const VRows& v, int nc,
-                                            uint8_t (*recs)[REC_BYTES], Step&& step) {
+                                            uint8_t (*recs)[K2_STAGE_BYTES], Step&& step) {
     K2Prefetch p0, p1;
     if (nc > 0) p0.load(rb, v, 0);
     if (nc > 1) p1.load(rb + REC_HBM_BYTES, v, 1);
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
                                           wave);
         RowChunk rc;
         const int nr = rows_of(tok0, end);
-        k1_load_chunk<GVA>(rs, 0, nr, nr, nr, lo, rc, wave);
+        k1_load_chunk<GVA>(rs, 0, nr, nr, lo, rc, wave);
         k1_stage(rc, wave, lane, lo, stg, (float*)(stg + STG_B));
         lds_barrier();
         RawChunk raw;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
         lds_barrier();
         u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + gc) * REC_HBM_BYTES);
         const u32x4* src = (const u32x4*)rec;
-        for (int i = threadIdx.x; i < REC_HBM_VEC; i += 512) dst[i] = src[rec_lds_vec(i)];
+        for (int i = threadIdx.x; i < REC_HBM_VEC; i += 512) dst[i] = src[i];
         lds_barrier();  // the record is read before the next item stages over it
     }
 }
@@ -333,12 +333,13 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 // unconditional and the compiler's wait for a register set covers only that
 // set's loads.
 // ---------------------------------------------------------------------------
-constexpr int F_STG = 0;                              // 2 staged chunks (q, k, v rows)
+constexpr int F_STG = 0;                              // 2 staged chunks (q, k rows)
 constexpr int F_SCR = F_STG + 2 * FSTG_NB;            // 2 K1 scratch areas (Gram factors)
 constexpr int F_LB = F_SCR + 2 * K1_NB;               // 2 shared L^T + beta
 constexpr int F_BETA = F_LB + 2 * LB_BYTES;           // betas: 2 staged [16], 2 scratch [16]
 constexpr int F_GR = (F_BETA + 256 + 255) / 256 * 256;  // 4 staged g chunks (direct-to-LDS)
-constexpr int F_REC = F_GR + 4 * GRING_BYTES;         // 4 records
+constexpr int F_VR = F_GR + 4 * GRING_BYTES;          // 5 V blocks (direct-to-LDS)
+constexpr int F_REC = F_VR + 5 * VBLK_BYTES;          // 4 records
 constexpr int F_MFL = F_REC + 4 * REC_BYTES;          // K1 pass: flags of the 8 transfer tiles
 constexpr int FUSED_LDS = F_MFL + 32;
 static_assert(F_LB <= 65536, "the K1 rings fit the immediate-offset range of LDS instructions");
@@ -371,6 +372,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
     uint8_t* lbs = smem + F_LB;                // 2 shared L^T + beta
     uint8_t* stgs = smem + F_STG;              // 2 staged chunks
     uint8_t* grs = smem + F_GR;                // 4 staged g chunks
+    uint8_t* vrs = smem + F_VR;                // 5 V blocks
     float* stg_betas = (float*)(smem + F_BETA);          // [2][16]
     float* scr_betas = (float*)(smem + F_BETA + 128);    // [2][16]
     const int H = a.c.H;
@@ -449,20 +451,22 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             u32x4* dst = (u32x4*)(a.c.rec + ((size_t)h * a.c.total_chunks + u.rec_chunk0 + c) * REC_HBM_BYTES);
             const u32x4* src = (const u32x4*)rec;
             const int v0 = (w8 < WAVE_QK ? w8 : w8 - 1) * 64 + lane, v1 = v0 + 7 * 64;
-            const u32x4 x0 = src[rec_lds_vec(v0)];
-            const u32x4 x1 = src[rec_lds_vec(v1)];
+            const u32x4 x0 = src[v0];
+            const u32x4 x1 = src[v1];
             dst[v0] = x0;
             dst[v1] = x1;
         };
+        // the V block of step i (5-slot ring)
+        auto vblk = [&](int i) __attribute__((always_inline)) { return vrs + ring_off((i % 5) * VBLK_BYTES); };
         auto step = [&](int c, int i, auto role) __attribute__((always_inline)) {
             const uint8_t* rec = recs + ring_off((i % 4) * REC_BYTES);
             if constexpr (BSUM) {
                 f32x4 unused[1];
-                if (u.out_slot >= 0) chain_step<1, true, false>(rec, S, w8, lane, unused);
+                if (u.out_slot >= 0) chain_step<1, true, false>(rec, vblk(i), S, w8, lane, unused);
                 if constexpr (decltype(role)::value != 2) copy_out(c, rec);
             } else {
                 f32x4 oacc[1];
-                chain_step<1, true, true>(rec, S, w8, lane, oacc);
+                chain_step<1, true, true>(rec, vblk(i), S, w8, lane, oacc);
                 store_output(a, h, tok0 + (int64_t)CH * c, chunk_rows(rem, c), oacc[0], w8, gg, m);
             }
         };
@@ -504,7 +508,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                     // the role's work first: interleaved with the two states'
                     // step it does not fit the registers
                     __builtin_amdgcn_sched_barrier(0);
-                    chain_step_warm(recs + ring_off((i % 4) * REC_BYTES), S, Z, w8, lane);
+                    chain_step_warm(recs + ring_off((i % 4) * REC_BYTES), vblk(i), S, Z, w8, lane);
                     lds_barrier();
                 }
                 const bool live = tile_nonzero(S);
@@ -529,7 +533,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                         solve(i0 + 1);
                         __builtin_amdgcn_sched_barrier(0);
                         const uint8_t* rec = recs + ring_off((i0 % 4) * REC_BYTES);
-                        chain_step_warm(rec, M, S, w8, lane);
+                        chain_step_warm(rec, vblk(i0), M, S, w8, lane);
                         if constexpr (R != 2) {
                             __builtin_amdgcn_sched_barrier(0);
                             copy_out(i0 - W, rec);
@@ -586,6 +590,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         RowChunkF r0, r1;
         const RowLaneOffsets lo = row_lane_offsets(H, a.c.Hk, w8, lane);
         const uint32_t g_off = g_dma_off(H, w8, lane);
+        const uint32_t v_off = v_dma_off(H, w8 & 3, lane);
         // rows from the first chunk the unit runs (its warm-up, if any)
         const int64_t tok_k1 = tok0 - (int64_t)CH * W;
         const RowStreams rs = row_streams(a.c.q, a.c.k, a.c.v, a.c.g, a.c.beta, H, a.c.Hk, tok_k1, h,
@@ -601,9 +606,14 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         auto load_g = [&](int i) __attribute__((always_inline)) {
             k1_load_g_dma(rs, i, chunk_rows(rem, i), g_off, w8, grs + (i & 3) * GRING_BYTES);
         };
+        // the V block of step i: block w8 & 3, by the wavefronts with
+        // (w8 >> 2) = i - 3 - (the odd interval that issues it), see below
+        auto load_v = [&](int i) __attribute__((always_inline)) {
+            k1_load_v_dma(rs, i, chunk_rows(rem, i), v_off, w8 & 3, vrs + ring_off((i % 5) * VBLK_BYTES));
+        };
         auto load_rows = [&](RowChunkF& rc, int i) __attribute__((always_inline)) {
             const int nr = chunk_rows(rem, i);
-            k1_load_rows_f<GVA>(rs, i, nr, i >= W ? nr : 0, nr, lo, rc, w8);
+            k1_load_rows_f<GVA>(rs, i, nr, i >= W ? nr : 0, lo, rc, w8);
         };
         auto load = [&](RowChunkF& rc, int i) __attribute__((always_inline)) {
             load_g(i);
@@ -614,7 +624,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
         auto stage = [&](RowChunkF& rc, auto slot) __attribute__((always_inline)) {
             constexpr int S = decltype(slot)::value;
             // the register set is read only from here on (see below)
-            asm volatile("" : "+v"(rc.qk), "+v"(rc.v), "+v"(rc.b));
+            asm volatile("" : "+v"(rc.qk), "+v"(rc.b));
             k1_stage_f(rc, w8, lane, lo, stgs + S * FSTG_NB, stg_betas + 16 * S);
         };
         // interval i works on chunk i + 3 (staging and scratch slot R = (i + 3) & 1)
@@ -628,6 +638,15 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             // the g rows of chunk i + 6 first: their slot was last read in
             // the previous interval
             load_g(i + 6);
+            // Every other interval (i odd: slot R = 0), the V blocks of
+            // steps i + 3 (wavefronts 8..11) and i + 4 (12..15). A V block
+            // is read by the state wavefronts in the interval of its step,
+            // so five are live in interval i: i .. i + 4 (slot (i + 4) % 5
+            // was last read in interval i - 1). Like the g rows, it is
+            // complete once the wait for this interval's register loads,
+            // issued after it, returns (two intervals on, before the
+            // barrier that precedes its read).
+            if constexpr (R == 0) load_v(i + 3 + (w8 >> 2));
             RawChunk raw;
             k1_read_staged_f(stgs + R * FSTG_NB, stg_betas + 16 * R, grs + ((i + 3) & 3) * GRING_BYTES, lane, lo, raw);
             // the record slot as an opaque uniform offset, so every record
@@ -684,7 +703,7 @@ __global__ __launch_bounds__(1024) void kda_k1_bsum(K2Args a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
     if (a.c.gate && *a.c.gate == 0) return;  // fallback not armed
-    __shared__ __align__(16) uint8_t recs[2][REC_BYTES];
+    __shared__ __align__(16) uint8_t recs[2][K2_STAGE_BYTES];
     const int H = a.c.H;
     const int h = blockIdx.x % H;
     const UnitDesc u = a.units[blockIdx.x / H];
@@ -700,7 +719,7 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
     const VRows vrows{(const uint8_t*)a.c.v + ((size_t)tok0 * H + h) * (D * 2), (uint32_t)H * (D * 2), rem};
     record_loop(rb, vrows, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
         f32x4 oacc[1];
-        chain_step<1, true, true, true>(r, S, wave, lane, oacc);
+        chain_step<1, true, true>(r, r + REC_BYTES, S, wave, lane, oacc);
         store_output(a, h, tok0 + (int64_t)CH * ci, chunk_rows(rem, ci), oacc[0], wave, gg, m);
     });
     store_unit_state(a, u, h, S, wave, gg, m);
