@@ -402,9 +402,8 @@ size_t kda_noalloc_scratch_bytes(void);
  * chunk (rows past the end of a short chunk are zero), c = channel.
  *   [0, 4096)      Qt = q * exp(G): [p 4][lane 64][j 8] = Qt[i][dkperm(p, g, j)]
  *   [4096, 8192)   X = k * exp(G): same layout as Qt
- *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][slot 64][j 4]; slot 16a + 4b + ((c + a) % 4)
- *                  (a, b, c = 0..3) holds the row segment Kt[4a + b][16t + 4c + j], which a
- *                  transposing LDS load (ds_read_b64_tr_b16) turns into MFMA fragments
+ *   [8192, 12288)  Kt = k * exp(G_C - G): [t 8][slot 64][j 4]; slot s(l) holds
+ *                  lane l's Kt[4g + j][16t + i], s(l) = (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2)
  *   [12288, 12800) A_qk (lower incl. diagonal): [lane 64][j 4] = A_qk[i][4g + j]
  *   [12800, 13312) exp(G_C): fp32 [128], channel 16t + 4g + j at position 32g + 4t + j
  *   [13312, 14336) T' = (I + L)^-1 diag(beta), L = strict-lower(diag(beta) A_kk),

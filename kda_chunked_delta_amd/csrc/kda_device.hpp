@@ -37,10 +37,13 @@ constexpr int CH = 16;   // chunk length
 // feeds the next MFMA as an operand without any shuffle.
 //   REC_Q  : Qt fragments [p 4][lane 64][8 bf16]: Qt[m][dkperm(p, gg, j)]
 //   REC_X  : X fragments, same layout as REC_Q
-//   REC_KT : Kt in 4-channel row segments [t 8][slot 64][4 bf16]: slot
-//            kv_store_slot(a, 4b + c) holds Kt[4a + b][16t + 4c + j]; lane l
-//            reads slot kv_load_slot(l) with a transposing load and gets its
-//            Kt^T fragment Kt[4gg + j][16t + m]
+//   REC_KT : Kt^T fragments [t 8][slot 64][4 bf16]: lane l's fragment
+//            Kt[4gg + j][16t + m] in slot kv_slot(l) (materialised records,
+//            and the LDS records of the K1 pass of the segmented pipeline);
+//            the fused kernel keeps them in LDS as 4-channel row segments
+//            instead: slot kv_store_slot(a, 4b + c) holds
+//            Kt[4a + b][16t + 4c + j], and lane l reads slot kv_load_slot(l)
+//            with a transposing load
 //   REC_AQK: A_qk fragment [lane 64][4 bf16]: A_qk[m][4gg + j] (masked i <= r)
 //   REC_GC : exp(G_C) [128] fp32, channel c = 16t + 4gg + v at position
 //            32gg + 4t + v: lane (gg, m) of a state wavefront reads the pair
@@ -170,7 +173,37 @@ __device__ __forceinline__ float row_newbcast(float x) {
     return __builtin_amdgcn_update_dpp(0.0f, x, 0x150 + K, 0xF, 0xF, true);
 }
 
-// Kt and V tiles: K1 lane (gg, m) holds token m, channels 4gg .. 4gg + 3 of
+// 4 x 4 transpose of 16-bit elements across the four lanes of a quad: lane j
+// holds elements x[0..3] as (x0 | x1 << 16, x2 | x3 << 16); afterwards it
+// holds element j of lanes 0..3, in lane order. First the 2 x 2 blocks of
+// dwords move between lanes j and j ^ 2, then each 2 x 2 block of halves is
+// transposed between lanes j and j ^ 1 (DPP quad permutes and a byte
+// permute).
+__device__ __forceinline__ u32x2 quad_transpose16(u32x2 x, int lane) {
+    const bool hi = (lane & 2) != 0;
+    const uint32_t send = hi ? x.x : x.y;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    const uint32_t y0 = hi ? recv : x.x;
+    const uint32_t y1 = hi ? x.y : recv;
+    const uint32_t p0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)y0, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)y1, 0xB1, 0xF, 0xF, false);
+    // even lane: own low half, then the partner's; odd lane: the partner's
+    // high half, then its own (v_perm_b32: bytes 0-3 from the second
+    // operand, 4-7 from the first)
+    const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
+    return u32x2{__builtin_amdgcn_perm(p0, y0, sel), __builtin_amdgcn_perm(p1, y1, sel)};
+}
+
+// Slot of lane l's 8-byte Kt^T fragment in the fragment layout: lane
+// l = 16g + 4a + j sits in slot 16g + 4((a + g) & 3) + j. The reads stay one
+// contiguous 512-byte tile (each half-wavefront's 32 reads on distinct
+// banks; two tiles per paired load), and the stores that K1 writes them with
+// (lane (gg, 4a + j) -> fragment of lane 16a + 4gg + j, after a quad
+// transpose) put each group of 16 lanes on 16 distinct 8-byte slots of a
+// 128-byte bank row, so neither side has a bank conflict.
+__device__ __forceinline__ int kv_slot(int l) { return (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2); }
+
+// Kt in the row-segment layout: K1 lane (gg, m) holds token m, channels 4gg .. 4gg + 3 of
 // a tile, an 8-byte row segment, and stores it untransposed in slot
 // kv_store_slot(gg, m). gfx950's transposing LDS load (ds_read_b64_tr_b16)
 // works on groups of 16 lanes: lane 4r + c of a group loads row segment
@@ -193,6 +226,19 @@ __device__ __forceinline__ u32x2 lds_load_tr16(const uint8_t* p) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+
+// Lane `lane`'s Kt^T fragment of tile t of a record: from the row-segment
+// layout by a transposing load (KT_TR), else from the fragment layout. The
+// fragment layout is the one records have in HBM: it serves two tiles per
+// paired load, which the two-state steps of the segmented pipeline's K1
+// pass need (with the transposing load its loads serialise, one per tile,
+// and that pass ran 30% slower under weak decay); the fused kernel saves the
+// quad transpose in K1 with the row segments.
+template <bool KT_TR>
+__device__ __forceinline__ u32x2 kt_frag(const uint8_t* rec, int t, int lane) {
+    if constexpr (KT_TR) return lds_load_tr16(rec + REC_KT + t * 512 + kv_load_slot(lane) * 8);
+    else return *(const u32x2*)(rec + REC_KT + t * 512 + kv_slot(lane) * 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -479,6 +525,7 @@ constexpr float G_TOKEN_FLOOR = 15.5f;
 
 // scr_b: the chunk's 16 betas (scr + K1_BETA where the layout keeps them
 // together)
+template <bool KT_TR>
 __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lane, uint8_t* rec,
                                           uint8_t* scr, float* scr_b) {
     const int gg = lane >> 4, m = lane & 15;
@@ -578,9 +625,20 @@ __device__ __forceinline__ void k1_phase1(const RawChunk& raw, int wave, int lan
     *(u32x2*)(scr + K1_KB + (wave >> 1) * 1024 + (wave & 1) * 512 + lane * 8) = pkb;
     *(u32x2*)(rec + REC_Q + fo) = pqt;
     *(u32x2*)(rec + REC_X + fo) = pxk;
-    // Kt of tile `wave`: the lane's row segment, untransposed (the state
-    // wavefronts transpose it as they load it)
-    *(u32x2*)(rec + REC_KT + wave * 512 + kv_store_slot(gg, m) * 8) = pkt;
+    if constexpr (KT_TR) {
+        // Kt of tile `wave`: the lane's row segment, untransposed (the state
+        // wavefronts transpose it as they load it)
+        *(u32x2*)(rec + REC_KT + wave * 512 + kv_store_slot(gg, m) * 8) = pkt;
+    } else {
+        // Kt^T: element (token m, channel 16 wave + 4gg + j) -> tile wave,
+        // lane (m >> 2) * 16 + 4gg + j, element m & 3. The four lanes of a
+        // quad (m = 4a .. 4a + 3) hold a 4 x 4 block of it (tokens x
+        // channels); after a 16-bit transpose inside the quad, lane
+        // (gg, 4a + j) holds channel 4gg + j for tokens 4a .. 4a + 3: the
+        // whole 8-byte fragment of lane 16a + 4gg + j, one store to its slot.
+        const int dl = 16 * (m >> 2) + 4 * gg + (m & 3);
+        *(u32x2*)(rec + REC_KT + wave * 512 + kv_slot(dl) * 8) = quad_transpose16(pkt, lane);
+    }
     // exp(G_C): the last row holds the chunk total (rows past nrows add 0)
     if (m == 15) *(f32x4*)(rec + REC_GC + (32 * gg + 4 * wave) * 4) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     if (wave == 0 && gg == 0) scr_b[m] = raw.b;
@@ -726,7 +784,7 @@ __device__ __forceinline__ void k1_phase2(int wave, int lane, uint8_t* rec, cons
 // accumulator oacc[n][v] is o[token m][16(n0 + n) + 4gg + v].
 // The arithmetic of a tile is identical in every instantiation.
 // ---------------------------------------------------------------------------
-template <int NT, bool WITH_V, bool WITH_OUT>
+template <int NT, bool WITH_V, bool WITH_OUT, bool KT_TR>
 __device__ __forceinline__ void chain_step(const uint8_t* rec, const uint8_t* vb, f32x4 (&S)[8][NT], int n0,
                                            int lane, f32x4 (&oacc)[NT]) {
     const int gg = lane >> 4;
@@ -800,7 +858,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, const uint8_t* vb
         constexpr int t = decltype(tc)::value;
         const f32x4 gcv = {row_newbcast<2 * t>(gcp[0]), row_newbcast<2 * t>(gcp[1]),
                            row_newbcast<2 * t + 1>(gcp[0]), row_newbcast<2 * t + 1>(gcp[1])};
-        const u32x2 kt = lds_load_tr16(rec + REC_KT + t * 512 + kv_load_slot(lane) * 8);
+        const u32x2 kt = kt_frag<KT_TR>(rec, t, lane);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             S[t][n] = gcv * S[t][n];
@@ -819,6 +877,7 @@ __device__ __forceinline__ void chain_step(const uint8_t* rec, const uint8_t* vb
 // chain_step<1, true, false>. The record's operands are read once for both,
 // and each bf16 operand of a state is packed just before its one use (no
 // output is formed), so the two states fit the registers beside the step.
+template <bool KT_TR>
 __device__ __forceinline__ void chain_step_warm(const uint8_t* rec, const uint8_t* vb, f32x4 (&M)[8][1],
                                                 f32x4 (&Z)[8][1], int n0, int lane) {
     f32x4 pm = {0.f, 0.f, 0.f, 0.f}, pz = {0.f, 0.f, 0.f, 0.f};
@@ -856,7 +915,7 @@ __device__ __forceinline__ void chain_step_warm(const uint8_t* rec, const uint8_
         constexpr int t = decltype(tc)::value;
         const f32x4 gcv = {row_newbcast<2 * t>(gcp[0]), row_newbcast<2 * t>(gcp[1]),
                            row_newbcast<2 * t + 1>(gcp[0]), row_newbcast<2 * t + 1>(gcp[1])};
-        const u32x2 kt = lds_load_tr16(rec + REC_KT + t * 512 + kv_load_slot(lane) * 8);
+        const u32x2 kt = kt_frag<KT_TR>(rec, t, lane);
         M[t][0] = gcv * M[t][0];
         M[t][0] = mfma_k16(kt, ubm, M[t][0]);
         Z[t][0] = gcv * Z[t][0];

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
         RawChunk raw;
         k1_read_staged(stg, (const float*)(stg + STG_B), lane, lo, raw);
         lds_barrier();  // the staging area is free again
-        k1_phase1(raw, wave, lane, rec, scr, (float*)(scr + K1_BETA));
+        k1_phase1<false>(raw, wave, lane, rec, scr, (float*)(scr + K1_BETA));
         lds_barrier();
         k1_phase2(wave, lane, rec, scr, lw);
         lds_barrier();
@@ -462,11 +462,11 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             const uint8_t* rec = recs + ring_off((i % 4) * REC_BYTES);
             if constexpr (BSUM) {
                 f32x4 unused[1];
-                if (u.out_slot >= 0) chain_step<1, true, false>(rec, vblk(i), S, w8, lane, unused);
+                if (u.out_slot >= 0) chain_step<1, true, false, !BSUM>(rec, vblk(i), S, w8, lane, unused);
                 if constexpr (decltype(role)::value != 2) copy_out(c, rec);
             } else {
                 f32x4 oacc[1];
-                chain_step<1, true, true>(rec, vblk(i), S, w8, lane, oacc);
+                chain_step<1, true, true, !BSUM>(rec, vblk(i), S, w8, lane, oacc);
                 store_output(a, h, tok0 + (int64_t)CH * c, chunk_rows(rem, c), oacc[0], w8, gg, m);
             }
         };
@@ -508,7 +508,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                     // the role's work first: interleaved with the two states'
                     // step it does not fit the registers
                     __builtin_amdgcn_sched_barrier(0);
-                    chain_step_warm(recs + ring_off((i % 4) * REC_BYTES), vblk(i), S, Z, w8, lane);
+                    chain_step_warm<!BSUM>(recs + ring_off((i % 4) * REC_BYTES), vblk(i), S, Z, w8, lane);
                     lds_barrier();
                 }
                 const bool live = tile_nonzero(S);
@@ -533,7 +533,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                         solve(i0 + 1);
                         __builtin_amdgcn_sched_barrier(0);
                         const uint8_t* rec = recs + ring_off((i0 % 4) * REC_BYTES);
-                        chain_step_warm(rec, vblk(i0), M, S, w8, lane);
+                        chain_step_warm<!BSUM>(rec, vblk(i0), M, S, w8, lane);
                         if constexpr (R != 2) {
                             __builtin_amdgcn_sched_barrier(0);
                             copy_out(i0 - W, rec);
@@ -651,7 +651,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             k1_read_staged_f(stgs + R * FSTG_NB, stg_betas + 16 * R, grs + ((i + 3) & 3) * GRING_BYTES, lane, lo, raw);
             // the record slot as an opaque uniform offset, so every record
             // access of the phase is one per-lane base plus immediate offsets
-            k1_phase1(raw, w8, lane, recs + ring_off(((i + 3) % 4) * REC_BYTES), scrs + R * K1_NB,
+            k1_phase1<!BSUM>(raw, w8, lane, recs + ring_off(((i + 3) % 4) * REC_BYTES), scrs + R * K1_NB,
                       scr_betas + 16 * R);
             stage(rc, std::integral_constant<int, 1 - R>{});
             load_rows(rc, i + 6);
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
     const VRows vrows{(const uint8_t*)a.c.v + ((size_t)tok0 * H + h) * (D * 2), (uint32_t)H * (D * 2), rem};
     record_loop(rb, vrows, u.n_chunks, recs, [&](int ci, const uint8_t* r) {
         f32x4 oacc[1];
-        chain_step<1, true, true>(r, r + REC_BYTES, S, wave, lane, oacc);
+        chain_step<1, true, true, false>(r, r + REC_BYTES, S, wave, lane, oacc);
         store_output(a, h, tok0 + (int64_t)CH * ci, chunk_rows(rem, ci), oacc[0], wave, gg, m);
     });
     store_unit_state(a, u, h, S, wave, gg, m);

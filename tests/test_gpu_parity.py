@@ -136,14 +136,13 @@ def decode_records(rec):
             for j in range(8):
                 x[i, 32 * p + 16 * (j // 4) + 4 * g + j % 4] = a[p, :, j]
         out[name] = x
-    # Kt: slot s = 16a + 4b + ((c + a) & 3) holds the row segment Kt[4a + b][16t + 4c + j]
-    a = bf(r[8192:12288].view(np.uint16).reshape(8, 64, 4))
+    # Kt: lane l's fragment sits in slot (l & 0x33) | ((((l >> 2) + (l >> 4)) & 3) << 2)
+    slot = (lanes & 0x33) | ((((lanes >> 2) + (lanes >> 4)) & 3) << 2)
+    a = bf(r[8192:12288].view(np.uint16).reshape(8, 64, 4))[:, slot, :]
     x = np.zeros((16, 128), np.float32)
-    for sl in range(64):
-        ra, rb = sl >> 4, (sl >> 2) & 3
-        c = ((sl & 3) - ra) & 3
-        for t in range(8):
-            x[4 * ra + rb, 16 * t + 4 * c:16 * t + 4 * c + 4] = a[t, sl, :]
+    for t in range(8):
+        for j in range(4):
+            x[4 * g + j, 16 * t + i] = a[t, :, j]
     out["Kt"] = x
     a = bf(r[12288:12800].view(np.uint16).reshape(64, 4))
     x = np.zeros((16, 16), np.float32)
