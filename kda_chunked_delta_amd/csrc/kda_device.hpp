@@ -112,6 +112,19 @@ constexpr int LB_BYTES = K1_LBYTES + 64;
 constexpr int N_WAVE_T = 4;
 constexpr int WAVE_QK = 5;
 
+// The fused kernel's T' wavefronts among its state wavefronts 0..7. State
+// wavefront w runs on SIMD w % 4 beside state wavefront w ^ 4 and two K1
+// wavefronts, so the T' role of WAVE_QK's SIMD partner (1) goes to wavefront
+// 6 instead: WAVE_QK's SIMD then carries the Gram role alone (measured 1-3%
+// faster on every fused workload than T' on wavefronts 0..3).
+// fused_t_role(w): wavefront w forms T' rows; fused_t_block(w): which block
+// of four rows it forms (meaningful only where fused_t_role(w) holds).
+__device__ __forceinline__ bool fused_t_role(int w) {
+    static_assert(WAVE_QK == 5, "the T' wavefronts avoid WAVE_QK's SIMD");
+    return w == 0 || w == 2 || w == 3 || w == 6;
+}
+__device__ __forceinline__ int fused_t_block(int w) { return w == 6 ? 1 : w; }
+
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -308,20 +308,22 @@ __global__ __launch_bounds__(512) void kda_k1_prepare(K1Args a) {
 // ends with barrier i:
 //   - wavefronts 0..7 hold the state (wavefront w: value columns
 //     16w..16w+15, in MFMA accumulators for the whole unit), advance it over
-//     chunk i and store that chunk's output. Wavefronts 0..3 also form rows
-//     4w..4w+3 of T' of chunk i+1 from the shared L^T; wavefront WAVE_QK
-//     forms A_qk of chunk i+2 and L of chunk i+2, once, into the shared L^T;
+//     chunk i and store that chunk's output. Four of them (fused_t_role)
+//     also form four rows each of T' of chunk i+1 from the shared L^T;
+//     wavefront WAVE_QK forms A_qk of chunk i+2 and L of chunk i+2, once,
+//     into the shared L^T;
 //   - wavefronts 8 + w issue the direct-to-LDS load of the g rows of chunk
-//     i+6, run K1 phase 1 of chunk i+3 (key channels and value columns
-//     16w..16w+15) from the staged rows, stage the q, k and v rows of chunk
-//     i+4 that they loaded two intervals earlier, and issue the register
-//     loads of those rows of chunk i+6 (into the register set just staged).
-//     Issuing the g load first spreads the loads over the interval.
+//     i+6 (and, every other interval, of two chunks' V blocks), run K1
+//     phase 1 of chunk i+3 (key channels 16w..16w+15) from the staged rows,
+//     stage the q and k rows of chunk i+4 that they loaded two intervals
+//     earlier, and issue the register loads of those rows of chunk i+6
+//     (into the register set just staged). Issuing the direct-to-LDS loads
+//     first spreads the loads over the interval.
 // Each SIMD holds two state wavefronts and two K1 wavefronts. Records and the
 // staged g rows live in 4-deep LDS rings (a g slot is written by the loads
-// issued three intervals before it is read, and read once); K1 scratch, the
-// shared L^T and the staged q, k, v rows in 2-deep ones. The staged q, k, v
-// rows and the K1 scratch (without their betas) lie in the first 64 KiB, so
+// issued three intervals before it is read, and read once), the V blocks in
+// a 5-deep one; K1 scratch, the shared L^T and the staged q, k rows in 2-deep
+// ones. The staged q, k rows and the K1 scratch (without their betas) lie in the first 64 KiB, so
 // that every K1 access to them is a per-lane base plus an immediate offset;
 // the K1 loop is unrolled over the two slots of those rings. A g slot is
 // complete once the compiler's wait for the same chunk's register loads,
@@ -486,7 +488,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             auto solve = [&](int c) __attribute__((always_inline)) {  // rows of T' of chunk c
                 if constexpr (R == 1) {
                     const float* lb = (const float*)(lbs + ring_off((c & 1) * LB_BYTES));
-                    k1_tsolve(lane, w8, recs + ring_off((c % 4) * REC_BYTES), lb, lb + LB_BETA / 4);
+                    k1_tsolve(lane, fused_t_block(w8), recs + ring_off((c % 4) * REC_BYTES), lb, lb + LB_BETA / 4);
                 }
             };
             lds_barrier();  // interval -3: phase 1 of chunk 0
@@ -559,7 +561,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
             }
             for (int i = n_steps; i < n_main; ++i) lds_barrier();
         };
-        if (w8 < N_WAVE_T) run(std::integral_constant<int, 1>{});
+        if (fused_t_role(w8)) run(std::integral_constant<int, 1>{});
         else if (w8 == WAVE_QK) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 0>{});
         if constexpr (BSUM) {
