@@ -137,6 +137,54 @@ __device__ __forceinline__ void store_state(float* so, const f32x4 (&S)[8][NT], 
                 so[(16 * t + 4 * gg + vv) * D + 16 * (n0 + n) + m] = S[t][n][vv];
 }
 
+// The transfer M in HBM, in the order the CP merge reads it as its MFMA A
+// operand. The merge's wavefront t forms carry rows 16t..16t+15; in its
+// product lane (gg, m) (lane = 16 gg + m) takes, at MFMA step q, key index
+// merge_k(gg, q), from M's row 16t + m. The lane's 32 entries lie in two runs
+// of 16 keys, so that the 64 lanes of each carry read fall on distinct LDS
+// banks. The stored order puts the entries one lane reads for steps
+// 4j..4j+3 in 16 consecutive bytes and the 64 lanes' in one 1 KiB block:
+// each of the merge's operand loads then reads 1 KiB of consecutive memory.
+__device__ __forceinline__ int merge_k(int gg, int q) { return (q < 16 ? 0 : 48) + 16 * gg + q; }
+__device__ __forceinline__ int m_operand_index(int i, int k) {
+    const int q = (k & 15) | ((k >> 2) & 16);  // merge_k(gg, q) == k
+    const int gg = (k >> 4) & 3;
+    return (((i >> 4) * 8 + (q >> 2)) * 64 + 16 * gg + (i & 15)) * 4 + (q & 3);
+}
+// A 4x4 block held by a lane quad (lane c of the quad: column c, rows 0..3)
+// transposed: lane c then holds row c (columns 0..3). Two butterfly stages
+// swap lane bit 0 with register bit 0, then lane bit 1 with register bit 1;
+// in each a lane sends its partner the two entries that belong there.
+__device__ __forceinline__ f32x4 quad_transpose_f32(f32x4 x, int lane) {
+    const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+    float s0 = b0 ? x[0] : x[1], s1 = b0 ? x[2] : x[3];
+    s0 = __builtin_amdgcn_update_dpp(0.0f, s0, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+    s1 = __builtin_amdgcn_update_dpp(0.0f, s1, 0xB1, 0xF, 0xF, true);
+    x = f32x4{b0 ? s0 : x[0], b0 ? x[1] : s0, b0 ? s1 : x[2], b0 ? x[3] : s1};
+    float t0 = b1 ? x[0] : x[2], t1 = b1 ? x[1] : x[3];
+    t0 = __builtin_amdgcn_update_dpp(0.0f, t0, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+    t1 = __builtin_amdgcn_update_dpp(0.0f, t1, 0x4E, 0xF, 0xF, true);
+    return f32x4{b1 ? t0 : x[0], b1 ? t1 : x[1], b1 ? x[2] : t0, b1 ? x[3] : t1};
+}
+// A wavefront's tiles of M (store_state's layout: value columns 16 n0 ..
+// 16 n0 + 15) written in that order, or zeros in their place. After a quad
+// transpose, lane 4a + c holds the entries of M row 16t + 4 gg + c at keys
+// 16 n0 + 4a .. + 3, which are 16 consecutive bytes of the stored order: one
+// 16-byte store per tile.
+__device__ __forceinline__ float* transfer_base(float* mo, int n0, int gg, int m) {
+    return mo + m_operand_index(4 * gg + (m & 3), 16 * n0 + (m & ~3));
+}
+__device__ __forceinline__ void store_transfer(float* mo, const f32x4 (&S)[8][1], int n0, int gg, int m) {
+    float* b = transfer_base(mo, n0, gg, m);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) *(f32x4*)(b + t * 2048) = quad_transpose_f32(S[t][0], m & 3);
+}
+__device__ __forceinline__ void zero_transfer(float* mo, int n0, int gg, int m) {
+    float* b = transfer_base(mo, n0, gg, m);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) *(f32x4*)(b + t * 2048) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 // The same for a bf16 state (loaded exactly; stored rounded to nearest even).
 template <int NT>
 __device__ __forceinline__ void load_state_bf16(const uint16_t* sin, f32x4 (&S)[8][NT], int n0, int gg, int m) {
@@ -550,7 +598,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                         m_flags[w8] = nz ? 1 : 0;
                     }
                     m_nz = nz;
-                    if (nz) store_state(a.m_out + ((size_t)u.out_slot * H + h) * (D * D), M, w8, gg, m);
+                    if (nz) store_transfer(a.m_out + ((size_t)u.out_slot * H + h) * (D * D), M, w8, gg, m);
                 }
             }
             for (int i = i0; i < n_steps; ++i) {
@@ -572,13 +620,7 @@ __device__ __forceinline__ void fused_body(const K2Args& a) {
                 int any = 0;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) any |= m_flags[j];
-                if (!m_nz && any) {
-                    float* mo = a.m_out + ((size_t)u.out_slot * H + h) * (D * D);
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-#pragma unroll
-                        for (int vv = 0; vv < 4; ++vv) mo[(16 * t + 4 * gg + vv) * D + 16 * w8 + m] = 0.f;
-                }
+                if (!m_nz && any) zero_transfer(a.m_out + ((size_t)u.out_slot * H + h) * (D * D), w8, gg, m);
             }
         }
         if (u.out_slot >= 0) store_state(a.carries + ((size_t)u.out_slot * H + h) * (D * D), S, w8, gg, m);
@@ -743,15 +785,15 @@ __global__ __launch_bounds__(512) void kda_k2_recur(K2Args a) {
 // The run's length is found before its first step, so the steps test no
 // flag, and the summaries of each step load while the step before it runs.
 // In the product M carry, lane group gg of MFMA step q takes key index
-// merge_k(gg, q): the lane's 32 entries of its M row come in two runs of 16,
-// and with the carry's LDS rows padded to MERGE_CST floats the 64 lanes of
-// each carry read fall on distinct banks. The carry is double-buffered in
+// merge_k(gg, q), and M comes in that operand order (m_operand_index), so
+// each of a step's eight M loads per wavefront reads 1 KiB of consecutive
+// memory; with the carry's LDS rows padded to MERGE_CST floats the 64 lanes
+// of each carry read fall on distinct banks. The carry is double-buffered in
 // LDS, so a step needs one barrier.
 // ---------------------------------------------------------------------------
 constexpr int MERGE_CST = 17;
-__device__ __forceinline__ int merge_k(int gg, int q) { return (q < 16 ? 0 : 48) + 16 * gg + q; }
 struct MergeOperands {
-    f32x4 m[8];  // M_s[16 wave + m][merge_k(gg, 4j) .. + 3], j = 0..7
+    f32x4 m[8];  // M_s[16 wave + m][merge_k(gg, 4j) .. + 3], j = 0..7 (m_operand_index order)
     f32x4 b;     // B_s[16 wave + 4 gg + v][16 vt + m], v = 0..3
 };
 
@@ -823,7 +865,7 @@ __global__ __launch_bounds__(512, 4) void kda_cp_merge(MergeArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             x.m[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                mr, (int)(((16 * wave + m) * D + merge_k(gg, 4 * k)) * 4), 0, 0));
+                mr, (int)(((wave * 8 + k) * 64 + lane) * 16), 0, 0));
     };
     // carry_{s0+s+1} = M carry + B
     auto step = [&](int s, MergeOperands& x) __attribute__((always_inline)) {
