@@ -367,6 +367,23 @@ def test_cp_weak_decay_within_tolerance():
     assert_close("out(serial)", o_ser, o_ref)
 
 
+def test_cp_merge_long_live_run():
+    """One run of 63 live transfers (64 segments of 4 chunks under very weak
+    decay): the merge chains 63 steps, each reading its transfer M in the
+    operand order the K1 pass stores it in, with its 16-byte quad-transposed
+    stores; outputs and final states match the oracle within 1e-2."""
+    d = draw([4096], 2, seed=23, state_std=0.1, device=DEV)
+    d["g"] = d["g"] * 0.02
+    say("case: 4096 tokens, H=2, 64 segments of 4 chunks, g x 0.02")
+    p = kda.plan_segments(d["cu_seqlens_host"], 2, 4, device=DEV)
+    info = p.info()
+    assert info["uses_cp"] == 1 and info["n_prescan"] == 63, info
+    o_cp, s_cp = run(d, plan=p)
+    o_ref, s_ref = oracle(d)
+    assert_close("out(cp)", o_cp, o_ref)
+    assert_close("final(cp)", s_cp, s_ref)
+
+
 def test_cp_merge_runs_starting_mid_sequence():
     """Decay that alternates by region: strong (g x 4) where a segment's
     transfer vanishes, weak (g x 0.05) where it survives. The merge then has
