@@ -170,20 +170,20 @@ __device__ __forceinline__ f32x4 quad_transpose_f32(f32x4 x, int lane) {
 // 16 n0 + 15) written in that order, or zeros in their place. After a quad
 // transpose, lane 4a + c holds the entries of M row 16t + 4 gg + c at keys
 // 16 n0 + 4a .. + 3, which are 16 consecutive bytes of the stored order: one
-// 16-byte store per tile (row tile t lies M_TILE_FLOATS further on).
-constexpr int M_TILE_FLOATS = 8 * 64 * 4;  // eight 1 KiB operand blocks per 16 rows
+// 16-byte store per tile (row tile t lies 2048 floats further on: eight
+// 1 KiB operand blocks per 16 rows).
 __device__ __forceinline__ float* transfer_base(float* mo, int n0, int gg, int m) {
     return mo + m_operand_index(4 * gg + (m & 3), 16 * n0 + (m & ~3));
 }
 __device__ __forceinline__ void store_transfer(float* mo, const f32x4 (&S)[8][1], int n0, int gg, int m) {
     float* b = transfer_base(mo, n0, gg, m);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) *(f32x4*)(b + t * M_TILE_FLOATS) = quad_transpose_f32(S[t][0], m & 3);
+    for (int t = 0; t < 8; ++t) *(f32x4*)(b + t * 2048) = quad_transpose_f32(S[t][0], m & 3);
 }
 __device__ __forceinline__ void zero_transfer(float* mo, int n0, int gg, int m) {
     float* b = transfer_base(mo, n0, gg, m);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) *(f32x4*)(b + t * M_TILE_FLOATS) = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) *(f32x4*)(b + t * 2048) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // load_state and store_state for a bf16 state (loaded exactly; stored
